@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the Gecko SCA + AWM forward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the product path. It
+shares no code with the HIP library or its binding.
+"""
+
+from .gecko_oracle import (  # noqa: F401
+    affine,
+    awm_head,
+    chunk_ranges,
+    feature_softmax,
+    forward,
+    forward_head,
+    sca_chunk,
+    sca_head,
+)

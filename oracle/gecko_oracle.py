@@ -1,0 +1,214 @@
+"""Plain fp64 CPU oracle for the Gecko per-layer forward: sliding chunk attention
+(SCA) plus adaptive working memory (AWM).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The
+product path (the HIP library and its Python binding) never touches it and it
+never touches the product path: the two share no code, no constants and no
+helpers.
+
+Sources (the pages this follows; cited by site and section):
+
+* [rainbus] "Gecko: An Efficient Neural Architecture Inherently Processing
+  Sequences with Arbitrary Lengths", structured summary on paper.rainbus.top.
+  Sections used: "Core method" (the position-aware online-softmax kernel, the
+  feature-softmax query map and the normaliser identity) and "Method steps"
+  (steps (2)-(5): the affine derivations, SCA, the memory update and the
+  readout).
+* [paperlayer] the same paper's section-by-section summary on paperlayer.ai.
+  Sections used: 3.2 "Sliding Chunk Attention", 3.3 "Adaptive Working
+  Memory" (chunk-by-chunk updates, normaliser fixed to one) and Appendix A
+  (the initial states of the memory).
+
+Readings taken where the pages are silent or garbled (each is repeated where it
+is used):
+
+* R1 memory update: the printed update lost its parentheses; the delta rule the
+  appendix names, with shapes that type-check, is
+  ``M'_s = (z^{s-2}/z^{s-1}) * M'_{s-1} + phi^{s-1}(K_{s-1})^T (V_{s-1} - psi(K_{s-1}) M'_{s-1})``.
+* R2 causality inside a chunk: key j is visible to query i iff j <= i; the whole
+  previous chunk is visible.
+* R3 attention logits carry no 1/sqrt(d) scale (none is printed in step (3)).
+* R4 the first chunk attends to itself only; the last chunk may be partial;
+  c >= n gives one chunk.
+* R5 inside AWM, K means the memory key K_m and Q the memory query Q_m; V is the
+  same V as in SCA.
+* R6 the ratio z^{s-2}/z^{s-1} scales row f (key feature f) of M'.
+* R7 z^0 = 0 (empty sum), so the ratio is 0 on the first update; M'_0 (read by
+  chunk 1) is taken as 0 like M'_1.
+* R8 the output is exactly O_SCA + O_m (no gate, no projection).
+
+Everything is evaluated in float64 on the exact (already rounded) input values
+the GPU receives. Inputs may be float32 (bf16-exact values are exact in
+float32); they are upcast per chunk so that long sequences stream.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "chunk_ranges",
+    "affine",
+    "feature_softmax",
+    "sca_chunk",
+    "sca_head",
+    "awm_head",
+    "forward_head",
+    "forward",
+]
+
+
+def chunk_ranges(n: int, c: int) -> list[tuple[int, int]]:
+    """Token ranges [start, end) of chunks 1..N, N = ceil(n / c).
+
+    [rainbus "Method steps" (3)]: the sequence is cut into chunks of c tokens;
+    R4: the last chunk holds the remainder.
+    """
+    if n < 0 or c < 1:
+        raise ValueError("need n >= 0 and c >= 1")
+    return [(s, min(s + c, n)) for s in range(0, n, c)]
+
+
+def affine(z: np.ndarray, scale: np.ndarray, shift: np.ndarray) -> np.ndarray:
+    """Per-feature affine map scale * z + shift, in float64.
+
+    [rainbus "Method steps" (2)] derives Q and K from Z' this way with
+    (kappa_q, nu_q) and (kappa_k, nu_k); step (4) derives Q_m and K_m with
+    (eta_q, rho_q) and (eta_k, rho_k).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    return z * np.asarray(scale, dtype=np.float64) + np.asarray(shift, dtype=np.float64)
+
+
+def feature_softmax(x: np.ndarray) -> np.ndarray:
+    """psi: softmax of each row over the feature axis.
+
+    [rainbus "Core method"]: the query-side map normalises exp(q) by the sum
+    of exp over the features of the same row.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sca_chunk(q_rows: np.ndarray, k_win: np.ndarray, v_win: np.ndarray,
+              query_pos: np.ndarray, key_pos: np.ndarray) -> np.ndarray:
+    """Softmax attention of the queries of one chunk over its window.
+
+    [rainbus "Method steps" (3)]: chunk s attends to the concatenated keys and
+    values of chunks s-1 and s. R2: key j is visible to query i iff j <= i
+    (positions are absolute token indices). R3: logits are plain dot products.
+    """
+    logits = np.asarray(q_rows, np.float64) @ np.asarray(k_win, np.float64).T
+    visible = key_pos[None, :] <= query_pos[:, None]
+    logits = np.where(visible, logits, -np.inf)
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ np.asarray(v_win, np.float64)
+
+
+def _window(n: int, c: int, s: int) -> tuple[int, int, int]:
+    """(first key, first query, end) of chunk s (0-based) and its window.
+
+    R4: chunk 0 has no previous chunk; [paperlayer 3.2]: the window of chunk s
+    is the previous chunk plus the current one.
+    """
+    q0 = s * c
+    q1 = min(q0 + c, n)
+    return max(0, q0 - c), q0, q1
+
+
+def sca_head(z, v, kappa_q, nu_q, kappa_k, nu_k, c: int, chunks=None) -> np.ndarray:
+    """O_SCA for one head: z [n, d], v [n, dv], affine vectors [d].
+
+    Returns float64 [n, dv]. If ``chunks`` (0-based chunk indices) is given,
+    only those chunks' rows are computed and the other rows are NaN.
+    """
+    n = z.shape[0]
+    out = np.full((n, v.shape[1]), np.nan)
+    nchunks = len(chunk_ranges(n, c))
+    for s in (range(nchunks) if chunks is None else chunks):
+        k0, q0, q1 = _window(n, c, s)
+        q = affine(z[q0:q1], kappa_q, nu_q)
+        k = affine(z[k0:q1], kappa_k, nu_k)
+        out[q0:q1] = sca_chunk(q, k, v[k0:q1], np.arange(q0, q1), np.arange(k0, q1))
+    return out
+
+
+def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
+             trace=None) -> np.ndarray:
+    """O_m for one head: z [n, d], v [n, dv], affine vectors [d].
+
+    Follows [rainbus "Method steps" (4)-(5)] and [rainbus "Core method"],
+    chunk by chunk as [paperlayer 3.3] states:
+
+    * K_m, Q_m come from Z' by the (eta, rho) affine map (step (4), R5).
+    * z^s is the per-feature sum of exp(k) over every token of chunks 1..s
+      ("Core method"); z^0 = 0 (R7).
+    * phi^s(k) = exp(k) / z^s, per feature ("Core method").
+    * psi is the feature softmax ("Core method").
+    * M'_1 = 0 ([paperlayer Appendix A]); M'_0 = 0 (R7).
+    * for s >= 2: M'_s = (z^{s-2}/z^{s-1}) * M'_{s-1}
+                   + phi^{s-1}(K_{s-1})^T (V_{s-1} - psi(K_{s-1}) M'_{s-1})   (R1, R6).
+      With ``no_delta`` the bracket is V_{s-1} alone (plain linear attention
+      with the online-softmax kernel; a test variant, not the method).
+    * readout of chunk s: O_m,s = psi(Q_m,s) M'_{s-1} (step (5)); no
+      denominator, since the normaliser is identically one ("Core method",
+      [paperlayer 3.3]).
+
+    ``trace``, if a list, receives one dict per chunk s (1-based) with the
+    float64 z^s, phi^s(K_s) and M'_{s-1} used by the readout.
+    """
+    n, d = z.shape
+    dv = v.shape[1]
+    out = np.zeros((n, dv))
+    ranges = chunk_ranges(n, c)
+    z_prev = np.zeros(d)              # z^{s-1}
+    mem_prev = np.zeros((d, dv))      # M'_{s-1}
+    mem_cur = np.zeros((d, dv))       # M'_s
+    for s, (a, b) in enumerate(ranges, start=1):
+        # readout of chunk s from M'_{s-1}
+        qm = affine(z[a:b], eta_q, rho_q)
+        out[a:b] = feature_softmax(qm) @ mem_prev
+        # chunk s enters the memory: z^s, then M'_{s+1} from M'_s
+        km = affine(z[a:b], eta_k, rho_k)
+        ek = np.exp(km)
+        z_cur = z_prev + ek.sum(axis=0)
+        phi = ek / z_cur
+        if no_delta:
+            resid = np.asarray(v[a:b], np.float64)
+        else:
+            resid = np.asarray(v[a:b], np.float64) - feature_softmax(km) @ mem_cur
+        mem_next = (z_prev / z_cur)[:, None] * mem_cur + phi.T @ resid
+        if trace is not None:
+            trace.append({"s": s, "z": z_cur.copy(), "phi": phi, "mem_read": mem_prev.copy()})
+        mem_prev, mem_cur = mem_cur, mem_next
+        z_prev = z_cur
+    return out
+
+
+def forward_head(z, v, p: dict, h: int, c: int, no_delta: bool = False,
+                 sca_chunks=None) -> dict:
+    """O = O_SCA + O_m for head h of one batch row ([rainbus "Method steps" (5)], R8).
+
+    ``p`` maps the eight affine-vector names to [H, d] arrays.
+    """
+    o_sca = sca_head(z, v, p["kappa_q"][h], p["nu_q"][h], p["kappa_k"][h], p["nu_k"][h],
+                     c, chunks=sca_chunks)
+    o_m = awm_head(z, v, p["eta_q"][h], p["rho_q"][h], p["eta_k"][h], p["rho_k"][h],
+                   c, no_delta=no_delta)
+    return {"o_sca": o_sca, "o_m": o_m, "o": o_sca + o_m}
+
+
+def forward(z, v, p: dict, c: int, no_delta: bool = False) -> dict:
+    """Whole-tensor forward: z [B, H, n, d], v [B, H, n, dv]; float64 outputs [B, H, n, dv]."""
+    B, H, n, _ = z.shape
+    dv = v.shape[3]
+    res = {key: np.empty((B, H, n, dv)) for key in ("o_sca", "o_m", "o")}
+    for b in range(B):
+        for h in range(H):
+            r = forward_head(z[b, h], v[b, h], p, h, c, no_delta=no_delta)
+            for key in res:
+                res[key][b, h] = r[key]
+    return res

@@ -1,0 +1,139 @@
+"""Independent formulations that pin the oracle (CPU, float64).
+
+Each function here computes something the pages or plain mathematics fix, in a
+form that differs from the oracle's own code (full masked matrices instead of a
+chunk loop, explicit transition-matrix products instead of the recurrence,
+closed forms, a library attention routine), so that a dropped term, a wrong
+sign, an off-by-one chunk index or a transposed operand in the oracle shows up
+as a mismatch. Nothing here imports the oracle or the HIP path.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import softmax as sp_softmax
+
+
+def band_mask(n: int, c: int) -> np.ndarray:
+    """Visibility of key j to query i: causal, and key chunk >= query chunk - 1."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i) & (j // c >= i // c - 1)
+
+
+def brute_sca(q, k, v, c):
+    """Full n x n masked softmax attention (scale 1) with the band mask."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    logits = q @ k.T
+    logits[~band_mask(q.shape[0], c)] = -np.inf
+    return sp_softmax(logits, axis=1) @ v
+
+
+def causal_attention_torch(q, k, v):
+    """Textbook causal softmax attention with scale 1, via torch's routine on CPU."""
+    import torch
+    import torch.nn.functional as F
+
+    t = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None] for a in (q, k, v)]
+    o = F.scaled_dot_product_attention(t[0], t[1], t[2], is_causal=True, scale=1.0)
+    return o[0, 0].numpy()
+
+
+def window_mean(v, c):
+    """Closed form of SCA when every logit is equal: the mean of v over the window.
+
+    The window of token i is [max(0, (i//c - 1) c), i]; prefix sums give each mean.
+    """
+    v = np.asarray(v, np.float64)
+    n = v.shape[0]
+    cs = np.vstack([np.zeros((1, v.shape[1])), np.cumsum(v, axis=0)])
+    i = np.arange(n)
+    lo = np.maximum(0, (i // c - 1) * c)
+    return (cs[i + 1] - cs[lo]) / (i + 1 - lo)[:, None]
+
+
+def _chunks(n, c):
+    return [(a, min(a + c, n)) for a in range(0, n, c)]
+
+
+def awm_unrolled(qm, km, v, c):
+    """O_m from the unrolled sum of transition-matrix products.
+
+    With z^t the cumulative per-feature exp-sum through chunk t,
+      T_t = diag(z^{t-1}/z^t) - diag(1/z^t) exp(K_t)^T psi(K_t)   (d x d)
+      B_t = diag(1/z^t) exp(K_t)^T V_t                           (d x dv)
+    the memory is M'_s = sum_{t=1}^{s-1} T_{s-1} ... T_{t+1} B_t, and chunk s reads
+    psi(Q_m,s) M'_{s-1} (zero for s <= 2). Products are formed explicitly.
+    """
+    qm, km, v = (np.asarray(a, np.float64) for a in (qm, km, v))
+    n, d = km.shape
+    dv = v.shape[1]
+    ch = _chunks(n, c)
+    N = len(ch)
+    z = [np.zeros(d)]
+    for a, b in ch:
+        z.append(z[-1] + np.exp(km[a:b]).sum(axis=0))
+    T = {}
+    Bm = {}
+    for t in range(1, N + 1):
+        a, b = ch[t - 1]
+        e = np.exp(km[a:b])
+        psi = sp_softmax(km[a:b], axis=1)
+        inv = np.diag(1.0 / z[t])
+        T[t] = np.diag(z[t - 1] / z[t]) - inv @ e.T @ psi
+        Bm[t] = inv @ e.T @ v[a:b]
+
+    def mem(s):
+        total = np.zeros((d, dv))
+        for t in range(1, s):
+            prod = np.eye(d)
+            for u in range(t + 1, s):
+                prod = T[u] @ prod
+            total += prod @ Bm[t]
+        return total
+
+    out = np.zeros((n, dv))
+    for s in range(3, N + 1):
+        a, b = ch[s - 1]
+        out[a:b] = sp_softmax(qm[a:b], axis=1) @ mem(s - 1)
+    return out
+
+
+def awm_no_delta_closed(qm, km, v, c):
+    """Closed form without the delta correction: linear attention with the
+    online-softmax kernel. M'_{s-1} = (sum over tokens of chunks 1..s-2 of
+    exp(k)^T v) / z^{s-2}, row f divided by z^{s-2}_f; chunk s reads psi(Q_m) M'_{s-1}."""
+    qm, km, v = (np.asarray(a, np.float64) for a in (qm, km, v))
+    n, d = km.shape
+    out = np.zeros((n, v.shape[1]))
+    ch = _chunks(n, c)
+    for s in range(3, len(ch) + 1):
+        end = ch[s - 3][1]  # last token of chunk s-2
+        e = np.exp(km[:end])
+        mem = (e.T @ v[:end]) / e.sum(axis=0)[:, None]
+        a, b = ch[s - 1]
+        out[a:b] = sp_softmax(qm[a:b], axis=1) @ mem
+    return out
+
+
+def awm_const_key_closed(v, c):
+    """Closed form when every memory key row is the same vector.
+
+    Then every row of M' is the same vector m_s, psi(Q_m) M' = m_s for any
+    query, and with vbar_t the mean of V over chunk t:
+      chunk s <= 2 reads 0; chunk 3 reads vbar_1;
+      chunk s >= 4 reads sum_{t=2}^{s-2} (t-1) vbar_t / ((s-2)(s-3)).
+    """
+    v = np.asarray(v, np.float64)
+    n = v.shape[0]
+    ch = _chunks(n, c)
+    vbar = [None] + [v[a:b].mean(axis=0) for a, b in ch]
+    out = np.zeros_like(v)
+    for s in range(3, len(ch) + 1):
+        a, b = ch[s - 1]
+        if s == 3:
+            row = vbar[1]
+        else:
+            row = sum((t - 1) * vbar[t] for t in range(2, s - 1)) / ((s - 2) * (s - 3))
+        out[a:b] = row
+    return out
