@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Throughput of the Gecko SCA + AWM forward on one MI355X.
+
+One step = one gecko_sca_awm_forward call over the whole 128K-token workload
+(B=1, H=8, n=131072, c=2048, d=128, dv=256, bf16 inputs, fp32 accumulation,
+bf16 output): memory chunk pass, denominator prefix, memory scan, then the
+attention kernel with the fused readout. Inputs are synthetic (seeded), and
+resident in HBM before the timed region starts.
+
+Prints one JSON line. ``value`` is tokens/s (B * n / step time).
+``roofline`` describes the attention kernel (the dominant one): algorithmic
+FLOPs per launch over its mean duration, measured with HIP events recorded on
+the library's stream between its kernels during the timed steps.
+``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
+workload on this host (not a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+METRIC = "SCA+AWM fwd tokens/s at 128K tokens, c=2048; % of bf16 MFMA peak"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt")
+KERNEL_SOURCES = ("sca_bf16.hip", "gecko_device.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "chunked_attention_memory_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_key: str):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or None if there is none or the kernel source changed since."""
+    try:
+        fields = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != launch_key:
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(host, w, budget_s: float):
+    """Time the oracle on head 0 over the first m chunks (m grows until the
+    budget is spent); scale to the workload's tokens/s (all H heads)."""
+    import numpy as np
+
+    import oracle
+
+    z, v, p = host["z"][0, 0], host["v"][0, 0], host["params"]
+    cores = len(os.sched_getaffinity(0))
+    m, spent, t_total, tok_total = 1, 0.0, 0.0, 0
+    while True:
+        ntok = min(m * w.c, w.n)
+        t0 = time.perf_counter()
+        oracle.forward_head(z[:ntok], v[:ntok], p, 0, w.c)
+        dt = time.perf_counter() - t0
+        t_total, tok_total, last_m = dt, ntok, m
+        spent += dt
+        if ntok >= w.n or spent >= budget_s:
+            break
+        per_chunk = dt / m
+        m = max(m + 1, min(w.nchunks, int((budget_s - spent) / max(per_chunk, 1e-9))))
+    value = tok_total / t_total / w.H
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle on head 0 of {w.H}, first {last_m} of {w.nchunks} chunks "
+                      f"({tok_total} tokens) in {t_total:.2f} s; tokens/s divided by {w.H} heads; "
+                      f"numpy {np.__version__} BLAS threads = {cores} host cores"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--out-dtype", choices=("bf16", "f32"), default="bf16")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from chunked_attention_memory_amd import configs, gecko, inputs
+
+    w = configs.WORKLOADS[2]
+    flops = configs.workload_flops(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    host = inputs.make_inputs(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed=0, tag=2)
+    gen_s = time.perf_counter() - t0
+    z, v, params = gecko.to_device_inputs(host, device=dev)
+    out_dt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, w.H, w.n, w.dv), dtype=out_dt, device=dev)
+    ws = gecko.alloc_workspace(z, v, w.c)
+    stream = torch.cuda.current_stream()
+    timer = gecko.Timer(max(args.steps, 1))
+
+    def step(tm=None):
+        gecko.gecko_sca_awm_forward(z, params, v, w.c, out=out, workspace=ws, stream=stream, timer=tm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(timer)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ev_ms = ev0.elapsed_time(ev1)
+    stages, calls = timer.read()
+    timer.close()
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.B * w.n
+    value = tokens / (ms_per_step / 1e3)
+    pct_peak = flops["total"] / (ms_per_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
+    stage_ms = {k: v_ / calls for k, v_ in stages.items()} if calls else {}
+    sca_ms = stage_ms.get("sca_readout")
+    sca_flops = flops["sca"] + flops["awm_read"]
+    achieved = sca_flops / (sca_ms / 1e3) / 1e12 if sca_ms else None
+    launch_key = f"{w.name}:{args.out_dtype}"
+    traffic = read_traffic(launch_key)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: L2-normalised Gaussian Z', silu(N(0,1)) V, N(1,.1)/N(0,.1) affine vectors)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "c": w.c, "d": w.d, "dv": w.dv,
+                   "in_dtype": "bf16", "out_dtype": args.out_dtype, "accumulate": "fp32"},
+        "pct_of_bf16_peak": pct_peak,
+        "flops_per_step": flops["total"],
+        "peak_tflops_used": PEAK_BF16_TFLOPS,
+        "ms_per_step_events": ev_ms / args.steps,
+        "stage_ms": stage_ms,
+        "roofline": {"kernel": "sca_bf16_kernel (attention + readout)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+                     "traffic": traffic, "flops_per_launch": sca_flops},
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(host, w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

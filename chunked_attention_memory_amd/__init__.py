@@ -13,7 +13,7 @@ __all__ = ["configs", "inputs", "gecko"]
 
 def __getattr__(name):
     if name == "gecko":
-        from . import gecko
+        import importlib
 
-        return gecko
+        return importlib.import_module(__name__ + ".gecko")
     raise AttributeError(name)

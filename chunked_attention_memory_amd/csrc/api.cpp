@@ -1,0 +1,316 @@
+// C ABI of the Gecko SCA + AWM forward (declarations and contract in
+// include/gecko.h): argument validation, workspace carve-up and the launch
+// sequence on the caller's stream.
+#include "gecko.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "gecko_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gecko_status fail(gecko_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gecko_status hip_fail(hipError_t e, const char* what) {
+  return fail(GECKO_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_d(int64_t d) { return d == 32 || d == 64 || d == 128; }
+bool valid_dv(int64_t dv) { return dv == 32 || dv == 64 || dv == 128 || dv == 256; }
+
+int64_t nchunks_of(int64_t n, int64_t c) { return (n + c - 1) / c; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+enum Mode { kModeSca = 1, kModeAwm = 2 };
+
+}  // namespace
+
+namespace gecko {
+
+Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv, int64_t nmem, bool bf16) {
+  Workspace w{};
+  const size_t rows = (size_t)BH * (size_t)nmem;
+  const size_t e16 = bf16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return static_cast<char*>(base) + at;
+  };
+  w.g = reinterpret_cast<float*>(take(rows * d * dv * 4));
+  w.h = take(rows * d * d * e16);
+  w.cmax = reinterpret_cast<float*>(take(rows * d * 4));
+  w.csum = reinterpret_cast<float*>(take(rows * d * 4));
+  w.decay = reinterpret_cast<float*>(take(rows * d * 4));
+  w.wscale = reinterpret_cast<float*>(take(rows * d * 4));
+  w.snap = take(rows * dv * d * e16);
+  w.rowstat = bf16 ? nullptr : reinterpret_cast<float*>(take((size_t)BH * n * 2 * 4));
+  w.bytes = nmem > 0 ? off : 0;
+  return w;
+}
+
+}  // namespace gecko
+
+struct gecko_timer {
+  std::vector<hipEvent_t> ev;  // 5 per recorded call
+  int capacity = 0;
+  int used = 0;
+};
+
+namespace {
+
+struct Call {
+  const void* z; const void* v; void* out;
+  const float* aff[8];
+  int64_t B, H, n, d, dv, c;
+  gecko_dtype in_dtype, out_dtype;
+  unsigned flags;
+  void* ws; size_t ws_bytes;
+  void* stream;
+  int mode;
+  gecko_timer* timer;
+};
+
+gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
+  if (k.B < 1 || k.H < 1 || k.n < 1 || k.c < 1)
+    return fail(GECKO_EINVAL, "sizes must be >= 1 (B=%lld H=%lld n=%lld c=%lld)", (long long)k.B, (long long)k.H,
+                (long long)k.n, (long long)k.c);
+  if (k.d < 1 || k.dv < 1) return fail(GECKO_EINVAL, "d and dv must be >= 1");
+  if (k.in_dtype != GECKO_F32 && k.in_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown input dtype %d", (int)k.in_dtype);
+  if (k.out_dtype != GECKO_F32 && k.out_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown output dtype %d", (int)k.out_dtype);
+  if (k.flags & ~(unsigned)GECKO_AWM_NO_DELTA) return fail(GECKO_EINVAL, "unknown flag bits 0x%x", k.flags);
+  if (!k.z || !k.v || !k.out) return fail(GECKO_EINVAL, "z, v and out must be non-null");
+  if (!aligned16(k.z) || !aligned16(k.v) || !aligned16(k.out))
+    return fail(GECKO_EINVAL, "z, v and out must be 16-byte aligned");
+  const bool need_sca = k.mode & kModeSca, need_awm = k.mode & kModeAwm;
+  for (int i = 0; i < 8; ++i) {
+    const bool needed = (i < 4) ? need_sca : need_awm;
+    if (needed && !k.aff[i]) return fail(GECKO_EINVAL, "affine vector %d is null", i);
+    if (needed && (reinterpret_cast<uintptr_t>(k.aff[i]) & 3u)) return fail(GECKO_EINVAL, "affine vector %d misaligned", i);
+  }
+  if (!valid_d(k.d) || !valid_dv(k.dv))
+    return fail(GECKO_EUNSUPPORTED, "unsupported (d, dv) = (%lld, %lld): d in {32,64,128}, dv in {32,64,128,256}",
+                (long long)k.d, (long long)k.dv);
+  bf16 = k.in_dtype == GECKO_BF16;
+  if (!bf16 && k.out_dtype != GECKO_F32) return fail(GECKO_EUNSUPPORTED, "float32 input needs float32 output");
+  if (bf16 && !gecko::bf16_shape_built(k.d, k.dv))
+    return fail(GECKO_EUNSUPPORTED, "bf16 kernels are built for (d, dv) in {(128,256), (128,128), (64,128), (64,64)}");
+  if (k.B > (1 << 20) || k.H > (1 << 20) || k.n > (int64_t(1) << 40))
+    return fail(GECKO_EINVAL, "sizes out of range");
+  const int64_t BH = k.B * k.H;
+  const int64_t N = nchunks_of(k.n, k.c);
+  const int64_t nmem = N > 2 ? N - 2 : 0;
+  if (!bf16 && (BH > 65535 || BH * nmem > 65535 || (k.dv / 32) > 65535))
+    return fail(GECKO_EUNSUPPORTED, "float32 path is limited to B*H*max(N-2,1) <= 65535");
+  const size_t esz = bf16 ? 2 : 4;
+  const size_t osz = k.out_dtype == GECKO_BF16 ? 2 : 4;
+  const size_t zb = (size_t)BH * k.n * k.d * esz, vb = (size_t)BH * k.n * k.dv * esz;
+  const size_t ob = (size_t)BH * k.n * k.dv * osz;
+  if (overlaps(k.out, ob, k.z, zb) || overlaps(k.out, ob, k.v, vb)) return fail(GECKO_EINVAL, "out aliases an input");
+  if (need_awm && nmem > 0) {
+    const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, bf16);
+    if (!k.ws) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", w.bytes);
+    if (k.ws_bytes < w.bytes) return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", k.ws_bytes, w.bytes);
+    if (reinterpret_cast<uintptr_t>(k.ws) & (kAlign - 1)) return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
+    if (overlaps(k.out, ob, k.ws, w.bytes)) return fail(GECKO_EINVAL, "out aliases the workspace");
+  }
+  p.z = k.z; p.v = k.v; p.out = k.out;
+  p.kappa_q = k.aff[0]; p.nu_q = k.aff[1]; p.kappa_k = k.aff[2]; p.nu_k = k.aff[3];
+  p.eta_q = k.aff[4]; p.rho_q = k.aff[5]; p.eta_k = k.aff[6]; p.rho_k = k.aff[7];
+  p.B = k.B; p.H = k.H; p.n = k.n; p.d = k.d; p.dv = k.dv; p.c = k.c;
+  p.nchunks = N; p.nmem = nmem; p.flags = k.flags;
+  p.out_f32 = k.out_dtype == GECKO_F32;
+  return GECKO_OK;
+}
+
+gecko_status run(const Call& k) {
+  gecko::Problem p;
+  bool bf16 = false;
+  gecko_status st = validate(k, p, bf16);
+  if (st != GECKO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(k.stream);
+  const bool do_awm = (k.mode & kModeAwm) && p.nmem > 0;
+  gecko::Workspace w{};
+  if (do_awm) w = gecko::carve_workspace(k.ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, bf16);
+
+  hipEvent_t* ev = nullptr;
+  if (k.timer && k.timer->used < k.timer->capacity) ev = &k.timer->ev[5 * k.timer->used++];
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (do_awm) {
+    e = bf16 ? gecko::launch_awm_chunk_bf16(p, w, s) : gecko::launch_awm_chunk_f32(p, w, s);
+    if (e != hipSuccess) return hip_fail(e, "memory chunk pass launch");
+    if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = gecko::launch_awm_zscan(p, w, s);
+    if (e != hipSuccess) return hip_fail(e, "denominator prefix launch");
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = bf16 ? gecko::launch_awm_scan_bf16(p, w, s) : gecko::launch_awm_scan_f32(p, w, s);
+    if (e != hipSuccess) return hip_fail(e, "memory scan launch");
+    if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  } else {
+    for (int i = 1; i <= 3; ++i)
+      if ((e = mark(i)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  // attention (bit 0) and readout (bit 1). With at most two chunks no chunk
+  // reads the memory and the readout writes its exact zeros.
+  const int mode = (k.mode & kModeSca ? 1 : 0) | (k.mode & kModeAwm ? 2 : 0);
+  e = bf16 ? gecko::launch_sca_bf16(p, w, mode, s) : gecko::launch_sca_f32(p, w, mode, s);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  g_last_error.clear();
+  return GECKO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gecko_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
+  if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv)) return (size_t)-1;
+  if (in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) return (size_t)-1;
+  const int64_t N = nchunks_of(n, c);
+  const int64_t nmem = N > 2 ? N - 2 : 0;
+  return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, in_dtype == GECKO_BF16).bytes;
+}
+
+gecko_status gecko_sca_awm_forward_timed(const void* z, const float* kappa_q, const float* nu_q,
+                                         const float* kappa_k, const float* nu_k, const float* eta_q,
+                                         const float* rho_q, const float* eta_k, const float* rho_k, const void* v,
+                                         void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                         gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, void* workspace,
+                                         size_t workspace_bytes, void* stream, gecko_timer* timer) {
+  try {
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, kModeSca | kModeAwm, timer};
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+gecko_status gecko_sca_awm_forward(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                                   const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
+                                   const float* rho_k, const void* v, void* out, int64_t B, int64_t H, int64_t n,
+                                   int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype,
+                                   unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return gecko_sca_awm_forward_timed(z, kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k, v, out, B, H, n, d,
+                                     dv, c, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+gecko_status gecko_sca_forward(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                               const float* nu_k, const void* v, void* out, int64_t B, int64_t H, int64_t n, int64_t d,
+                               int64_t dv, int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype, void* stream) {
+  try {
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, nullptr, nullptr, nullptr, nullptr}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, 0u, nullptr, 0, stream, kModeSca, nullptr};
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+gecko_status gecko_awm_forward(const void* z, const float* eta_q, const float* rho_q, const float* eta_k,
+                               const float* rho_k, const void* v, void* out, int64_t B, int64_t H, int64_t n, int64_t d,
+                               int64_t dv, int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Call k{z, v, out, {nullptr, nullptr, nullptr, nullptr, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, kModeAwm, nullptr};
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+gecko_status gecko_timer_create(int capacity, gecko_timer** timer) {
+  if (!timer || capacity < 1 || capacity > (1 << 20)) return fail(GECKO_EINVAL, "bad timer arguments");
+  gecko_timer* t = new (std::nothrow) gecko_timer;
+  if (!t) return fail(GECKO_EINVAL, "out of host memory");
+  t->capacity = capacity;
+  t->ev.resize((size_t)capacity * 5);
+  for (size_t i = 0; i < t->ev.size(); ++i) {
+    hipError_t e = hipEventCreate(&t->ev[i]);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
+      delete t;
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  *timer = t;
+  return GECKO_OK;
+}
+
+gecko_status gecko_timer_reset(gecko_timer* timer) {
+  if (!timer) return fail(GECKO_EINVAL, "null timer");
+  timer->used = 0;
+  return GECKO_OK;
+}
+
+gecko_status gecko_timer_read(gecko_timer* timer, float* ms4, int* calls) {
+  if (!timer || !ms4 || !calls) return fail(GECKO_EINVAL, "null argument");
+  for (int i = 0; i < 4; ++i) ms4[i] = 0.f;
+  for (int k = 0; k < timer->used; ++k) {
+    hipEvent_t* ev = &timer->ev[5 * k];
+    hipError_t e = hipEventSynchronize(ev[4]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int i = 0; i < 4; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      ms4[i] += ms;
+    }
+  }
+  *calls = timer->used;
+  return GECKO_OK;
+}
+
+gecko_status gecko_timer_destroy(gecko_timer* timer) {
+  if (!timer) return GECKO_OK;
+  for (hipEvent_t e : timer->ev) (void)hipEventDestroy(e);
+  delete timer;
+  return GECKO_OK;
+}
+
+const char* gecko_status_string(gecko_status status) {
+  switch (status) {
+    case GECKO_OK: return "GECKO_OK: success";
+    case GECKO_EINVAL: return "GECKO_EINVAL: invalid argument";
+    case GECKO_EUNSUPPORTED: return "GECKO_EUNSUPPORTED: shape or dtype not supported";
+    case GECKO_EWORKSPACE: return "GECKO_EWORKSPACE: workspace missing or too small";
+    case GECKO_EHIP: return "GECKO_EHIP: HIP runtime error";
+  }
+  return "unknown gecko_status";
+}
+
+const char* gecko_last_error(void) { return g_last_error.c_str(); }
+
+int gecko_version(void) { return 100; }
+
+}  // extern "C"

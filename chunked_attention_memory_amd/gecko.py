@@ -1,0 +1,236 @@
+"""ctypes binding of libgecko.so (declared in include/gecko.h).
+
+Argument marshalling only: every step of the forward runs in the HIP library.
+Tensors are torch tensors on the GPU (torch provides device memory and the
+stream); shapes are taken from them. Importing this module loads the library
+and raises if it has not been built (``python -m chunked_attention_memory_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libgecko.so")
+
+GECKO_OK, GECKO_EINVAL, GECKO_EUNSUPPORTED, GECKO_EWORKSPACE, GECKO_EHIP = range(5)
+GECKO_F32, GECKO_BF16 = 0, 1
+GECKO_AWM_NO_DELTA = 1 << 0
+
+EXPORTED = (
+    "gecko_workspace_size", "gecko_sca_awm_forward", "gecko_sca_forward", "gecko_awm_forward",
+    "gecko_timer_create", "gecko_timer_reset", "gecko_timer_read", "gecko_timer_destroy",
+    "gecko_sca_awm_forward_timed", "gecko_status_string", "gecko_last_error", "gecko_version",
+)
+
+
+class GeckoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m chunked_attention_memory_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, F, I64, U, SZ = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
+    I = ctypes.c_int
+    lib.gecko_workspace_size.restype = SZ
+    lib.gecko_workspace_size.argtypes = [I64] * 6 + [I]
+    fwd = [P] + [F] * 8 + [P, P] + [I64] * 6 + [I, I, U, P, SZ, P]
+    lib.gecko_sca_awm_forward.restype = I
+    lib.gecko_sca_awm_forward.argtypes = fwd
+    lib.gecko_sca_awm_forward_timed.restype = I
+    lib.gecko_sca_awm_forward_timed.argtypes = fwd + [P]
+    lib.gecko_sca_forward.restype = I
+    lib.gecko_sca_forward.argtypes = [P] + [F] * 4 + [P, P] + [I64] * 6 + [I, I, P]
+    lib.gecko_awm_forward.restype = I
+    lib.gecko_awm_forward.argtypes = [P] + [F] * 4 + [P, P] + [I64] * 6 + [I, I, U, P, SZ, P]
+    lib.gecko_timer_create.restype = I
+    lib.gecko_timer_create.argtypes = [I, ctypes.POINTER(P)]
+    lib.gecko_timer_reset.restype = I
+    lib.gecko_timer_reset.argtypes = [P]
+    lib.gecko_timer_read.restype = I
+    lib.gecko_timer_read.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I)]
+    lib.gecko_timer_destroy.restype = I
+    lib.gecko_timer_destroy.argtypes = [P]
+    lib.gecko_status_string.restype = ctypes.c_char_p
+    lib.gecko_status_string.argtypes = [I]
+    lib.gecko_last_error.restype = ctypes.c_char_p
+    lib.gecko_last_error.argtypes = []
+    lib.gecko_version.restype = I
+    lib.gecko_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != GECKO_OK:
+        msg = lib.gecko_last_error().decode() or lib.gecko_status_string(status).decode()
+        raise GeckoError(status, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return GECKO_BF16
+    if t.dtype == torch.float32:
+        return GECKO_F32
+    raise GeckoError(GECKO_EUNSUPPORTED, f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(z, v):
+    if z.dim() != 4 or v.dim() != 4:
+        raise GeckoError(GECKO_EINVAL, "z and v must be [B, H, n, d] / [B, H, n, dv]")
+    B, H, n, d = z.shape
+    if tuple(v.shape[:3]) != (B, H, n):
+        raise GeckoError(GECKO_EINVAL, "z and v disagree on (B, H, n)")
+    for t in (z, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise GeckoError(GECKO_EINVAL, "z and v must be contiguous device tensors")
+    return B, H, n, d, v.shape[3]
+
+
+def gecko_version() -> int:
+    return lib.gecko_version()
+
+
+def gecko_status_string(status: int) -> str:
+    return lib.gecko_status_string(status).decode()
+
+
+def gecko_workspace_size(B, H, n, d, dv, c, dtype_code) -> int:
+    r = lib.gecko_workspace_size(B, H, n, d, dv, c, dtype_code)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_workspace_size")
+    return r
+
+
+def alloc_workspace(z, v, c):
+    """Device workspace (uint8 tensor, 256-byte aligned by torch) for a forward on z, v."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    nbytes = gecko_workspace_size(B, H, n, d, dv, c, _dtype_code(z))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+
+
+def _params(p, names, device, H, d):
+    import torch
+
+    out = []
+    for k in names:
+        t = p[k]
+        if t.device != device or t.dtype != torch.float32 or t.numel() != H * d or not t.is_contiguous():
+            raise GeckoError(GECKO_EINVAL, f"affine vector {k} must be a contiguous float32 [H, d] device tensor")
+        out.append(_ptr(t))
+    return out
+
+
+Q_NAMES = ("kappa_q", "nu_q", "kappa_k", "nu_k")
+M_NAMES = ("eta_q", "rho_q", "eta_k", "rho_k")
+
+
+def gecko_sca_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, workspace=None, stream=None, timer=None):
+    """O = O_SCA + O_m. ``params`` maps the eight affine-vector names to float32 [H, d] tensors."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    if workspace is None:
+        workspace = alloc_workspace(z, v, c)
+    dt = _dtype_code(z)
+    args = [_ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
+            B, H, n, d, dv, c, dt, _dtype_code(out), flags, _ptr(workspace), workspace.numel(), _stream(stream)]
+    if timer is not None:
+        _check(lib.gecko_sca_awm_forward_timed(*args, timer.handle))
+    else:
+        _check(lib.gecko_sca_awm_forward(*args))
+    return out
+
+
+def gecko_sca_forward(z, params, v, c, out=None, out_dtype=None, stream=None):
+    """O = O_SCA only."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    _check(lib.gecko_sca_forward(_ptr(z), *_params(params, Q_NAMES, z.device, H, d), _ptr(v), _ptr(out),
+                                 B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def gecko_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, workspace=None, stream=None):
+    """O = O_m only (exact zeros on chunks 1 and 2)."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    if workspace is None:
+        workspace = alloc_workspace(z, v, c)
+    _check(lib.gecko_awm_forward(_ptr(z), *_params(params, M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
+                                 B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags,
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+class Timer:
+    """HIP events between the kernels of gecko_sca_awm_forward (see gecko_timer_* in gecko.h)."""
+
+    STAGES = ("awm_chunk", "awm_zscan", "awm_scan", "sca_readout")
+
+    def __init__(self, capacity: int):
+        h = ctypes.c_void_p()
+        _check(lib.gecko_timer_create(capacity, ctypes.byref(h)))
+        self.handle = h
+
+    def reset(self):
+        _check(lib.gecko_timer_reset(self.handle))
+
+    def read(self):
+        ms = (ctypes.c_float * 4)()
+        calls = ctypes.c_int()
+        _check(lib.gecko_timer_read(self.handle, ms, ctypes.byref(calls)))
+        return {k: ms[i] for i, k in enumerate(self.STAGES)}, calls.value
+
+    def close(self):
+        if self.handle:
+            lib.gecko_timer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def to_device_inputs(host: dict, device="cuda"):
+    """Move inputs from ``inputs.make_inputs`` (float32, dtype-exact) to the device in the run dtype."""
+    import torch
+
+    tdt = torch.bfloat16 if host["dtype"] == "bf16" else torch.float32
+    z = torch.from_numpy(host["z"]).to(device=device).to(tdt).contiguous()
+    v = torch.from_numpy(host["v"]).to(device=device).to(tdt).contiguous()
+    params = {k: torch.from_numpy(a).to(device=device, dtype=torch.float32).contiguous()
+              for k, a in host["params"].items()}
+    return z, v, params

@@ -1,0 +1,146 @@
+/*
+ * gecko.h - C ABI of the MI355X (gfx950) Gecko per-layer forward:
+ * sliding chunk attention (SCA) plus adaptive working memory (AWM).
+ *
+ * Operation (sources: the Gecko summary on paper.rainbus.top, sections
+ * "Method steps" (2)-(5) and "Core method"; the paperlayer.ai summary,
+ * sections 3.2, 3.3 and Appendix A):
+ *
+ *   Q   = kappa_q * Z' + nu_q     K   = kappa_k * Z' + nu_k      (per feature)
+ *   Q_m = eta_q   * Z' + rho_q    K_m = eta_k   * Z' + rho_k
+ *   O_SCA rows of chunk s = softmax(Q_s [K_{s-1}; K_s]^T) [V_{s-1}; V_s],
+ *       causal inside chunk s, logits unscaled;
+ *   z^s = per-feature sum of exp(K_m) over chunks 1..s;  phi^s(k) = exp(k)/z^s;
+ *   psi = softmax over the features of a row;
+ *   M'_1 = 0;  M'_s = (z^{s-2}/z^{s-1}) * M'_{s-1}
+ *                    + phi^{s-1}(K_m,{s-1})^T (V_{s-1} - psi(K_m,{s-1}) M'_{s-1});
+ *   O_m rows of chunk s = psi(Q_m,s) M'_{s-1}   (zero for chunks 1 and 2);
+ *   O = O_SCA + O_m.
+ *
+ * Layout: every tensor is dense row-major. Z' is [B][H][n][d], V and O are
+ * [B][H][n][dv], each affine vector is [H][d] float32. Chunks are consecutive
+ * runs of c tokens; the last one may be shorter; c >= n means one chunk.
+ *
+ * Memory: all data pointers are DEVICE pointers owned by the caller. The
+ * library allocates nothing on these calls and keeps no state between them.
+ * Inputs are read-only; O must not alias any input or the workspace.
+ * Calls are asynchronous and ordered on the given HIP stream (a hipStream_t
+ * passed as void*; NULL means the default stream). No host synchronisation.
+ *
+ * Errors: arguments are validated on the host before any launch. Nothing is
+ * launched when a call returns an error. No C++ exception crosses this ABI.
+ * gecko_last_error() gives a thread-local text for the last failing call.
+ */
+#ifndef GECKO_H
+#define GECKO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GECKO_OK = 0,
+    GECKO_EINVAL = 1,       /* null/misaligned pointer, size < 1, inconsistent arguments */
+    GECKO_EUNSUPPORTED = 2, /* valid but not built: d, dv or dtype combination */
+    GECKO_EWORKSPACE = 3,   /* workspace pointer null or smaller than gecko_workspace_size() */
+    GECKO_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} gecko_status;
+
+typedef enum { GECKO_F32 = 0, GECKO_BF16 = 1 } gecko_dtype;
+
+/* flags */
+enum {
+    /* Test variant: drop the -psi(K_m) M' term of the update, leaving plain
+     * linear attention with the online-softmax kernel. Not the method. */
+    GECKO_AWM_NO_DELTA = 1u << 0
+};
+
+/*
+ * Supported shapes: d in {32, 64, 128}; dv in {32, 64, 128, 256}. The bf16
+ * kernels are built for (d, dv) in {(64,64), (64,128), (128,128), (128,256)};
+ * float32 accepts every pair of the two sets (B*H*max(N-2,1) <= 65535).
+ * float32 input writes float32 output; bf16 input writes bf16 output
+ * (round to nearest even of the fp32 accumulator) or float32 output (the
+ * accumulator itself). n >= 1, c >= 1, B >= 1, H >= 1. z, v and out must be
+ * 16-byte aligned, the workspace 256-byte aligned, the affine vectors 4-byte
+ * aligned.
+ */
+
+/* Bytes of device workspace gecko_sca_awm_forward / gecko_awm_forward need
+ * for these sizes (0 if none, (size_t)-1 if the sizes are invalid).
+ * It holds, per (batch, head) and per chunk 1..N-2, the chunk's memory-write
+ * and correction products, its key statistics, its decay factors and the
+ * memory-state snapshots that the readout uses. */
+size_t gecko_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                            int64_t c, gecko_dtype in_dtype);
+
+/* O = O_SCA + O_m (the whole forward). Workspace: gecko_workspace_size()
+ * bytes of caller-owned device memory; its contents on entry do not matter
+ * and are clobbered. */
+gecko_status gecko_sca_awm_forward(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* O = O_SCA only (needs no workspace; the memory vectors are not read). */
+gecko_status gecko_sca_forward(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, void* stream);
+
+/* O = O_m only (exact zeros on chunks 1 and 2). Workspace as above. */
+gecko_status gecko_awm_forward(
+    const void* z,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement helper: HIP events recorded between the kernels of a forward.
+ * gecko_timer_create allocates the host object and `capacity` event sets;
+ * each gecko_sca_awm_forward_timed call records one set (calls beyond the
+ * capacity are not recorded). gecko_timer_read waits for the recorded events
+ * and writes, per stage, the summed milliseconds over the recorded calls:
+ * ms[0] memory chunk pass, ms[1] denominator prefix, ms[2] memory scan,
+ * ms[3] attention + readout kernel; *calls receives the number of calls. */
+typedef struct gecko_timer gecko_timer;
+gecko_status gecko_timer_create(int capacity, gecko_timer** timer);
+gecko_status gecko_timer_reset(gecko_timer* timer);
+gecko_status gecko_timer_read(gecko_timer* timer, float* ms4, int* calls);
+gecko_status gecko_timer_destroy(gecko_timer* timer);
+
+/* gecko_sca_awm_forward that also records one event set into `timer` (may be NULL). */
+gecko_status gecko_sca_awm_forward_timed(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+    void* workspace, size_t workspace_bytes, void* stream, gecko_timer* timer);
+
+/* Static description of a status code. */
+const char* gecko_status_string(gecko_status status);
+
+/* Thread-local description of the last error returned on this thread
+ * ("" if none). Valid until the next call on the same thread. */
+const char* gecko_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int gecko_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GECKO_H */

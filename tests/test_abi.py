@@ -1,0 +1,124 @@
+"""CPU tier: the C-ABI library loads, exports what include/gecko.h declares, and
+rejects bad arguments on the host before launching anything. No call here
+reaches a device: every call fails validation first."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gecko.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    from chunked_attention_memory_amd import build
+
+    lib = os.path.join(ROOT, "chunked_attention_memory_amd", "_lib", "libgecko.so")
+    if not os.path.exists(lib):
+        build.build()
+    from chunked_attention_memory_amd import gecko
+
+    return gecko
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gecko_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(g):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(g.lib, name), name
+    assert set(names) == set(g.EXPORTED)
+
+
+def test_version_and_status_strings(g):
+    assert g.gecko_version() == 100
+    for s in range(5):
+        assert g.gecko_status_string(s).startswith("GECKO_")
+    assert "unknown" in g.gecko_status_string(99)
+
+
+def test_workspace_size(g):
+    # at most two chunks: nothing to store
+    assert g.gecko_workspace_size(1, 1, 100, 128, 256, 50, g.GECKO_BF16) == 0
+    a = g.gecko_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16)
+    rows = 8 * 62
+    expect_min = rows * (128 * 256 * 4 + 128 * 128 * 2 + 4 * 128 * 4 + 256 * 128 * 2)
+    assert expect_min <= a <= expect_min + 7 * 256
+    # doubling the heads doubles the workspace (up to alignment)
+    b = g.gecko_workspace_size(2, 8, 131072, 128, 256, 2048, g.GECKO_BF16)
+    assert abs(b - 2 * a) <= 7 * 256
+    f = g.gecko_workspace_size(1, 1, 256, 32, 32, 64, g.GECKO_F32)
+    assert f >= 2 * (32 * 32 * 4 * 2 + 4 * 32 * 4 + 32 * 32 * 4) + 256 * 2 * 4
+    with pytest.raises(g.GeckoError):
+        g.gecko_workspace_size(1, 1, 0, 128, 256, 64, g.GECKO_BF16)
+    with pytest.raises(g.GeckoError):
+        g.gecko_workspace_size(1, 1, 10, 48, 256, 64, g.GECKO_BF16)
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+def call_full(g, **kw):
+    a = dict(z=FAKE, aff=[FAKE + 64 * i for i in range(8)], v=2 * FAKE, out=3 * FAKE, B=1, H=1, n=1000,
+             d=128, dv=256, c=100, din=g.GECKO_BF16, dout=g.GECKO_BF16, flags=0, ws=0, wsb=0)
+    a.update(kw)
+    st = g.lib.gecko_sca_awm_forward(a["z"], *a["aff"], a["v"], a["out"], a["B"], a["H"], a["n"], a["d"], a["dv"],
+                                     a["c"], a["din"], a["dout"], a["flags"], a["ws"], a["wsb"], None)
+    return st, g.lib.gecko_last_error().decode()
+
+
+def test_validation_errors(g):
+    st, msg = call_full(g, z=0)
+    assert st == g.GECKO_EINVAL and "non-null" in msg
+    st, _ = call_full(g, n=0)
+    assert st == g.GECKO_EINVAL
+    st, _ = call_full(g, c=0)
+    assert st == g.GECKO_EINVAL
+    st, _ = call_full(g, z=FAKE + 2)
+    assert st == g.GECKO_EINVAL
+    st, _ = call_full(g, aff=[FAKE] * 7 + [0])
+    assert st == g.GECKO_EINVAL
+    st, _ = call_full(g, flags=1 << 5)
+    assert st == g.GECKO_EINVAL
+    st, _ = call_full(g, d=96)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, _ = call_full(g, d=32, dv=32)  # built only for float32
+    assert st == g.GECKO_EUNSUPPORTED
+    st, _ = call_full(g, din=g.GECKO_F32, dout=g.GECKO_BF16)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, _ = call_full(g, din=7)
+    assert st == g.GECKO_EINVAL
+    st, msg = call_full(g)  # N = 10 chunks and no workspace
+    assert st == g.GECKO_EWORKSPACE and "null" in msg
+    st, msg = call_full(g, ws=8 * FAKE, wsb=1024)
+    assert st == g.GECKO_EWORKSPACE and "too small" in msg
+    st, msg = call_full(g, out=FAKE + 4096)  # overlaps z
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call_full(g, din=g.GECKO_F32, dout=g.GECKO_F32, B=70000, H=1, n=10, c=1, d=32, dv=32)
+    assert st == g.GECKO_EINVAL or st == g.GECKO_EUNSUPPORTED
+
+
+def test_sca_and_awm_entry_validation(g):
+    st = g.lib.gecko_sca_forward(FAKE, FAKE, FAKE, FAKE, 0, 2 * FAKE, 3 * FAKE, 1, 1, 10, 128, 256, 4,
+                                 g.GECKO_BF16, g.GECKO_BF16, None)
+    assert st == g.GECKO_EINVAL
+    st = g.lib.gecko_awm_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 2 * FAKE, 3 * FAKE, 1, 1, 100, 128, 256, 4,
+                                 g.GECKO_BF16, g.GECKO_BF16, 0, 0, 0, None)
+    assert st == g.GECKO_EWORKSPACE
+
+
+def test_timer_argument_errors(g):
+    h = ctypes.c_void_p()
+    assert g.lib.gecko_timer_create(0, ctypes.byref(h)) == g.GECKO_EINVAL
+    assert g.lib.gecko_timer_reset(None) == g.GECKO_EINVAL
+    assert g.lib.gecko_timer_destroy(None) == g.GECKO_OK

@@ -1,0 +1,134 @@
+"""GPU tier: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Tolerances: float32 path max |y-x| / max(|x|, 1e-3 rms(x))
+<= 1e-4; bf16 inputs with fp32 accumulation max |y-x| / rms(x) <= 2e-2,
+measured on the float32 output; the bf16 output is checked to be exactly the
+round-to-nearest-even of that float32 output. Index and mask logic exact."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from chunked_attention_memory_amd import configs
+from gpu_helpers import BF16_TOL, F32_TOL, floor_rel_err, make, oracle_parts, rms_err, run, run_raw
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(parts, key, heads):
+    return np.stack([parts[bh][key] for bh in heads])
+
+
+def _gpu_heads(arr, heads):
+    return np.stack([arr[b, h] for b, h in heads])
+
+
+def test_f32_tiny_workload_all_parts():
+    w = configs.WORKLOADS[0]
+    host = make(w.B, w.H, w.n, w.d, w.dv, "f32", tag=0)
+    heads = [(0, 0)]
+    ref = oracle_parts(host, w.c)
+    for entry, key in (("full", "o"), ("sca", "o_sca"), ("awm", "o_m")):
+        got = _gpu_heads(run(host, w.c, entry), heads)
+        err = floor_rel_err(got, _stack(ref, key, heads))
+        assert err <= F32_TOL, (entry, err)
+
+
+F32_SHAPES = [
+    (1, 2, 300, 64, 32, 64),
+    (2, 1, 129, 16, 64, 32),
+    (1, 1, 50, 1, 32, 32),
+    (1, 1, 100, 128, 128, 256),
+]
+
+
+@pytest.mark.parametrize("B,H,n,c,d,dv", F32_SHAPES)
+def test_f32_shapes(B, H, n, c, d, dv):
+    host = make(B, H, n, d, dv, "f32", tag=1)
+    ref = oracle_parts(host, c)
+    heads = list(ref)
+    got = _gpu_heads(run(host, c, "full"), heads)
+    assert floor_rel_err(got, _stack(ref, "o", heads)) <= F32_TOL
+
+
+BF16_SHAPES = [
+    (1, 2, 700, 128, 128, 256),   # ragged tail, 6 chunks
+    (1, 1, 1000, 256, 128, 256),  # 4 chunks, ragged
+    (2, 1, 513, 64, 128, 256),    # chunk smaller than a query tile
+    (1, 1, 300, 300, 128, 256),   # one chunk: causal attention
+    (1, 1, 200, 1000, 128, 256),  # c > n
+    (1, 1, 1, 7, 128, 256),       # single token
+    (1, 1, 40, 1, 128, 256),      # one token per chunk
+    (1, 2, 640, 128, 64, 128),
+    (1, 1, 777, 100, 128, 128),   # c not a multiple of the tile sizes
+    (1, 1, 450, 64, 64, 64),
+    (1, 1, 4096, 512, 128, 256),  # several full tiles per chunk
+]
+
+
+@pytest.mark.parametrize("B,H,n,c,d,dv", BF16_SHAPES)
+def test_bf16_shapes(B, H, n, c, d, dv):
+    host = make(B, H, n, d, dv, "bf16", tag=2)
+    ref = oracle_parts(host, c)
+    heads = list(ref)
+    got = _gpu_heads(run(host, c, "full"), heads)
+    assert rms_err(got, _stack(ref, "o", heads)) <= BF16_TOL
+    got = _gpu_heads(run(host, c, "sca"), heads)
+    assert rms_err(got, _stack(ref, "o_sca", heads)) <= BF16_TOL
+    want_m = _stack(ref, "o_m", heads)
+    got_m = _gpu_heads(run(host, c, "awm"), heads)
+    if np.any(want_m != 0):
+        assert rms_err(got_m, want_m) <= BF16_TOL
+    else:
+        assert np.all(got_m == 0)
+
+
+def test_bf16_batched_16k_sampled_heads():
+    w = configs.WORKLOADS[1]
+    host = make(w.B, w.H, w.n, w.d, w.dv, "bf16", tag=1)
+    heads = [(0, 0), (1, 5), (3, 7)]
+    out = run(host, w.c, "full")
+    ref = oracle_parts(host, w.c, heads=heads)
+    assert rms_err(_gpu_heads(out, heads), _stack(ref, "o", heads)) <= BF16_TOL
+
+
+def test_bf16_headline_128k_sampled_chunks():
+    w = configs.WORKLOADS[2]
+    host = make(w.B, w.H, w.n, w.d, w.dv, "bf16", tag=2)
+    N = w.nchunks
+    chunks = [0, 1, 2, 3, N // 2, N - 2, N - 1]
+    out = run(host, w.c, "full")
+    heads = [(0, h) for h in range(w.H)]
+    ref = oracle_parts(host, w.c, heads=heads, sca_chunks=chunks)
+    rows = np.concatenate([np.arange(s * w.c, min((s + 1) * w.c, w.n)) for s in chunks])
+    got = _gpu_heads(out, heads)[:, rows]
+    want = _stack(ref, "o", heads)[:, rows]
+    assert rms_err(got, want) <= BF16_TOL
+    # the memory part alone, over every row
+    want_m = _stack(ref, "o_m", heads)
+    got_m = _gpu_heads(run(host, w.c, "awm"), heads)
+    assert rms_err(got_m, want_m) <= BF16_TOL
+
+
+def _rne_bf16(t):
+    """Round a float32 tensor to bf16 (nearest even) on the host, bit by bit."""
+    import numpy as np
+
+    u = t.detach().cpu().numpy().view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+@pytest.mark.parametrize("entry", ["full", "sca", "awm"])
+def test_bf16_output_is_rounded_fp32_output(entry):
+    import torch
+
+    from chunked_attention_memory_amd import gecko as g
+
+    host = make(1, 2, 1500, 128, 256, "bf16", tag=3)
+    dev = g.to_device_inputs(host)
+    f32 = run_raw(host, 256, entry, device_inputs=dev, out_f32=True)
+    b16 = run_raw(host, 256, entry, device_inputs=dev, out_f32=False)
+    assert b16.dtype == torch.bfloat16
+    got = b16.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _rne_bf16(f32))
