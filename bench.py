@@ -94,6 +94,9 @@ def main(argv=None) -> int:
     ap.add_argument("--out-dtype", choices=("bf16", "f32"), default="bf16")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -140,6 +143,14 @@ def main(argv=None) -> int:
     ev_ms = ev0.elapsed_time(ev1)
     stages, calls = timer.read()
     timer.close()
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.B * w.n

@@ -125,6 +125,15 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   const int64_t BH = k.B * k.H;
   const int64_t N = nchunks_of(k.n, k.c);
   const int64_t nmem = N > 2 ? N - 2 : 0;
+  if (bf16) {
+    // the bf16 kernels address one (batch, head) slab with 32-bit byte offsets
+    const int64_t widest = k.d > k.dv ? k.d : k.dv;
+    if ((k.n + 512) * widest * 2 > (int64_t)0xFFFFFFFF)
+      return fail(GECKO_EUNSUPPORTED, "bf16 path needs n * max(d, dv) * 2 < 4 GiB per (batch, head) slab");
+    const int64_t cc = k.c < k.n ? k.c : k.n;
+    if (BH * N * ((cc + 127) / 128) >= ((int64_t)1 << 31) || BH * nmem >= ((int64_t)1 << 31))
+      return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
+  }
   if (!bf16 && (BH > 65535 || BH * nmem > 65535 || (k.dv / 32) > 65535))
     return fail(GECKO_EUNSUPPORTED, "float32 path is limited to B*H*max(N-2,1) <= 65535");
   const size_t esz = bf16 ? 2 : 4;

@@ -8,21 +8,41 @@
 //
 // Work decomposition: one workgroup = 128 consecutive queries of one chunk of
 // one (batch, head); 4 waves x 32 queries. The key window [(s-1)c, last query]
-// is streamed in tiles of 64 keys through double-buffered LDS.
+// is streamed in tiles of 64 keys.
 //
 // Per tile and wave:
 //   S^T (64 keys x 32 queries) = K_tile Q^T       (A = K from LDS, B = Q in VGPRs)
-//   online softmax over keys, lane-local per query (a query's 64 keys are
-//   split between lane l and lane l ^ 32)
+//   P^T = exp2(S^T - m), lane-local per query (a query's 64 keys are split
+//   between lane l and lane l ^ 32)
 //   O^T (dv x 32 queries) += V^T P^T               (A = V^T from LDS, B = P in VGPRs)
-// Holding O transposed keeps each query's accumulator column, its running max
-// and its running sum in the same lane, so rescaling never crosses lanes.
+// Holding O transposed keeps each query's accumulator column and its
+// exp-sum in the same lane.
+//
+// Staging: K and V tiles go from HBM straight into LDS with buffer loads that
+// write LDS (no registers, out-of-range rows read as zero). Rows are stored
+// dense with their 16-byte chunks XOR-swizzled by row, so that the MFMA
+// operand reads below hit every LDS bank once per 8 lanes. V stays row-major
+// in LDS; its transposed MFMA operand comes from the gfx950 LDS transpose
+// read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i
+// of a 4-row x 16-column block).
+//
+// Pipeline: K is staged two tiles ahead and V one tile ahead, so iteration kt
+// computes S for tile kt+1 on the matrix cores while the vector ALUs turn
+// S(kt) into P(kt).
+//
+// Softmax offset: m is fixed at the row's exact maximum over the first tile
+// (2^(s - m) can then grow above 1 but stays far from the fp32/bf16 range);
+// the final exp-sum shows whether any logit exceeded m by 2^63, and only then
+// is the workgroup recomputed with the exact row maximum found by a max-only
+// pass. No accumulator is ever rescaled inside the loop.
 //
 // Algebra used to drop the key-side affine map: q . (kappa_k * z_j + nu_k)
 // = (q * kappa_k) . z_j + q . nu_k. The second term is the same for every key
 // of query i, and softmax is invariant to a per-row shift, so the kernel uses
 // q' = (kappa_q * z_i + nu_q) * kappa_k * log2(e) against the raw z_j. The
 // log2(e) factor lets the exponentials run on the hardware exp2.
+#include <type_traits>
+
 #include "gecko_device.hpp"
 #include "gecko_internal.hpp"
 
@@ -32,17 +52,19 @@ namespace {
 constexpr int kBM = 128;       // queries per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 waves
-constexpr float kLazy = 8.0f;  // rescale only when the running max grows by > 2^8
+constexpr float kOverflow = 0x1p63f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D, int DV>
 struct ScaTile {
-  static constexpr int KROW = D + 8;    // LDS row of K (bf16 elements), +16 B pad
-  static constexpr int VROW = kBN + 8;  // LDS row of V^T
-  static constexpr int KELEMS = kBN * KROW;
-  static constexpr int VELEMS = DV * VROW;
-  static constexpr int STAGE = KELEMS + VELEMS;
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(uint16_t);
-  static constexpr int KPIECES = kBN * D / 8 / kThreads;  // 16-byte pieces per thread
+  static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
+  static constexpr int VBYTES = kBN * DV * 2;
+  static constexpr size_t LDS_BYTES = 2 * (size_t)KBYTES + 2 * (size_t)VBYTES;
+  static constexpr int KLOADS = KBYTES / 16 / kThreads;  // 16-byte loads per thread per tile
+  static constexpr int VLOADS = VBYTES / 16 / kThreads;
 };
 
 struct ScaArgs {
@@ -55,46 +77,71 @@ struct ScaArgs {
   const float* eta_q;
   const float* rho_q;
   const uint16_t* snap;  // [bh][nmem][dv][d]; slot t is the state read by chunk t + 2 (0-based)
-  int64_t n, c, nchunks, nmem, qtiles, nblocks, per_xcd;
-  int H;
+  int64_t n;
+  int c, nchunks, nmem, qtiles, nblocks, per_xcd, H;
 };
+
+__device__ __forceinline__ float other_half_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// buffer resource over rows [row0, n) of a row-major bf16 matrix with `width` columns
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int row0, int n, int width) {
+  const int rows = n > row0 ? n - row0 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * width), (short)0,
+                                           (int)((uint32_t)rows * (uint32_t)width * 2u), 0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
   using T = ScaTile<D, DV>;
   constexpr int KS = D / 16;   // 16-feature k-steps of Q K^T
   constexpr int NMV = DV / 32; // 32-row blocks of O^T
+  constexpr int KCH = D / 8;   // 16-byte chunks per K row
+  constexpr int VCH = DV / 8;  // 16-byte chunks per V row
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
   // run of logical blocks so the q-tiles of one chunk share an L2.
-  const int64_t bid = blockIdx.x;
-  const int64_t lb = (bid & 7) * a.per_xcd + (bid >> 3);
-  if (lb >= a.nblocks) return;
-  const int qt = (int)(a.qtiles - 1 - lb % a.qtiles);  // longest q-tiles first
-  const int64_t rest = lb / a.qtiles;
-  const int64_t s = rest % a.nchunks;
-  const int64_t bh = rest / a.nchunks;
-  const int h = (int)(bh % a.H);
-  const int64_t n = a.n, c = a.c;
-  const int64_t q0 = s * c + (int64_t)qt * kBM;
-  const int64_t cend = min((s + 1) * c, n);
+  const uint32_t bid = blockIdx.x;
+  const uint32_t lb = (bid & 7u) * (uint32_t)a.per_xcd + (bid >> 3);
+  if (lb >= (uint32_t)a.nblocks) return;
+  const uint32_t qtiles = (uint32_t)a.qtiles, nchunks = (uint32_t)a.nchunks;
+  const int qt = (int)(qtiles - 1 - lb % qtiles);  // longest q-tiles first
+  const uint32_t rest = lb / qtiles;
+  const int s = (int)(rest % nchunks);
+  const uint32_t bh = rest / nchunks;
+  const int h = (int)(bh % (uint32_t)a.H);
+  const int n = (int)a.n, c = a.c;  // n * max(d, dv) * 2 < 2^32 (validated on the host)
+  const int q0 = s * c + qt * kBM;
+  const int cend = min((s + 1) * c, n);
   if (q0 >= cend) return;
-  const int64_t qend = min(q0 + (int64_t)kBM, cend);
+  const int qend = min(q0 + kBM, cend);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
-  const int64_t myq = q0 + w * 32 + lq;
+  const int lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int myq = q0 + w * 32 + lq;
   const bool qvalid = myq < qend;
-  const int64_t qrow = qvalid ? myq : qend - 1;
-  const uint16_t* zbh = a.z + bh * n * D;
+  const int qrow = qvalid ? myq : qend - 1;
+  const uint16_t* zbh = a.z + (size_t)bh * (size_t)n * D;
 
   f32x16 oacc[NMV];
 #pragma unroll
   for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
 
   if constexpr (kSca) {
-    const uint16_t* vbh = a.v + bh * n * DV;
+    const uint16_t* vbh = a.v + (size_t)bh * (size_t)n * DV;
+    char* const kbuf = reinterpret_cast<char*>(lds);
+    char* const vbuf = kbuf + 2 * T::KBYTES;
+
     // ---- query fragments: lane holds query lq, features 16 ks + 8 g + [0, 8)
     u32x4 qf[KS];
     {
@@ -104,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int f0 = 16 * ks + 8 * g;
-        const u32x4 raw = ld16(zbh + qrow * D + f0);
+        const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -117,141 +164,185 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
       }
     }
 
-    const int64_t kbeg = s > 0 ? (s - 1) * c : 0;
-    const int64_t kend = qend;
-    const int ntiles = (int)((kend - kbeg + kBN - 1) / kBN);
-    const int64_t wave_q0 = q0 + w * 32;
+    const int kbeg = s > 0 ? (s - 1) * c : 0;
+    const int kend = qend;
+    const int ntiles = (kend - kbeg + kBN - 1) / kBN;
+    // tiles whose every key is visible to every query of the workgroup
+    const int nfull = q0 - kbeg >= kBN - 1 ? min(ntiles, (q0 - kbeg + 1) / kBN) : 0;
 
-    u32x4 kreg[T::KPIECES];
-    u32x4 vreg[8];
-    // V is staged as 8x8 blocks: block (kg, vg) covers tile positions
-    // [8 kg, 8 kg + 8) and value columns [8 vg, 8 vg + 8).
-    constexpr int VG = DV / 8;
-    const bool vthread = tid < 8 * VG;
-    const int kg = tid / VG, vg = tid % VG;
-
-    auto load_tile = [&](int kt) {
-      const int64_t kb = kbeg + (int64_t)kt * kBN;
+    // ---- staging offsets (constant over tiles). Load i of wave w covers the
+    // 1 KiB piece 4 i + w of the tile; lane l writes LDS chunk (4 i + w) 64 + l,
+    // which is physical chunk p of row r holding logical chunk p ^ swz(r).
+    uint32_t koff[T::KLOADS], voff[T::VLOADS];
 #pragma unroll
-      for (int i = 0; i < T::KPIECES; ++i) {
-        const int p = tid + kThreads * i;
-        const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-        const int64_t key = kb + row;
-        kreg[i] = key < n ? ld16(zbh + key * D + col) : u32x4{};
-      }
-      if (vthread) {
+    for (int i = 0; i < T::KLOADS; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int r = P / KCH, p = P % KCH;
+      koff[i] = (uint32_t)(r * D + 8 * (p ^ (r & 7))) * 2u;
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          // tile position 8 kg + i holds key perm_row(8 kg + i): inside each
-          // 16-key group, bits 2 and 3 of the key index are swapped, which is
-          // the order the S^T accumulator hands P to the P V product.
-          const int64_t key = kb + perm_row(8 * kg + i);
-          vreg[i] = key < n ? ld16(vbh + key * DV + 8 * vg) : u32x4{};
-        }
-      }
+    for (int i = 0; i < T::VLOADS; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int r = P / VCH, p = P % VCH;
+      voff[i] = (uint32_t)(r * DV + 8 * (p ^ ((r & 3) << 1))) * 2u;
+    }
+    auto stage_k = [&](int kt, int slot) {
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(zbh, kbeg + kt * kBN, n, D);
+#pragma unroll
+      for (int i = 0; i < T::KLOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(kbuf + slot * T::KBYTES + (4 * i + w) * 1024), 16, koff[i], 0, 0, 0);
     };
-    auto store_tile = [&](int buf) {
-      uint16_t* Ks = lds + buf * T::STAGE;
-      uint16_t* Vs = Ks + T::KELEMS;
+    auto stage_v = [&](int kt, int slot) {
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(vbh, kbeg + kt * kBN, n, DV);
 #pragma unroll
-      for (int i = 0; i < T::KPIECES; ++i) {
-        const int p = tid + kThreads * i;
-        const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-        st16(Ks + row * T::KROW + col, kreg[i]);
-      }
-      if (vthread) {
-        u32x4 tr[8];
-        transpose8x8(vreg, tr);
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const int vcol = 8 * vg + cc;
-          // value column v lives in LDS row perm_row(v) of its 32-block, so a
-          // lane reading row l of the block gets v = perm_row(l): accumulator
-          // rows then come out as 8 consecutive values per lane half.
-          const int vrow = (vcol & ~31) | perm_row(vcol & 31);
-          st16(Vs + vrow * T::VROW + 8 * kg, tr[cc]);
-        }
-      }
+      for (int i = 0; i < T::VLOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(vbuf + slot * T::VBYTES + (4 * i + w) * 1024), 16, voff[i], 0, 0, 0);
     };
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // ---- operand read addresses (bytes, relative to a stage)
+    // K: lane reads row 32 mb + lq, logical chunk 2 ks + g
+    auto k_addr = [&](int mb, int ks) {
+      const int r = 32 * mb + lq;
+      return r * (D * 2) + 16 * ((2 * ks + g) ^ (r & 7));
+    };
+    // V^T block for O rows 32 mv + [0, 32) and P keys of k-step (mb, hh):
+    // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
+    //                                      [32 mv + perm_row(lq)].
+    // Transpose read jj supplies j = 4 jj + j': source lane s of each 16-lane
+    // group points at key 32 mb + 16 hh + 8 jj + 4 g + s / 4 and values
+    // 32 mv + 16 (group % 2) + 4 perm2(s % 4) + [0, 4).
+    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+    const int perm2 = ((sl & 3) >> 1) | (((sl & 3) & 1) << 1);
+    auto v_addr = [&](int mv, int mb, int hh, int jj) {
+      const int r = 32 * mb + 16 * hh + 8 * jj + 4 * g + (sl >> 2);
+      const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+      return r * (DV * 2) + 16 * ((col >> 3) ^ ((r & 3) << 1)) + 2 * (col & 7);
+    };
 
-    float mrun = kNegInf;  // running max of the row (log2 units), same in lanes l and l^32
-    float lrun = 0.f;      // this lane's share of the running exp-sum
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < ntiles) load_tile(kt + 1);
-      const uint16_t* Ks = lds + buf * T::STAGE;
-      const uint16_t* Vs = Ks + T::KELEMS;
-
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    auto qk = [&](int slot, f32x16 (&sa)[2]) {
+      const char* Kb = kbuf + slot * T::KBYTES;
+      sa[0] = f32x16{};
+      sa[1] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 af = ld16(Ks + (32 * mb + lq) * T::KROW + 16 * ks + 8 * g);
-          sacc[mb] = mfma_bf16(af, qf[ks], sacc[mb]);
+          const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
+          sa[mb] = mfma_bf16(af, qf[ks], sa[mb]);
         }
       }
+    };
+    auto pv = [&](int slot, const u32x4 (&pf)[2][2]) {
+      const char* Vb = vbuf + slot * T::VBYTES;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int mv = 0; mv < NMV; ++mv) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[mb][hh], oacc[mv]);
+          }
+    };
 
-      // accumulator (mb, r) holds key kb + 32 mb + 8 (r >> 2) + 4 g + (r & 3)
-      const int64_t kb = kbeg + (int64_t)kt * kBN;
-      if (kb + kBN - 1 > wave_q0 || kb + kBN > kend) {
+    // one tile: P(kt) from S(kt) while S(kt+1) runs; then O += V(kt)^T P(kt).
+    // accumulator (mb, r) of S holds key kb + 32 mb + 8 (r >> 2) + 4 g + (r & 3)
+    auto tile = [&](int kt, float msub, f32x16 (&scur)[2], float& lrun, auto masked) {
+      stage_k(kt + 2, kt & 1);          // replaces K(kt), read last iteration
+      stage_v(kt + 1, (kt + 1) & 1);    // replaces V(kt-1)
+      f32x16 snext[2];
+      qk((kt + 1) & 1, snext);
+      float e[2][16];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[mb][r] = exp2_fast(scur[mb][r] - msub);
+      if constexpr (decltype(masked)::value) {
+        const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);  // last visible key offset
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t key = kb + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > myq || key >= kend) sacc[mb][r] = kNegInf;
+            const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+            e[mb][r] = ko > lim ? 0.f : e[mb][r];
           }
       }
-
-      float tmax = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[mb][r]);
-      tmax = fmaxf(tmax, wave_xor32(tmax));
-      const float mnew = fmaxf(mrun, tmax);
-      if (__any(mnew > mrun + kLazy)) {
-        const float alpha = (mnew == kNegInf) ? 1.f : exp2_fast(mrun - mnew);
-        lrun *= alpha;
-#pragma unroll
-        for (int i = 0; i < NMV; ++i) oacc[i] *= alpha;
-        mrun = mnew;
-      }
-      const float msub = (mrun == kNegInf) ? 0.f : mrun;
+      u32x4 pf[2][2];
       float psum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(sacc[mb][r] - msub);
-          sacc[mb][r] = p;
-          psum += p;
+        for (int hh = 0; hh < 2; ++hh) {
+          const float* x = e[mb] + 8 * hh;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) psum += x[i];
+          pf[mb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
         }
       lrun += psum;
+      pv(kt & 1, pf);
+      wait_vmem();
+      __syncthreads();
+      scur[0] = snext[0];
+      scur[1] = snext[1];
+    };
 
+    // full pipelined pass with a fixed softmax offset; returns the row exp-sum
+    auto pass = [&](float msub, f32x16 (&scur)[2]) {
+      float lrun = 0.f;
+      for (int kt = 0; kt < nfull; ++kt) tile(kt, msub, scur, lrun, std::false_type{});
+      for (int kt = nfull; kt < ntiles; ++kt) tile(kt, msub, scur, lrun, std::true_type{});
+      return other_half_sum(lrun);
+    };
+    auto prologue = [&](f32x16 (&scur)[2]) {
+      stage_k(0, 0);
+      stage_v(0, 0);
+      stage_k(1, 1);
+      wait_vmem();
+      __syncthreads();
+      qk(0, scur);
+    };
+    auto masked_max = [&](const f32x16 (&sc)[2], int kt) {
+      const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);
+      float mx = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const f32x16& sp = sacc[mb];
-          const u32x4 pf{pack2(sp[8 * hh + 0], sp[8 * hh + 1]), pack2(sp[8 * hh + 2], sp[8 * hh + 3]),
-                         pack2(sp[8 * hh + 4], sp[8 * hh + 5]), pack2(sp[8 * hh + 6], sp[8 * hh + 7])};
-#pragma unroll
-          for (int mv = 0; mv < NMV; ++mv) {
-            const u32x4 af = ld16(Vs + (32 * mv + lq) * T::VROW + 32 * mb + 16 * hh + 8 * g);
-            oacc[mv] = mfma_bf16(af, pf, oacc[mv]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+          mx = fmaxf(mx, ko > lim ? kNegInf : sc[mb][r]);
         }
+      return mx;
+    };
 
-      if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    f32x16 scur[2];
+    prologue(scur);
+    // every valid query sees at least one key of the first tile
+    const float m0 = other_half_max(masked_max(scur, 0));
+    float ltot = pass(m0, scur);
+    if (__syncthreads_or(!(ltot <= kOverflow))) {
+      // some logit exceeded the first tile's maximum by 2^63: find the exact
+      // row maximum, then redo the pass with it (every 2^(s - m) <= 1)
       __syncthreads();
+      float mx = kNegInf;
+      for (int kt = 0; kt < ntiles; ++kt) {
+        stage_k(kt, 0);
+        wait_vmem();
+        __syncthreads();
+        f32x16 sc[2];
+        qk(0, sc);
+        mx = fmaxf(mx, masked_max(sc, kt));
+        __syncthreads();
+      }
+      mx = other_half_max(mx);
+#pragma unroll
+      for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
+      prologue(scur);
+      ltot = pass(mx, scur);
     }
-    const float ltot = lrun + wave_xor32(lrun);
     const float inv = 1.f / ltot;
 #pragma unroll
     for (int i = 0; i < NMV; ++i) oacc[i] *= inv;
@@ -267,25 +358,25 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int f0 = 16 * ks + 8 * g;
-        const u32x4 raw = ld16(zbh + qrow * D + f0);
+        const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          qm[8 * ks + 2 * j] = eq[f0 + 2 * j] * bf_lo(raw[j]) + rq[f0 + 2 * j];
-          qm[8 * ks + 2 * j + 1] = eq[f0 + 2 * j + 1] * bf_hi(raw[j]) + rq[f0 + 2 * j + 1];
+          qm[8 * ks + 2 * j] = (eq[f0 + 2 * j] * bf_lo(raw[j]) + rq[f0 + 2 * j]) * kLog2e;
+          qm[8 * ks + 2 * j + 1] = (eq[f0 + 2 * j + 1] * bf_hi(raw[j]) + rq[f0 + 2 * j + 1]) * kLog2e;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, qm[8 * ks + i]);
       }
-      mx = fmaxf(mx, wave_xor32(mx));
+      mx = other_half_max(mx);
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < KS * 8; ++i) {
-        qm[i] = exp2_fast((qm[i] - mx) * kLog2e);
+        qm[i] = exp2_fast(qm[i] - mx);
         sum += qm[i];
       }
-      sum += wave_xor32(sum);
+      sum = other_half_sum(sum);
       const float inv = 1.f / sum;
-      const uint16_t* sn = a.snap + ((bh * a.nmem + (s - 2)) * DV) * D;
+      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(DV * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const float* e = qm + 8 * ks;
@@ -305,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
   // 32 mv + 16 (r >> 3) + 8 g + (r & 7): two runs of 8 per lane
   if (qvalid) {
     if constexpr (kOutF32) {
-      float* orow = static_cast<float*>(a.out) + (bh * n + myq) * DV;
+      float* orow = static_cast<float*>(a.out) + ((size_t)bh * n + myq) * DV;
 #pragma unroll
       for (int mv = 0; mv < NMV; ++mv)
 #pragma unroll
@@ -316,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[8 * hh + 4], o[8 * hh + 5], o[8 * hh + 6], o[8 * hh + 7]};
         }
     } else {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + (bh * n + myq) * DV;
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)bh * n + myq) * DV;
 #pragma unroll
       for (int mv = 0; mv < NMV; ++mv)
 #pragma unroll
@@ -377,10 +468,15 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   a.kappa_q = p.kappa_q; a.nu_q = p.nu_q; a.kappa_k = p.kappa_k;
   a.eta_q = p.eta_q; a.rho_q = p.rho_q;
   a.snap = static_cast<const uint16_t*>(w.snap);
-  a.n = p.n; a.c = p.c; a.nchunks = p.nchunks; a.nmem = p.nmem; a.H = (int)p.H;
-  a.qtiles = (min(p.c, p.n) + kBM - 1) / kBM;
-  a.nblocks = p.B * p.H * p.nchunks * a.qtiles;
-  a.per_xcd = (a.nblocks + 7) / 8;
+  a.n = p.n;
+  // the host validated n * max(d, dv) * 2 < 2^32 and the block count < 2^31
+  const int64_t cc = min(p.c, p.n);  // a chunk longer than the sequence is the sequence
+  a.c = (int)cc;
+  a.nchunks = (int)p.nchunks; a.nmem = (int)p.nmem; a.H = (int)p.H;
+  a.qtiles = (int)((cc + kBM - 1) / kBM);
+  const int64_t nblocks = p.B * p.H * p.nchunks * a.qtiles;
+  a.nblocks = (int)nblocks;
+  a.per_xcd = (int)((nblocks + 7) / 8);
   if (p.d == 128 && p.dv == 256) return launch_shape<128, 256>(a, mode, p.out_f32, stream);
   if (p.d == 128 && p.dv == 128) return launch_shape<128, 128>(a, mode, p.out_f32, stream);
   if (p.d == 64 && p.dv == 128) return launch_shape<64, 128>(a, mode, p.out_f32, stream);

@@ -132,3 +132,21 @@ def test_bf16_output_is_rounded_fp32_output(entry):
     assert b16.dtype == torch.bfloat16
     got = b16.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(got, _rne_bf16(f32))
+
+
+@pytest.mark.parametrize("scale", [80.0, 200.0])
+def test_bf16_logits_beyond_first_tile_range(scale):
+    """Logits that grow past the first key tile's maximum by more than 2^63
+    (in base 2) take the kernel's exact-maximum path; with a large query
+    scale each query attends almost only to itself, which keeps the bf16
+    comparison well conditioned."""
+    host = make(1, 2, 1100, 128, 256, "bf16", tag=4)
+    host["params"]["kappa_q"][:] = scale
+    host["params"]["nu_q"][:] = 0.0
+    host["params"]["kappa_k"][:] = 1.0
+    ref = oracle_parts(host, 256)
+    heads = list(ref)
+    got = _gpu_heads(run(host, 256, "sca"), heads)
+    want = _stack(ref, "o_sca", heads)
+    assert np.all(np.isfinite(got))
+    assert rms_err(got, want) <= BF16_TOL
