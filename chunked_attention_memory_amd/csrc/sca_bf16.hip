@@ -41,8 +41,6 @@
 // of query i, and softmax is invariant to a per-row shift, so the kernel uses
 // q' = (kappa_q * z_i + nu_q) * kappa_k * log2(e) against the raw z_j. The
 // log2(e) factor lets the exponentials run on the hardware exp2.
-#include <type_traits>
-
 #include "gecko_device.hpp"
 #include "gecko_internal.hpp"
 
@@ -90,22 +88,260 @@ __device__ __forceinline__ float other_half_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// buffer resource over rows [row0, n) of a row-major bf16 matrix with `width` columns
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int row0, int n, int width) {
-  const int rows = n > row0 ? n - row0 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * width), (short)0,
-                                           (int)((uint32_t)rows * (uint32_t)width * 2u), 0x00020000);
+// Copy one key tile (rows [row0, row0 + 64) of a row-major bf16 matrix with
+// `width` columns) into LDS with buffer loads that write LDS directly; rows at
+// or past n read as zero. Load i of this wave fills the 1 KiB piece 4 i + w.
+// A __device__ function on purpose: the buffer resource type may not appear in
+// a lambda inside the kernel, which is compiled for the host as well.
+__device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile, int w,
+                                           const uint32_t* off, int nloads) {
+  const uint32_t rows = (uint32_t)(n > row0 ? n - row0 : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + (size_t)row0 * width), (short)0, (int)(rows * (uint32_t)width * 2u), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < nloads; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (4 * i + w) * 1024), 16, off[i], 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The attention loop of one workgroup. Member functions rather than lambdas:
+// lambdas inside a kernel are compiled for the host too, where the buffer and
+// LDS builtins used here do not exist.
+template <int D, int DV>
+struct ScaLoop {
+  using T = ScaTile<D, DV>;
+  static constexpr int KS = D / 16;   // 16-feature k-steps of Q K^T
+  static constexpr int NMV = DV / 32; // 32-row blocks of O^T
+  static constexpr int KCH = D / 8;   // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;  // 16-byte chunks per V row
+
+  const uint16_t* zbh;
+  const uint16_t* vbh;
+  char* kbuf;  // two K stages
+  char* vbuf;  // two V stages
+  int n, kbeg, kend, ntiles, nfull, myq, w, g, lq, sl, grp2, perm2;
+  u32x4 qf[KS];
+  uint32_t koff[T::KLOADS], voff[T::VLOADS];
+
+  __device__ __forceinline__ void init(const ScaArgs& a, uint32_t bh, int h, int n_, int s, int c, int q0,
+                                       int qend, int qrow, int myq_, int w_, int lane, uint16_t* lds) {
+    n = n_;
+    myq = myq_;
+    w = w_;
+    g = lane >> 5;
+    lq = lane & 31;
+    zbh = a.z + (size_t)bh * (size_t)n * D;
+    vbh = a.v + (size_t)bh * (size_t)n * DV;
+    kbuf = reinterpret_cast<char*>(lds);
+    vbuf = kbuf + 2 * T::KBYTES;
+
+    // query fragments: lane holds query lq, features 16 ks + 8 g + [0, 8)
+    const float* kq = a.kappa_q + h * D;
+    const float* nq = a.nu_q + h * D;
+    const float* kk = a.kappa_k + h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int f0 = 16 * ks + 8 * g;
+      const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf_lo(raw[j]);
+        x[2 * j + 1] = bf_hi(raw[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (kq[f0 + i] * x[i] + nq[f0 + i]) * (kk[f0 + i] * kLog2e);
+      qf[ks] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+    }
+
+    kbeg = s > 0 ? (s - 1) * c : 0;
+    kend = qend;
+    ntiles = (kend - kbeg + kBN - 1) / kBN;
+    // tiles whose every key is visible to every query of the workgroup
+    nfull = q0 - kbeg >= kBN - 1 ? min(ntiles, (q0 - kbeg + 1) / kBN) : 0;
+
+    // staging offsets (constant over tiles). Load i of wave w covers the
+    // 1 KiB piece 4 i + w of the tile; lane l writes LDS chunk (4 i + w) 64 + l,
+    // which is physical chunk p of row r holding logical chunk p ^ swz(r).
+#pragma unroll
+    for (int i = 0; i < T::KLOADS; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int r = P / KCH, p = P % KCH;
+      koff[i] = (uint32_t)(r * D + 8 * (p ^ (r & 7))) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < T::VLOADS; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int r = P / VCH, p = P % VCH;
+      voff[i] = (uint32_t)(r * DV + 8 * (p ^ ((r & 3) << 1))) * 2u;
+    }
+    sl = lane & 15;
+    grp2 = (lane >> 4) & 1;
+    perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+  }
+
+  __device__ __forceinline__ void stage_k(int kt, int slot) const {
+    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, w, koff, T::KLOADS);
+  }
+  __device__ __forceinline__ void stage_v(int kt, int slot) const {
+    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, w, voff, T::VLOADS);
+  }
+
+  // K operand: lane reads row 32 mb + lq, logical chunk 2 ks + g
+  __device__ __forceinline__ int k_addr(int mb, int ks) const {
+    const int r = 32 * mb + lq;
+    return r * (D * 2) + 16 * ((2 * ks + g) ^ (r & 7));
+  }
+  // V^T block for O rows 32 mv + [0, 32) and the P keys of k-step (mb, hh):
+  // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
+  //                                      [32 mv + perm_row(lq)].
+  // Transpose read jj supplies j = 4 jj + j': source lane s of each 16-lane
+  // group points at key 32 mb + 16 hh + 8 jj + 4 g + s / 4 and at values
+  // 32 mv + 16 (group % 2) + 4 perm2(s % 4) + [0, 4), perm2 swapping two bits.
+  __device__ __forceinline__ int v_addr(int mv, int mb, int hh, int jj) const {
+    const int r = 32 * mb + 16 * hh + 8 * jj + 4 * g + (sl >> 2);
+    const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+    return r * (DV * 2) + 16 * ((col >> 3) ^ ((r & 3) << 1)) + 2 * (col & 7);
+  }
+
+  __device__ __forceinline__ void qk(int slot, f32x16 (&sa)[2]) const {
+    const char* Kb = kbuf + slot * T::KBYTES;
+    sa[0] = f32x16{};
+    sa[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
+        sa[mb] = mfma_bf16(af, qf[ks], sa[mb]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void pv(int slot, const u32x4 (&pf)[2][2], f32x16 (&oacc)[NMV]) const {
+    const char* Vb = vbuf + slot * T::VBYTES;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mv = 0; mv < NMV; ++mv) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[mb][hh], oacc[mv]);
+        }
+  }
+
+  // accumulator (mb, r) of S holds key kb + 32 mb + 8 (r >> 2) + 4 g + (r & 3)
+  __device__ __forceinline__ float masked_max(const f32x16 (&sc)[2], int kt) const {
+    const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);  // last visible key offset
+    float mx = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+        mx = fmaxf(mx, ko > lim ? kNegInf : sc[mb][r]);
+      }
+    return mx;
+  }
+
+  // one tile: P(kt) from S(kt) while S(kt+1) runs; then O += V(kt)^T P(kt)
+  __device__ __forceinline__ void tile(int kt, float msub, f32x16 (&scur)[2], float& lrun, bool masked,
+                                       f32x16 (&oacc)[NMV]) const {
+    stage_k(kt + 2, kt & 1);          // replaces K(kt), read last iteration
+    stage_v(kt + 1, (kt + 1) & 1);    // replaces V(kt-1)
+    f32x16 snext[2];
+    qk((kt + 1) & 1, snext);
+    float e[2][16];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[mb][r] = exp2_fast(scur[mb][r] - msub);
+    if (masked) {
+      const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+          e[mb][r] = ko > lim ? 0.f : e[mb][r];
+        }
+    }
+    u32x4 pf[2][2];
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float* x = e[mb] + 8 * hh;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) psum += x[i];
+        pf[mb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+      }
+    lrun += psum;
+    pv(kt & 1, pf, oacc);
+    wait_vmem();
+    __syncthreads();
+    scur[0] = snext[0];
+    scur[1] = snext[1];
+  }
+
+  __device__ __forceinline__ void prologue(f32x16 (&scur)[2]) const {
+    stage_k(0, 0);
+    stage_v(0, 0);
+    stage_k(1, 1);
+    wait_vmem();
+    __syncthreads();
+    qk(0, scur);
+  }
+
+  // full pipelined pass with a fixed softmax offset; returns the row exp-sum
+  __device__ __forceinline__ float pass(float msub, f32x16 (&scur)[2], f32x16 (&oacc)[NMV]) const {
+    float lrun = 0.f;
+    for (int kt = 0; kt < nfull; ++kt) tile(kt, msub, scur, lrun, false, oacc);
+    for (int kt = nfull; kt < ntiles; ++kt) tile(kt, msub, scur, lrun, true, oacc);
+    return other_half_sum(lrun);
+  }
+
+  // O^T for the workgroup's queries, normalised
+  __device__ __forceinline__ void run(f32x16 (&oacc)[NMV]) const {
+    f32x16 scur[2];
+    prologue(scur);
+    // every valid query sees at least one key of the first tile
+    const float m0 = other_half_max(masked_max(scur, 0));
+    float ltot = pass(m0, scur, oacc);
+    if (__syncthreads_or(!(ltot <= kOverflow))) {
+      // some logit exceeded the first tile's maximum by 2^63: find the exact
+      // row maximum, then redo the pass with it (every 2^(s - m) <= 1)
+      float mx = kNegInf;
+      for (int kt = 0; kt < ntiles; ++kt) {
+        stage_k(kt, 0);
+        wait_vmem();
+        __syncthreads();
+        f32x16 sc[2];
+        qk(0, sc);
+        mx = fmaxf(mx, masked_max(sc, kt));
+        __syncthreads();
+      }
+      mx = other_half_max(mx);
+#pragma unroll
+      for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
+      prologue(scur);
+      ltot = pass(mx, scur, oacc);
+    }
+    const float inv = 1.f / ltot;
+#pragma unroll
+    for (int i = 0; i < NMV; ++i) oacc[i] *= inv;
+  }
+};
+
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
-  using T = ScaTile<D, DV>;
-  constexpr int KS = D / 16;   // 16-feature k-steps of Q K^T
+  constexpr int KS = D / 16;   // 16-feature k-steps of the readout
   constexpr int NMV = DV / 32; // 32-row blocks of O^T
-  constexpr int KCH = D / 8;   // 16-byte chunks per K row
-  constexpr int VCH = DV / 8;  // 16-byte chunks per V row
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -138,214 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
   for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
 
   if constexpr (kSca) {
-    const uint16_t* vbh = a.v + (size_t)bh * (size_t)n * DV;
-    char* const kbuf = reinterpret_cast<char*>(lds);
-    char* const vbuf = kbuf + 2 * T::KBYTES;
-
-    // ---- query fragments: lane holds query lq, features 16 ks + 8 g + [0, 8)
-    u32x4 qf[KS];
-    {
-      const float* kq = a.kappa_q + h * D;
-      const float* nq = a.nu_q + h * D;
-      const float* kk = a.kappa_k + h * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int f0 = 16 * ks + 8 * g;
-        const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[2 * j] = bf_lo(raw[j]);
-          x[2 * j + 1] = bf_hi(raw[j]);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (kq[f0 + i] * x[i] + nq[f0 + i]) * (kk[f0 + i] * kLog2e);
-        qf[ks] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
-      }
-    }
-
-    const int kbeg = s > 0 ? (s - 1) * c : 0;
-    const int kend = qend;
-    const int ntiles = (kend - kbeg + kBN - 1) / kBN;
-    // tiles whose every key is visible to every query of the workgroup
-    const int nfull = q0 - kbeg >= kBN - 1 ? min(ntiles, (q0 - kbeg + 1) / kBN) : 0;
-
-    // ---- staging offsets (constant over tiles). Load i of wave w covers the
-    // 1 KiB piece 4 i + w of the tile; lane l writes LDS chunk (4 i + w) 64 + l,
-    // which is physical chunk p of row r holding logical chunk p ^ swz(r).
-    uint32_t koff[T::KLOADS], voff[T::VLOADS];
-#pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
-      const int r = P / KCH, p = P % KCH;
-      koff[i] = (uint32_t)(r * D + 8 * (p ^ (r & 7))) * 2u;
-    }
-#pragma unroll
-    for (int i = 0; i < T::VLOADS; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
-      const int r = P / VCH, p = P % VCH;
-      voff[i] = (uint32_t)(r * DV + 8 * (p ^ ((r & 3) << 1))) * 2u;
-    }
-    auto stage_k = [&](int kt, int slot) {
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(zbh, kbeg + kt * kBN, n, D);
-#pragma unroll
-      for (int i = 0; i < T::KLOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(kbuf + slot * T::KBYTES + (4 * i + w) * 1024), 16, koff[i], 0, 0, 0);
-    };
-    auto stage_v = [&](int kt, int slot) {
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(vbh, kbeg + kt * kBN, n, DV);
-#pragma unroll
-      for (int i = 0; i < T::VLOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(vbuf + slot * T::VBYTES + (4 * i + w) * 1024), 16, voff[i], 0, 0, 0);
-    };
-
-    // ---- operand read addresses (bytes, relative to a stage)
-    // K: lane reads row 32 mb + lq, logical chunk 2 ks + g
-    auto k_addr = [&](int mb, int ks) {
-      const int r = 32 * mb + lq;
-      return r * (D * 2) + 16 * ((2 * ks + g) ^ (r & 7));
-    };
-    // V^T block for O rows 32 mv + [0, 32) and P keys of k-step (mb, hh):
-    // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
-    //                                      [32 mv + perm_row(lq)].
-    // Transpose read jj supplies j = 4 jj + j': source lane s of each 16-lane
-    // group points at key 32 mb + 16 hh + 8 jj + 4 g + s / 4 and values
-    // 32 mv + 16 (group % 2) + 4 perm2(s % 4) + [0, 4).
-    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
-    const int perm2 = ((sl & 3) >> 1) | (((sl & 3) & 1) << 1);
-    auto v_addr = [&](int mv, int mb, int hh, int jj) {
-      const int r = 32 * mb + 16 * hh + 8 * jj + 4 * g + (sl >> 2);
-      const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-      return r * (DV * 2) + 16 * ((col >> 3) ^ ((r & 3) << 1)) + 2 * (col & 7);
-    };
-
-    auto qk = [&](int slot, f32x16 (&sa)[2]) {
-      const char* Kb = kbuf + slot * T::KBYTES;
-      sa[0] = f32x16{};
-      sa[1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
-          sa[mb] = mfma_bf16(af, qf[ks], sa[mb]);
-        }
-      }
-    };
-    auto pv = [&](int slot, const u32x4 (&pf)[2][2]) {
-      const char* Vb = vbuf + slot * T::VBYTES;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int mv = 0; mv < NMV; ++mv) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[mb][hh], oacc[mv]);
-          }
-    };
-
-    // one tile: P(kt) from S(kt) while S(kt+1) runs; then O += V(kt)^T P(kt).
-    // accumulator (mb, r) of S holds key kb + 32 mb + 8 (r >> 2) + 4 g + (r & 3)
-    auto tile = [&](int kt, float msub, f32x16 (&scur)[2], float& lrun, auto masked) {
-      stage_k(kt + 2, kt & 1);          // replaces K(kt), read last iteration
-      stage_v(kt + 1, (kt + 1) & 1);    // replaces V(kt-1)
-      f32x16 snext[2];
-      qk((kt + 1) & 1, snext);
-      float e[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[mb][r] = exp2_fast(scur[mb][r] - msub);
-      if constexpr (decltype(masked)::value) {
-        const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);  // last visible key offset
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-            e[mb][r] = ko > lim ? 0.f : e[mb][r];
-          }
-      }
-      u32x4 pf[2][2];
-      float psum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const float* x = e[mb] + 8 * hh;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) psum += x[i];
-          pf[mb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
-        }
-      lrun += psum;
-      pv(kt & 1, pf);
-      wait_vmem();
-      __syncthreads();
-      scur[0] = snext[0];
-      scur[1] = snext[1];
-    };
-
-    // full pipelined pass with a fixed softmax offset; returns the row exp-sum
-    auto pass = [&](float msub, f32x16 (&scur)[2]) {
-      float lrun = 0.f;
-      for (int kt = 0; kt < nfull; ++kt) tile(kt, msub, scur, lrun, std::false_type{});
-      for (int kt = nfull; kt < ntiles; ++kt) tile(kt, msub, scur, lrun, std::true_type{});
-      return other_half_sum(lrun);
-    };
-    auto prologue = [&](f32x16 (&scur)[2]) {
-      stage_k(0, 0);
-      stage_v(0, 0);
-      stage_k(1, 1);
-      wait_vmem();
-      __syncthreads();
-      qk(0, scur);
-    };
-    auto masked_max = [&](const f32x16 (&sc)[2], int kt) {
-      const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);
-      float mx = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-          mx = fmaxf(mx, ko > lim ? kNegInf : sc[mb][r]);
-        }
-      return mx;
-    };
-
-    f32x16 scur[2];
-    prologue(scur);
-    // every valid query sees at least one key of the first tile
-    const float m0 = other_half_max(masked_max(scur, 0));
-    float ltot = pass(m0, scur);
-    if (__syncthreads_or(!(ltot <= kOverflow))) {
-      // some logit exceeded the first tile's maximum by 2^63: find the exact
-      // row maximum, then redo the pass with it (every 2^(s - m) <= 1)
-      __syncthreads();
-      float mx = kNegInf;
-      for (int kt = 0; kt < ntiles; ++kt) {
-        stage_k(kt, 0);
-        wait_vmem();
-        __syncthreads();
-        f32x16 sc[2];
-        qk(0, sc);
-        mx = fmaxf(mx, masked_max(sc, kt));
-        __syncthreads();
-      }
-      mx = other_half_max(mx);
-#pragma unroll
-      for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
-      prologue(scur);
-      ltot = pass(mx, scur);
-    }
-    const float inv = 1.f / ltot;
-#pragma unroll
-    for (int i = 0; i < NMV; ++i) oacc[i] *= inv;
+    ScaLoop<D, DV> L;
+    L.init(a, bh, h, n, s, c, q0, qend, qrow, myq, w, lane, lds);
+    L.run(oacc);
   }
 
   if constexpr (kRead) {
