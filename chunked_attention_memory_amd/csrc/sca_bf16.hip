@@ -6,13 +6,15 @@
 //   O_i = softmax_j(q_i . k_j) v_j over keys j of chunks s-1 and s with j <= i
 //         + psi(Q_m,i) M'_{s-1}            (readout; chunks s >= 3, 1-based)
 //
-// Work decomposition: one workgroup = 128 consecutive queries of one chunk of
-// one (batch, head); 4 waves x 32 queries. The key window [(s-1)c, last query]
-// is streamed in tiles of 64 keys.
+// Work decomposition: one workgroup = 256 consecutive queries of one chunk of
+// one (batch, head); 8 waves x 32 queries, two waves per SIMD so that one
+// wave's exponentials overlap the other's matrix instructions. The key window
+// [(s-1)c, last query] is streamed in tiles of 64 keys, processed as two
+// 32-key halves.
 //
-// Per tile and wave:
-//   S^T (64 keys x 32 queries) = K_tile Q^T       (A = K from LDS, B = Q in VGPRs)
-//   P^T = exp2(S^T - m), lane-local per query (a query's 64 keys are split
+// Per 32-key half-tile and wave:
+//   S^T (32 keys x 32 queries) = K Q^T            (A = K from LDS, B = Q in VGPRs)
+//   P^T = exp2(S^T - m), lane-local per query (a query's 32 keys are split
 //   between lane l and lane l ^ 32)
 //   O^T (dv x 32 queries) += V^T P^T               (A = V^T from LDS, B = P in VGPRs)
 // Holding O transposed keeps each query's accumulator column and its
@@ -21,16 +23,15 @@
 // Staging: K and V tiles go from HBM straight into LDS with buffer loads that
 // write LDS (no registers, out-of-range rows read as zero). Rows are stored
 // dense with their 16-byte chunks XOR-swizzled by row, so that the MFMA
-// operand reads below hit every LDS bank once per 8 lanes. V stays row-major
+// operand reads below hit each of the 64 LDS banks once per pass. V stays row-major
 // in LDS; its transposed MFMA operand comes from the gfx950 LDS transpose
 // read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i
 // of a 4-row x 16-column block).
 //
-// Pipeline: K is staged two tiles ahead and V one tile ahead, so iteration kt
-// computes S for tile kt+1 on the matrix cores while the vector ALUs turn
-// S(kt) into P(kt).
+// Pipeline: tile kt+1 is loaded into the other LDS stage while tile kt is
+// computed.
 //
-// Softmax offset: m is fixed at the row's exact maximum over the first tile
+// Softmax offset: m is fixed at the row's exact maximum over the first 32 keys
 // (2^(s - m) can then grow above 1 but stays far from the fp32/bf16 range);
 // the final exp-sum shows whether any logit exceeded m by 2^63, and only then
 // is the workgroup recomputed with the exact row maximum found by a max-only
@@ -47,9 +48,10 @@
 namespace gecko {
 namespace {
 
-constexpr int kBM = 128;       // queries per workgroup
-constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = 8;              // two waves per SIMD
+constexpr int kBM = 32 * kWaves;       // queries per workgroup
+constexpr int kBN = 64;                // keys per tile
+constexpr int kThreads = 64 * kWaves;
 constexpr float kOverflow = 0x1p63f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -64,6 +66,14 @@ struct ScaTile {
   static constexpr int KLOADS = KBYTES / 16 / kThreads;  // 16-byte loads per thread per tile
   static constexpr int VLOADS = VBYTES / 16 / kThreads;
 };
+
+// XOR swizzles of the 16-byte chunks of a staged row, chosen so that the
+// operand reads below touch each of the 64 LDS banks once per pass (16 lanes
+// for 16-byte reads, 32 lanes for 8-byte transpose reads).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int DV>
+__device__ __forceinline__ int vswz(int r) { return DV >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 struct ScaArgs {
   const uint16_t* z;
@@ -90,7 +100,7 @@ __device__ __forceinline__ float other_half_sum(float x) {
 
 // Copy one key tile (rows [row0, row0 + 64) of a row-major bf16 matrix with
 // `width` columns) into LDS with buffer loads that write LDS directly; rows at
-// or past n read as zero. Load i of this wave fills the 1 KiB piece 4 i + w.
+// or past n read as zero. Load i of wave w fills the 1 KiB piece kWaves i + w.
 // A __device__ function on purpose: the buffer resource type may not appear in
 // a lambda inside the kernel, which is compiled for the host as well.
 __device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile, int w,
@@ -100,7 +110,7 @@ __device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n
       (void*)(base + (size_t)row0 * width), (short)0, (int)(rows * (uint32_t)width * 2u), 0x00020000);
 #pragma unroll
   for (int i = 0; i < nloads; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (4 * i + w) * 1024), 16, off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (kWaves * i + w) * 1024), 16, off[i], 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -120,7 +130,7 @@ struct ScaLoop {
   const uint16_t* vbh;
   char* kbuf;  // two K stages
   char* vbuf;  // two V stages
-  int n, kbeg, kend, ntiles, nfull, myq, w, g, lq, sl, grp2, perm2;
+  int n, kbeg, kend, ntiles, myq, wave_q0, w, g, lq, sl, grp2, perm2;
   u32x4 qf[KS];
   uint32_t koff[T::KLOADS], voff[T::VLOADS];
 
@@ -129,6 +139,7 @@ struct ScaLoop {
     n = n_;
     myq = myq_;
     w = w_;
+    wave_q0 = q0 + 32 * w;
     g = lane >> 5;
     lq = lane & 31;
     zbh = a.z + (size_t)bh * (size_t)n * D;
@@ -158,40 +169,37 @@ struct ScaLoop {
     kbeg = s > 0 ? (s - 1) * c : 0;
     kend = qend;
     ntiles = (kend - kbeg + kBN - 1) / kBN;
-    // tiles whose every key is visible to every query of the workgroup
-    nfull = q0 - kbeg >= kBN - 1 ? min(ntiles, (q0 - kbeg + 1) / kBN) : 0;
 
     // staging offsets (constant over tiles). Load i of wave w covers the
-    // 1 KiB piece 4 i + w of the tile; lane l writes LDS chunk (4 i + w) 64 + l,
-    // which is physical chunk p of row r holding logical chunk p ^ swz(r).
+    // 1 KiB piece kWaves i + w of the tile; lane l writes LDS chunk
+    // (kWaves i + w) 64 + l, which is physical chunk p of row r holding
+    // logical chunk p ^ swz(r).
 #pragma unroll
     for (int i = 0; i < T::KLOADS; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
+      const int P = (kWaves * i + w) * 64 + lane;
       const int r = P / KCH, p = P % KCH;
-      koff[i] = (uint32_t)(r * D + 8 * (p ^ (r & 7))) * 2u;
+      koff[i] = (uint32_t)(r * D + 8 * (p ^ kswz<D>(r))) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < T::VLOADS; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
+      const int P = (kWaves * i + w) * 64 + lane;
       const int r = P / VCH, p = P % VCH;
-      voff[i] = (uint32_t)(r * DV + 8 * (p ^ ((r & 3) << 1))) * 2u;
+      voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
     }
     sl = lane & 15;
     grp2 = (lane >> 4) & 1;
     perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
   }
 
-  __device__ __forceinline__ void stage_k(int kt, int slot) const {
+  __device__ __forceinline__ void stage(int kt, int slot) const {
     stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, w, koff, T::KLOADS);
-  }
-  __device__ __forceinline__ void stage_v(int kt, int slot) const {
     stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, w, voff, T::VLOADS);
   }
 
   // K operand: lane reads row 32 mb + lq, logical chunk 2 ks + g
   __device__ __forceinline__ int k_addr(int mb, int ks) const {
     const int r = 32 * mb + lq;
-    return r * (D * 2) + 16 * ((2 * ks + g) ^ (r & 7));
+    return r * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(r));
   }
   // V^T block for O rows 32 mv + [0, 32) and the P keys of k-step (mb, hh):
   // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
@@ -202,135 +210,121 @@ struct ScaLoop {
   __device__ __forceinline__ int v_addr(int mv, int mb, int hh, int jj) const {
     const int r = 32 * mb + 16 * hh + 8 * jj + 4 * g + (sl >> 2);
     const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-    return r * (DV * 2) + 16 * ((col >> 3) ^ ((r & 3) << 1)) + 2 * (col & 7);
+    return r * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(r)) + 2 * (col & 7);
   }
 
-  __device__ __forceinline__ void qk(int slot, f32x16 (&sa)[2]) const {
+  // S^T for keys 32 mb + [0, 32) of the tile in `slot`:
+  // register r holds key 32 mb + 8 (r >> 2) + 4 g + (r & 3)
+  __device__ __forceinline__ f32x16 qk(int slot, int mb) const {
     const char* Kb = kbuf + slot * T::KBYTES;
-    sa[0] = f32x16{};
-    sa[1] = f32x16{};
+    f32x16 sa = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
-        sa[mb] = mfma_bf16(af, qf[ks], sa[mb]);
-      }
+      const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
+      sa = mfma_bf16(af, qf[ks], sa);
     }
+    return sa;
   }
 
-  __device__ __forceinline__ void pv(int slot, const u32x4 (&pf)[2][2], f32x16 (&oacc)[NMV]) const {
+  __device__ __forceinline__ void pv(int slot, int mb, const u32x4 (&pf)[2], f32x16 (&oacc)[NMV]) const {
     const char* Vb = vbuf + slot * T::VBYTES;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int mv = 0; mv < NMV; ++mv) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[mb][hh], oacc[mv]);
-        }
+      for (int mv = 0; mv < NMV; ++mv) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[hh], oacc[mv]);
+      }
   }
 
-  // accumulator (mb, r) of S holds key kb + 32 mb + 8 (r >> 2) + 4 g + (r & 3)
-  __device__ __forceinline__ float masked_max(const f32x16 (&sc)[2], int kt) const {
-    const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);  // last visible key offset
+  // last visible key offset within tile kt for this lane's query
+  __device__ __forceinline__ int last_visible(int kt) const { return min(myq, kend - 1) - (kbeg + kt * kBN); }
+  __device__ __forceinline__ bool needs_mask(int kt) const {
+    const int kb = kbeg + kt * kBN;
+    return kb + kBN - 1 > wave_q0 || kb + kBN > kend;
+  }
+
+  __device__ __forceinline__ float masked_max(const f32x16& sc, int kt, int mb) const {
+    const int lim = last_visible(kt);
     float mx = kNegInf;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-        mx = fmaxf(mx, ko > lim ? kNegInf : sc[mb][r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+      mx = fmaxf(mx, ko > lim ? kNegInf : sc[r]);
+    }
     return mx;
   }
 
-  // one tile: P(kt) from S(kt) while S(kt+1) runs; then O += V(kt)^T P(kt)
-  __device__ __forceinline__ void tile(int kt, float msub, f32x16 (&scur)[2], float& lrun, bool masked,
-                                       f32x16 (&oacc)[NMV]) const {
-    stage_k(kt + 2, kt & 1);          // replaces K(kt), read last iteration
-    stage_v(kt + 1, (kt + 1) & 1);    // replaces V(kt-1)
-    f32x16 snext[2];
-    qk((kt + 1) & 1, snext);
-    float e[2][16];
+  // one tile: for each 32-key half, S^T, P = 2^(S - m), O^T += V^T P^T
+  __device__ __forceinline__ void tile(int kt, float msub, float& lrun, f32x16 (&oacc)[NMV]) const {
+    const int slot = kt & 1;
+    stage(kt + 1, slot ^ 1);  // replaces tile kt-1, read last iteration
+    const bool masked = needs_mask(kt);
+    const int lim = last_visible(kt);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      const f32x16 sc = qk(slot, mb);
+      float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[mb][r] = exp2_fast(scur[mb][r] - msub);
-    if (masked) {
-      const int lim = min(myq, kend - 1) - (kbeg + kt * kBN);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int r = 0; r < 16; ++r) e[r] = exp2_fast(sc[r] - msub);
+      if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-          e[mb][r] = ko > lim ? 0.f : e[mb][r];
+          e[r] = ko > lim ? 0.f : e[r];
         }
-    }
-    u32x4 pf[2][2];
-    float psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      }
+      u32x4 pf[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const float* x = e[mb] + 8 * hh;
+        const float* x = e + 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) psum += x[i];
-        pf[mb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+        for (int i = 0; i < 8; ++i) lrun += x[i];
+        pf[hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
       }
-    lrun += psum;
-    pv(kt & 1, pf, oacc);
+      pv(slot, mb, pf, oacc);
+    }
     wait_vmem();
     __syncthreads();
-    scur[0] = snext[0];
-    scur[1] = snext[1];
   }
 
-  __device__ __forceinline__ void prologue(f32x16 (&scur)[2]) const {
-    stage_k(0, 0);
-    stage_v(0, 0);
-    stage_k(1, 1);
+  // full pass with a fixed softmax offset; returns the row exp-sum
+  __device__ __forceinline__ float pass(float msub, f32x16 (&oacc)[NMV]) const {
+    stage(0, 0);
     wait_vmem();
     __syncthreads();
-    qk(0, scur);
-  }
-
-  // full pipelined pass with a fixed softmax offset; returns the row exp-sum
-  __device__ __forceinline__ float pass(float msub, f32x16 (&scur)[2], f32x16 (&oacc)[NMV]) const {
     float lrun = 0.f;
-    for (int kt = 0; kt < nfull; ++kt) tile(kt, msub, scur, lrun, false, oacc);
-    for (int kt = nfull; kt < ntiles; ++kt) tile(kt, msub, scur, lrun, true, oacc);
+    for (int kt = 0; kt < ntiles; ++kt) tile(kt, msub, lrun, oacc);
     return other_half_sum(lrun);
   }
 
   // O^T for the workgroup's queries, normalised
   __device__ __forceinline__ void run(f32x16 (&oacc)[NMV]) const {
-    f32x16 scur[2];
-    prologue(scur);
-    // every valid query sees at least one key of the first tile
-    const float m0 = other_half_max(masked_max(scur, 0));
-    float ltot = pass(m0, scur, oacc);
+    // softmax offset: exact row maximum over the first 32 keys of the window
+    // (every valid query sees the first key of its window)
+    stage(0, 0);
+    wait_vmem();
+    __syncthreads();
+    const float m0 = other_half_max(masked_max(qk(0, 0), 0, 0));
+    __syncthreads();
+    float ltot = pass(m0, oacc);
     if (__syncthreads_or(!(ltot <= kOverflow))) {
-      // some logit exceeded the first tile's maximum by 2^63: find the exact
-      // row maximum, then redo the pass with it (every 2^(s - m) <= 1)
+      // some logit exceeded m0 by 2^63: find the exact row maximum, then redo
+      // the pass with it (every 2^(s - m) <= 1)
       float mx = kNegInf;
       for (int kt = 0; kt < ntiles; ++kt) {
-        stage_k(kt, 0);
+        stage(kt, 0);
         wait_vmem();
         __syncthreads();
-        f32x16 sc[2];
-        qk(0, sc);
-        mx = fmaxf(mx, masked_max(sc, kt));
+        mx = fmaxf(mx, fmaxf(masked_max(qk(0, 0), kt, 0), masked_max(qk(0, 1), kt, 1)));
         __syncthreads();
       }
       mx = other_half_max(mx);
 #pragma unroll
       for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
-      prologue(scur);
-      ltot = pass(mx, scur, oacc);
+      ltot = pass(mx, oacc);
     }
     const float inv = 1.f / ltot;
 #pragma unroll
