@@ -23,40 +23,50 @@
 namespace gecko {
 namespace {
 
-constexpr int kBT = 64;          // tokens per tile of the chunk pass
-constexpr float kLazy = 8.0f;    // rescale accumulators only when the max grows by > 2^8
+constexpr int kBT = 64;                 // tokens per tile of the chunk pass
+constexpr float kOverflow = 0x1p63f;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
-
-// reduction over aligned groups of G lanes (G = 8 or 16) with DPP lane swaps
-template <int G>
+// reductions over aligned groups of P = 2 or 4 consecutive lanes
+template <int P>
 __device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-  if constexpr (G == 16) x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+  x = fmaxf(x, dpp<0xB1>(x));                       // quad_perm [1,0,3,2]
+  if constexpr (P == 4) x = fmaxf(x, dpp<0x4E>(x));  // quad_perm [2,3,0,1]
   return x;
 }
-template <int G>
+template <int P>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  if constexpr (G == 16) x += dpp<0x140>(x);
+  if constexpr (P == 4) x += dpp<0x4E>(x);
   return x;
+}
+
+// XOR swizzle of the 16-byte chunks of a staged Z' (and psi) row, chosen so
+// that both the row reads of the psi phase (16 lanes x 16 bytes per pass) and
+// the 4-row transpose reads of the MFMA phase (32 lanes x 8 bytes per pass)
+// touch each of the 64 LDS banks once.
+template <int D>
+__device__ __forceinline__ int zswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | (r & 3);
+  const int rho = (r >> 1) & 3;
+  return rho ^ ((rho & 1) << 2);
 }
 
 template <int D, int DV>
 struct ChunkTile {
-  static constexpr int ROW = kBT + 8;  // LDS row (bf16 elements) of Z^T, psi^T and V^T
-  static constexpr int ZELEMS = D * ROW;
-  static constexpr int PELEMS = D * ROW;
-  static constexpr int VELEMS = DV * ROW;
-  static constexpr size_t LDS_BYTES = (size_t)(ZELEMS + PELEMS + VELEMS) * sizeof(uint16_t);
-  static constexpr int THREADS = 2 * D;  // D / 32 waves, one 32-feature block each
+  static constexpr int NW = D / 32;          // one wave per 32 key features
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int ZBYTES = kBT * D * 2;
+  static constexpr int VBYTES = kBT * DV * 2;
+  static constexpr int ZLOADS = ZBYTES / 16 / THREADS;
+  static constexpr int VLOADS = VBYTES / 16 / THREADS;
+  static constexpr int PARTS = THREADS / kBT;  // threads per token row in the psi phase (32 features each)
+  static constexpr int STAGE = ZBYTES + VBYTES;
+  // two (Z', V) stages, the psi tile, then the (log2-scaled) eta_k and rho_k vectors
+  static constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + ZBYTES + 2 * D * sizeof(float);
 };
 
 struct ChunkArgs {
@@ -74,170 +84,259 @@ struct ChunkArgs {
 
 // One workgroup per (batch*head, chunk t). Wave w owns key features
 // [32 w, 32 w + 32) and accumulates, transposed,
-//   G^T (dv x 32) += V^T E and H^T (d x 32) += psi^T E
-// over 64-token tiles, with E = exp(K_m - m) under a running per-feature max.
+//   G^T (dv x 32) += V^T E  and  H^T (d x 32) += psi^T E
+// over 64-token tiles, E = 2^(K_m log2(e) - m) with m fixed per feature at the
+// exact maximum over the chunk's first tile (a final exp-sum above 2^63 sends
+// the workgroup through an exact-maximum recompute). Per tile: Z' and V are
+// staged straight into LDS; the psi phase writes psi(K_m) for the tile's 64
+// tokens into LDS (computed once, shared by the waves); the MFMA phase forms
+// E from transpose reads of Z' and reads V^T and psi^T with transpose reads.
+// Member functions rather than lambdas: lambdas in a kernel are compiled for
+// the host too, where the buffer and LDS builtins do not exist.
+template <int D, int DV>
+struct ChunkLoop {
+  using T = ChunkTile<D, DV>;
+  static constexpr int NMV = DV / 32;
+  static constexpr int NMF = D / 32;
+  const uint16_t* zbh;
+  const uint16_t* vbh;
+  char* st;  // stage s: Z' tile at st + s STAGE, V tile after it
+  char* ps;
+  const float* e2s;  // eta_k * log2(e), in LDS
+  const float* r2s;  // rho_k * log2(e), in LDS
+  int n, cbeg, cend, ntiles, w, lane, g, lq, sl, g2;
+  float ekf, rkf;  // this lane's feature
+  uint32_t zoff[T::ZLOADS], voff[T::VLOADS];
+
+  __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* lds) {
+    const int h = (int)(bh % a.H);
+    n = (int)a.n;
+    cbeg = (int)(t * a.c);
+    cend = cbeg + (int)a.c;  // chunks 0..nmem-1 are full
+    ntiles = (int)((a.c + kBT - 1) / kBT);
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    g = lane >> 5;
+    lq = lane & 31;
+    sl = lane & 15;
+    g2 = (lane >> 4) & 1;
+    zbh = a.z + (size_t)bh * (size_t)n * D;
+    vbh = a.v + (size_t)bh * (size_t)n * DV;
+    st = lds;
+    ps = st + 2 * T::STAGE;
+    float* e2 = reinterpret_cast<float*>(ps + T::ZBYTES);
+    float* r2 = e2 + D;
+    if (tid < D) {
+      e2[tid] = a.eta_k[h * D + tid] * kLog2e;
+      r2[tid] = a.rho_k[h * D + tid] * kLog2e;
+    }
+    e2s = e2;
+    r2s = r2;
+    const int f = 32 * w + lq;
+    ekf = a.eta_k[h * D + f] * kLog2e;
+    rkf = a.rho_k[h * D + f] * kLog2e;
+#pragma unroll
+    for (int i = 0; i < T::ZLOADS; ++i) {
+      const int P = (T::NW * i + w) * 64 + lane;
+      const int r = P / (D / 8), p = P % (D / 8);
+      zoff[i] = (uint32_t)(r * D + 8 * (p ^ zswz<D>(r))) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < T::VLOADS; ++i) {
+      const int P = (T::NW * i + w) * 64 + lane;
+      const int r = P / (DV / 8), p = P % (DV / 8);
+      voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
+    }
+  }
+
+  __device__ __forceinline__ const char* zs(int slot) const { return st + slot * T::STAGE; }
+  __device__ __forceinline__ const char* vs(int slot) const { return st + slot * T::STAGE + T::ZBYTES; }
+  __device__ __forceinline__ void stage_z(int it, int slot) const {
+    stage_rows(zbh, cbeg + it * kBT, n, D, st + slot * T::STAGE, T::NW, w, zoff, T::ZLOADS);
+  }
+  __device__ __forceinline__ void stage_v(int it, int slot) const {
+    stage_rows(vbh, cbeg + it * kBT, n, DV, st + slot * T::STAGE + T::ZBYTES, T::NW, w, voff, T::VLOADS);
+  }
+
+  // Transpose-read operand: element j of lane (lq, g) is M[16 ks + 8 g + j][32 blk + lq]
+  // for a row-major staged tile M with `width` columns and swizzle `swz`.
+  // Read jj supplies j = 4 jj + j': source lane s of each 16-lane group points
+  // at row 16 ks + 8 g + 4 jj + s / 4 and columns 32 blk + 16 (group % 2) + 4 (s % 4).
+  template <int WIDTH, bool kZ>
+  __device__ __forceinline__ u32x4 tr_operand(const char* base, int blk, int ks) const {
+    u32x2 part[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int r = 16 * ks + 8 * g + 4 * jj + (sl >> 2);
+      const int col = 32 * blk + 16 * g2 + 4 * (sl & 3);
+      const int sw = kZ ? zswz<D>(r) : vswz<DV>(r);
+      part[jj] = lds_read_tr(base + r * WIDTH * 2 + 16 * ((col >> 3) ^ sw) + 2 * (col & 7));
+    }
+    return u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
+  }
+
+  // K_m of this lane's feature (log2 units) for tokens 16 ks + 8 g + [0, 8) of the tile in `slot`
+  __device__ __forceinline__ void keys(int slot, int ks, float (&k)[8]) const {
+    const u32x4 zr = tr_operand<D, true>(zs(slot), w, ks);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      k[2 * j] = ekf * bf_lo(zr[j]) + rkf;
+      k[2 * j + 1] = ekf * bf_hi(zr[j]) + rkf;
+    }
+  }
+
+  // maximum of this lane's keys over the valid tokens of tile it, staged in `slot`
+  __device__ __forceinline__ float tile_max(int it, int slot) const {
+    const int valid = cend - (cbeg + it * kBT);  // tokens of the tile inside the chunk
+    float mx = kNegInf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float k[8];
+      keys(slot, ks, k);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, 16 * ks + 8 * g + j < valid ? k[j] : kNegInf);
+    }
+    return mx;
+  }
+
+  // psi(K_m) for the tile's tokens into LDS: thread -> token tid / PARTS,
+  // features 32 (tid % PARTS) + [0, 32)
+  __device__ __forceinline__ void psi_phase(int slot) const {
+    const int tid = threadIdx.x;
+    const int tk = tid / T::PARTS, q = tid % T::PARTS;
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(zs(slot) + tk * D * 2 + 16 * ((4 * q + k) ^ zswz<D>(tk)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * k + 2 * j] = bf_lo(raw[j]);
+        x[8 * k + 2 * j + 1] = bf_hi(raw[j]);
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int f4 = 0; f4 < 8; ++f4) {
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(e2s + 32 * q + 4 * f4);
+      const f32x4 r4 = *reinterpret_cast<const f32x4*>(r2s + 32 * q + 4 * f4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[4 * f4 + i] = e4[i] * x[4 * f4 + i] + r4[i];
+        mx = fmaxf(mx, x[4 * f4 + i]);
+      }
+    }
+    mx = group_max<T::PARTS>(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      x[f] = exp2_fast(x[f] - mx);
+      sm += x[f];
+    }
+    sm = group_sum<T::PARTS>(sm);
+    const float inv = 1.f / sm;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float* y = x + 8 * k;
+      const u32x4 pk{pack2(y[0] * inv, y[1] * inv), pack2(y[2] * inv, y[3] * inv), pack2(y[4] * inv, y[5] * inv),
+                     pack2(y[6] * inv, y[7] * inv)};
+      *reinterpret_cast<u32x4*>(ps + tk * D * 2 + 16 * ((4 * q + k) ^ zswz<D>(tk))) = pk;
+    }
+  }
+
+  // E for k-step ks, accumulate its sum, and the two products
+  __device__ __forceinline__ void mfma_phase(int it, int slot, float msub, float& lsum, f32x16 (&accg)[NMV],
+                                             f32x16 (&acch)[NMF]) const {
+    const int valid = cend - (cbeg + it * kBT);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float k[8];
+      keys(slot, ks, k);
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = 16 * ks + 8 * g + j < valid ? exp2_fast(k[j] - msub) : 0.f;
+        lsum += e[j];
+      }
+      const u32x4 ef{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+#pragma unroll
+      for (int mv = 0; mv < NMV; ++mv) accg[mv] = mfma_bf16(tr_operand<DV, false>(vs(slot), mv, ks), ef, accg[mv]);
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf) acch[mf] = mfma_bf16(tr_operand<D, true>(ps, mf, ks), ef, acch[mf]);
+    }
+  }
+
+  // one pass over the chunk with a fixed per-feature offset; returns the
+  // exp-sum. Expects tile 0 staged in slot 0; tile it+1 loads while tile it
+  // is computed.
+  __device__ __forceinline__ float pass(float msub, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF]) const {
+    float lsum = 0.f;
+    for (int it = 0; it < ntiles; ++it) {
+      const int slot = it & 1;
+      if (it + 1 < ntiles) {
+        stage_z(it + 1, slot ^ 1);  // replaces tile it-1, whose reads are done
+        stage_v(it + 1, slot ^ 1);
+      }
+      psi_phase(slot);
+      __syncthreads();
+      mfma_phase(it, slot, msub, lsum, accg, acch);
+      wait_vmem();
+      __syncthreads();
+    }
+    return other_half_sum(lsum);
+  }
+};
+
 template <int D, int DV>
 __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
   using T = ChunkTile<D, DV>;
   constexpr int NMV = DV / 32;
   constexpr int NMF = D / 32;
-  constexpr int FG = D / 8;   // 8-feature groups per token row
-  constexpr int VG = DV / 8;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* Zt = lds;                 // [d][ROW]  raw z, token-contiguous
-  uint16_t* Pt = Zt + T::ZELEMS;      // [d][ROW]  psi(K_m)^T
-  uint16_t* Vt = Pt + T::PELEMS;      // [dv][ROW] V^T
-
+  extern __shared__ __attribute__((aligned(16))) char clds[];
   const int64_t bh = blockIdx.x / a.nmem;
   const int64_t t = blockIdx.x % a.nmem;
-  const int h = (int)(bh % a.H);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
-  const int64_t n = a.n;
-  const int64_t cbeg = t * a.c;
-  const int64_t cend = cbeg + a.c;  // chunks 0..nmem-1 are full
-  const uint16_t* zbh = a.z + bh * n * D;
-  const uint16_t* vbh = a.v + bh * n * DV;
-  const float* ek = a.eta_k + h * D;
-  const float* rk = a.rho_k + h * D;
-
-  // this lane's feature in the MFMA phase
-  const int f = 32 * w + lq;
-  const float ekf = ek[f] * kLog2e, rkf = rk[f] * kLog2e;
+  ChunkLoop<D, DV> L;
+  L.init(a, bh, t, clds);
 
   f32x16 accg[NMV], acch[NMF];
 #pragma unroll
   for (int i = 0; i < NMV; ++i) accg[i] = f32x16{};
 #pragma unroll
   for (int i = 0; i < NMF; ++i) acch[i] = f32x16{};
-  float mrun = kNegInf, lrun = 0.f;
 
-  const int ntiles = (int)((a.c + kBT - 1) / kBT);
-  for (int it = 0; it < ntiles; ++it) {
-    const int64_t tb = cbeg + (int64_t)it * kBT;
-    __syncthreads();  // previous tile's LDS reads are done
-    // ---- stage Z^T and psi^T: thread b < D owns 8 tokens x 8 features
-    if (tid < D) {
-      const int tg = tid / FG, fg = tid % FG;
-      u32x4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t tok = tb + 8 * tg + i;
-        raw[i] = tok < cend ? ld16(zbh + tok * D + 8 * fg) : u32x4{};
-      }
-      u32x4 tr[8];
-      transpose8x8(raw, tr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st16(Zt + (8 * fg + j) * T::ROW + 8 * tg, tr[j]);
-      // memory keys of this block (log2 units) and the row softmax psi
-      float e2[8], r2[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        e2[j] = ek[8 * fg + j] * kLog2e;
-        r2[j] = rk[8 * fg + j] * kLog2e;
-      }
-      u32x4 prow[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float km[8];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          km[2 * jj] = e2[2 * jj] * bf_lo(raw[i][jj]) + r2[2 * jj];
-          km[2 * jj + 1] = e2[2 * jj + 1] * bf_hi(raw[i][jj]) + r2[2 * jj + 1];
-        }
-        float mx = km[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, km[j]);
-        mx = group_max<FG>(mx);
-        float sm = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          km[j] = exp2_fast(km[j] - mx);
-          sm += km[j];
-        }
-        sm = group_sum<FG>(sm);
-        const float inv = 1.f / sm;
-        prow[i] = u32x4{pack2(km[0] * inv, km[1] * inv), pack2(km[2] * inv, km[3] * inv),
-                        pack2(km[4] * inv, km[5] * inv), pack2(km[6] * inv, km[7] * inv)};
-      }
-      transpose8x8(prow, tr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st16(Pt + (8 * fg + j) * T::ROW + 8 * tg, tr[j]);
+  L.stage_z(0, 0);
+  L.stage_v(0, 0);
+  wait_vmem();
+  __syncthreads();
+  float m = other_half_max(L.tile_max(0, 0));  // the first token is always valid
+  float ltot = L.pass(m, accg, acch);
+  if (__syncthreads_or(!(ltot <= kOverflow))) {
+    // a key exceeded the first tile's maximum by 2^63: exact maximum, then redo
+    float mx = kNegInf;
+    for (int it = 0; it < L.ntiles; ++it) {
+      L.stage_z(it, 0);
+      wait_vmem();
+      __syncthreads();
+      mx = fmaxf(mx, L.tile_max(it, 0));
+      __syncthreads();
     }
-    // ---- stage V^T: 8x8 blocks spread over all threads
-    for (int b = (tid + D) % (2 * D); b < DV; b += 2 * D) {
-      const int vtg = b / VG, vg = b % VG;
-      u32x4 raw[8];
+    m = other_half_max(mx);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t tok = tb + 8 * vtg + i;
-        raw[i] = tok < cend ? ld16(vbh + tok * DV + 8 * vg) : u32x4{};
-      }
-      u32x4 tr[8];
-      transpose8x8(raw, tr);
+    for (int i = 0; i < NMV; ++i) accg[i] = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st16(Vt + (8 * vg + j) * T::ROW + 8 * vtg, tr[j]);
-    }
+    for (int i = 0; i < NMF; ++i) acch[i] = f32x16{};
+    L.stage_z(0, 0);
+    L.stage_v(0, 0);
+    wait_vmem();
     __syncthreads();
-
-    // ---- E fragments for feature f: tokens 16 ks + 8 g + [0, 8)
-    float km[32];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 zr = ld16(Zt + f * T::ROW + 16 * ks + 8 * g);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        km[8 * ks + 2 * jj] = ekf * bf_lo(zr[jj]) + rkf;
-        km[8 * ks + 2 * jj + 1] = ekf * bf_hi(zr[jj]) + rkf;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (tb + 16 * ks + 8 * g + i >= cend) km[8 * ks + i] = kNegInf;
-        tmax = fmaxf(tmax, km[8 * ks + i]);
-      }
-    }
-    tmax = fmaxf(tmax, wave_xor32(tmax));
-    const float mnew = fmaxf(mrun, tmax);
-    if (__any(mnew > mrun + kLazy)) {
-      const float alpha = (mnew == kNegInf) ? 1.f : exp2_fast(mrun - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int i = 0; i < NMV; ++i) accg[i] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NMF; ++i) acch[i] *= alpha;
-      mrun = mnew;
-    }
-    const float msub = (mrun == kNegInf) ? 0.f : mrun;
-    u32x4 ef[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = exp2_fast(km[8 * ks + i] - msub);
-        lrun += e[i];
-      }
-      ef[ks] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mv = 0; mv < NMV; ++mv) {
-        const u32x4 af = ld16(Vt + (32 * mv + lq) * T::ROW + 16 * ks + 8 * g);
-        accg[mv] = mfma_bf16(af, ef[ks], accg[mv]);
-      }
-#pragma unroll
-      for (int mf = 0; mf < NMF; ++mf) {
-        const u32x4 af = ld16(Pt + (32 * mf + lq) * T::ROW + 16 * ks + 8 * g);
-        acch[mf] = mfma_bf16(af, ef[ks], acch[mf]);
-      }
-    }
+    ltot = L.pass(m, accg, acch);
   }
 
-  const float ltot = lrun + wave_xor32(lrun);
+  const int f = 32 * L.w + L.lq;
+  const int g = L.g;
   const int64_t row = bh * a.nmem + t;
   if (g == 0) {
-    a.cmax[row * D + f] = mrun;
+    a.cmax[row * D + f] = m;
     a.csum[row * D + f] = ltot;
   }
   // accumulator (block, r): column f, row 8 (r >> 2) + 4 g + (r & 3) of the block
@@ -261,24 +360,43 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------- z prefix
 // One thread per (batch*head, feature): running z^t = 2^M L in log2 space.
-__global__ void awm_zscan_kernel(const float* cmax, const float* csum, float* decay, float* wscale,
-                                 int64_t nmem, int D) {
-  const int64_t bh = blockIdx.x;
+// Loads are batched ahead of the dependent recurrence.
+__global__ void awm_zscan_kernel(const float* __restrict__ cmax, const float* __restrict__ csum,
+                                 float* __restrict__ decay, float* __restrict__ wscale, int64_t nmem, int D) {
+  constexpr int kBatch = 8;
   const int f = threadIdx.x;
   if (f >= D) return;
+  const int64_t off = (int64_t)blockIdx.x * nmem * D + f;
+  const float* pm = cmax + off;
+  const float* pl = csum + off;
+  float* pd = decay + off;
+  float* pw = wscale + off;
   float M = kNegInf, L = 0.f;
-  const int64_t base = bh * nmem * D + f;
-  for (int64_t t = 0; t < nmem; ++t) {
-    const float m = cmax[base + t * D];
-    const float l = csum[base + t * D];
-    const float Mn = fmaxf(M, m);
-    const float old = (M == kNegInf) ? 0.f : L * exp2_fast(M - Mn);
-    const float cur = l * exp2_fast(m - Mn);
-    const float Ln = old + cur;
-    decay[base + t * D] = old / Ln;              // z^{t-1} / z^t
-    wscale[base + t * D] = exp2_fast(m - Mn) / Ln;  // 2^{m_t} / z^t
-    M = Mn;
-    L = Ln;
+  for (int64_t t0 = 0; t0 < nmem; t0 += kBatch) {
+    const int cnt = (int)min((int64_t)kBatch, nmem - t0);
+    float mb[kBatch], lb[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      mb[j] = j < cnt ? pm[j * D] : 0.f;
+      lb[j] = j < cnt ? pl[j * D] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < cnt) {
+        const float Mn = fmaxf(M, mb[j]);
+        const float old = (M == kNegInf) ? 0.f : L * exp2_fast(M - Mn);
+        const float cur = exp2_fast(mb[j] - Mn);
+        const float Ln = old + lb[j] * cur;
+        pd[j * D] = old / Ln;  // z^{t-1} / z^t
+        pw[j * D] = cur / Ln;  // 2^{m_t} / z^t
+        M = Mn;
+        L = Ln;
+      }
+    }
+    pm += kBatch * D;
+    pl += kBatch * D;
+    pd += kBatch * D;
+    pw += kBatch * D;
   }
 }
 
@@ -293,72 +411,77 @@ struct ScanArgs {
   int no_delta;    // drop the H_t M' term (test variant)
 };
 
+// Operands of one scan step, loaded ahead of use.
+template <int D>
+struct ScanStep {
+  static constexpr int KS = D / 16;
+  u32x4 hf[KS];  // rows 32 w + lq of H_t, features 16 ks + 8 g + [0, 8)
+  float gv[16], dc[16], ws[16];
+};
+
 // One workgroup per (batch*head, 32-column slice of M'). Wave w keeps rows
 // [32 w, 32 w + 32) of the slice in fp32 registers (MFMA accumulator layout);
 // a bf16 copy of the whole slice goes through LDS each step as the B operand
-// of H_t M' and is written out as the snapshot that chunk t + 2 reads.
+// of H_t M' and is written out as the snapshot that chunk t + 2 reads. Step
+// operands are prefetched kDepth steps ahead; block b handles slice b / BH
+// of batch*head b % BH, so with BH a multiple of 8 all slices of a head run
+// on one XCD and share its L2.
 template <int D, int DV>
 __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
   constexpr int NMV = DV / 32;
   constexpr int KS = D / 16;
   constexpr int MROW = D + 8;
+  constexpr int kDepth = 4;
   __shared__ __attribute__((aligned(16))) uint16_t mt[2][32 * MROW];
 
-  const int64_t bh = blockIdx.x / NMV;
-  const int j = (int)(blockIdx.x % NMV);
+  const int64_t BH = gridDim.x / NMV;
+  const int64_t bh = blockIdx.x % BH;
+  const int j = (int)(blockIdx.x / BH);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int64_t nmem = a.nmem;
 
-  f32x16 mst = f32x16{};
-  // operands of step t, loaded one step ahead
-  u32x4 hf[KS];
-  float gv[16], dc[16], ws[16];
-  auto load_step = [&](int64_t t, u32x4 (&hq)[KS], float (&gq)[16], float (&dq)[16], float (&wq)[16]) {
+  auto load_step = [&](int64_t t, ScanStep<D>& q) {
     const int64_t row = bh * nmem + t;
     const uint16_t* ht = a.hm + row * (int64_t)D * D + (int64_t)(32 * w + lq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) hq[ks] = ld16(ht + 16 * ks + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(ht + 16 * ks + 8 * g);
     const float* gt = a.g + ((row * NMV + j) * D) * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int fr = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-      gq[r] = gt[(int64_t)fr * 32 + lq];
+      q.gv[r] = gt[(int64_t)fr * 32 + lq];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int fr = 32 * w + 8 * q + 4 * g;
+    for (int qq = 0; qq < 4; ++qq) {
+      const int fr = 32 * w + 8 * qq + 4 * g;
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(a.decay + row * D + fr);
       const f32x4 w4 = *reinterpret_cast<const f32x4*>(a.wscale + row * D + fr);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dq[4 * q + i] = d4[i];
-        wq[4 * q + i] = w4[i];
+        q.dc[4 * qq + i] = d4[i];
+        q.ws[4 * qq + i] = w4[i];
       }
     }
   };
 
-  load_step(0, hf, gv, dc, ws);
+  f32x16 mst = f32x16{};
   int buf = 0;
-  for (int64_t t = 0; t < nmem; ++t) {
-    u32x4 hn[KS];
-    float gn[16], dn[16], wn[16];
-    if (t + 1 < nmem) load_step(t + 1, hn, gn, dn, wn);
-
+  auto step = [&](int64_t t, const ScanStep<D>& q) {
     f32x16 p0 = f32x16{}, p1 = f32x16{};
     if (t > 0 && !a.no_delta) {
 #pragma unroll
       for (int ks = 0; ks < KS; ks += 2) {
-        p0 = mfma_bf16(hf[ks], ld16(&mt[buf][lq * MROW + 16 * ks + 8 * g]), p0);
-        p1 = mfma_bf16(hf[ks + 1], ld16(&mt[buf][lq * MROW + 16 * (ks + 1) + 8 * g]), p1);
+        p0 = mfma_bf16(q.hf[ks], ld16(&mt[buf][lq * MROW + 16 * ks + 8 * g]), p0);
+        p1 = mfma_bf16(q.hf[ks + 1], ld16(&mt[buf][lq * MROW + 16 * (ks + 1) + 8 * g]), p1);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mst[r] = dc[r] * mst[r] + ws[r] * (gv[r] - (p0[r] + p1[r]));
-    // bf16 copy: row v = lq of the slice, features 32 w + 8 q + 4 g + [0, 4)
+    for (int r = 0; r < 16; ++r) mst[r] = q.dc[r] * mst[r] + q.ws[r] * (q.gv[r] - (p0[r] + p1[r]));
+    // bf16 copy: row v = lq of the slice, features 32 w + 8 qq + 4 g + [0, 4)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x2 pk{pack2(mst[4 * q], mst[4 * q + 1]), pack2(mst[4 * q + 2], mst[4 * q + 3])};
-      *reinterpret_cast<u32x2*>(&mt[buf ^ 1][lq * MROW + 32 * w + 8 * q + 4 * g]) = pk;
+    for (int qq = 0; qq < 4; ++qq) {
+      const u32x2 pk{pack2(mst[4 * qq], mst[4 * qq + 1]), pack2(mst[4 * qq + 2], mst[4 * qq + 3])};
+      *reinterpret_cast<u32x2*>(&mt[buf ^ 1][lq * MROW + 32 * w + 8 * qq + 4 * g]) = pk;
     }
     __syncthreads();
     // snapshot rows 32 j .. 32 j + 31 of M'_{t+2}^T
@@ -368,14 +491,19 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
       st16(sn + (int64_t)r * D + cc, ld16(&mt[buf ^ 1][r * MROW + cc]));
     }
     buf ^= 1;
-    if (t + 1 < nmem) {
+  };
+
+  ScanStep<D> ring[kDepth];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) hf[ks] = hn[ks];
+  for (int k = 0; k < kDepth; ++k)
+    if (k < nmem) load_step(k, ring[k]);
+  for (int64_t t0 = 0; t0 < nmem; t0 += kDepth) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        gv[r] = gn[r];
-        dc[r] = dn[r];
-        ws[r] = wn[r];
+    for (int k = 0; k < kDepth; ++k) {
+      const int64_t t = t0 + k;
+      if (t < nmem) {
+        step(t, ring[k]);
+        if (t + kDepth < nmem) load_step(t + kDepth, ring[k]);
       }
     }
   }

@@ -72,4 +72,50 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Sum / max of a value with the same lane of the other 32-lane half.
+__device__ __forceinline__ float other_half_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copy rows [row0, row0 + rows_in_tile) of a row-major bf16 matrix with `width`
+// columns into LDS with buffer loads that write LDS directly (lane l of a
+// load lands at 16 l bytes past the load's LDS base); rows at or past n read
+// as zero. Load i of wave w fills the 1 KiB piece nwaves i + w of the tile;
+// off[i] is the byte offset, within the rows starting at row0, that this lane
+// fetches for load i. A plain __device__ function on purpose: the buffer
+// resource type may not appear in a lambda inside a kernel, which is also
+// compiled for the host.
+__device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile,
+                                           int nwaves, int w, const uint32_t* off, int nloads) {
+  const uint32_t rows = (uint32_t)(n > row0 ? n - row0 : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + (size_t)row0 * width), (short)0, (int)(rows * (uint32_t)width * 2u), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < nloads; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (nwaves * i + w) * 1024), 16, off[i], 0, 0, 0);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): in each 16-lane group,
+// source lane s addresses 4 consecutive bf16 values M[s][0..3]; lane i
+// receives M[4 j + i / 4][i % 4] for j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
+// XOR swizzle of the 16-byte chunks of a staged row-major V row (dv values),
+// for transpose reads of 4 rows x 32 columns (32 lanes per pass, 64 banks).
+template <int DV>
+__device__ __forceinline__ int vswz(int r) { return DV >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+
 }  // namespace gecko

@@ -54,10 +54,6 @@ constexpr int kBN = 64;                // keys per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr float kOverflow = 0x1p63f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 template <int D, int DV>
 struct ScaTile {
   static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
@@ -67,13 +63,11 @@ struct ScaTile {
   static constexpr int VLOADS = VBYTES / 16 / kThreads;
 };
 
-// XOR swizzles of the 16-byte chunks of a staged row, chosen so that the
-// operand reads below touch each of the 64 LDS banks once per pass (16 lanes
-// for 16-byte reads, 32 lanes for 8-byte transpose reads).
+// XOR swizzle of the 16-byte chunks of a staged K row, chosen so that the
+// 16-byte operand reads below touch each of the 64 LDS banks once per pass of
+// 16 lanes (V rows use vswz, for the 8-byte transpose reads).
 template <int D>
 __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int DV>
-__device__ __forceinline__ int vswz(int r) { return DV >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 struct ScaArgs {
   const uint16_t* z;
@@ -88,32 +82,6 @@ struct ScaArgs {
   int64_t n;
   int c, nchunks, nmem, qtiles, nblocks, per_xcd, H;
 };
-
-__device__ __forceinline__ float other_half_max(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-__device__ __forceinline__ float other_half_sum(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-// Copy one key tile (rows [row0, row0 + 64) of a row-major bf16 matrix with
-// `width` columns) into LDS with buffer loads that write LDS directly; rows at
-// or past n read as zero. Load i of wave w fills the 1 KiB piece kWaves i + w.
-// A __device__ function on purpose: the buffer resource type may not appear in
-// a lambda inside the kernel, which is compiled for the host as well.
-__device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile, int w,
-                                           const uint32_t* off, int nloads) {
-  const uint32_t rows = (uint32_t)(n > row0 ? n - row0 : 0);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + (size_t)row0 * width), (short)0, (int)(rows * (uint32_t)width * 2u), 0x00020000);
-#pragma unroll
-  for (int i = 0; i < nloads; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (kWaves * i + w) * 1024), 16, off[i], 0, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // The attention loop of one workgroup. Member functions rather than lambdas:
 // lambdas inside a kernel are compiled for the host too, where the buffer and
@@ -192,8 +160,8 @@ struct ScaLoop {
   }
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
-    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, w, koff, T::KLOADS);
-    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, w, voff, T::VLOADS);
+    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, kWaves, w, koff, T::KLOADS);
+    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, kWaves, w, voff, T::VLOADS);
   }
 
   // K operand: lane reads row 32 mb + lq, logical chunk 2 ks + g
@@ -232,9 +200,8 @@ struct ScaLoop {
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int mv = 0; mv < NMV; ++mv) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 0)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + v_addr(mv, mb, hh, 1)));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x2 l2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 0));
+        const u32x2 h2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 1));
         oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[hh], oacc[mv]);
       }
   }
