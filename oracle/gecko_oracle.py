@@ -122,22 +122,26 @@ def _window(n: int, c: int, s: int) -> tuple[int, int, int]:
 def sca_head(z, v, kappa_q, nu_q, kappa_k, nu_k, c: int, chunks=None) -> np.ndarray:
     """O_SCA for one head: z [n, d], v [n, dv], affine vectors [d].
 
-    Returns float64 [n, dv]. If ``chunks`` (0-based chunk indices) is given,
-    only those chunks' rows are computed and the other rows are NaN.
+    Returns float64 [n, dv]; or, if ``chunks`` (0-based chunk indices) is
+    given, a dict mapping each of those chunks to its rows.
     """
     n = z.shape[0]
-    out = np.full((n, v.shape[1]), np.nan)
+    out = np.empty((n, v.shape[1])) if chunks is None else {}
     nchunks = len(chunk_ranges(n, c))
     for s in (range(nchunks) if chunks is None else chunks):
         k0, q0, q1 = _window(n, c, s)
         q = affine(z[q0:q1], kappa_q, nu_q)
         k = affine(z[k0:q1], kappa_k, nu_k)
-        out[q0:q1] = sca_chunk(q, k, v[k0:q1], np.arange(q0, q1), np.arange(k0, q1))
+        rows = sca_chunk(q, k, v[k0:q1], np.arange(q0, q1), np.arange(k0, q1))
+        if chunks is None:
+            out[q0:q1] = rows
+        else:
+            out[s] = rows
     return out
 
 
 def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
-             trace=None) -> np.ndarray:
+             trace=None, readout_chunks=None):
     """O_m for one head: z [n, d], v [n, dv], affine vectors [d].
 
     Follows [rainbus "Method steps" (4)-(5)] and [rainbus "Core method"],
@@ -159,18 +163,28 @@ def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
 
     ``trace``, if a list, receives one dict per chunk s (1-based) with the
     float64 z^s, phi^s(K_s) and M'_{s-1} used by the readout.
+
+    Returns float64 [n, dv]; or, if ``readout_chunks`` (0-based chunk indices)
+    is given, a dict mapping each of those chunks to its rows (the memory
+    still passes through every chunk; only the readout is restricted, which
+    keeps long sequences within host memory).
     """
     n, d = z.shape
     dv = v.shape[1]
-    out = np.zeros((n, dv))
+    wanted = None if readout_chunks is None else set(readout_chunks)
+    out = np.zeros((n, dv)) if wanted is None else {}
     ranges = chunk_ranges(n, c)
     z_prev = np.zeros(d)              # z^{s-1}
     mem_prev = np.zeros((d, dv))      # M'_{s-1}
     mem_cur = np.zeros((d, dv))       # M'_s
     for s, (a, b) in enumerate(ranges, start=1):
         # readout of chunk s from M'_{s-1}
-        qm = affine(z[a:b], eta_q, rho_q)
-        out[a:b] = feature_softmax(qm) @ mem_prev
+        if wanted is None or s - 1 in wanted:
+            rows = feature_softmax(affine(z[a:b], eta_q, rho_q)) @ mem_prev
+            if wanted is None:
+                out[a:b] = rows
+            else:
+                out[s - 1] = rows
         # chunk s enters the memory: z^s, then M'_{s+1} from M'_s
         km = affine(z[a:b], eta_k, rho_k)
         ek = np.exp(km)
@@ -192,13 +206,16 @@ def forward_head(z, v, p: dict, h: int, c: int, no_delta: bool = False,
                  sca_chunks=None) -> dict:
     """O = O_SCA + O_m for head h of one batch row ([rainbus "Method steps" (5)], R8).
 
-    ``p`` maps the eight affine-vector names to [H, d] arrays.
+    ``p`` maps the eight affine-vector names to [H, d] arrays. With
+    ``sca_chunks`` (0-based) every entry is a dict of those chunks' rows.
     """
     o_sca = sca_head(z, v, p["kappa_q"][h], p["nu_q"][h], p["kappa_k"][h], p["nu_k"][h],
                      c, chunks=sca_chunks)
     o_m = awm_head(z, v, p["eta_q"][h], p["rho_q"][h], p["eta_k"][h], p["rho_k"][h],
-                   c, no_delta=no_delta)
-    return {"o_sca": o_sca, "o_m": o_m, "o": o_sca + o_m}
+                   c, no_delta=no_delta, readout_chunks=sca_chunks)
+    if sca_chunks is None:
+        return {"o_sca": o_sca, "o_m": o_m, "o": o_sca + o_m}
+    return {"o_sca": o_sca, "o_m": o_m, "o": {s: o_sca[s] + o_m[s] for s in sca_chunks}}
 
 
 def forward(z, v, p: dict, c: int, no_delta: bool = False) -> dict:

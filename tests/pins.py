@@ -116,24 +116,34 @@ def awm_no_delta_closed(qm, km, v, c):
     return out
 
 
-def awm_const_key_closed(v, c):
-    """Closed form when every memory key row is the same vector.
+def awm_const_key_chunk_rows(v, c):
+    """Closed form when every memory key row is the same vector, one row per chunk.
 
     Then every row of M' is the same vector m_s, psi(Q_m) M' = m_s for any
-    query, and with vbar_t the mean of V over chunk t:
+    query, and with vbar_t the mean of V over chunk t (1-based):
       chunk s <= 2 reads 0; chunk 3 reads vbar_1;
       chunk s >= 4 reads sum_{t=2}^{s-2} (t-1) vbar_t / ((s-2)(s-3)).
+    Returns [N, dv]: row s-1 is what every query of chunk s reads.
     """
     v = np.asarray(v, np.float64)
-    n = v.shape[0]
-    ch = _chunks(n, c)
-    vbar = [None] + [v[a:b].mean(axis=0) for a, b in ch]
+    ch = _chunks(v.shape[0], c)
+    N = len(ch)
+    vbar = np.stack([v[a:b].mean(axis=0) for a, b in ch])        # row t-1 = vbar_t
+    t = np.arange(1, N + 1, dtype=np.float64)
+    w = np.cumsum((t - 1.0)[:, None] * vbar, axis=0)              # row u-1 = sum_{t<=u} (t-1) vbar_t
+    rows = np.zeros((N, v.shape[1]))
+    if N >= 3:
+        rows[2] = vbar[0]
+    for s in range(4, N + 1):
+        rows[s - 1] = w[s - 3] / ((s - 2) * (s - 3))
+    return rows
+
+
+def awm_const_key_closed(v, c):
+    """awm_const_key_chunk_rows expanded to every token row."""
+    v = np.asarray(v, np.float64)
+    rows = awm_const_key_chunk_rows(v, c)
     out = np.zeros_like(v)
-    for s in range(3, len(ch) + 1):
-        a, b = ch[s - 1]
-        if s == 3:
-            row = vbar[1]
-        else:
-            row = sum((t - 1) * vbar[t] for t in range(2, s - 1)) / ((s - 2) * (s - 3))
-        out[a:b] = row
+    for s, (a, b) in enumerate(_chunks(v.shape[0], c)):
+        out[a:b] = rows[s]
     return out

@@ -260,3 +260,14 @@ def test_pins_catch_planted_sca_mistakes(kind):
             qp[1:] -= 1  # first row keeps itself so the row is not empty
         out[q0:q1] = oracle.sca_chunk(qq, k[k0:q1], v[k0:q1], qp, kp)
     assert np.max(np.abs(out - pins.brute_sca(q, k, v, c))) > 1e-3
+
+
+def test_awm_readout_chunks_subset_matches_full():
+    n, c = 70, 8
+    z, v, a = rand_head(n, 5, 4, seed=4, key_scale=2.0)
+    args = (z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c)
+    full = oracle.awm_head(*args)
+    part = oracle.awm_head(*args, readout_chunks=[0, 3, 8])
+    assert sorted(part) == [0, 3, 8]
+    for s, rows in part.items():
+        np.testing.assert_array_equal(rows, full[s * c:min((s + 1) * c, n)])
