@@ -7,10 +7,12 @@
 //         + psi(Q_m,i) M'_{s-1}            (readout; chunks s >= 3, 1-based)
 //
 // Work decomposition: one workgroup = 256 consecutive queries of one chunk of
-// one (batch, head); 8 waves x 32 queries, two waves per SIMD so that one
-// wave's exponentials overlap the other's matrix instructions. The key window
-// [(s-1)c, last query] is streamed in tiles of 64 keys, processed as two
-// 32-key halves.
+// one (batch, head). With dv = 256: 8 waves x 32 queries, two waves per SIMD
+// so that one wave's exponentials overlap the other's matrix instructions;
+// with dv <= 128: 4 waves x 64 queries, one wave per SIMD, each K / V operand
+// read serving two MFMAs. The key window [(s-1)c, last query] is streamed in
+// tiles of 64 keys, processed as two 32-key halves; a wave skips the halves
+// that lie past all of its queries.
 //
 // Per 32-key half-tile and wave:
 //   S^T (32 keys x 32 queries) = K Q^T            (A = K from LDS, B = Q in VGPRs)
@@ -29,7 +31,9 @@
 // of a 4-row x 16-column block).
 //
 // Pipeline: tile kt+1 is loaded into the other LDS stage while tile kt is
-// computed.
+// computed; operand reads from LDS run a few MFMAs ahead of their use, and
+// the loop is unrolled by two tiles so every LDS address is a per-lane base
+// plus a constant offset.
 //
 // Softmax offset: m is fixed at the row's exact maximum over the first 32 keys
 // (2^(s - m) can then grow above 1 but stays far from the fp32/bf16 range);
@@ -48,19 +52,45 @@
 namespace gecko {
 namespace {
 
-constexpr int kWaves = 8;              // two waves per SIMD
-constexpr int kBM = 32 * kWaves;       // queries per workgroup
+// Scheduling of LDS operand reads: KAHEAD (VAHEAD) K (V) operands are read
+// ahead of the MFMA that consumes them; SCHED adds group barriers that keep
+// the compiler to that interleave.
+#ifndef GECKO_SCA_SCHED
+#define GECKO_SCA_SCHED 1
+#endif
+#ifndef GECKO_SCA_KAHEAD
+#define GECKO_SCA_KAHEAD 3
+#endif
+#ifndef GECKO_SCA_VAHEAD
+#define GECKO_SCA_VAHEAD 4
+#endif
+
+constexpr int kBM = 256;               // queries per workgroup
 constexpr int kBN = 64;                // keys per tile
-constexpr int kThreads = 64 * kWaves;
 constexpr float kOverflow = 0x1p63f;
 
-template <int D, int DV>
+// QB 32-query blocks per wave, NW waves per workgroup (32 QB NW = kBM).
+// QB = 2 reads each K / V operand from LDS once for two MFMAs and gives a
+// wave the whole register file of its SIMD (one wave per SIMD); QB = 1 runs
+// two waves per SIMD with half the registers each.
+template <int D, int DV, int QB>
 struct ScaTile {
+  static constexpr int NW = kBM / (32 * QB);
+  static constexpr int THREADS = 64 * NW;
   static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
   static constexpr int VBYTES = kBN * DV * 2;
   static constexpr size_t LDS_BYTES = 2 * (size_t)KBYTES + 2 * (size_t)VBYTES;
-  static constexpr int KLOADS = KBYTES / 16 / kThreads;  // 16-byte loads per thread per tile
-  static constexpr int VLOADS = VBYTES / 16 / kThreads;
+  static constexpr int KLOADS = KBYTES / 16 / THREADS;  // 16-byte loads per thread per tile
+  static constexpr int VLOADS = VBYTES / 16 / THREADS;
+  static_assert(32 * QB * NW == kBM, "tile shape");
+};
+
+// query blocks per wave for each built shape: with DV = 256, two blocks'
+// accumulators (256 registers) plus the scores exceed the accumulator
+// registers and the compiler shuttles values between register files.
+template <int D, int DV>
+struct ScaShape {
+  static constexpr int QB = DV >= 256 ? 1 : 2;
 };
 
 // XOR swizzle of the 16-byte chunks of a staged K row, chosen so that the
@@ -86,9 +116,10 @@ struct ScaArgs {
 // The attention loop of one workgroup. Member functions rather than lambdas:
 // lambdas inside a kernel are compiled for the host too, where the buffer and
 // LDS builtins used here do not exist.
-template <int D, int DV>
+template <int D, int DV, int QB>
 struct ScaLoop {
-  using T = ScaTile<D, DV>;
+  using T = ScaTile<D, DV, QB>;
+  static constexpr int NW = T::NW;
   static constexpr int KS = D / 16;   // 16-feature k-steps of Q K^T
   static constexpr int NMV = DV / 32; // 32-row blocks of O^T
   static constexpr int KCH = D / 8;   // 16-byte chunks per K row
@@ -98,123 +129,176 @@ struct ScaLoop {
   const uint16_t* vbh;
   char* kbuf;  // two K stages
   char* vbuf;  // two V stages
-  int n, kbeg, kend, ntiles, myq, wave_q0, w, g, lq, sl, grp2, perm2;
-  u32x4 qf[KS];
+  int n, kbeg, kend, ntiles, myq0, wave_q0, wave_last, w, g, lq;
+  u32x4 qf[QB][KS];
   uint32_t koff[T::KLOADS], voff[T::VLOADS];
+  int ka[KS];    // K operand byte offset in a stage for k-step ks, key block 0
+  int va[NMV];   // V transpose-read byte offset in a stage for value block mv, key row 0
 
   __device__ __forceinline__ void init(const ScaArgs& a, uint32_t bh, int h, int n_, int s, int c, int q0,
-                                       int qend, int qrow, int myq_, int w_, int lane, uint16_t* lds) {
+                                       int qend, int w_, int lane, uint16_t* lds) {
     n = n_;
-    myq = myq_;
     w = w_;
-    wave_q0 = q0 + 32 * w;
+    wave_q0 = q0 + 32 * QB * w;
     g = lane >> 5;
     lq = lane & 31;
+    myq0 = wave_q0 + lq;
     zbh = a.z + (size_t)bh * (size_t)n * D;
     vbh = a.v + (size_t)bh * (size_t)n * DV;
     kbuf = reinterpret_cast<char*>(lds);
     vbuf = kbuf + 2 * T::KBYTES;
 
-    // query fragments: lane holds query lq, features 16 ks + 8 g + [0, 8)
+    // query fragments: lane holds query 32 qb + lq of the wave, features
+    // 16 ks + 8 g + [0, 8); rows past the tile repeat its last query
     const float* kq = a.kappa_q + h * D;
     const float* nq = a.nu_q + h * D;
     const float* kk = a.kappa_k + h * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int f0 = 16 * ks + 8 * g;
-      const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
-      float x[8];
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = min(myq0 + 32 * qb, qend - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = bf_lo(raw[j]);
-        x[2 * j + 1] = bf_hi(raw[j]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int f0 = 16 * ks + 8 * g;
+        const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = bf_lo(raw[j]);
+          x[2 * j + 1] = bf_hi(raw[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (kq[f0 + i] * x[i] + nq[f0 + i]) * (kk[f0 + i] * kLog2e);
+        qf[qb][ks] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (kq[f0 + i] * x[i] + nq[f0 + i]) * (kk[f0 + i] * kLog2e);
-      qf[ks] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
     }
 
     kbeg = s > 0 ? (s - 1) * c : 0;
     kend = qend;
     ntiles = (kend - kbeg + kBN - 1) / kBN;
+    // last key any query of this wave can see; -1 (every key tile skipped)
+    // if the wave holds no query of the tile
+    wave_last = wave_q0 < kend ? min(wave_q0 + 32 * QB, kend) - 1 : -1;
 
     // staging offsets (constant over tiles). Load i of wave w covers the
-    // 1 KiB piece kWaves i + w of the tile; lane l writes LDS chunk
-    // (kWaves i + w) 64 + l, which is physical chunk p of row r holding
+    // 1 KiB piece NW i + w of the tile; lane l writes LDS chunk
+    // (NW i + w) 64 + l, which is physical chunk p of row r holding
     // logical chunk p ^ swz(r).
 #pragma unroll
     for (int i = 0; i < T::KLOADS; ++i) {
-      const int P = (kWaves * i + w) * 64 + lane;
+      const int P = (NW * i + w) * 64 + lane;
       const int r = P / KCH, p = P % KCH;
       koff[i] = (uint32_t)(r * D + 8 * (p ^ kswz<D>(r))) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < T::VLOADS; ++i) {
-      const int P = (kWaves * i + w) * 64 + lane;
+      const int P = (NW * i + w) * 64 + lane;
       const int r = P / VCH, p = P % VCH;
       voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
     }
-    sl = lane & 15;
-    grp2 = (lane >> 4) & 1;
-    perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+    // Operand reads. K: lane reads row 32 mb + lq, logical chunk 2 ks + g;
+    // the swizzle of row r depends on r mod 16 only, so mb adds a constant.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = lq * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(lq));
+    // V^T block for O rows 32 mv + [0, 32) and the P keys of k-step (mb, hh):
+    // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
+    //                                      [32 mv + perm_row(lq)].
+    // Transpose read jj supplies j = 4 jj + j': source lane sl of each
+    // 16-lane group points at key 32 mb + 16 hh + 8 jj + 4 g + sl / 4 and at
+    // values 32 mv + 16 (group % 2) + 4 perm2(sl % 4) + [0, 4), perm2 swapping
+    // two bits. The V swizzle depends on the row mod 4 = sl / 4 only, so
+    // (mb, hh, jj) add a constant.
+    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+    const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+    const int r0 = 4 * g + (sl >> 2);
+#pragma unroll
+    for (int mv = 0; mv < NMV; ++mv) {
+      const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+      va[mv] = r0 * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
+    }
   }
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
-    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, kWaves, w, koff, T::KLOADS);
-    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, kWaves, w, voff, T::VLOADS);
+    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, NW, w, koff, T::KLOADS);
+    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, NW, w, voff, T::VLOADS);
   }
 
-  // K operand: lane reads row 32 mb + lq, logical chunk 2 ks + g
-  __device__ __forceinline__ int k_addr(int mb, int ks) const {
-    const int r = 32 * mb + lq;
-    return r * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(r));
-  }
-  // V^T block for O rows 32 mv + [0, 32) and the P keys of k-step (mb, hh):
-  // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
-  //                                      [32 mv + perm_row(lq)].
-  // Transpose read jj supplies j = 4 jj + j': source lane s of each 16-lane
-  // group points at key 32 mb + 16 hh + 8 jj + 4 g + s / 4 and at values
-  // 32 mv + 16 (group % 2) + 4 perm2(s % 4) + [0, 4), perm2 swapping two bits.
+  __device__ __forceinline__ int k_addr(int mb, int ks) const { return ka[ks] + 32 * mb * (D * 2); }
   __device__ __forceinline__ int v_addr(int mv, int mb, int hh, int jj) const {
-    const int r = 32 * mb + 16 * hh + 8 * jj + 4 * g + (sl >> 2);
-    const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-    return r * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(r)) + 2 * (col & 7);
+    return va[mv] + (32 * mb + 16 * hh + 8 * jj) * (DV * 2);
   }
 
-  // S^T for keys 32 mb + [0, 32) of the tile in `slot`:
+  // S^T for keys 32 mb + [0, 32) of the tile in `slot`, every query block:
   // register r holds key 32 mb + 8 (r >> 2) + 4 g + (r & 3)
-  __device__ __forceinline__ f32x16 qk(int slot, int mb) const {
+  __device__ __forceinline__ void qk(int slot, int mb, f32x16 (&sc)[QB]) const {
     const char* Kb = kbuf + slot * T::KBYTES;
-    f32x16 sa = f32x16{};
+    constexpr int AH = GECKO_SCA_KAHEAD;
+    u32x4 op[AH + 1];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < AH; ++i) op[i] = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, i));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks));
-      sa = mfma_bf16(af, qf[ks], sa);
+      if (ks + AH < KS) op[(ks + AH) % (AH + 1)] = *reinterpret_cast<const u32x4*>(Kb + k_addr(mb, ks + AH));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = mfma_bf16(op[ks % (AH + 1)], qf[qb][ks], sc[qb]);
     }
-    return sa;
+#if GECKO_SCA_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS - AH; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, QB * AH, 0);
+#endif
   }
 
-  __device__ __forceinline__ void pv(int slot, int mb, const u32x4 (&pf)[2], f32x16 (&oacc)[NMV]) const {
+  __device__ __forceinline__ u32x4 v_operand(const char* Vb, int i, int mb) const {
+    const int hh = i / NMV, mv = i % NMV;
+    const u32x2 l2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 0));
+    const u32x2 h2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 1));
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+
+  // O^T += V^T P^T for the 32 keys of half mb; the V operand of MFMA i + AH
+  // is read from LDS before MFMA i is issued.
+  __device__ __forceinline__ void pv(int slot, int mb, const u32x4 (&pf)[QB][2], f32x16 (&oacc)[QB][NMV]) const {
     const char* Vb = vbuf + slot * T::VBYTES;
+    constexpr int NI = 2 * NMV;
+    constexpr int AH = GECKO_SCA_VAHEAD;
+    u32x4 op[AH + 1];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int i = 0; i < AH; ++i) op[i] = v_operand(Vb, i, mb);
 #pragma unroll
-      for (int mv = 0; mv < NMV; ++mv) {
-        const u32x2 l2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 0));
-        const u32x2 h2 = lds_read_tr(Vb + v_addr(mv, mb, hh, 1));
-        oacc[mv] = mfma_bf16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[hh], oacc[mv]);
-      }
+    for (int i = 0; i < NI; ++i) {
+      if (i + AH < NI) op[(i + AH) % (AH + 1)] = v_operand(Vb, i + AH, mb);
+      const int hh = i / NMV, mv = i % NMV;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(op[i % (AH + 1)], pf[qb][hh], oacc[qb][mv]);
+    }
+#if GECKO_SCA_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+    for (int i = 0; i < NI - AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, QB * AH, 0);
+#endif
   }
 
-  // last visible key offset within tile kt for this lane's query
-  __device__ __forceinline__ int last_visible(int kt) const { return min(myq, kend - 1) - (kbeg + kt * kBN); }
+  // last visible key offset within tile kt for query block qb of this lane
+  __device__ __forceinline__ int last_visible(int kt, int qb) const {
+    return min(myq0 + 32 * qb, kend - 1) - (kbeg + kt * kBN);
+  }
   __device__ __forceinline__ bool needs_mask(int kt) const {
     const int kb = kbeg + kt * kBN;
     return kb + kBN - 1 > wave_q0 || kb + kBN > kend;
   }
 
-  __device__ __forceinline__ float masked_max(const f32x16& sc, int kt, int mb) const {
-    const int lim = last_visible(kt);
+  __device__ __forceinline__ float masked_max(const f32x16& sc, int kt, int mb, int qb) const {
+    const int lim = last_visible(kt, qb);
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -224,32 +308,43 @@ struct ScaLoop {
     return mx;
   }
 
-  // one tile: for each 32-key half, S^T, P = 2^(S - m), O^T += V^T P^T
-  __device__ __forceinline__ void tile(int kt, float msub, float& lrun, f32x16 (&oacc)[NMV]) const {
-    const int slot = kt & 1;
+  // one tile (in LDS stage SLOT = kt mod 2, a constant so that operand
+  // addresses fold into the read offsets): for each 32-key half, S^T,
+  // P = 2^(S - m), O^T += V^T P^T. Halves whose first key is past every
+  // query of the wave are skipped.
+  template <int SLOT>
+  __device__ __forceinline__ void tile(int kt, const float (&msub)[QB], float (&lrun)[QB],
+                                       f32x16 (&oacc)[QB][NMV]) const {
+    constexpr int slot = SLOT;
     stage(kt + 1, slot ^ 1);  // replaces tile kt-1, read last iteration
+    const int kb = kbeg + kt * kBN;
     const bool masked = needs_mask(kt);
-    const int lim = last_visible(kt);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const f32x16 sc = qk(slot, mb);
-      float e[16];
+      if (kb + 32 * mb > wave_last) break;  // wave-uniform
+      f32x16 sc[QB];
+      qk(slot, mb, sc);
+      u32x4 pf[QB][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = exp2_fast(sc[r] - msub);
-      if (masked) {
+      for (int qb = 0; qb < QB; ++qb) {
+        float e[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-          e[r] = ko > lim ? 0.f : e[r];
+        for (int r = 0; r < 16; ++r) e[r] = exp2_fast(sc[qb][r] - msub[qb]);
+        if (masked) {
+          const int lim = last_visible(kt, qb);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+            e[r] = ko > lim ? 0.f : e[r];
+          }
         }
-      }
-      u32x4 pf[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float* x = e + 8 * hh;
+        for (int hh = 0; hh < 2; ++hh) {
+          const float* x = e + 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lrun += x[i];
-        pf[hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+          for (int i = 0; i < 8; ++i) lrun[qb] += x[i];
+          pf[qb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+        }
       }
       pv(slot, mb, pf, oacc);
     }
@@ -257,50 +352,80 @@ struct ScaLoop {
     __syncthreads();
   }
 
-  // full pass with a fixed softmax offset; returns the row exp-sum
-  __device__ __forceinline__ float pass(float msub, f32x16 (&oacc)[NMV]) const {
+  // full pass with fixed softmax offsets; returns the row exp-sums
+  __device__ __forceinline__ void pass(const float (&msub)[QB], float (&ltot)[QB], f32x16 (&oacc)[QB][NMV]) const {
     stage(0, 0);
     wait_vmem();
     __syncthreads();
-    float lrun = 0.f;
-    for (int kt = 0; kt < ntiles; ++kt) tile(kt, msub, lrun, oacc);
-    return other_half_sum(lrun);
+    float lrun[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile<0>(kt, msub, lrun, oacc);
+      if (kt + 1 < ntiles) tile<1>(kt + 1, msub, lrun, oacc);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ltot[qb] = other_half_sum(lrun[qb]);
   }
 
-  // O^T for the workgroup's queries, normalised
-  __device__ __forceinline__ void run(f32x16 (&oacc)[NMV]) const {
+  // O^T for the wave's queries, normalised
+  __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV]) const {
     // softmax offset: exact row maximum over the first 32 keys of the window
     // (every valid query sees the first key of its window)
     stage(0, 0);
     wait_vmem();
     __syncthreads();
-    const float m0 = other_half_max(masked_max(qk(0, 0), 0, 0));
+    float msub[QB], ltot[QB];
+    {
+      f32x16 sc[QB];
+      qk(0, 0, sc);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) msub[qb] = other_half_max(masked_max(sc[qb], 0, 0, qb));
+    }
     __syncthreads();
-    float ltot = pass(m0, oacc);
-    if (__syncthreads_or(!(ltot <= kOverflow))) {
-      // some logit exceeded m0 by 2^63: find the exact row maximum, then redo
-      // the pass with it (every 2^(s - m) <= 1)
-      float mx = kNegInf;
+    pass(msub, ltot, oacc);
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) over = over || !(ltot[qb] <= kOverflow);
+    if (__syncthreads_or(over)) {
+      // some logit exceeded its offset by 2^63: find the exact row maxima,
+      // then redo the pass with them (every 2^(s - m) <= 1)
+      float mx[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = kNegInf;
       for (int kt = 0; kt < ntiles; ++kt) {
         stage(kt, 0);
         wait_vmem();
         __syncthreads();
-        mx = fmaxf(mx, fmaxf(masked_max(qk(0, 0), kt, 0), masked_max(qk(0, 1), kt, 1)));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          f32x16 sc[QB];
+          qk(0, mb, sc);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx[qb], masked_max(sc[qb], kt, mb, qb));
+        }
         __syncthreads();
       }
-      mx = other_half_max(mx);
 #pragma unroll
-      for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
-      ltot = pass(mx, oacc);
+      for (int qb = 0; qb < QB; ++qb) {
+        msub[qb] = other_half_max(mx[qb]);
+#pragma unroll
+        for (int i = 0; i < NMV; ++i) oacc[qb][i] = f32x16{};
+      }
+      pass(msub, ltot, oacc);
     }
-    const float inv = 1.f / ltot;
 #pragma unroll
-    for (int i = 0; i < NMV; ++i) oacc[i] *= inv;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float inv = 1.f / ltot[qb];
+#pragma unroll
+      for (int i = 0; i < NMV; ++i) oacc[qb][i] *= inv;
+    }
   }
 };
 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
-__global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
+__global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) void sca_bf16_kernel(ScaArgs a) {
+  constexpr int QB = ScaShape<D, DV>::QB;
   constexpr int KS = D / 16;   // 16-feature k-steps of the readout
   constexpr int NMV = DV / 32; // 32-row blocks of O^T
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -325,60 +450,64 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int myq = q0 + w * 32 + lq;
-  const bool qvalid = myq < qend;
-  const int qrow = qvalid ? myq : qend - 1;
+  const int myq0 = q0 + 32 * QB * w + lq;  // query of block qb: myq0 + 32 qb
   const uint16_t* zbh = a.z + (size_t)bh * (size_t)n * D;
 
-  f32x16 oacc[NMV];
+  f32x16 oacc[QB][NMV];
 #pragma unroll
-  for (int i = 0; i < NMV; ++i) oacc[i] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < NMV; ++i) oacc[qb][i] = f32x16{};
 
   if constexpr (kSca) {
-    ScaLoop<D, DV> L;
-    L.init(a, bh, h, n, s, c, q0, qend, qrow, myq, w, lane, lds);
+    ScaLoop<D, DV, QB> L;
+    L.init(a, bh, h, n, s, c, q0, qend, w, lane, lds);
     L.run(oacc);
   }
 
   if constexpr (kRead) {
     if (s >= 2) {
-      // psi(Q_m) of this lane's query, features 16 ks + 8 g + [0, 8)
       const float* eq = a.eta_q + h * D;
       const float* rq = a.rho_q + h * D;
-      float qm[KS * 8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int f0 = 16 * ks + 8 * g;
-        const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          qm[8 * ks + 2 * j] = (eq[f0 + 2 * j] * bf_lo(raw[j]) + rq[f0 + 2 * j]) * kLog2e;
-          qm[8 * ks + 2 * j + 1] = (eq[f0 + 2 * j + 1] * bf_hi(raw[j]) + rq[f0 + 2 * j + 1]) * kLog2e;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, qm[8 * ks + i]);
-      }
-      mx = other_half_max(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < KS * 8; ++i) {
-        qm[i] = exp2_fast(qm[i] - mx);
-        sum += qm[i];
-      }
-      sum = other_half_sum(sum);
-      const float inv = 1.f / sum;
       const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(DV * D);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float* e = qm + 8 * ks;
-        const u32x4 pf{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
-                       pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+      for (int qb = 0; qb < QB; ++qb) {
+        // psi(Q_m) of this lane's query, features 16 ks + 8 g + [0, 8)
+        const int qrow = min(myq0 + 32 * qb, qend - 1);
+        float qm[KS * 8];
+        float mx = kNegInf;
 #pragma unroll
-        for (int mv = 0; mv < NMV; ++mv) {
-          const int vrow = 32 * mv + perm_row(lq);
-          const u32x4 af = ld16(sn + vrow * D + 16 * ks + 8 * g);
-          oacc[mv] = mfma_bf16(af, pf, oacc[mv]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int f0 = 16 * ks + 8 * g;
+          const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            qm[8 * ks + 2 * j] = (eq[f0 + 2 * j] * bf_lo(raw[j]) + rq[f0 + 2 * j]) * kLog2e;
+            qm[8 * ks + 2 * j + 1] = (eq[f0 + 2 * j + 1] * bf_hi(raw[j]) + rq[f0 + 2 * j + 1]) * kLog2e;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mx = fmaxf(mx, qm[8 * ks + i]);
+        }
+        mx = other_half_max(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < KS * 8; ++i) {
+          qm[i] = exp2_fast(qm[i] - mx);
+          sum += qm[i];
+        }
+        sum = other_half_sum(sum);
+        const float inv = 1.f / sum;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const float* e = qm + 8 * ks;
+          const u32x4 pf{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
+                         pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+#pragma unroll
+          for (int mv = 0; mv < NMV; ++mv) {
+            const int vrow = 32 * mv + perm_row(lq);
+            const u32x4 af = ld16(sn + vrow * D + 16 * ks + 8 * g);
+            oacc[qb][mv] = mfma_bf16(af, pf, oacc[qb][mv]);
+          }
         }
       }
     }
@@ -386,14 +515,17 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
 
   // accumulator register r of block mv holds value column
   // 32 mv + 16 (r >> 3) + 8 g + (r & 7): two runs of 8 per lane
-  if (qvalid) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int myq = myq0 + 32 * qb;
+    if (myq >= qend) continue;
     if constexpr (kOutF32) {
       float* orow = static_cast<float*>(a.out) + ((size_t)bh * n + myq) * DV;
 #pragma unroll
       for (int mv = 0; mv < NMV; ++mv)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const f32x16& o = oacc[mv];
+          const f32x16& o = oacc[qb][mv];
           float* dst = orow + 32 * mv + 16 * hh + 8 * g;
           *reinterpret_cast<f32x4*>(dst) = f32x4{o[8 * hh + 0], o[8 * hh + 1], o[8 * hh + 2], o[8 * hh + 3]};
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[8 * hh + 4], o[8 * hh + 5], o[8 * hh + 6], o[8 * hh + 7]};
@@ -404,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
       for (int mv = 0; mv < NMV; ++mv)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const f32x16& o = oacc[mv];
+          const f32x16& o = oacc[qb][mv];
           const u32x4 pk{pack2(o[8 * hh + 0], o[8 * hh + 1]), pack2(o[8 * hh + 2], o[8 * hh + 3]),
                          pack2(o[8 * hh + 4], o[8 * hh + 5]), pack2(o[8 * hh + 6], o[8 * hh + 7])};
           st16(orow + 32 * mv + 16 * hh + 8 * g, pk);
@@ -415,8 +547,9 @@ __global__ __launch_bounds__(kThreads, 1) void sca_bf16_kernel(ScaArgs a) {
 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 hipError_t launch_one(const ScaArgs& a, hipStream_t stream) {
+  using T = ScaTile<D, DV, ScaShape<D, DV>::QB>;
   auto kern = sca_bf16_kernel<D, DV, kSca, kRead, kOutF32>;
-  const size_t lds = kSca ? ScaTile<D, DV>::LDS_BYTES : 0;
+  const size_t lds = kSca ? T::LDS_BYTES : 0;
   if (lds > 65536) {
     static bool attr_set = false;  // per instantiation
     if (!attr_set) {
@@ -427,7 +560,7 @@ hipError_t launch_one(const ScaArgs& a, hipStream_t stream) {
     }
   }
   const dim3 grid((unsigned)(8 * a.per_xcd));
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, grid, dim3(T::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
