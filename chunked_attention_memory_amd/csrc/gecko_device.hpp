@@ -48,6 +48,12 @@ __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// acc + lo + hi of a word holding two bf16 values (v_dot2 against (1, 1)).
+__device__ __forceinline__ float sum2_bf16(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_xor32(float x) {

@@ -35,11 +35,12 @@
 // the loop is unrolled by two tiles so every LDS address is a per-lane base
 // plus a constant offset.
 //
-// Softmax offset: m is fixed at the row's exact maximum over the first 32 keys
-// (2^(s - m) can then grow above 1 but stays far from the fp32/bf16 range);
-// the final exp-sum shows whether any logit exceeded m by 2^63, and only then
-// is the workgroup recomputed with the exact row maximum found by a max-only
-// pass. No accumulator is ever rescaled inside the loop.
+// Softmax offset: the first pass uses none (P = 2^s; bf16 and fp32 share the
+// exponent range, so P keeps its relative precision at any scale). The final
+// row sum shows whether that was safe: outside [2^-60, 2^63] (an overflow, or
+// every term tiny) the workgroup finds the exact row maxima with a max-only
+// pass and recomputes with them. No accumulator is ever rescaled inside the
+// loop, and the row sums add the bf16 P values that multiply V.
 //
 // Algebra used to drop the key-side affine map: q . (kappa_k * z_j + nu_k)
 // = (q * kappa_k) . z_j + q . nu_k. The second term is the same for every key
@@ -59,15 +60,16 @@ namespace {
 #define GECKO_SCA_SCHED 1
 #endif
 #ifndef GECKO_SCA_KAHEAD
-#define GECKO_SCA_KAHEAD 3
+#define GECKO_SCA_KAHEAD 2
 #endif
 #ifndef GECKO_SCA_VAHEAD
-#define GECKO_SCA_VAHEAD 4
+#define GECKO_SCA_VAHEAD 2
 #endif
 
 constexpr int kBM = 256;               // queries per workgroup
 constexpr int kBN = 64;                // keys per tile
-constexpr float kOverflow = 0x1p63f;
+constexpr float kOverflow = 0x1p63f;   // row-sum range of the offset-free pass
+constexpr float kUnderflow = 0x1p-60f;
 
 // QB 32-query blocks per wave, NW waves per workgroup (32 QB NW = kBM).
 // QB = 2 reads each K / V operand from LDS once for two MFMAs and gives a
@@ -310,9 +312,10 @@ struct ScaLoop {
 
   // one tile (in LDS stage SLOT = kt mod 2, a constant so that operand
   // addresses fold into the read offsets): for each 32-key half, S^T,
-  // P = 2^(S - m), O^T += V^T P^T. Halves whose first key is past every
-  // query of the wave are skipped.
-  template <int SLOT>
+  // P = 2^(S - m) (m = 0 unless kSub), O^T += V^T P^T, and the row sums of
+  // the bf16 P actually multiplied into V. Halves whose first key is past
+  // every query of the wave are skipped.
+  template <int SLOT, bool kSub>
   __device__ __forceinline__ void tile(int kt, const float (&msub)[QB], float (&lrun)[QB],
                                        f32x16 (&oacc)[QB][NMV]) const {
     constexpr int slot = SLOT;
@@ -329,7 +332,7 @@ struct ScaLoop {
       for (int qb = 0; qb < QB; ++qb) {
         float e[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = exp2_fast(sc[qb][r] - msub[qb]);
+        for (int r = 0; r < 16; ++r) e[r] = exp2_fast(kSub ? sc[qb][r] - msub[qb] : sc[qb][r]);
         if (masked) {
           const int lim = last_visible(kt, qb);
 #pragma unroll
@@ -341,9 +344,9 @@ struct ScaLoop {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const float* x = e + 8 * hh;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lrun[qb] += x[i];
           pf[qb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lrun[qb] = sum2_bf16(pf[qb][hh][i], lrun[qb]);
         }
       }
       pv(slot, mb, pf, oacc);
@@ -353,6 +356,7 @@ struct ScaLoop {
   }
 
   // full pass with fixed softmax offsets; returns the row exp-sums
+  template <bool kSub>
   __device__ __forceinline__ void pass(const float (&msub)[QB], float (&ltot)[QB], f32x16 (&oacc)[QB][NMV]) const {
     stage(0, 0);
     wait_vmem();
@@ -361,8 +365,8 @@ struct ScaLoop {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
     for (int kt = 0; kt < ntiles; kt += 2) {
-      tile<0>(kt, msub, lrun, oacc);
-      if (kt + 1 < ntiles) tile<1>(kt + 1, msub, lrun, oacc);
+      tile<0, kSub>(kt, msub, lrun, oacc);
+      if (kt + 1 < ntiles) tile<1, kSub>(kt + 1, msub, lrun, oacc);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) ltot[qb] = other_half_sum(lrun[qb]);
@@ -370,26 +374,19 @@ struct ScaLoop {
 
   // O^T for the wave's queries, normalised
   __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV]) const {
-    // softmax offset: exact row maximum over the first 32 keys of the window
-    // (every valid query sees the first key of its window)
-    stage(0, 0);
-    wait_vmem();
-    __syncthreads();
+    // First pass without an offset: P = 2^s. The row sums show whether that
+    // was safe: if a valid query's sum lies outside [2^-60, 2^63] (some 2^s
+    // overflowed, or every term is tiny), the workgroup finds the exact row
+    // maxima with a max-only pass and redoes the pass with them.
     float msub[QB], ltot[QB];
-    {
-      f32x16 sc[QB];
-      qk(0, 0, sc);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) msub[qb] = other_half_max(masked_max(sc[qb], 0, 0, qb));
-    }
-    __syncthreads();
-    pass(msub, ltot, oacc);
-    bool over = false;
+    for (int qb = 0; qb < QB; ++qb) msub[qb] = 0.f;
+    pass<false>(msub, ltot, oacc);
+    bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) over = over || !(ltot[qb] <= kOverflow);
-    if (__syncthreads_or(over)) {
-      // some logit exceeded its offset by 2^63: find the exact row maxima,
-      // then redo the pass with them (every 2^(s - m) <= 1)
+    for (int qb = 0; qb < QB; ++qb)
+      redo = redo || (myq0 + 32 * qb < kend && !(ltot[qb] >= kUnderflow && ltot[qb] <= kOverflow));
+    if (__syncthreads_or(redo)) {
       float mx[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = kNegInf;
@@ -412,7 +409,7 @@ struct ScaLoop {
 #pragma unroll
         for (int i = 0; i < NMV; ++i) oacc[qb][i] = f32x16{};
       }
-      pass(msub, ltot, oacc);
+      pass<true>(msub, ltot, oacc);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -467,9 +464,33 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 
   if constexpr (kRead) {
     if (s >= 2) {
+      // M'_{s-1} (stored transposed: dv rows of d features) goes to LDS once
+      // per workgroup, rows chunk-swizzled like K; the attention loop ended
+      // with a barrier, so its stages are free.
+      using T = ScaTile<D, DV, QB>;
+      constexpr int RB = 64;                          // rows per staging call
+      constexpr int SLOADS = RB * D * 2 / 16 / T::THREADS;
+      constexpr int KCH = D / 8;
+      char* sbuf = reinterpret_cast<char*>(lds);
+      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(DV * D);
+      {
+        uint32_t soff[SLOADS];
+#pragma unroll
+        for (int i = 0; i < SLOADS; ++i) {
+          const int P = (T::NW * i + w) * 64 + lane;
+          const int r = P / KCH, p = P % KCH;
+          soff[i] = (uint32_t)(r * D + 8 * (p ^ kswz<D>(r))) * 2u;
+        }
+#pragma unroll
+        for (int rb = 0; rb < DV / RB; ++rb)
+          stage_rows(sn, rb * RB, DV, D, sbuf + rb * RB * D * 2, T::NW, w, soff, SLOADS);
+      }
+      // A operand of value block mv, k-step ks: row 32 mv + perm_row(lq),
+      // logical chunk 2 ks + g (the swizzle depends on the row mod 16 only)
+      const int prow = perm_row(lq);
       const float* eq = a.eta_q + h * D;
       const float* rq = a.rho_q + h * D;
-      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(DV * D);
+      u32x4 pf[QB][KS];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         // psi(Q_m) of this lane's query, features 16 ks + 8 g + [0, 8)
@@ -500,14 +521,20 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const float* e = qm + 8 * ks;
-          const u32x4 pf{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
-                         pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+          pf[qb][ks] = u32x4{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
+                             pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+        }
+      }
+      wait_vmem();
+      __syncthreads();
 #pragma unroll
-          for (int mv = 0; mv < NMV; ++mv) {
-            const int vrow = 32 * mv + perm_row(lq);
-            const u32x4 af = ld16(sn + vrow * D + 16 * ks + 8 * g);
-            oacc[qb][mv] = mfma_bf16(af, pf, oacc[qb][mv]);
-          }
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = prow * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(prow));
+#pragma unroll
+        for (int mv = 0; mv < NMV; ++mv) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(sbuf + off + 32 * mv * (D * 2));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(af, pf[qb][ks], oacc[qb][mv]);
         }
       }
     }
@@ -549,7 +576,7 @@ template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 hipError_t launch_one(const ScaArgs& a, hipStream_t stream) {
   using T = ScaTile<D, DV, ScaShape<D, DV>::QB>;
   auto kern = sca_bf16_kernel<D, DV, kSca, kRead, kOutF32>;
-  const size_t lds = kSca ? T::LDS_BYTES : 0;
+  const size_t lds = max(kSca ? T::LDS_BYTES : (size_t)0, kRead ? (size_t)(DV * D * 2) : (size_t)0);
   if (lds > 65536) {
     static bool attr_set = false;  // per instantiation
     if (!attr_set) {
