@@ -30,17 +30,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
-// reductions over aligned groups of P = 2 or 4 consecutive lanes
+// reductions over aligned groups of P = 2, 4 or 8 consecutive lanes
 template <int P>
 __device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));                       // quad_perm [1,0,3,2]
-  if constexpr (P == 4) x = fmaxf(x, dpp<0x4E>(x));  // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0xB1>(x));                        // quad_perm [1,0,3,2]
+  if constexpr (P >= 4) x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  if constexpr (P >= 8) x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
   return x;
 }
 template <int P>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0xB1>(x);
-  if constexpr (P == 4) x += dpp<0x4E>(x);
+  if constexpr (P >= 4) x += dpp<0x4E>(x);
+  if constexpr (P >= 8) x += dpp<0x141>(x);
   return x;
 }
 
@@ -63,7 +65,10 @@ struct ChunkTile {
   static constexpr int VBYTES = kBT * DV * 2;
   static constexpr int ZLOADS = ZBYTES / 16 / THREADS;
   static constexpr int VLOADS = VBYTES / 16 / THREADS;
-  static constexpr int PARTS = THREADS / kBT;  // threads per token row in the psi phase (32 features each)
+  static constexpr int PARTS = THREADS / kBT;  // threads per token row in the psi phase
+  static constexpr int FPT = D / PARTS;        // features per thread in the psi phase
+  static constexpr int KT = kBT / 16;          // 16-token k-steps per tile
+  static_assert(FPT % 8 == 0 && (PARTS == 2 || PARTS == 4 || PARTS == 8), "psi phase split");
   static constexpr int STAGE = ZBYTES + VBYTES;
   // two (Z', V) stages, the psi tile, then the (log2-scaled) eta_k and rho_k vectors
   static constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + ZBYTES + 2 * D * sizeof(float);
@@ -104,9 +109,13 @@ struct ChunkLoop {
   char* ps;
   const float* e2s;  // eta_k * log2(e), in LDS
   const float* r2s;  // rho_k * log2(e), in LDS
-  int n, cbeg, cend, ntiles, w, lane, g, lq, sl, g2;
+  int n, cbeg, cend, ntiles, w, lane, g, lq;
   float ekf, rkf;  // this lane's feature
   uint32_t zoff[T::ZLOADS], voff[T::VLOADS];
+  // Transpose-read bases (byte offsets within a stage / the psi tile) for
+  // read jj of block blk at k-step 0; k-step ks adds 16 ks rows. See tr_base.
+  int zb[2], vb[2][NMV], pb[2][NMF];
+  int poff[T::FPT / 8];  // psi phase: this thread's 16-byte chunks of its token row
 
   __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* lds) {
     const int h = (int)(bh % a.H);
@@ -119,8 +128,6 @@ struct ChunkLoop {
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     g = lane >> 5;
     lq = lane & 31;
-    sl = lane & 15;
-    g2 = (lane >> 4) & 1;
     zbh = a.z + (size_t)bh * (size_t)n * D;
     vbh = a.v + (size_t)bh * (size_t)n * DV;
     st = lds;
@@ -148,6 +155,40 @@ struct ChunkLoop {
       const int r = P / (DV / 8), p = P % (DV / 8);
       voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
     }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      zb[jj] = tr_base<D, true>(w, jj);
+#pragma unroll
+      for (int mv = 0; mv < NMV; ++mv) vb[jj][mv] = tr_base<DV, false>(mv, jj);
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf) pb[jj][mf] = tr_base<D, true>(mf, jj);
+    }
+    {
+      const int tk = tid / T::PARTS, q = tid % T::PARTS;
+#pragma unroll
+      for (int k = 0; k < T::FPT / 8; ++k) poff[k] = tk * D * 2 + 16 * ((T::FPT / 8 * q + k) ^ zswz<D>(tk));
+    }
+  }
+
+  // Transpose-read operand: element j of lane (lq, g) is M[16 ks + 8 g + j][32 blk + lq]
+  // for a row-major staged tile M with WIDTH columns and its chunk swizzle.
+  // Read jj supplies j = 4 jj + j': source lane s of each 16-lane group points
+  // at row 16 ks + 8 g + 4 jj + s / 4 and columns 32 blk + 16 (group % 2) + 4 (s % 4).
+  // Both swizzles depend on row bits 0..2 only, so k-step ks adds 16 ks rows
+  // to the offset computed here for ks = 0.
+  template <int WIDTH, bool kZ>
+  __device__ __forceinline__ int tr_base(int blk, int jj) const {
+    const int sl = lane & 15, g2 = (lane >> 4) & 1;
+    const int r = 8 * g + 4 * jj + (sl >> 2);
+    const int col = 32 * blk + 16 * g2 + 4 * (sl & 3);
+    const int sw = kZ ? zswz<D>(r) : vswz<DV>(r);
+    return r * WIDTH * 2 + 16 * ((col >> 3) ^ sw) + 2 * (col & 7);
+  }
+  template <int WIDTH>
+  __device__ __forceinline__ u32x4 tr_operand(const char* base, int b0, int b1, int ks) const {
+    const u32x2 lo = lds_read_tr(base + b0 + 16 * ks * WIDTH * 2);
+    const u32x2 hi = lds_read_tr(base + b1 + 16 * ks * WIDTH * 2);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 
   __device__ __forceinline__ const char* zs(int slot) const { return st + slot * T::STAGE; }
@@ -159,26 +200,9 @@ struct ChunkLoop {
     stage_rows(vbh, cbeg + it * kBT, n, DV, st + slot * T::STAGE + T::ZBYTES, T::NW, w, voff, T::VLOADS);
   }
 
-  // Transpose-read operand: element j of lane (lq, g) is M[16 ks + 8 g + j][32 blk + lq]
-  // for a row-major staged tile M with `width` columns and swizzle `swz`.
-  // Read jj supplies j = 4 jj + j': source lane s of each 16-lane group points
-  // at row 16 ks + 8 g + 4 jj + s / 4 and columns 32 blk + 16 (group % 2) + 4 (s % 4).
-  template <int WIDTH, bool kZ>
-  __device__ __forceinline__ u32x4 tr_operand(const char* base, int blk, int ks) const {
-    u32x2 part[2];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int r = 16 * ks + 8 * g + 4 * jj + (sl >> 2);
-      const int col = 32 * blk + 16 * g2 + 4 * (sl & 3);
-      const int sw = kZ ? zswz<D>(r) : vswz<DV>(r);
-      part[jj] = lds_read_tr(base + r * WIDTH * 2 + 16 * ((col >> 3) ^ sw) + 2 * (col & 7));
-    }
-    return u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
-  }
-
   // K_m of this lane's feature (log2 units) for tokens 16 ks + 8 g + [0, 8) of the tile in `slot`
   __device__ __forceinline__ void keys(int slot, int ks, float (&k)[8]) const {
-    const u32x4 zr = tr_operand<D, true>(zs(slot), w, ks);
+    const u32x4 zr = tr_operand<D>(zs(slot), zb[0], zb[1], ks);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       k[2 * j] = ekf * bf_lo(zr[j]) + rkf;
@@ -191,7 +215,7 @@ struct ChunkLoop {
     const int valid = cend - (cbeg + it * kBT);  // tokens of the tile inside the chunk
     float mx = kNegInf;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < T::KT; ++ks) {
       float k[8];
       keys(slot, ks, k);
 #pragma unroll
@@ -201,14 +225,14 @@ struct ChunkLoop {
   }
 
   // psi(K_m) for the tile's tokens into LDS: thread -> token tid / PARTS,
-  // features 32 (tid % PARTS) + [0, 32)
+  // features FPT (tid % PARTS) + [0, FPT)
   __device__ __forceinline__ void psi_phase(int slot) const {
-    const int tid = threadIdx.x;
-    const int tk = tid / T::PARTS, q = tid % T::PARTS;
-    float x[32];
+    constexpr int FPT = T::FPT, CH = FPT / 8;
+    const int q = threadIdx.x % T::PARTS;
+    float x[FPT];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(zs(slot) + tk * D * 2 + 16 * ((4 * q + k) ^ zswz<D>(tk)));
+    for (int k = 0; k < CH; ++k) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(zs(slot) + poff[k]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[8 * k + 2 * j] = bf_lo(raw[j]);
@@ -217,9 +241,9 @@ struct ChunkLoop {
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int f4 = 0; f4 < 8; ++f4) {
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(e2s + 32 * q + 4 * f4);
-      const f32x4 r4 = *reinterpret_cast<const f32x4*>(r2s + 32 * q + 4 * f4);
+    for (int f4 = 0; f4 < FPT / 4; ++f4) {
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(e2s + FPT * q + 4 * f4);
+      const f32x4 r4 = *reinterpret_cast<const f32x4*>(r2s + FPT * q + 4 * f4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[4 * f4 + i] = e4[i] * x[4 * f4 + i] + r4[i];
@@ -229,27 +253,29 @@ struct ChunkLoop {
     mx = group_max<T::PARTS>(mx);
     float sm = 0.f;
 #pragma unroll
-    for (int f = 0; f < 32; ++f) {
+    for (int f = 0; f < FPT; ++f) {
       x[f] = exp2_fast(x[f] - mx);
       sm += x[f];
     }
     sm = group_sum<T::PARTS>(sm);
     const float inv = 1.f / sm;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < CH; ++k) {
       const float* y = x + 8 * k;
       const u32x4 pk{pack2(y[0] * inv, y[1] * inv), pack2(y[2] * inv, y[3] * inv), pack2(y[4] * inv, y[5] * inv),
                      pack2(y[6] * inv, y[7] * inv)};
-      *reinterpret_cast<u32x4*>(ps + tk * D * 2 + 16 * ((4 * q + k) ^ zswz<D>(tk))) = pk;
+      *reinterpret_cast<u32x4*>(ps + poff[k]) = pk;
     }
   }
 
-  // E for k-step ks, accumulate its sum, and the two products
+  // E for every k-step of the tile (its sum accumulated), then the two
+  // products; the operand of MFMA i + AH is read from LDS before MFMA i.
   __device__ __forceinline__ void mfma_phase(int it, int slot, float msub, float& lsum, f32x16 (&accg)[NMV],
                                              f32x16 (&acch)[NMF]) const {
     const int valid = cend - (cbeg + it * kBT);
+    u32x4 ef[T::KT];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < T::KT; ++ks) {
       float k[8];
       keys(slot, ks, k);
       float e[8];
@@ -258,30 +284,48 @@ struct ChunkLoop {
         e[j] = 16 * ks + 8 * g + j < valid ? exp2_fast(k[j] - msub) : 0.f;
         lsum += e[j];
       }
-      const u32x4 ef{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+      ef[ks] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+    }
+    constexpr int NB = NMV + NMF, NI = T::KT * NB, AH = 2;
+    const char* vsb = vs(slot);
+    u32x4 op[AH + 1];
 #pragma unroll
-      for (int mv = 0; mv < NMV; ++mv) accg[mv] = mfma_bf16(tr_operand<DV, false>(vs(slot), mv, ks), ef, accg[mv]);
-#pragma unroll
-      for (int mf = 0; mf < NMF; ++mf) acch[mf] = mfma_bf16(tr_operand<D, true>(ps, mf, ks), ef, acch[mf]);
+    for (int i = 0; i < NI + AH; ++i) {
+      if (i < NI) {
+        const int ks = i / NB, b = i % NB;
+        op[i % (AH + 1)] = b < NMV ? tr_operand<DV>(vsb, vb[0][b] , vb[1][b], ks) : tr_operand<D>(ps, pb[0][b - NMV], pb[1][b - NMV], ks);
+      }
+      if (i >= AH) {
+        const int m = i - AH, ks = m / NB, b = m % NB;
+        if (b < NMV) accg[b] = mfma_bf16(op[m % (AH + 1)], ef[ks], accg[b]);
+        else acch[b - NMV] = mfma_bf16(op[m % (AH + 1)], ef[ks], acch[b - NMV]);
+      }
     }
   }
 
   // one pass over the chunk with a fixed per-feature offset; returns the
   // exp-sum. Expects tile 0 staged in slot 0; tile it+1 loads while tile it
   // is computed.
+  // one tile in LDS stage SLOT (a constant, so LDS offsets fold into the reads)
+  template <int SLOT>
+  __device__ __forceinline__ void tile(int it, float msub, float& lsum, f32x16 (&accg)[NMV],
+                                       f32x16 (&acch)[NMF]) const {
+    if (it + 1 < ntiles) {
+      stage_z(it + 1, SLOT ^ 1);  // replaces tile it-1, whose reads are done
+      stage_v(it + 1, SLOT ^ 1);
+    }
+    psi_phase(SLOT);
+    __syncthreads();
+    mfma_phase(it, SLOT, msub, lsum, accg, acch);
+    wait_vmem();
+    __syncthreads();
+  }
+
   __device__ __forceinline__ float pass(float msub, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF]) const {
     float lsum = 0.f;
-    for (int it = 0; it < ntiles; ++it) {
-      const int slot = it & 1;
-      if (it + 1 < ntiles) {
-        stage_z(it + 1, slot ^ 1);  // replaces tile it-1, whose reads are done
-        stage_v(it + 1, slot ^ 1);
-      }
-      psi_phase(slot);
-      __syncthreads();
-      mfma_phase(it, slot, msub, lsum, accg, acch);
-      wait_vmem();
-      __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+      tile<0>(it, msub, lsum, accg, acch);
+      if (it + 1 < ntiles) tile<1>(it + 1, msub, lsum, accg, acch);
     }
     return other_half_sum(lsum);
   }

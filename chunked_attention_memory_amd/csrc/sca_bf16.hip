@@ -59,6 +59,14 @@ namespace {
 #ifndef GECKO_SCA_SCHED
 #define GECKO_SCA_SCHED 1
 #endif
+// LDS stages of the 8-wave layout (2 or 3) and, with 3, whether waves 4..7
+// run half a tile behind waves 0..3.
+#ifndef GECKO_SCA_STAGES
+#define GECKO_SCA_STAGES 2
+#endif
+#ifndef GECKO_SCA_PINGPONG
+#define GECKO_SCA_PINGPONG 0
+#endif
 #ifndef GECKO_SCA_KAHEAD
 #define GECKO_SCA_KAHEAD 2
 #endif
@@ -81,7 +89,9 @@ struct ScaTile {
   static constexpr int THREADS = 64 * NW;
   static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
   static constexpr int VBYTES = kBN * DV * 2;
-  static constexpr size_t LDS_BYTES = 2 * (size_t)KBYTES + 2 * (size_t)VBYTES;
+  // (K, V) stages in LDS; the wave groups can run out of phase only with three
+  static constexpr int NSTAGE = NW == 8 ? GECKO_SCA_STAGES : 2;
+  static constexpr size_t LDS_BYTES = NSTAGE * ((size_t)KBYTES + (size_t)VBYTES);
   static constexpr int KLOADS = KBYTES / 16 / THREADS;  // 16-byte loads per thread per tile
   static constexpr int VLOADS = VBYTES / 16 / THREADS;
   static_assert(32 * QB * NW == kBM, "tile shape");
@@ -129,8 +139,8 @@ struct ScaLoop {
 
   const uint16_t* zbh;
   const uint16_t* vbh;
-  char* kbuf;  // two K stages
-  char* vbuf;  // two V stages
+  char* kbuf;  // K stages
+  char* vbuf;  // V stages
   int n, kbeg, kend, ntiles, myq0, wave_q0, wave_last, w, g, lq;
   u32x4 qf[QB][KS];
   uint32_t koff[T::KLOADS], voff[T::VLOADS];
@@ -148,7 +158,7 @@ struct ScaLoop {
     zbh = a.z + (size_t)bh * (size_t)n * D;
     vbh = a.v + (size_t)bh * (size_t)n * DV;
     kbuf = reinterpret_cast<char*>(lds);
-    vbuf = kbuf + 2 * T::KBYTES;
+    vbuf = kbuf + T::NSTAGE * T::KBYTES;
 
     // query fragments: lane holds query 32 qb + lq of the wave, features
     // 16 ks + 8 g + [0, 8); rows past the tile repeat its last query
@@ -310,46 +320,81 @@ struct ScaLoop {
     return mx;
   }
 
-  // one tile (in LDS stage SLOT = kt mod 2, a constant so that operand
-  // addresses fold into the read offsets): for each 32-key half, S^T,
-  // P = 2^(S - m) (m = 0 unless kSub), O^T += V^T P^T, and the row sums of
-  // the bf16 P actually multiplied into V. Halves whose first key is past
-  // every query of the wave are skipped.
-  template <int SLOT, bool kSub>
-  __device__ __forceinline__ void tile(int kt, const float (&msub)[QB], float (&lrun)[QB],
-                                       f32x16 (&oacc)[QB][NMV]) const {
-    constexpr int slot = SLOT;
-    stage(kt + 1, slot ^ 1);  // replaces tile kt-1, read last iteration
-    const int kb = kbeg + kt * kBN;
+  // whether half mb of key tile kt has a key some query of this wave sees
+  // (wave-uniform)
+  __device__ __forceinline__ bool live(int kt, int mb) const {
+    return kt < ntiles && kbeg + kt * kBN + 32 * mb <= wave_last;
+  }
+
+  // P = 2^(S - m) (m = 0 unless kSub) for half mb of tile kt, packed as the
+  // B operand of V^T P^T, and the row sums of the bf16 P that multiply V
+  template <bool kSub>
+  __device__ __forceinline__ void softmax_half(int kt, int mb, const float (&msub)[QB], const f32x16 (&sc)[QB],
+                                               float (&lrun)[QB], u32x4 (&pf)[QB][2]) const {
     const bool masked = needs_mask(kt);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      if (kb + 32 * mb > wave_last) break;  // wave-uniform
-      f32x16 sc[QB];
-      qk(slot, mb, sc);
-      u32x4 pf[QB][2];
+    for (int qb = 0; qb < QB; ++qb) {
+      float e[16];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float e[16];
+      for (int r = 0; r < 16; ++r) e[r] = exp2_fast(kSub ? sc[qb][r] - msub[qb] : sc[qb][r]);
+      if (masked) {
+        const int lim = last_visible(kt, qb);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = exp2_fast(kSub ? sc[qb][r] - msub[qb] : sc[qb][r]);
-        if (masked) {
-          const int lim = last_visible(kt, qb);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-            e[r] = ko > lim ? 0.f : e[r];
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const float* x = e + 8 * hh;
-          pf[qb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lrun[qb] = sum2_bf16(pf[qb][hh][i], lrun[qb]);
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+          e[r] = ko > lim ? 0.f : e[r];
         }
       }
-      pv(slot, mb, pf, oacc);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float* x = e + 8 * hh;
+        pf[qb][hh] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lrun[qb] = sum2_bf16(pf[qb][hh][i], lrun[qb]);
+      }
+    }
+  }
+
+  // S^T, softmax and O^T += V^T P^T for half mb of tile kt (in stage STG)
+  template <int STG, bool kSub>
+  __device__ __forceinline__ void half(int kt, int mb, const float (&msub)[QB], float (&lrun)[QB],
+                                       f32x16 (&oacc)[QB][NMV]) const {
+    f32x16 sc[QB];
+    qk(STG, mb, sc);
+    u32x4 pf[QB][2];
+    softmax_half<kSub>(kt, mb, msub, sc, lrun, pf);
+    pv(STG, mb, pf, oacc);
+  }
+
+  // Interval k of a pass (k = 0 .. ntiles; STG = k mod NSTAGE, a constant so
+  // that operand addresses fold into the read offsets). Every wave stages
+  // its share of tile k + 1 and ends at the barrier. Without phase offset
+  // (or for waves 0..3) the interval computes tile k. With three stages,
+  // waves 4..7 run half a tile behind: they first finish half 1 of tile
+  // k - 1 (scores computed last interval, kept in sc1), then do half 0 of
+  // tile k and only the scores of its half 1; so while one wave of a SIMD is
+  // in its exponentials the other is issuing MFMAs. The stage being filled,
+  // (k + 1) mod 3, was last read in interval k - 1. Both groups run the same
+  // code so that register allocation is shared.
+  template <int STG, bool kSub>
+  __device__ __forceinline__ void interval(int k, const float (&msub)[QB], float (&lrun)[QB],
+                                           f32x16 (&oacc)[QB][NMV], f32x16 (&sc1)[QB]) const {
+    constexpr int NS = T::NSTAGE;
+    const bool late = GECKO_SCA_PINGPONG && NS == 3 && w >= 4;  // wave-uniform
+    if (k + 1 < ntiles) stage(k + 1, (STG + 1) % NS);
+    if (late && k >= 1 && live(k - 1, 1)) {
+      u32x4 pf[QB][2];
+      softmax_half<kSub>(k - 1, 1, msub, sc1, lrun, pf);
+      pv((STG + NS - 1) % NS, 1, pf, oacc);
+    }
+    if (live(k, 0)) half<STG, kSub>(k, 0, msub, lrun, oacc);
+    if (live(k, 1)) {
+      qk(STG, 1, sc1);
+      if (!late) {
+        u32x4 pf[QB][2];
+        softmax_half<kSub>(k, 1, msub, sc1, lrun, pf);
+        pv(STG, 1, pf, oacc);
+      }
     }
     wait_vmem();
     __syncthreads();
@@ -358,15 +403,20 @@ struct ScaLoop {
   // full pass with fixed softmax offsets; returns the row exp-sums
   template <bool kSub>
   __device__ __forceinline__ void pass(const float (&msub)[QB], float (&ltot)[QB], f32x16 (&oacc)[QB][NMV]) const {
+    constexpr int NS = T::NSTAGE;
     stage(0, 0);
     wait_vmem();
     __syncthreads();
     float lrun[QB];
+    f32x16 sc1[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      tile<0, kSub>(kt, msub, lrun, oacc);
-      if (kt + 1 < ntiles) tile<1, kSub>(kt + 1, msub, lrun, oacc);
+    const int nint = (GECKO_SCA_PINGPONG && NS == 3) ? ntiles + 1 : ntiles;
+    for (int k = 0; k < nint; k += NS) {
+      interval<0, kSub>(k, msub, lrun, oacc, sc1);
+      if (k + 1 < nint) interval<1, kSub>(k + 1, msub, lrun, oacc, sc1);
+      if constexpr (NS == 3)
+        if (k + 2 < nint) interval<2, kSub>(k + 2, msub, lrun, oacc, sc1);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) ltot[qb] = other_half_sum(lrun[qb]);
