@@ -177,8 +177,10 @@ gecko_status run(const Call& k) {
     e = bf16 ? gecko::launch_awm_chunk_bf16(p, w, s) : gecko::launch_awm_chunk_f32(p, w, s);
     if (e != hipSuccess) return hip_fail(e, "memory chunk pass launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = gecko::launch_awm_zscan(p, w, s);
-    if (e != hipSuccess) return hip_fail(e, "denominator prefix launch");
+    if (!bf16) {  // the bf16 scan keeps the running denominator itself
+      e = gecko::launch_awm_zscan(p, w, s);
+      if (e != hipSuccess) return hip_fail(e, "denominator prefix launch");
+    }
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = bf16 ? gecko::launch_awm_scan_bf16(p, w, s) : gecko::launch_awm_scan_f32(p, w, s);
     if (e != hipSuccess) return hip_fail(e, "memory scan launch");

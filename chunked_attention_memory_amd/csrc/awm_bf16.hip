@@ -79,8 +79,8 @@ struct ChunkArgs {
   const uint16_t* v;
   const float* eta_k;
   const float* rho_k;
-  float* g;          // [bh][t][dv/32][d][32]
-  uint16_t* hm;      // [bh][t][d][d]
+  float* g;          // G^T accumulators, [bh][t][dv/32][d/32][64 lanes][16]
+  uint16_t* hm;      // H^T accumulators in scan-operand order, [bh][t][d/16][d/32][64 lanes][8]
   float* cmax;       // [bh][t][d] (log2 units)
   float* csum;       // [bh][t][d]
   int64_t n, c, nmem;
@@ -383,22 +383,29 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
     a.cmax[row * D + f] = m;
     a.csum[row * D + f] = ltot;
   }
-  // accumulator (block, r): column f, row 8 (r >> 2) + 4 g + (r & 3) of the block
-  float* gt = a.g + row * (int64_t)NMV * D * 32;
+  // G^T accumulators as they are: block mv, wave w, lane, 16 registers
+  // (column f, value rows 32 mv + 8 (r >> 2) + 4 g + (r & 3)); the scan reads
+  // them back in the same layout
 #pragma unroll
-  for (int mv = 0; mv < NMV; ++mv)
+  for (int mv = 0; mv < NMV; ++mv) {
+    f32x4* gt = reinterpret_cast<f32x4*>(a.g + ((((row * NMV + mv) * T::NW + L.w) * 64) + L.lane) * 16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 val{accg[mv][4 * q], accg[mv][4 * q + 1], accg[mv][4 * q + 2], accg[mv][4 * q + 3]};
-      *reinterpret_cast<f32x4*>(gt + ((int64_t)mv * D + f) * 32 + 8 * q + 4 * g) = val;
-    }
-  uint16_t* ht = a.hm + row * (int64_t)D * D + (int64_t)f * D;
+    for (int q = 0; q < 4; ++q) gt[q] = f32x4{accg[mv][4 * q], accg[mv][4 * q + 1], accg[mv][4 * q + 2], accg[mv][4 * q + 3]};
+  }
+  // H^T accumulators (column f, rows f' = 32 mf + 8 (r >> 2) + 4 g + (r & 3)) as
+  // the scan's B operand: k-step ks = 2 mf + p holds registers 8 p .. 8 p + 7,
+  // i.e. f' = 32 mf + 16 p + 8 (e >> 2) + 4 g + (e & 3) for element e; stored
+  // [ks][wave][lane][8] so that a scan load of 16 bytes per lane is contiguous
+  uint16_t* ht = a.hm + row * (int64_t)D * D;
 #pragma unroll
   for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x2 val{pack2(acch[mf][4 * q], acch[mf][4 * q + 1]), pack2(acch[mf][4 * q + 2], acch[mf][4 * q + 3])};
-      *reinterpret_cast<u32x2*>(ht + 32 * mf + 8 * q + 4 * g) = val;
+    for (int pp = 0; pp < 2; ++pp) {
+      const f32x16& x = acch[mf];
+      const int o = 8 * pp;
+      const u32x4 val{pack2(x[o], x[o + 1]), pack2(x[o + 2], x[o + 3]), pack2(x[o + 4], x[o + 5]),
+                      pack2(x[o + 6], x[o + 7])};
+      st16(ht + ((int64_t)((2 * mf + pp) * T::NW + L.w) * 64 + L.lane) * 8, val);
     }
 }
 
@@ -446,111 +453,135 @@ __global__ void awm_zscan_kernel(const float* __restrict__ cmax, const float* __
 
 // ---------------------------------------------------------------- scan
 struct ScanArgs {
-  const float* g;
-  const uint16_t* hm;
-  const float* decay;
-  const float* wscale;
-  uint16_t* snap;  // [bh][t][dv][d]
+  const float* g;      // chunk-pass accumulators of G^T, [bh][t][dv/32][d/32][64 lanes][16]
+  const uint16_t* hm;  // [bh][t][d/16][d/32][64 lanes][8] bf16, see the chunk pass
+  const float* cmax;   // [bh][t][d] (log2 units)
+  const float* csum;   // [bh][t][d]
+  uint16_t* snap;      // [bh][t][d][dv]: M'_{t+2}, read by chunk t + 2 (0-based)
   int64_t nmem;
-  int no_delta;    // drop the H_t M' term (test variant)
+  int no_delta;        // drop the H_t M' term (test variant)
 };
 
-// Operands of one scan step, loaded ahead of use.
+// Operands of one scan step for one lane, loaded ahead of use.
 template <int D>
 struct ScanStep {
   static constexpr int KS = D / 16;
-  u32x4 hf[KS];  // rows 32 w + lq of H_t, features 16 ks + 8 g + [0, 8)
-  float gv[16], dc[16], ws[16];
+  u32x4 hf[KS];  // H_t[f][f'] for k-step ks: f' = 16 ks + 8 (e >> 2) + 4 g + (e & 3)
+  f32x4 gv[4];   // G_t^T of this lane's 16 accumulator cells
+  float cm, cs;  // max (log2) and exp-sum of feature f over chunk t
 };
 
-// One workgroup per (batch*head, 32-column slice of M'). Wave w keeps rows
-// [32 w, 32 w + 32) of the slice in fp32 registers (MFMA accumulator layout);
-// a bf16 copy of the whole slice goes through LDS each step as the B operand
-// of H_t M' and is written out as the snapshot that chunk t + 2 reads. Step
-// operands are prefetched kDepth steps ahead; block b handles slice b / BH
-// of batch*head b % BH, so with BH a multiple of 8 all slices of a head run
-// on one XCD and share its L2.
-template <int D, int DV>
+// One workgroup per (batch*head, 32-value slice j of M'), working on the
+// transpose: wave w holds M'^T[v][f] for features f = 32 w + lq (one per
+// lane, both halves of the wave) and the slice's values v in MFMA
+// accumulator layout (register r: v = 8 (r >> 2) + 4 g + (r & 3)), which is
+// also the layout in which the chunk pass stored G^T, so a lane's G_t is 64
+// contiguous bytes. A step is
+//   M'^T <- decay_f M'^T + wscale_f (G_t^T - M'^T H_t^T)
+// with decay_f = z^{t-1}/z^t and wscale_f = 2^{m_t}/z^t from the running
+// per-feature exp-sum z^t = 2^M L (kept in log2 form by each lane for its
+// feature). M'^T H_t^T is one MFMA chain: A = M'^T read (transposed) from a
+// bf16 copy of the slice in LDS ([f][v]), B = rows of H_t from HBM. The copy
+// is also the snapshot that chunk t + 2 reads. Step operands are prefetched
+// kDepth steps ahead; block b handles slice b / BH of batch*head b % BH, so
+// with BH a multiple of 8 all slices of a head run on one XCD.
+template <int D, int DV, bool kNoDelta>
 __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
   constexpr int NMV = DV / 32;
+  constexpr int NW = D / 32;
   constexpr int KS = D / 16;
-  constexpr int MROW = D + 8;
   constexpr int kDepth = 4;
-  __shared__ __attribute__((aligned(16))) uint16_t mt[2][32 * MROW];
+  __shared__ __attribute__((aligned(16))) uint16_t mt[2][D * 32];  // [f][v] bf16
 
   const int64_t BH = gridDim.x / NMV;
   const int64_t bh = blockIdx.x % BH;
   const int j = (int)(blockIdx.x / BH);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
+  const int f = 32 * w + lq;
   const int64_t nmem = a.nmem;
+  // transpose read of the copy, in the k order of the H operand: element e =
+  // 4 jj + e' of lane (lq, g) at k-step ks is mt[16 ks + 8 jj + 4 g + e'][lq];
+  // source lane s of each 16-lane group points at row 16 ks + 8 jj + 4 g +
+  // s / 4, columns 16 (group % 2) + 4 (s % 4) + [0, 4). Rows are 64 bytes, so
+  // the 32 lanes of a pass read 4 whole rows: every LDS bank once.
+  const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+  const int trb = (4 * g + (sl >> 2)) * 64 + (16 * grp2 + 4 * (sl & 3)) * 2;
 
+  ScanStep<D> ring[kDepth];
   auto load_step = [&](int64_t t, ScanStep<D>& q) {
     const int64_t row = bh * nmem + t;
-    const uint16_t* ht = a.hm + row * (int64_t)D * D + (int64_t)(32 * w + lq) * D;
+    const uint16_t* ht = a.hm + row * (int64_t)D * D + ((int64_t)w * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(ht + 16 * ks + 8 * g);
-    const float* gt = a.g + ((row * NMV + j) * D) * 32;
+    for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(ht + (int64_t)ks * NW * 64 * 8);
+    const f32x4* gt = reinterpret_cast<const f32x4*>(a.g + ((((row * NMV + j) * NW + w) * 64) + lane) * 16);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int fr = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-      q.gv[r] = gt[(int64_t)fr * 32 + lq];
-    }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int fr = 32 * w + 8 * qq + 4 * g;
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(a.decay + row * D + fr);
-      const f32x4 w4 = *reinterpret_cast<const f32x4*>(a.wscale + row * D + fr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q.dc[4 * qq + i] = d4[i];
-        q.ws[4 * qq + i] = w4[i];
-      }
-    }
+    for (int i = 0; i < 4; ++i) q.gv[i] = gt[i];
+    q.cm = a.cmax[row * D + f];
+    q.cs = a.csum[row * D + f];
   };
 
   f32x16 mst = f32x16{};
+  float zM = kNegInf, zL = 0.f;
   int buf = 0;
   auto step = [&](int64_t t, const ScanStep<D>& q) {
+    // running denominator of feature f
+    const float Mn = fmaxf(zM, q.cm);
+    const float old = zM == kNegInf ? 0.f : zL * exp2_fast(zM - Mn);
+    const float cur = exp2_fast(q.cm - Mn);
+    const float Ln = old + q.cs * cur;
+    const float inv = 1.f / Ln;
+    const float dc = old * inv, ws = cur * inv;
+    zM = Mn;
+    zL = Ln;
     f32x16 p0 = f32x16{}, p1 = f32x16{};
-    if (t > 0 && !a.no_delta) {
+    if constexpr (!kNoDelta) {  // at t = 0 the copy holds M'_1 = 0
+      const char* mb = reinterpret_cast<const char*>(mt[buf]) + trb;
 #pragma unroll
       for (int ks = 0; ks < KS; ks += 2) {
-        p0 = mfma_bf16(q.hf[ks], ld16(&mt[buf][lq * MROW + 16 * ks + 8 * g]), p0);
-        p1 = mfma_bf16(q.hf[ks + 1], ld16(&mt[buf][lq * MROW + 16 * (ks + 1) + 8 * g]), p1);
+        const u32x2 a0 = lds_read_tr(mb + (16 * ks) * 64), a1 = lds_read_tr(mb + (16 * ks + 8) * 64);
+        const u32x2 b0 = lds_read_tr(mb + (16 * ks + 16) * 64), b1 = lds_read_tr(mb + (16 * ks + 24) * 64);
+        p0 = mfma_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, q.hf[ks], p0);
+        p1 = mfma_bf16(u32x4{b0[0], b0[1], b1[0], b1[1]}, q.hf[ks + 1], p1);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mst[r] = q.dc[r] * mst[r] + q.ws[r] * (q.gv[r] - (p0[r] + p1[r]));
-    // bf16 copy: row v = lq of the slice, features 32 w + 8 qq + 4 g + [0, 4)
+    for (int r = 0; r < 16; ++r) mst[r] = dc * mst[r] + ws * (q.gv[r >> 2][r & 3] - (p0[r] + p1[r]));
+    // bf16 copy: column f, values 8 qq + 4 g + [0, 4)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const u32x2 pk{pack2(mst[4 * qq], mst[4 * qq + 1]), pack2(mst[4 * qq + 2], mst[4 * qq + 3])};
-      *reinterpret_cast<u32x2*>(&mt[buf ^ 1][lq * MROW + 32 * w + 8 * qq + 4 * g]) = pk;
+      *reinterpret_cast<u32x2*>(&mt[buf ^ 1][f * 32 + 8 * qq + 4 * g]) = pk;
     }
     __syncthreads();
-    // snapshot rows 32 j .. 32 j + 31 of M'_{t+2}^T
-    uint16_t* sn = a.snap + ((bh * nmem + t) * DV + 32 * j) * D;
-    for (int e = tid; e < 32 * D / 8; e += 2 * D) {
-      const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-      st16(sn + (int64_t)r * D + cc, ld16(&mt[buf ^ 1][r * MROW + cc]));
+    // snapshot rows f of M'_{t+2}, values 32 j .. 32 j + 31: 64 bytes per row
+    uint16_t* sn = a.snap + (bh * nmem + t) * (int64_t)D * DV + 32 * j;
+#pragma unroll
+    for (int e = tid; e < D * 4; e += 2 * D) {
+      const int r = e >> 2, cc = (e & 3) * 8;
+      st16(sn + (int64_t)r * DV + cc, ld16(&mt[buf ^ 1][r * 32 + cc]));
     }
     buf ^= 1;
   };
 
-  ScanStep<D> ring[kDepth];
+  // M'_1 = 0
+  for (int e = tid; e < D * 32 / 8; e += 2 * D) st16(&mt[0][8 * e], u32x4{0u, 0u, 0u, 0u});
+  __syncthreads();
+  // Steady state without branches, so that the compiler can count the loads
+  // in flight exactly; loads past the last step re-read it (unused).
+  const int64_t last = nmem - 1;
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k)
-    if (k < nmem) load_step(k, ring[k]);
-  for (int64_t t0 = 0; t0 < nmem; t0 += kDepth) {
+  for (int k = 0; k < kDepth; ++k) load_step(min((int64_t)k, last), ring[k]);
+  int64_t t0 = 0;
+  for (; t0 + kDepth <= nmem; t0 += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      const int64_t t = t0 + k;
-      if (t < nmem) {
-        step(t, ring[k]);
-        if (t + kDepth < nmem) load_step(t + kDepth, ring[k]);
-      }
+      step(t0 + k, ring[k]);
+      load_step(min(t0 + k + kDepth, last), ring[k]);
     }
   }
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k)
+    if (t0 + k < nmem) step(t0 + k, ring[k]);
 }
 
 template <int D, int DV>
@@ -572,7 +603,11 @@ hipError_t launch_chunk(const ChunkArgs& a, int64_t BH, hipStream_t s) {
 
 template <int D, int DV>
 hipError_t launch_scan(const ScanArgs& a, int64_t BH, hipStream_t s) {
-  hipLaunchKernelGGL((awm_scan_bf16_kernel<D, DV>), dim3((unsigned)(BH * (DV / 32))), dim3(2 * D), 0, s, a);
+  const dim3 grid((unsigned)(BH * (DV / 32)));
+  if (a.no_delta)
+    hipLaunchKernelGGL((awm_scan_bf16_kernel<D, DV, true>), grid, dim3(2 * D), 0, s, a);
+  else
+    hipLaunchKernelGGL((awm_scan_bf16_kernel<D, DV, false>), grid, dim3(2 * D), 0, s, a);
   return hipGetLastError();
 }
 
@@ -602,7 +637,7 @@ hipError_t launch_awm_zscan(const Problem& p, const Workspace& w, hipStream_t s)
 
 hipError_t launch_awm_scan_bf16(const Problem& p, const Workspace& w, hipStream_t s) {
   ScanArgs a;
-  a.g = w.g; a.hm = static_cast<const uint16_t*>(w.h); a.decay = w.decay; a.wscale = w.wscale;
+  a.g = w.g; a.hm = static_cast<const uint16_t*>(w.h); a.cmax = w.cmax; a.csum = w.csum;
   a.snap = static_cast<uint16_t*>(w.snap); a.nmem = p.nmem;
   a.no_delta = (p.flags & GECKO_AWM_NO_DELTA_BIT) ? 1 : 0;
   const int64_t BH = p.B * p.H;

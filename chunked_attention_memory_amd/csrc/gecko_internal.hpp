@@ -27,13 +27,14 @@ struct Problem {
 // Workspace carve-up (byte offsets from the workspace base). Every array is
 // indexed [bh][t] with t = 0..nmem-1 the 0-based chunk that is written.
 struct Workspace {
-  float* g;        // memory-write product E^T V        [bh][t][dv/32][d][32] fp32
+  float* g;        // memory-write product E^T V, fp32: bf16 path [bh][t][dv/32][d/32][64][16]
+                   //   (MFMA accumulator layout), fp32 path [bh][t][dv/32][d][32]
   void* h;         // correction product E^T psi(K_m)   [bh][t][d][d]  (bf16 or fp32)
   float* cmax;     // per-feature max of K_m over the chunk   [bh][t][d]
   float* csum;     // per-feature sum of exp(K_m - cmax)     [bh][t][d]
-  float* decay;    // z^{t-1} / z^t                          [bh][t][d]
-  float* wscale;   // exp(cmax) / z^t                        [bh][t][d]
-  void* snap;      // state read by chunk t+2: [bh][t][dv][d]  (bf16 or fp32)
+  float* decay;    // z^{t-1} / z^t (fp32 path)              [bh][t][d]
+  float* wscale;   // exp(cmax) / z^t (fp32 path)            [bh][t][d]
+  void* snap;      // state read by chunk t+2: bf16 [bh][t][d][dv], fp32 [bh][t][dv][d]
   float* rowstat;  // fp32 path only: per-token (max, sum) of K_m rows  [bh][n][2]
   size_t bytes;
 };

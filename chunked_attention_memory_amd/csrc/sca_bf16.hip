@@ -120,7 +120,7 @@ struct ScaArgs {
   const float* kappa_k;
   const float* eta_q;
   const float* rho_q;
-  const uint16_t* snap;  // [bh][nmem][dv][d]; slot t is the state read by chunk t + 2 (0-based)
+  const uint16_t* snap;  // [bh][nmem][d][dv]; slot t is the state read by chunk t + 2 (0-based)
   int64_t n;
   int c, nchunks, nmem, qtiles, nblocks, per_xcd, H;
 };
@@ -514,78 +514,99 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 
   if constexpr (kRead) {
     if (s >= 2) {
-      // M'_{s-1} (stored transposed: dv rows of d features) goes to LDS once
-      // per workgroup, rows chunk-swizzled like K; the attention loop ended
-      // with a barrier, so its stages are free.
+      // M'_{s-1} ([d][dv], feature rows) goes to LDS once per workgroup with
+      // the V tiles' layout and swizzle: the readout psi(Q_m) M' is then the
+      // PV product with features in the role of keys. The attention loop
+      // ended with a barrier, so its stages are free.
       using T = ScaTile<D, DV, QB>;
-      constexpr int RB = 64;                          // rows per staging call
-      constexpr int SLOADS = RB * D * 2 / 16 / T::THREADS;
-      constexpr int KCH = D / 8;
+      constexpr int RB = 64;                             // rows per staging call
+      constexpr int SLOADS = RB * DV * 2 / 16 / T::THREADS;
+      constexpr int VCH = DV / 8;
       char* sbuf = reinterpret_cast<char*>(lds);
-      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(DV * D);
+      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(D * DV);
       {
         uint32_t soff[SLOADS];
 #pragma unroll
         for (int i = 0; i < SLOADS; ++i) {
           const int P = (T::NW * i + w) * 64 + lane;
-          const int r = P / KCH, p = P % KCH;
-          soff[i] = (uint32_t)(r * D + 8 * (p ^ kswz<D>(r))) * 2u;
+          const int r = P / VCH, p = P % VCH;
+          soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
         }
 #pragma unroll
-        for (int rb = 0; rb < DV / RB; ++rb)
-          stage_rows(sn, rb * RB, DV, D, sbuf + rb * RB * D * 2, T::NW, w, soff, SLOADS);
+        for (int rb = 0; rb < D / RB; ++rb)
+          stage_rows(sn, rb * RB, D, DV, sbuf + rb * RB * DV * 2, T::NW, w, soff, SLOADS);
       }
-      // A operand of value block mv, k-step ks: row 32 mv + perm_row(lq),
-      // logical chunk 2 ks + g (the swizzle depends on the row mod 16 only)
-      const int prow = perm_row(lq);
+      // psi(Q_m) as the B operand: element e of lane (lq, g) in k-step
+      // (fb, hh) is feature 32 fb + 16 hh + 8 (e >> 2) + 4 g + (e & 3)
+      constexpr int NFB = D / 32;
       const float* eq = a.eta_q + h * D;
       const float* rq = a.rho_q + h * D;
-      u32x4 pf[QB][KS];
+      u32x4 pf[QB][NFB][2];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        // psi(Q_m) of this lane's query, features 16 ks + 8 g + [0, 8)
         const int qrow = min(myq0 + 32 * qb, qend - 1);
-        float qm[KS * 8];
+        float qm[NFB][2][8];
         float mx = kNegInf;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int f0 = 16 * ks + 8 * g;
-          const u32x4 raw = ld16(zbh + (size_t)qrow * D + f0);
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            qm[8 * ks + 2 * j] = (eq[f0 + 2 * j] * bf_lo(raw[j]) + rq[f0 + 2 * j]) * kLog2e;
-            qm[8 * ks + 2 * j + 1] = (eq[f0 + 2 * j + 1] * bf_hi(raw[j]) + rq[f0 + 2 * j + 1]) * kLog2e;
-          }
+          for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) mx = fmaxf(mx, qm[8 * ks + i]);
-        }
+            for (int jh = 0; jh < 2; ++jh) {
+              const int f0 = 32 * fb + 16 * hh + 8 * jh + 4 * g;
+              const u32x2 raw = *reinterpret_cast<const u32x2*>(zbh + (size_t)qrow * D + f0);
+              const f32x4 e4 = *reinterpret_cast<const f32x4*>(eq + f0);
+              const f32x4 r4 = *reinterpret_cast<const f32x4*>(rq + f0);
+              float* x = qm[fb][hh] + 4 * jh;
+              x[0] = (e4[0] * bf_lo(raw[0]) + r4[0]) * kLog2e;
+              x[1] = (e4[1] * bf_hi(raw[0]) + r4[1]) * kLog2e;
+              x[2] = (e4[2] * bf_lo(raw[1]) + r4[2]) * kLog2e;
+              x[3] = (e4[3] * bf_hi(raw[1]) + r4[3]) * kLog2e;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[i]);
+            }
         mx = other_half_max(mx);
         float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < KS * 8; ++i) {
-          qm[i] = exp2_fast(qm[i] - mx);
-          sum += qm[i];
-        }
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              qm[fb][hh][e] = exp2_fast(qm[fb][hh][e] - mx);
+              sum += qm[fb][hh][e];
+            }
         sum = other_half_sum(sum);
         const float inv = 1.f / sum;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const float* e = qm + 8 * ks;
-          pf[qb][ks] = u32x4{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
-                             pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
-        }
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float* e = qm[fb][hh];
+            pf[qb][fb][hh] = u32x4{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
+                                   pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+          }
       }
       wait_vmem();
       __syncthreads();
+      // A operand: V^T-style transpose reads of the staged M' (see ScaLoop::v_addr)
+      const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+      const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+      const int r0 = 4 * g + (sl >> 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = prow * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(prow));
+      for (int mv = 0; mv < NMV; ++mv) {
+        const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+        const char* base = sbuf + r0 * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
 #pragma unroll
-        for (int mv = 0; mv < NMV; ++mv) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(sbuf + off + 32 * mv * (D * 2));
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(af, pf[qb][ks], oacc[qb][mv]);
-        }
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x2 l2 = lds_read_tr(base + (32 * fb + 16 * hh) * (DV * 2));
+            const u32x2 h2 = lds_read_tr(base + (32 * fb + 16 * hh + 8) * (DV * 2));
+            const u32x4 af{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(af, pf[qb][fb][hh], oacc[qb][mv]);
+          }
       }
     }
   }
