@@ -59,14 +59,6 @@ namespace {
 #ifndef GECKO_SCA_SCHED
 #define GECKO_SCA_SCHED 1
 #endif
-// LDS stages of the 8-wave layout (2 or 3) and, with 3, whether waves 4..7
-// run half a tile behind waves 0..3.
-#ifndef GECKO_SCA_STAGES
-#define GECKO_SCA_STAGES 2
-#endif
-#ifndef GECKO_SCA_PINGPONG
-#define GECKO_SCA_PINGPONG 0
-#endif
 #ifndef GECKO_SCA_KAHEAD
 #define GECKO_SCA_KAHEAD 2
 #endif
@@ -89,9 +81,12 @@ struct ScaTile {
   static constexpr int THREADS = 64 * NW;
   static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
   static constexpr int VBYTES = kBN * DV * 2;
-  // (K, V) stages in LDS; the wave groups can run out of phase only with three
-  static constexpr int NSTAGE = NW == 8 ? GECKO_SCA_STAGES : 2;
-  static constexpr size_t LDS_BYTES = NSTAGE * ((size_t)KBYTES + (size_t)VBYTES);
+  static constexpr int NSTAGE = 2;  // (K, V) stages in LDS
+  static constexpr size_t STAGE_BYTES = NSTAGE * ((size_t)KBYTES + (size_t)VBYTES);
+  static constexpr size_t SNAP_BYTES = (size_t)D * DV * 2;  // the memory state for the readout
+  static constexpr size_t lds_bytes(bool sca, bool read) {
+    return (sca ? STAGE_BYTES : 0) + (read ? SNAP_BYTES : 0);
+  }
   static constexpr int KLOADS = KBYTES / 16 / THREADS;  // 16-byte loads per thread per tile
   static constexpr int VLOADS = VBYTES / 16 / THREADS;
   static_assert(32 * QB * NW == kBM, "tile shape");
@@ -366,36 +361,16 @@ struct ScaLoop {
     pv(STG, mb, pf, oacc);
   }
 
-  // Interval k of a pass (k = 0 .. ntiles; STG = k mod NSTAGE, a constant so
-  // that operand addresses fold into the read offsets). Every wave stages
-  // its share of tile k + 1 and ends at the barrier. Without phase offset
-  // (or for waves 0..3) the interval computes tile k. With three stages,
-  // waves 4..7 run half a tile behind: they first finish half 1 of tile
-  // k - 1 (scores computed last interval, kept in sc1), then do half 0 of
-  // tile k and only the scores of its half 1; so while one wave of a SIMD is
-  // in its exponentials the other is issuing MFMAs. The stage being filled,
-  // (k + 1) mod 3, was last read in interval k - 1. Both groups run the same
-  // code so that register allocation is shared.
+  // Tile k of a pass in stage STG = k mod 2 (a constant, so that operand
+  // addresses fold into the read offsets): stage this wave's share of tile
+  // k + 1 into the other stage (read last iteration), compute the halves of
+  // tile k that some query of the wave sees, end at the barrier.
   template <int STG, bool kSub>
-  __device__ __forceinline__ void interval(int k, const float (&msub)[QB], float (&lrun)[QB],
-                                           f32x16 (&oacc)[QB][NMV], f32x16 (&sc1)[QB]) const {
-    constexpr int NS = T::NSTAGE;
-    const bool late = GECKO_SCA_PINGPONG && NS == 3 && w >= 4;  // wave-uniform
-    if (k + 1 < ntiles) stage(k + 1, (STG + 1) % NS);
-    if (late && k >= 1 && live(k - 1, 1)) {
-      u32x4 pf[QB][2];
-      softmax_half<kSub>(k - 1, 1, msub, sc1, lrun, pf);
-      pv((STG + NS - 1) % NS, 1, pf, oacc);
-    }
+  __device__ __forceinline__ void tile(int k, const float (&msub)[QB], float (&lrun)[QB],
+                                       f32x16 (&oacc)[QB][NMV]) const {
+    if (k + 1 < ntiles) stage(k + 1, STG ^ 1);
     if (live(k, 0)) half<STG, kSub>(k, 0, msub, lrun, oacc);
-    if (live(k, 1)) {
-      qk(STG, 1, sc1);
-      if (!late) {
-        u32x4 pf[QB][2];
-        softmax_half<kSub>(k, 1, msub, sc1, lrun, pf);
-        pv(STG, 1, pf, oacc);
-      }
-    }
+    if (live(k, 1)) half<STG, kSub>(k, 1, msub, lrun, oacc);
     wait_vmem();
     __syncthreads();
   }
@@ -403,23 +378,31 @@ struct ScaLoop {
   // full pass with fixed softmax offsets; returns the row exp-sums
   template <bool kSub>
   __device__ __forceinline__ void pass(const float (&msub)[QB], float (&ltot)[QB], f32x16 (&oacc)[QB][NMV]) const {
-    constexpr int NS = T::NSTAGE;
     stage(0, 0);
     wait_vmem();
     __syncthreads();
     float lrun[QB];
-    f32x16 sc1[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
-    const int nint = (GECKO_SCA_PINGPONG && NS == 3) ? ntiles + 1 : ntiles;
-    for (int k = 0; k < nint; k += NS) {
-      interval<0, kSub>(k, msub, lrun, oacc, sc1);
-      if (k + 1 < nint) interval<1, kSub>(k + 1, msub, lrun, oacc, sc1);
-      if constexpr (NS == 3)
-        if (k + 2 < nint) interval<2, kSub>(k + 2, msub, lrun, oacc, sc1);
+    for (int k = 0; k < ntiles; k += 2) {
+      tile<0, kSub>(k, msub, lrun, oacc);
+      if (k + 1 < ntiles) tile<1, kSub>(k + 1, msub, lrun, oacc);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) ltot[qb] = other_half_sum(lrun[qb]);
+  }
+
+  // OR of a per-lane flag over the workgroup, through a word of the K stage
+  // memory (free between passes; every wave is past the pass's last barrier)
+  __device__ __forceinline__ bool block_any(bool x) const {
+    volatile int* flag = reinterpret_cast<volatile int*>(kbuf);
+    if (threadIdx.x == 0) *flag = 0;
+    __syncthreads();
+    if (x) *flag = 1;
+    __syncthreads();
+    const bool any = *flag != 0;
+    __syncthreads();
+    return any;
   }
 
   // O^T for the wave's queries, normalised
@@ -436,7 +419,7 @@ struct ScaLoop {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
       redo = redo || (myq0 + 32 * qb < kend && !(ltot[qb] >= kUnderflow && ltot[qb] <= kOverflow));
-    if (__syncthreads_or(redo)) {
+    if (block_any(redo)) {
       float mx[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = kNegInf;
@@ -469,6 +452,23 @@ struct ScaLoop {
     }
   }
 };
+
+// A operand i of the readout (value block mv = i / (2 NFB), feature block
+// fb = (i / 2) % NFB, half hh = i % 2) from the staged state: the V^T
+// transpose reads of ScaLoop::v_addr with features in the role of keys.
+// A plain device function: a lambda in a kernel is compiled for the host too.
+template <int D, int DV>
+__device__ __forceinline__ u32x4 snap_operand(const char* sbuf, int lane, int i) {
+  constexpr int NFB = D / 32;
+  const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
+  const int g = lane >> 5, sl = lane & 15, grp2 = (lane >> 4) & 1;
+  const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+  const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+  const char* base = sbuf + (4 * g + (sl >> 2)) * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
+  const u32x2 l2 = lds_read_tr(base + (32 * fb + 16 * hh) * (DV * 2));
+  const u32x2 h2 = lds_read_tr(base + (32 * fb + 16 * hh + 8) * (DV * 2));
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) void sca_bf16_kernel(ScaArgs a) {
@@ -506,6 +506,31 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 #pragma unroll
     for (int i = 0; i < NMV; ++i) oacc[qb][i] = f32x16{};
 
+  // The memory state M'_{s-1} ([d][dv], feature rows) is final before this
+  // kernel starts: it goes to its own LDS region now, behind the attention
+  // loop, with the V tiles' layout and swizzle (the readout psi(Q_m) M' is
+  // the PV product with features in the role of keys).
+  using T = ScaTile<D, DV, QB>;
+  char* sbuf = reinterpret_cast<char*>(lds) + (kSca ? T::STAGE_BYTES : 0);
+  if constexpr (kRead) {
+    if (s >= 2) {
+      constexpr int RB = 64;  // rows per staging call
+      constexpr int SLOADS = RB * DV * 2 / 16 / T::THREADS;
+      constexpr int VCH = DV / 8;
+      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(D * DV);
+      uint32_t soff[SLOADS];
+#pragma unroll
+      for (int i = 0; i < SLOADS; ++i) {
+        const int P = (T::NW * i + w) * 64 + lane;
+        const int r = P / VCH, p = P % VCH;
+        soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
+      }
+#pragma unroll
+      for (int rb = 0; rb < D / RB; ++rb)
+        stage_rows(sn, rb * RB, D, DV, sbuf + rb * RB * DV * 2, T::NW, w, soff, SLOADS);
+    }
+  }
+
   if constexpr (kSca) {
     ScaLoop<D, DV, QB> L;
     L.init(a, bh, h, n, s, c, q0, qend, w, lane, lds);
@@ -514,28 +539,6 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 
   if constexpr (kRead) {
     if (s >= 2) {
-      // M'_{s-1} ([d][dv], feature rows) goes to LDS once per workgroup with
-      // the V tiles' layout and swizzle: the readout psi(Q_m) M' is then the
-      // PV product with features in the role of keys. The attention loop
-      // ended with a barrier, so its stages are free.
-      using T = ScaTile<D, DV, QB>;
-      constexpr int RB = 64;                             // rows per staging call
-      constexpr int SLOADS = RB * DV * 2 / 16 / T::THREADS;
-      constexpr int VCH = DV / 8;
-      char* sbuf = reinterpret_cast<char*>(lds);
-      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(D * DV);
-      {
-        uint32_t soff[SLOADS];
-#pragma unroll
-        for (int i = 0; i < SLOADS; ++i) {
-          const int P = (T::NW * i + w) * 64 + lane;
-          const int r = P / VCH, p = P % VCH;
-          soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
-        }
-#pragma unroll
-        for (int rb = 0; rb < D / RB; ++rb)
-          stage_rows(sn, rb * RB, D, DV, sbuf + rb * RB * DV * 2, T::NW, w, soff, SLOADS);
-      }
       // psi(Q_m) as the B operand: element e of lane (lq, g) in k-step
       // (fb, hh) is feature 32 fb + 16 hh + 8 (e >> 2) + 4 g + (e & 3)
       constexpr int NFB = D / 32;
@@ -589,24 +592,18 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
       }
       wait_vmem();
       __syncthreads();
-      // A operand: V^T-style transpose reads of the staged M' (see ScaLoop::v_addr)
-      const int sl = lane & 15, grp2 = (lane >> 4) & 1;
-      const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
-      const int r0 = 4 * g + (sl >> 2);
+      // A operand: V^T-style transpose reads of the staged M' (see
+      // ScaLoop::v_addr), read AH MFMA operands ahead
+      constexpr int NI = NMV * NFB * 2, AH = 2;
+      u32x4 op[AH + 1];
 #pragma unroll
-      for (int mv = 0; mv < NMV; ++mv) {
-        const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-        const char* base = sbuf + r0 * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
+      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV>(sbuf, lane, i);
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
+      for (int i = 0; i < NI; ++i) {
+        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV>(sbuf, lane, i + AH);
+        const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x2 l2 = lds_read_tr(base + (32 * fb + 16 * hh) * (DV * 2));
-            const u32x2 h2 = lds_read_tr(base + (32 * fb + 16 * hh + 8) * (DV * 2));
-            const u32x4 af{l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(af, pf[qb][fb][hh], oacc[qb][mv]);
-          }
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(op[i % (AH + 1)], pf[qb][fb][hh], oacc[qb][mv]);
       }
     }
   }
@@ -647,7 +644,8 @@ template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 hipError_t launch_one(const ScaArgs& a, hipStream_t stream) {
   using T = ScaTile<D, DV, ScaShape<D, DV>::QB>;
   auto kern = sca_bf16_kernel<D, DV, kSca, kRead, kOutF32>;
-  const size_t lds = max(kSca ? T::LDS_BYTES : (size_t)0, kRead ? (size_t)(DV * D * 2) : (size_t)0);
+  constexpr size_t lds = T::lds_bytes(kSca, kRead);
+  static_assert(lds <= 160 * 1024, "LDS per workgroup");
   if (lds > 65536) {
     static bool attr_set = false;  // per instantiation
     if (!attr_set) {
