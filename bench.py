@@ -3,14 +3,16 @@
 
 One step = one gecko_sca_awm_forward call over the whole 128K-token workload
 (B=1, H=8, n=131072, c=2048, d=128, dv=256, bf16 inputs, fp32 accumulation,
-bf16 output): memory chunk pass, denominator prefix, memory scan, then the
-attention kernel with the fused readout. Inputs are synthetic (seeded), and
-resident in HBM before the timed region starts.
+bf16 output): memory chunk pass, memory scan (with its running denominator),
+then the attention kernel with the fused readout. Inputs are synthetic
+(seeded), and resident in HBM before the timed region starts.
 
 Prints one JSON line. ``value`` is tokens/s (B * n / step time).
 ``roofline`` describes the attention kernel (the dominant one): algorithmic
 FLOPs per launch over its mean duration, measured with HIP events recorded on
 the library's stream between its kernels during the timed steps.
+``awm_scan`` gives the memory scan's mean duration and its HBM rate, from the
+algorithmic bytes and from the committed counter summary's measured bytes.
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
 workload on this host (not a target).
 """
@@ -29,61 +31,71 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 METRIC = "SCA+AWM fwd tokens/s at 128K tokens, c=2048; % of bf16 MFMA peak"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt")
-KERNEL_SOURCES = ("sca_bf16.hip", "gecko_device.hpp")
+# committed counter summaries: (file, kernel sources it was measured on)
+PMC_SCA = (os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt"), ("sca_bf16.hip", "gecko_device.hpp"))
+PMC_SCAN = (os.path.join(ROOT, "profiles", "awm_scan_128k_pmc.txt"), ("awm_bf16.hip", "gecko_device.hpp"))
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "chunked_attention_memory_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(launch_key: str):
-    """HBM bytes per launch of the attention kernel from the committed counter
-    summary, or None if there is none or the kernel source changed since."""
+def read_traffic(summary, launch_key: str):
+    """HBM bytes per launch of a kernel from its committed counter summary, or
+    None if there is none or the kernel sources changed since it was taken."""
+    path, sources = summary
     try:
         fields = {}
-        with open(PMC_SUMMARY) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
-                    fields[k.strip()] = v.strip()
-        if fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != launch_key:
+                    fields[k.strip()] = v.strip().split()[0]
+        if fields.get("source_hash") != kernel_source_hash(sources) or fields.get("workload") != launch_key:
             return None
         return float(fields["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except (OSError, KeyError, ValueError, IndexError):
         return None
 
 
 def cpu_baseline(host, w, budget_s: float):
-    """Time the oracle on head 0 over the first m chunks (m grows until the
-    budget is spent); scale to the workload's tokens/s (all H heads)."""
+    """Time the fp64 oracle on a bounded sample of the workload: the first m
+    chunks of head 0, m grown until one call takes most of the budget; if a
+    whole head takes less, further whole heads until the budget is spent.
+    Scaled to the workload's tokens/s (every token passes all H heads)."""
     import numpy as np
 
     import oracle
 
-    z, v, p = host["z"][0, 0], host["v"][0, 0], host["params"]
+    p = host["params"]
     cores = len(os.sched_getaffinity(0))
-    m, spent, t_total, tok_total = 1, 0.0, 0.0, 0
+    z, v = host["z"][0, 0], host["v"][0, 0]
+    m = 1
     while True:
         ntok = min(m * w.c, w.n)
         t0 = time.perf_counter()
         oracle.forward_head(z[:ntok], v[:ntok], p, 0, w.c)
         dt = time.perf_counter() - t0
-        t_total, tok_total, last_m = dt, ntok, m
-        spent += dt
-        if ntok >= w.n or spent >= budget_s:
+        if ntok >= w.n or dt >= 0.6 * budget_s:
             break
-        per_chunk = dt / m
-        m = max(m + 1, min(w.nchunks, int((budget_s - spent) / max(per_chunk, 1e-9))))
-    value = tok_total / t_total / w.H
+        m = min(w.nchunks, max(2 * m, int(m * budget_s / max(dt, 1e-9))))
+    t_total, head_tokens, heads = dt, ntok, 1
+    while ntok >= w.n and heads < w.H and t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.forward_head(host["z"][0, heads], host["v"][0, heads], p, heads, w.c)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    value = head_tokens * heads / t_total / w.H
+    what = (f"heads 0..{heads - 1} of {w.H}, all {w.nchunks} chunks" if ntok >= w.n
+            else f"head 0 of {w.H}, first {m} of {w.nchunks} chunks")
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle on head 0 of {w.H}, first {last_m} of {w.nchunks} chunks "
-                      f"({tok_total} tokens) in {t_total:.2f} s; tokens/s divided by {w.H} heads; "
-                      f"numpy {np.__version__} BLAS threads = {cores} host cores"}
+            "sample": f"fp64 oracle on {what} ({head_tokens * heads} head-tokens) in {t_total:.2f} s; "
+                      f"head-tokens/s divided by {w.H} heads; numpy {np.__version__}, "
+                      f"BLAS threads up to {cores} host cores"}
 
 
 def main(argv=None) -> int:
@@ -161,7 +173,12 @@ def main(argv=None) -> int:
     sca_flops = flops["sca"] + flops["awm_read"]
     achieved = sca_flops / (sca_ms / 1e3) / 1e12 if sca_ms else None
     launch_key = f"{w.name}:{args.out_dtype}"
-    traffic = read_traffic(launch_key)
+    traffic = read_traffic(PMC_SCA, launch_key)
+    scan_ms = stage_ms.get("awm_scan")
+    rows = w.B * w.H * max(w.nchunks - 2, 0)
+    # per (batch*head, chunk): G^T fp32 and H bf16 read, chunk max/sum read, bf16 state written
+    scan_alg = rows * (w.d * w.dv * 4 + w.d * w.d * 2 + 2 * w.d * 4 + w.d * w.dv * 2)
+    scan_meas = read_traffic(PMC_SCAN, launch_key)
 
     res = {
         "metric": METRIC,
@@ -187,6 +204,11 @@ def main(argv=None) -> int:
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
                      "traffic": traffic, "flops_per_launch": sca_flops},
+        "awm_scan": {"kernel": "awm_scan_bf16_kernel", "ms": scan_ms,
+                     "algorithmic_bytes": scan_alg,
+                     "algorithmic_GBps": scan_alg / (scan_ms / 1e3) / 1e9 if scan_ms else None,
+                     "hbm_bytes": scan_meas,
+                     "hbm_GBps": scan_meas / (scan_ms / 1e3) / 1e9 if (scan_meas and scan_ms) else None},
         "input_gen_s": gen_s,
     }
     if not args.no_cpu_baseline:

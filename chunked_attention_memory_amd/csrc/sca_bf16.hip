@@ -143,7 +143,7 @@ struct ScaLoop {
   int va[NMV];   // V transpose-read byte offset in a stage for value block mv, key row 0
 
   __device__ __forceinline__ void init(const ScaArgs& a, uint32_t bh, int h, int n_, int s, int c, int q0,
-                                       int qend, int w_, int lane, uint16_t* lds) {
+                                       int qend, int w_, int lane, uint16_t* lds, const int (&va_)[NMV]) {
     n = n_;
     w = w_;
     wave_q0 = q0 + 32 * QB * w;
@@ -206,22 +206,9 @@ struct ScaLoop {
     // the swizzle of row r depends on r mod 16 only, so mb adds a constant.
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ka[ks] = lq * (D * 2) + 16 * ((2 * ks + g) ^ kswz<D>(lq));
-    // V^T block for O rows 32 mv + [0, 32) and the P keys of k-step (mb, hh):
-    // element j of lane (lq, g) must be V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)]
-    //                                      [32 mv + perm_row(lq)].
-    // Transpose read jj supplies j = 4 jj + j': source lane sl of each
-    // 16-lane group points at key 32 mb + 16 hh + 8 jj + 4 g + sl / 4 and at
-    // values 32 mv + 16 (group % 2) + 4 perm2(sl % 4) + [0, 4), perm2 swapping
-    // two bits. The V swizzle depends on the row mod 4 = sl / 4 only, so
-    // (mb, hh, jj) add a constant.
-    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
-    const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
-    const int r0 = 4 * g + (sl >> 2);
+    // V operand bases va[mv]: see v_operand_base.
 #pragma unroll
-    for (int mv = 0; mv < NMV; ++mv) {
-      const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-      va[mv] = r0 * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
-    }
+    for (int mv = 0; mv < NMV; ++mv) va[mv] = va_[mv];
   }
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
@@ -405,8 +392,8 @@ struct ScaLoop {
     return any;
   }
 
-  // O^T for the wave's queries, normalised
-  __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV]) const {
+  // O^T for the wave's queries, not yet divided by the row sums (lsum)
+  __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV], float (&lsum)[QB]) const {
     // First pass without an offset: P = 2^s. The row sums show whether that
     // was safe: if a valid query's sum lies outside [2^-60, 2^63] (some 2^s
     // overflowed, or every term is tiny), the workgroup finds the exact row
@@ -445,11 +432,7 @@ struct ScaLoop {
       pass<true>(msub, ltot, oacc);
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float inv = 1.f / ltot[qb];
-#pragma unroll
-      for (int i = 0; i < NMV; ++i) oacc[qb][i] *= inv;
-    }
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] = ltot[qb];
   }
 };
 
@@ -458,16 +441,30 @@ struct ScaLoop {
 // transpose reads of ScaLoop::v_addr with features in the role of keys.
 // A plain device function: a lambda in a kernel is compiled for the host too.
 template <int D, int DV>
-__device__ __forceinline__ u32x4 snap_operand(const char* sbuf, int lane, int i) {
+__device__ __forceinline__ u32x4 snap_operand(const char* sbuf, const int (&va)[DV / 32], int i) {
   constexpr int NFB = D / 32;
   const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
-  const int g = lane >> 5, sl = lane & 15, grp2 = (lane >> 4) & 1;
-  const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
-  const int col = 32 * mv + 16 * grp2 + 4 * perm2;
-  const char* base = sbuf + (4 * g + (sl >> 2)) * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
+  const char* base = sbuf + va[mv];
   const u32x2 l2 = lds_read_tr(base + (32 * fb + 16 * hh) * (DV * 2));
   const u32x2 h2 = lds_read_tr(base + (32 * fb + 16 * hh + 8) * (DV * 2));
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Byte offset, in a staged V tile (rows of DV values), of the transpose read
+// for O rows 32 mv + [0, 32), key row 0. The V^T block for O rows
+// 32 mv + [0, 32) and the P keys of k-step (mb, hh) needs, at element j of
+// lane (lq, g), V[32 mb + 16 hh + 8 (j >> 2) + 4 g + (j & 3)][32 mv + perm_row(lq)].
+// Transpose read jj supplies j = 4 jj + j': source lane sl of each 16-lane
+// group points at key 32 mb + 16 hh + 8 jj + 4 g + sl / 4 and at values
+// 32 mv + 16 (group % 2) + 4 perm2(sl % 4) + [0, 4), perm2 swapping two bits.
+// The V swizzle depends on the row mod 4 = sl / 4 only, so (mb, hh, jj) add
+// a constant to this base.
+template <int DV>
+__device__ __forceinline__ int v_operand_base(int lane, int mv) {
+  const int g = lane >> 5, sl = lane & 15, grp2 = (lane >> 4) & 1;
+  const int perm2 = ((sl & 3) >> 1) | ((sl & 1) << 1);
+  const int col = 32 * mv + 16 * grp2 + 4 * perm2;
+  return (4 * g + (sl >> 2)) * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
 }
 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
@@ -531,64 +528,71 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
     }
   }
 
+  // attention row sums: O = oacc / lsum (+ readout)
+  float lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lsum[qb] = 1.f;
+  int va[NMV];  // V / state transpose-read bases, shared by the loop and the readout
+#pragma unroll
+  for (int mv = 0; mv < NMV; ++mv) va[mv] = v_operand_base<DV>(lane, mv);
   if constexpr (kSca) {
     ScaLoop<D, DV, QB> L;
-    L.init(a, bh, h, n, s, c, q0, qend, w, lane, lds);
-    L.run(oacc);
+    L.init(a, bh, h, n, s, c, q0, qend, w, lane, lds, va);
+    L.run(oacc, lsum);
   }
 
   if constexpr (kRead) {
     if (s >= 2) {
       // psi(Q_m) as the B operand: element e of lane (lq, g) in k-step
-      // (fb, hh) is feature 32 fb + 16 hh + 8 (e >> 2) + 4 g + (e & 3)
+      // (fb, hh) is feature 32 fb + 16 hh + 8 (e >> 2) + 4 g + (e & 3). It is
+      // packed unnormalised (2^(x - max)); the accumulators are scaled by the
+      // psi row sum before the readout MFMAs and divided by it afterwards, so
+      // that O = attention / lsum + psi M'.
       constexpr int NFB = D / 32;
       const float* eq = a.eta_q + h * D;
       const float* rq = a.rho_q + h * D;
       u32x4 pf[QB][NFB][2];
+      float psum[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(myq0 + 32 * qb, qend - 1);
-        float qm[NFB][2][8];
+        const uint16_t* zq = zbh + (size_t)min(myq0 + 32 * qb, qend - 1) * D + 4 * g;
         float mx = kNegInf;
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int jh = 0; jh < 2; ++jh) {
-              const int f0 = 32 * fb + 16 * hh + 8 * jh + 4 * g;
-              const u32x2 raw = *reinterpret_cast<const u32x2*>(zbh + (size_t)qrow * D + f0);
-              const f32x4 e4 = *reinterpret_cast<const f32x4*>(eq + f0);
-              const f32x4 r4 = *reinterpret_cast<const f32x4*>(rq + f0);
-              float* x = qm[fb][hh] + 4 * jh;
-              x[0] = (e4[0] * bf_lo(raw[0]) + r4[0]) * kLog2e;
-              x[1] = (e4[1] * bf_hi(raw[0]) + r4[1]) * kLog2e;
-              x[2] = (e4[2] * bf_lo(raw[1]) + r4[2]) * kLog2e;
-              x[3] = (e4[3] * bf_hi(raw[1]) + r4[3]) * kLog2e;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[i]);
-            }
-        mx = other_half_max(mx);
+        for (int k = 0; k < 4 * NFB; ++k) {  // k = 4 fb + 2 hh + jh: features 8 k + 4 g + [0, 4)
+          const u32x2 raw = *reinterpret_cast<const u32x2*>(zq + 8 * k);
+          const f32x4 e4 = *reinterpret_cast<const f32x4*>(eq + 8 * k + 4 * g);
+          const f32x4 r4 = *reinterpret_cast<const f32x4*>(rq + 8 * k + 4 * g);
+          mx = fmaxf(mx, fmaxf(fmaxf(e4[0] * bf_lo(raw[0]) + r4[0], e4[1] * bf_hi(raw[0]) + r4[1]),
+                               fmaxf(e4[2] * bf_lo(raw[1]) + r4[2], e4[3] * bf_hi(raw[1]) + r4[3])));
+        }
+        mx = other_half_max(mx) * kLog2e;
         float sum = 0.f;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              qm[fb][hh][e] = exp2_fast(qm[fb][hh][e] - mx);
-              sum += qm[fb][hh][e];
-            }
-        sum = other_half_sum(sum);
-        const float inv = 1.f / sum;
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const float* e = qm[fb][hh];
-            pf[qb][fb][hh] = u32x4{pack2(e[0] * inv, e[1] * inv), pack2(e[2] * inv, e[3] * inv),
-                                   pack2(e[4] * inv, e[5] * inv), pack2(e[6] * inv, e[7] * inv)};
+            uint32_t wd[4];
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) {
+              const int k = 4 * fb + 2 * hh + jh;
+              const u32x2 raw = *reinterpret_cast<const u32x2*>(zq + 8 * k);
+              const f32x4 e4 = *reinterpret_cast<const f32x4*>(eq + 8 * k + 4 * g);
+              const f32x4 r4 = *reinterpret_cast<const f32x4*>(rq + 8 * k + 4 * g);
+              const float x0 = exp2_fast((e4[0] * bf_lo(raw[0]) + r4[0]) * kLog2e - mx);
+              const float x1 = exp2_fast((e4[1] * bf_hi(raw[0]) + r4[1]) * kLog2e - mx);
+              const float x2 = exp2_fast((e4[2] * bf_lo(raw[1]) + r4[2]) * kLog2e - mx);
+              const float x3 = exp2_fast((e4[3] * bf_hi(raw[1]) + r4[3]) * kLog2e - mx);
+              wd[2 * jh] = pack2(x0, x1);
+              wd[2 * jh + 1] = pack2(x2, x3);
+              sum = sum2_bf16(wd[2 * jh], sum2_bf16(wd[2 * jh + 1], sum));
+            }
+            pf[qb][fb][hh] = u32x4{wd[0], wd[1], wd[2], wd[3]};
           }
+        psum[qb] = other_half_sum(sum);
+        const float scale = psum[qb] / lsum[qb];
+#pragma unroll
+        for (int i = 0; i < NMV; ++i) oacc[qb][i] *= scale;
+        lsum[qb] = psum[qb];
       }
       wait_vmem();
       __syncthreads();
@@ -597,15 +601,23 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
       constexpr int NI = NMV * NFB * 2, AH = 2;
       u32x4 op[AH + 1];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV>(sbuf, lane, i);
+      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV>(sbuf, va, i);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV>(sbuf, lane, i + AH);
+        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV>(sbuf, va, i + AH);
         const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(op[i % (AH + 1)], pf[qb][fb][hh], oacc[qb][mv]);
       }
     }
+  }
+
+  // divide by the row sums (attention's, or psi's after the readout)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.f / lsum[qb];
+#pragma unroll
+    for (int i = 0; i < NMV; ++i) oacc[qb][i] *= inv;
   }
 
   // accumulator register r of block mv holds value column
