@@ -6,6 +6,7 @@ shares no code with the HIP library or its binding.
 """
 
 from .gecko_oracle import (  # noqa: F401
+    HeadStream,
     affine,
     awm_head,
     chunk_ranges,

@@ -19,6 +19,8 @@ Sources (the pages this follows; cited by site and section):
   Sections used: 3.2 "Sliding Chunk Attention", 3.3 "Adaptive Working
   Memory" (chunk-by-chunk updates, normaliser fixed to one) and Appendix A
   (the initial states of the memory).
+* [chatpaper] the abstract on chatpaper.ai (sequences of arbitrary length,
+  processed in one pass; used by ``HeadStream``).
 
 Readings taken where the pages are silent or garbled (each is repeated where it
 is used):
@@ -56,6 +58,7 @@ __all__ = [
     "awm_head",
     "forward_head",
     "forward",
+    "HeadStream",
 ]
 
 
@@ -229,3 +232,75 @@ def forward(z, v, p: dict, c: int, no_delta: bool = False) -> dict:
             for key in res:
                 res[key][b, h] = r[key]
     return res
+
+
+class HeadStream:
+    """Forward of one head over a sequence handed over in consecutive segments.
+
+    Gecko is built to run on sequences of any length ([chatpaper] abstract;
+    [paperlayer 3.3]: the memory is updated chunk by chunk and carries what
+    the attention window no longer sees). Pushing the segments of a sequence
+    one after another gives exactly the rows that one ``forward_head`` call
+    on the whole sequence gives. What has to be carried from one segment to
+    the next follows from the definitions in ``sca_head`` and ``awm_head``:
+
+    * SCA: the rows of the last chunk (the previous chunk of the next one);
+    * AWM: z^{s-1}, M'_{s-1} and M'_s, where s is the next chunk (1-based).
+
+    Chunks are counted from the start of the sequence, so every segment but
+    the last must hold a whole number of chunks; a push after a segment that
+    ended inside a chunk raises ValueError.
+    """
+
+    def __init__(self, p: dict, h: int, c: int, no_delta: bool = False):
+        if c < 1:
+            raise ValueError("need c >= 1")
+        self.p, self.h, self.c, self.no_delta = p, h, c, no_delta
+        self.pos = 0            # tokens pushed so far
+        self.prev = None        # (z rows, v rows) of the last chunk pushed
+        self.z_prev = None      # z^{s-1}
+        self.mem_prev = None    # M'_{s-1}
+        self.mem_cur = None     # M'_s
+
+    def push(self, z, v) -> dict:
+        """Rows of this segment: dict of float64 ``o_sca``, ``o_m``, ``o`` [len(z), dv]."""
+        if self.pos % self.c:
+            raise ValueError("an earlier segment ended inside a chunk")
+        p, h, c = self.p, self.h, self.c
+        z = np.asarray(z, np.float64)
+        v = np.asarray(v, np.float64)
+        n, d = z.shape
+        dv = v.shape[1]
+        if self.mem_cur is None:
+            self.z_prev = np.zeros(d)
+            self.mem_prev = np.zeros((d, dv))
+            self.mem_cur = np.zeros((d, dv))
+        o_sca = np.empty((n, dv))
+        o_m = np.empty((n, dv))
+        for a, b in chunk_ranges(n, c):
+            # SCA over [previous chunk; this chunk], positions absolute
+            # ([rainbus "Method steps" (3)], R2-R4)
+            if a > 0:
+                pz, pv = z[a - c:a], v[a - c:a]
+            elif self.prev is not None:
+                pz, pv = self.prev
+            else:
+                pz, pv = z[:0], v[:0]
+            g0 = self.pos + a
+            kz = np.concatenate([pz, z[a:b]])
+            kv = np.concatenate([pv, v[a:b]])
+            o_sca[a:b] = sca_chunk(affine(z[a:b], p["kappa_q"][h], p["nu_q"][h]),
+                                   affine(kz, p["kappa_k"][h], p["nu_k"][h]), kv,
+                                   np.arange(g0, g0 + b - a), np.arange(g0 - len(pz), g0 + b - a))
+            # readout from M'_{s-1}, then chunk s enters the memory (as in awm_head)
+            o_m[a:b] = feature_softmax(affine(z[a:b], p["eta_q"][h], p["rho_q"][h])) @ self.mem_prev
+            km = affine(z[a:b], p["eta_k"][h], p["rho_k"][h])
+            ek = np.exp(km)
+            z_cur = self.z_prev + ek.sum(axis=0)
+            resid = v[a:b] if self.no_delta else v[a:b] - feature_softmax(km) @ self.mem_cur
+            mem_next = (self.z_prev / z_cur)[:, None] * self.mem_cur + (ek / z_cur).T @ resid
+            self.mem_prev, self.mem_cur, self.z_prev = self.mem_cur, mem_next, z_cur
+        last = chunk_ranges(n, c)[-1][0] if n else 0
+        self.prev = (z[last:], v[last:])
+        self.pos += n
+        return {"o_sca": o_sca, "o_m": o_m, "o": o_sca + o_m}

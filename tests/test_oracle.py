@@ -271,3 +271,56 @@ def test_awm_readout_chunks_subset_matches_full():
     assert sorted(part) == [0, 3, 8]
     for s, rows in part.items():
         np.testing.assert_array_equal(rows, full[s * c:min((s + 1) * c, n)])
+
+
+STREAM_SPLITS = [
+    (96, 16, [96]),                  # one segment
+    (96, 16, [16, 16, 64]),          # one-chunk segments first
+    (100, 16, [32, 48, 20]),         # ragged last segment
+    (70, 7, [7] * 9 + [7]),          # every chunk its own segment
+    (50, 10, [20, 30]),
+    (41, 64, [41]),                  # one partial chunk
+    (130, 64, [64, 64, 2]),          # last segment shorter than a chunk
+]
+
+
+def _stream(z, v, a, c, splits, no_delta=False):
+    p = {k: np.asarray(x)[None, :] for k, x in a.items()}
+    st = oracle.HeadStream(p, 0, c, no_delta=no_delta)
+    parts, at = [], 0
+    for m in splits:
+        parts.append(st.push(z[at:at + m], v[at:at + m]))
+        at += m
+    assert at == len(z)
+    return {k: np.concatenate([r[k] for r in parts]) for k in ("o_sca", "o_m", "o")}
+
+
+@pytest.mark.parametrize("n,c,splits", STREAM_SPLITS)
+def test_stream_matches_brute_force_and_unrolled_memory(n, c, splits):
+    # the streamed rows against the independent formulations of both parts
+    z, v, a = rand_head(n, 6, 5, seed=n + 11 * c + len(splits), key_scale=2.5)
+    got = _stream(z, v, a, c, splits)
+    q, k = z * a["kappa_q"] + a["nu_q"], z * a["kappa_k"] + a["nu_k"]
+    qm, km = z * a["eta_q"] + a["rho_q"], z * a["eta_k"] + a["rho_k"]
+    np.testing.assert_allclose(got["o_sca"], pins.brute_sca(q, k, v, c), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(got["o_m"], pins.awm_unrolled(qm, km, v, c), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,c,splits", STREAM_SPLITS[:4])
+def test_stream_equals_one_call(n, c, splits):
+    z, v, a = rand_head(n, 8, 4, seed=3 * n + c, key_scale=2.0)
+    p = {k: np.asarray(x)[None, :] for k, x in a.items()}
+    for no_delta in (False, True):
+        want = oracle.forward_head(z, v, p, 0, c, no_delta=no_delta)
+        got = _stream(z, v, a, c, splits, no_delta=no_delta)
+        for key in ("o_sca", "o_m", "o"):
+            np.testing.assert_allclose(got[key], want[key], rtol=1e-12, atol=1e-14)
+
+
+def test_stream_rejects_a_push_after_a_partial_chunk():
+    z, v, a = rand_head(40, 4, 3, seed=5)
+    p = {k: np.asarray(x)[None, :] for k, x in a.items()}
+    st = oracle.HeadStream(p, 0, 16)
+    st.push(z[:20], v[:20])
+    with pytest.raises(ValueError):
+        st.push(z[20:], v[20:])
