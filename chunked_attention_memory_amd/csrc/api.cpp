@@ -52,7 +52,8 @@ enum Mode { kModeSca = 1, kModeAwm = 2 };
 
 namespace gecko {
 
-Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv, int64_t nmem, bool bf16) {
+Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv, int64_t nmem, int64_t nsnap,
+                          bool bf16, bool stream) {
   Workspace w{};
   const size_t rows = (size_t)BH * (size_t)nmem;
   const size_t e16 = bf16 ? 2 : 4;
@@ -68,10 +69,38 @@ Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t 
   w.csum = reinterpret_cast<float*>(take(rows * d * 4));
   w.decay = reinterpret_cast<float*>(take(rows * d * 4));
   w.wscale = reinterpret_cast<float*>(take(rows * d * 4));
-  w.snap = take(rows * dv * d * e16);
+  w.snap = take((size_t)BH * (size_t)nsnap * dv * d * e16);
   w.rowstat = bf16 ? nullptr : reinterpret_cast<float*>(take((size_t)BH * n * 2 * 4));
+  w.zfinal = stream ? reinterpret_cast<float*>(take((size_t)BH * d * 2 * 4)) : nullptr;
   w.bytes = nmem > 0 ? off : 0;
   return w;
+}
+
+// Streaming state (caller-owned device memory, 256-byte aligned arrays):
+// the fp32 memory state M'^T in the scan's register layout, the running
+// denominator (M, L) per feature, and the carried chunk of Z' and V.
+struct StreamState {
+  float* mstate;   // [BH][dv/32][d/32][64][16]
+  float* zstate;   // [BH][d][2]
+  void* zcarry;    // [BH][c][d]  bf16
+  void* vcarry;    // [BH][c][dv] bf16
+  size_t bytes;
+};
+
+StreamState carve_state(void* base, int64_t BH, int64_t d, int64_t dv, int64_t c) {
+  StreamState t{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return static_cast<char*>(base) + at;
+  };
+  t.mstate = reinterpret_cast<float*>(take((size_t)BH * d * dv * 4));
+  t.zstate = reinterpret_cast<float*>(take((size_t)BH * d * 2 * 4));
+  t.zcarry = take((size_t)BH * c * d * 2);
+  t.vcarry = take((size_t)BH * c * dv * 2);
+  t.bytes = off;
+  return t;
 }
 
 }  // namespace gecko
@@ -94,7 +123,22 @@ struct Call {
   void* stream;
   int mode;
   gecko_timer* timer;
+  // streaming (gecko_sca_awm_forward_stream)
+  bool streaming;
+  int64_t pos;
+  void* state; size_t state_bytes;
 };
+
+// memory steps and snapshot slots of a call (see gecko::Problem)
+void mem_counts(int64_t N, bool stream, bool has_prev, int64_t& nmem, int64_t& nsnap) {
+  if (stream) {
+    nmem = (has_prev ? 1 : 0) + N - 1;
+    nsnap = nmem + (has_prev ? 1 : 0);
+  } else {
+    nmem = N > 2 ? N - 2 : 0;
+    nsnap = nmem;
+  }
+}
 
 gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   if (k.B < 1 || k.H < 1 || k.n < 1 || k.c < 1)
@@ -124,14 +168,24 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
     return fail(GECKO_EINVAL, "sizes out of range");
   const int64_t BH = k.B * k.H;
   const int64_t N = nchunks_of(k.n, k.c);
-  const int64_t nmem = N > 2 ? N - 2 : 0;
+  const bool has_prev = k.streaming && k.pos > 0;
+  int64_t nmem = 0, nsnap = 0;
+  mem_counts(N, k.streaming, has_prev, nmem, nsnap);
+  if (k.streaming) {
+    if (!bf16) return fail(GECKO_EUNSUPPORTED, "the streaming forward is built for bf16 inputs only");
+    if (k.c % 64) return fail(GECKO_EUNSUPPORTED, "the streaming forward needs c to be a multiple of 64");
+    if (k.pos < 0 || k.pos % k.c)
+      return fail(GECKO_EINVAL, "pos (%lld) must be a non-negative multiple of c (%lld)", (long long)k.pos,
+                  (long long)k.c);
+  }
   if (bf16) {
     // the bf16 kernels address one (batch, head) slab with 32-bit byte offsets
     const int64_t widest = k.d > k.dv ? k.d : k.dv;
     if ((k.n + 512) * widest * 2 > (int64_t)0xFFFFFFFF)
       return fail(GECKO_EUNSUPPORTED, "bf16 path needs n * max(d, dv) * 2 < 4 GiB per (batch, head) slab");
     const int64_t cc = k.c < k.n ? k.c : k.n;
-    if (BH * N * ((cc + 127) / 128) >= ((int64_t)1 << 31) || BH * nmem >= ((int64_t)1 << 31))
+    if (BH * N * ((cc + 127) / 128) >= ((int64_t)1 << 31) || BH * nmem >= ((int64_t)1 << 31) ||
+        BH * (k.dv / 32) >= ((int64_t)1 << 31) || (k.streaming && k.c * k.dv * 2 > (int64_t)0xFFFFFFFF))
       return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
   }
   if (!bf16 && (BH > 65535 || BH * nmem > 65535 || (k.dv / 32) > 65535))
@@ -141,8 +195,21 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   const size_t zb = (size_t)BH * k.n * k.d * esz, vb = (size_t)BH * k.n * k.dv * esz;
   const size_t ob = (size_t)BH * k.n * k.dv * osz;
   if (overlaps(k.out, ob, k.z, zb) || overlaps(k.out, ob, k.v, vb)) return fail(GECKO_EINVAL, "out aliases an input");
+  if (k.streaming) {
+    const gecko::StreamState t = gecko::carve_state(nullptr, BH, k.d, k.dv, k.c);
+    if (!k.state) return fail(GECKO_EINVAL, "streaming state is null (need %zu bytes)", t.bytes);
+    if (k.state_bytes < t.bytes)
+      return fail(GECKO_EINVAL, "streaming state too small: %zu < %zu bytes", k.state_bytes, t.bytes);
+    if (reinterpret_cast<uintptr_t>(k.state) & (kAlign - 1))
+      return fail(GECKO_EINVAL, "streaming state must be 256-byte aligned");
+    if (overlaps(k.state, t.bytes, k.z, zb) || overlaps(k.state, t.bytes, k.v, vb) ||
+        overlaps(k.state, t.bytes, k.out, ob))
+      return fail(GECKO_EINVAL, "streaming state aliases an input or the output");
+    if (k.ws && overlaps(k.state, t.bytes, k.ws, k.ws_bytes))
+      return fail(GECKO_EINVAL, "streaming state aliases the workspace");
+  }
   if (need_awm && nmem > 0) {
-    const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, bf16);
+    const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, nsnap, bf16, k.streaming);
     if (!k.ws) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", w.bytes);
     if (k.ws_bytes < w.bytes) return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", k.ws_bytes, w.bytes);
     if (reinterpret_cast<uintptr_t>(k.ws) & (kAlign - 1)) return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
@@ -152,8 +219,26 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   p.kappa_q = k.aff[0]; p.nu_q = k.aff[1]; p.kappa_k = k.aff[2]; p.nu_k = k.aff[3];
   p.eta_q = k.aff[4]; p.rho_q = k.aff[5]; p.eta_k = k.aff[6]; p.rho_k = k.aff[7];
   p.B = k.B; p.H = k.H; p.n = k.n; p.d = k.d; p.dv = k.dv; p.c = k.c;
-  p.nchunks = N; p.nmem = nmem; p.flags = k.flags;
+  p.nchunks = N; p.nmem = nmem; p.nsnap = nsnap; p.flags = k.flags;
+  {
+    const int64_t before = k.streaming ? k.pos / k.c : 0;  // chunks of the sequence before this call
+    p.first_read = before >= 2 ? 0 : 2 - before;
+  }
   p.out_f32 = k.out_dtype == GECKO_F32;
+  p.stream = k.streaming;
+  p.has_prev = has_prev;
+  p.zprev = p.vprev = nullptr;
+  p.mstate = nullptr;
+  p.zstate = nullptr;
+  if (k.streaming) {
+    const gecko::StreamState t = gecko::carve_state(k.state, BH, k.d, k.dv, k.c);
+    p.mstate = t.mstate;
+    p.zstate = t.zstate;
+    if (has_prev) {
+      p.zprev = t.zcarry;
+      p.vprev = t.vcarry;
+    }
+  }
   return GECKO_OK;
 }
 
@@ -165,7 +250,7 @@ gecko_status run(const Call& k) {
   hipStream_t s = static_cast<hipStream_t>(k.stream);
   const bool do_awm = (k.mode & kModeAwm) && p.nmem > 0;
   gecko::Workspace w{};
-  if (do_awm) w = gecko::carve_workspace(k.ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, bf16);
+  if (do_awm) w = gecko::carve_workspace(k.ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, p.nsnap, bf16, p.stream);
 
   hipEvent_t* ev = nullptr;
   if (k.timer && k.timer->used < k.timer->capacity) ev = &k.timer->ev[5 * k.timer->used++];
@@ -195,6 +280,16 @@ gecko_status run(const Call& k) {
   e = bf16 ? gecko::launch_sca_bf16(p, w, mode, s) : gecko::launch_sca_f32(p, w, mode, s);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (p.stream) {
+    // a sequence whose first call enters nothing: empty memory state
+    const gecko::StreamState t = gecko::carve_state(k.state, p.B * p.H, p.d, p.dv, p.c);
+    if (p.nmem == 0 && (e = gecko::launch_stream_reset(t.mstate, t.zstate, p.B * p.H, p.d, p.dv, s)) != hipSuccess)
+      return hip_fail(e, "stream state reset launch");
+    // the last chunk of this call is carried to the next one
+    const int64_t row0 = (p.nchunks - 1) * p.c;
+    e = gecko::launch_stream_finish(p, w, t.zcarry, t.vcarry, t.zstate, row0, p.n - row0, s);
+    if (e != hipSuccess) return hip_fail(e, "stream state update launch");
+  }
   g_last_error.clear();
   return GECKO_OK;
 }
@@ -206,9 +301,9 @@ extern "C" {
 size_t gecko_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
   if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv)) return (size_t)-1;
   if (in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) return (size_t)-1;
-  const int64_t N = nchunks_of(n, c);
-  const int64_t nmem = N > 2 ? N - 2 : 0;
-  return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, in_dtype == GECKO_BF16).bytes;
+  int64_t nmem = 0, nsnap = 0;
+  mem_counts(nchunks_of(n, c), false, false, nmem, nsnap);
+  return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, in_dtype == GECKO_BF16, false).bytes;
 }
 
 gecko_status gecko_sca_awm_forward_timed(const void* z, const float* kappa_q, const float* nu_q,
@@ -254,6 +349,36 @@ gecko_status gecko_awm_forward(const void* z, const float* eta_q, const float* r
   try {
     Call k{z, v, out, {nullptr, nullptr, nullptr, nullptr, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
            in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, kModeAwm, nullptr};
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+size_t gecko_stream_state_size(int64_t B, int64_t H, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
+  if (B < 1 || H < 1 || c < 1 || !valid_d(d) || !valid_dv(dv) || in_dtype != GECKO_BF16) return (size_t)-1;
+  return gecko::carve_state(nullptr, B * H, d, dv, c).bytes;
+}
+
+size_t gecko_stream_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                   gecko_dtype in_dtype) {
+  if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv) || in_dtype != GECKO_BF16) return (size_t)-1;
+  int64_t nmem = 0, nsnap = 0;
+  mem_counts(nchunks_of(n, c), true, true, nmem, nsnap);  // the larger case: a carried chunk
+  return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, true, true).bytes;
+}
+
+gecko_status gecko_sca_awm_forward_stream(const void* z, const float* kappa_q, const float* nu_q,
+                                          const float* kappa_k, const float* nu_k, const float* eta_q,
+                                          const float* rho_q, const float* eta_k, const float* rho_k, const void* v,
+                                          void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                          int64_t c, int64_t pos, gecko_dtype in_dtype, gecko_dtype out_dtype,
+                                          unsigned flags, void* state, size_t state_bytes, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  try {
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, kModeSca | kModeAwm, nullptr,
+           true, pos, state, state_bytes};
     return run(k);
   } catch (...) {
     return fail(GECKO_EHIP, "internal error");
@@ -322,6 +447,6 @@ const char* gecko_status_string(gecko_status status) {
 
 const char* gecko_last_error(void) { return g_last_error.c_str(); }
 
-int gecko_version(void) { return 100; }
+int gecko_version(void) { return 101; }
 
 }  // extern "C"

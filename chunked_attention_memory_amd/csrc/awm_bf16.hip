@@ -17,6 +17,8 @@
 // pass); decay and wscale come from a running log-space prefix of (m_t, l_t);
 // the product H_t M'_{t+1} is the only sequential part (scan).
 // All maxima and logarithms are kept in base 2 (exp2 on the hardware).
+#include <algorithm>
+
 #include "gecko_device.hpp"
 #include "gecko_internal.hpp"
 
@@ -83,8 +85,10 @@ struct ChunkArgs {
   uint16_t* hm;      // H^T accumulators in scan-operand order, [bh][t][d/16][d/32][64 lanes][8]
   float* cmax;       // [bh][t][d] (log2 units)
   float* csum;       // [bh][t][d]
+  const uint16_t* zprev;  // streaming: chunk t = 0 is the carried chunk [bh][c][d] / [bh][c][dv]
+  const uint16_t* vprev;
   int64_t n, c, nmem;
-  int H;
+  int H, has_prev;
 };
 
 // One workgroup per (batch*head, chunk t). Wave w owns key features
@@ -119,17 +123,26 @@ struct ChunkLoop {
 
   __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* lds) {
     const int h = (int)(bh % a.H);
-    n = (int)a.n;
-    cbeg = (int)(t * a.c);
-    cend = cbeg + (int)a.c;  // chunks 0..nmem-1 are full
+    // chunk t of the virtual sequence [carried chunk (streaming)] + this
+    // call's chunks; every chunk entered into the memory is full
+    if (a.has_prev && t == 0) {
+      n = (int)a.c;
+      cbeg = 0;
+      zbh = a.zprev + (size_t)bh * (size_t)a.c * D;
+      vbh = a.vprev + (size_t)bh * (size_t)a.c * DV;
+    } else {
+      n = (int)a.n;
+      cbeg = (int)((t - a.has_prev) * a.c);
+      zbh = a.z + (size_t)bh * (size_t)n * D;
+      vbh = a.v + (size_t)bh * (size_t)n * DV;
+    }
+    cend = cbeg + (int)a.c;
     ntiles = (int)((a.c + kBT - 1) / kBT);
     const int tid = threadIdx.x;
     lane = tid & 63;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     g = lane >> 5;
     lq = lane & 31;
-    zbh = a.z + (size_t)bh * (size_t)n * D;
-    vbh = a.v + (size_t)bh * (size_t)n * DV;
     st = lds;
     ps = st + 2 * T::STAGE;
     float* e2 = reinterpret_cast<float*>(ps + T::ZBYTES);
@@ -457,9 +470,14 @@ struct ScanArgs {
   const uint16_t* hm;  // [bh][t][d/16][d/32][64 lanes][8] bf16, see the chunk pass
   const float* cmax;   // [bh][t][d] (log2 units)
   const float* csum;   // [bh][t][d]
-  uint16_t* snap;      // [bh][t][d][dv]: M'_{t+2}, read by chunk t + 2 (0-based)
-  int64_t nmem;
+  uint16_t* snap;      // [bh][nsnap][d][dv]: slot t + has_prev holds the state after step t
+  float* mstate;       // streaming: fp32 M'^T in this kernel's register layout
+                       //   [bh][dv/32][d/32][64 lanes][16]; read if has_prev, written if stream
+  const float* zstate; // streaming: (M, L) per feature before the call [bh][d][2], read if has_prev
+  float* zfinal;       // streaming: (M, L) per feature after the call [bh][d][2], written if stream
+  int64_t nmem, nsnap;
   int no_delta;        // drop the H_t M' term (test variant)
+  int has_prev, stream;
 };
 
 // Operands of one scan step for one lane, loaded ahead of use.
@@ -523,6 +541,18 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
   f32x16 mst = f32x16{};
   float zM = kNegInf, zL = 0.f;
   int buf = 0;
+  // this lane's 16 cells of the state in the streaming state arrays
+  const int64_t scell = (((bh * NMV + j) * NW + w) * 64 + lane) * 16;
+  const int hp = a.has_prev;
+  // one 32-value slice of a snapshot from the bf16 copy in LDS
+  auto write_snap = [&](int64_t slot, const uint16_t* src) {
+    uint16_t* sn = a.snap + (bh * a.nsnap + slot) * (int64_t)D * DV + 32 * j;
+#pragma unroll
+    for (int e = tid; e < D * 4; e += 2 * D) {
+      const int r = e >> 2, cc = (e & 3) * 8;
+      st16(sn + (int64_t)r * DV + cc, ld16(&src[r * 32 + cc]));
+    }
+  };
   auto step = [&](int64_t t, const ScanStep<D>& q) {
     // running denominator of feature f
     const float Mn = fmaxf(zM, q.cm);
@@ -553,19 +583,37 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
       *reinterpret_cast<u32x2*>(&mt[buf ^ 1][f * 32 + 8 * qq + 4 * g]) = pk;
     }
     __syncthreads();
-    // snapshot rows f of M'_{t+2}, values 32 j .. 32 j + 31: 64 bytes per row
-    uint16_t* sn = a.snap + (bh * nmem + t) * (int64_t)D * DV + 32 * j;
-#pragma unroll
-    for (int e = tid; e < D * 4; e += 2 * D) {
-      const int r = e >> 2, cc = (e & 3) * 8;
-      st16(sn + (int64_t)r * DV + cc, ld16(&mt[buf ^ 1][r * 32 + cc]));
-    }
+    // snapshot rows f of the state after step t, values 32 j .. 32 j + 31:
+    // 64 bytes per row
+    write_snap(t + hp, mt[buf ^ 1]);
     buf ^= 1;
   };
 
-  // M'_1 = 0
-  for (int e = tid; e < D * 32 / 8; e += 2 * D) st16(&mt[0][8 * e], u32x4{0u, 0u, 0u, 0u});
-  __syncthreads();
+  if (hp) {
+    // continue a sequence: the state and the running denominator carried
+    // over from the previous call; its bf16 copy is both the first MFMA
+    // operand and snapshot slot 0 (read by the call's first chunk)
+    const f32x4* ms = reinterpret_cast<const f32x4*>(a.mstate + scell);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = ms[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mst[4 * q + i] = x[i];
+    }
+    zM = a.zstate[(bh * D + f) * 2];
+    zL = a.zstate[(bh * D + f) * 2 + 1];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const u32x2 pk{pack2(mst[4 * qq], mst[4 * qq + 1]), pack2(mst[4 * qq + 2], mst[4 * qq + 3])};
+      *reinterpret_cast<u32x2*>(&mt[0][f * 32 + 8 * qq + 4 * g]) = pk;
+    }
+    __syncthreads();
+    write_snap(0, mt[0]);
+  } else {
+    // M'_1 = 0
+    for (int e = tid; e < D * 32 / 8; e += 2 * D) st16(&mt[0][8 * e], u32x4{0u, 0u, 0u, 0u});
+    __syncthreads();
+  }
   // Steady state without branches, so that the compiler can count the loads
   // in flight exactly; loads past the last step re-read it (unused).
   const int64_t last = nmem - 1;
@@ -582,6 +630,55 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
   for (int k = 0; k < kDepth; ++k)
     if (t0 + k < nmem) step(t0 + k, ring[k]);
+
+  if (a.stream) {  // the state after the last step, for the next call
+    f32x4* ms = reinterpret_cast<f32x4*>(a.mstate + scell);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ms[q] = f32x4{mst[4 * q], mst[4 * q + 1], mst[4 * q + 2], mst[4 * q + 3]};
+    if (j == 0 && g == 0) {
+      a.zfinal[(bh * D + f) * 2] = zM;
+      a.zfinal[(bh * D + f) * 2 + 1] = zL;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- streaming state
+// A new sequence whose first call enters no chunk into the memory: M' = 0 and
+// an empty running denominator (M, L) = (-inf, 0).
+__global__ void stream_reset_kernel(float* __restrict__ mstate, float* __restrict__ zstate, int64_t mcells,
+                                    int64_t zfeat) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mcells; i += stride) mstate[i] = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zfeat; i += stride) {
+    zstate[2 * i] = kNegInf;
+    zstate[2 * i + 1] = 0.f;
+  }
+}
+
+// End of a streaming call, after every kernel that reads the old carried
+// chunk: rows [row0, row0 + rows) of each (b, h) slab of Z' and V become the
+// carried chunk, and the scan's final running denominator the carried one.
+// Block b serves slab b / per_bh; 16-byte copies (d and dv are multiples of 8).
+__global__ void stream_finish_kernel(const uint16_t* __restrict__ z, const uint16_t* __restrict__ v,
+                                     uint16_t* __restrict__ zc, uint16_t* __restrict__ vc,
+                                     const float* __restrict__ zfinal, float* __restrict__ zstate, int64_t n,
+                                     int64_t c, int d, int dv, int64_t row0, int64_t rows, int per_bh) {
+  const int64_t bh = blockIdx.x / per_bh;
+  const int part = (int)(blockIdx.x % per_bh);
+  const int64_t zch = rows * d / 8, vch = rows * dv / 8;
+  const u32x4* zs = reinterpret_cast<const u32x4*>(z + (bh * n + row0) * d);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(v + (bh * n + row0) * dv);
+  u32x4* zd = reinterpret_cast<u32x4*>(zc + bh * c * d);
+  u32x4* vd = reinterpret_cast<u32x4*>(vc + bh * c * dv);
+  const int64_t stride = (int64_t)per_bh * blockDim.x;
+  for (int64_t i = (int64_t)part * blockDim.x + threadIdx.x; i < zch + vch; i += stride) {
+    if (i < zch)
+      zd[i] = zs[i];
+    else
+      vd[i - zch] = vs[i - zch];
+  }
+  if (zfinal && part == 0)
+    for (int k = threadIdx.x; k < 2 * d; k += blockDim.x) zstate[bh * 2 * d + k] = zfinal[bh * 2 * d + k];
 }
 
 template <int D, int DV>
@@ -619,7 +716,9 @@ hipError_t launch_awm_chunk_bf16(const Problem& p, const Workspace& w, hipStream
   a.v = static_cast<const uint16_t*>(p.v);
   a.eta_k = p.eta_k; a.rho_k = p.rho_k;
   a.g = w.g; a.hm = static_cast<uint16_t*>(w.h); a.cmax = w.cmax; a.csum = w.csum;
-  a.n = p.n; a.c = p.c; a.nmem = p.nmem; a.H = (int)p.H;
+  a.zprev = static_cast<const uint16_t*>(p.zprev);
+  a.vprev = static_cast<const uint16_t*>(p.vprev);
+  a.n = p.n; a.c = p.c; a.nmem = p.nmem; a.H = (int)p.H; a.has_prev = p.has_prev ? 1 : 0;
   const int64_t BH = p.B * p.H;
   if (p.d == 128 && p.dv == 256) return launch_chunk<128, 256>(a, BH, s);
   if (p.d == 128 && p.dv == 128) return launch_chunk<128, 128>(a, BH, s);
@@ -638,14 +737,35 @@ hipError_t launch_awm_zscan(const Problem& p, const Workspace& w, hipStream_t s)
 hipError_t launch_awm_scan_bf16(const Problem& p, const Workspace& w, hipStream_t s) {
   ScanArgs a;
   a.g = w.g; a.hm = static_cast<const uint16_t*>(w.h); a.cmax = w.cmax; a.csum = w.csum;
-  a.snap = static_cast<uint16_t*>(w.snap); a.nmem = p.nmem;
+  a.snap = static_cast<uint16_t*>(w.snap); a.nmem = p.nmem; a.nsnap = p.nsnap;
   a.no_delta = (p.flags & GECKO_AWM_NO_DELTA_BIT) ? 1 : 0;
+  a.mstate = p.mstate; a.zstate = p.zstate; a.zfinal = w.zfinal;
+  a.has_prev = p.has_prev ? 1 : 0; a.stream = p.stream ? 1 : 0;
   const int64_t BH = p.B * p.H;
   if (p.d == 128 && p.dv == 256) return launch_scan<128, 256>(a, BH, s);
   if (p.d == 128 && p.dv == 128) return launch_scan<128, 128>(a, BH, s);
   if (p.d == 64 && p.dv == 128) return launch_scan<64, 128>(a, BH, s);
   if (p.d == 64 && p.dv == 64) return launch_scan<64, 64>(a, BH, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_reset(float* mstate, float* zstate, int64_t BH, int64_t d, int64_t dv, hipStream_t s) {
+  const int64_t mcells = BH * d * dv, zfeat = BH * d;
+  const int64_t blocks = std::min<int64_t>((mcells + 255) / 256, 1024);
+  hipLaunchKernelGGL(stream_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, s, mstate, zstate, mcells, zfeat);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_finish(const Problem& p, const Workspace& w, void* zcarry, void* vcarry, float* zstate,
+                                int64_t row0, int64_t rows, hipStream_t s) {
+  const int64_t BH = p.B * p.H;
+  const int64_t chunks16 = rows * (p.d + p.dv) / 8;
+  const int per_bh = (int)std::max<int64_t>(1, std::min<int64_t>((chunks16 + 255) / 256, 32));
+  hipLaunchKernelGGL(stream_finish_kernel, dim3((unsigned)(BH * per_bh)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(p.z), static_cast<const uint16_t*>(p.v),
+                     static_cast<uint16_t*>(zcarry), static_cast<uint16_t*>(vcarry),
+                     p.nmem > 0 ? w.zfinal : nullptr, zstate, p.n, p.c, (int)p.d, (int)p.dv, row0, rows, per_bh);
+  return hipGetLastError();
 }
 
 }  // namespace gecko

@@ -18,10 +18,25 @@ struct Problem {
   const float* kappa_q; const float* nu_q; const float* kappa_k; const float* nu_k;
   const float* eta_q; const float* rho_q; const float* eta_k; const float* rho_k;
   int64_t B, H, n, d, dv, c;
-  int64_t nchunks;      // N = ceil(n / c)
-  int64_t nmem;         // chunks written into the memory that some chunk reads: max(N - 2, 0)
+  int64_t nchunks;      // N = ceil(n / c) chunks of this call
+  int64_t nmem;         // chunks entered into the memory by this call (scan steps):
+                        //   one call: max(N - 2, 0); streaming: has_prev + N - 1
   unsigned flags;
   bool out_f32;         // output dtype (bf16 inputs may write float32 output)
+  // Streaming (bf16 only). The memory pass and the scan see a virtual
+  // sequence [carried chunk (if has_prev)] + this call's chunks; attention
+  // and output cover this call's tokens. Chunk s of the call reads scan
+  // output r = s - 2 + has_prev, stored in snapshot slot r + has_prev; slot 0
+  // of a call with has_prev holds the incoming state (r = -1).
+  int64_t nsnap;        // snapshot slots per (b, h): nmem + has_prev
+  int64_t first_read;   // first chunk of the call that reads the memory: the
+                        //   sequence's first two chunks read none (2 - chunks before, at least 0)
+  bool stream;          // keep the memory state after this call (mstate, zfinal)
+  bool has_prev;        // tokens were processed before: a carried chunk and an incoming state
+  const void* zprev;    // [BH][c][d]  carried chunk (the last chunk of the previous call)
+  const void* vprev;    // [BH][c][dv]
+  float* mstate;        // [BH][dv/32][d/32][64][16] fp32 state M'^T (scan accumulator layout), in/out
+  const float* zstate;  // [BH][d][2] running (M, L) per feature (log2 max, scaled sum) before this call
 };
 
 // Workspace carve-up (byte offsets from the workspace base). Every array is
@@ -34,13 +49,14 @@ struct Workspace {
   float* csum;     // per-feature sum of exp(K_m - cmax)     [bh][t][d]
   float* decay;    // z^{t-1} / z^t (fp32 path)              [bh][t][d]
   float* wscale;   // exp(cmax) / z^t (fp32 path)            [bh][t][d]
-  void* snap;      // state read by chunk t+2: bf16 [bh][t][d][dv], fp32 [bh][t][dv][d]
+  void* snap;      // state read by chunk t+2: bf16 [bh][nsnap][d][dv], fp32 [bh][t][dv][d]
   float* rowstat;  // fp32 path only: per-token (max, sum) of K_m rows  [bh][n][2]
+  float* zfinal;   // streaming: running (M, L) per feature after the call  [bh][d][2]
   size_t bytes;
 };
 
 Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv,
-                          int64_t nmem, bool bf16);
+                          int64_t nmem, int64_t nsnap, bool bf16, bool stream);
 
 // Launchers (stream-ordered, asynchronous). Each returns the launch status.
 hipError_t launch_awm_chunk_bf16(const Problem& p, const Workspace& w, hipStream_t s);
@@ -52,6 +68,14 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
 hipError_t launch_awm_chunk_f32(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t launch_awm_scan_f32(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t launch_sca_f32(const Problem& p, const Workspace& w, int mode, hipStream_t s);
+// Streaming state. reset: M' = 0 and (M, L) = (-inf, 0) for a sequence whose
+// first call enters nothing into the memory. finish (after the attention
+// kernel, which reads the old carried chunk): the last chunk of this call
+// (`rows` rows starting at row0) becomes the carried chunk, and zfinal the
+// running denominator.
+hipError_t launch_stream_reset(float* mstate, float* zstate, int64_t BH, int64_t d, int64_t dv, hipStream_t s);
+hipError_t launch_stream_finish(const Problem& p, const Workspace& w, void* zcarry, void* vcarry, float* zstate,
+                                int64_t row0, int64_t rows, hipStream_t s);
 
 bool bf16_shape_built(int64_t d, int64_t dv);
 

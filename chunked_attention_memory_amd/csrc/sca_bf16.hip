@@ -115,9 +115,13 @@ struct ScaArgs {
   const float* kappa_k;
   const float* eta_q;
   const float* rho_q;
-  const uint16_t* snap;  // [bh][nmem][d][dv]; slot t is the state read by chunk t + 2 (0-based)
+  const uint16_t* snap;  // [bh][nsnap][d][dv]; chunk s reads slot s - 2 + 2 has_prev (0-based)
+  // streaming: the chunk before this call's first one (keys at rows -c .. -1)
+  const uint16_t* zprev;   // [bh][c][d]
+  const uint16_t* vprev;   // [bh][c][dv]
   int64_t n;
-  int c, nchunks, nmem, qtiles, nblocks, per_xcd, H;
+  int c, nchunks, nsnap, qtiles, nblocks, per_xcd, H, has_prev;
+  int first_read;  // chunks before it read no memory (the sequence's first two chunks)
 };
 
 // The attention loop of one workgroup. Member functions rather than lambdas:
@@ -134,6 +138,9 @@ struct ScaLoop {
 
   const uint16_t* zbh;
   const uint16_t* vbh;
+  const uint16_t* zpv;  // carried chunk (keys at negative rows), streaming only
+  const uint16_t* vpv;
+  int cl;               // chunk length
   char* kbuf;  // K stages
   char* vbuf;  // V stages
   int n, kbeg, kend, ntiles, myq0, wave_q0, wave_last, w, g, lq;
@@ -152,6 +159,9 @@ struct ScaLoop {
     myq0 = wave_q0 + lq;
     zbh = a.z + (size_t)bh * (size_t)n * D;
     vbh = a.v + (size_t)bh * (size_t)n * DV;
+    cl = c;
+    zpv = a.has_prev ? a.zprev + (size_t)bh * (size_t)c * D : nullptr;
+    vpv = a.has_prev ? a.vprev + (size_t)bh * (size_t)c * DV : nullptr;
     kbuf = reinterpret_cast<char*>(lds);
     vbuf = kbuf + T::NSTAGE * T::KBYTES;
 
@@ -179,7 +189,9 @@ struct ScaLoop {
       }
     }
 
-    kbeg = s > 0 ? (s - 1) * c : 0;
+    // key window: the previous chunk (rows -c .. -1 are the carried chunk of
+    // a streaming call) and this chunk up to its last query
+    kbeg = (s > 0 || a.has_prev) ? (s - 1) * c : 0;
     kend = qend;
     ntiles = (kend - kbeg + kBN - 1) / kBN;
     // last key any query of this wave can see; -1 (every key tile skipped)
@@ -212,8 +224,14 @@ struct ScaLoop {
   }
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
-    stage_rows(zbh, kbeg + kt * kBN, n, D, kbuf + slot * T::KBYTES, NW, w, koff, T::KLOADS);
-    stage_rows(vbh, kbeg + kt * kBN, n, DV, vbuf + slot * T::VBYTES, NW, w, voff, T::VLOADS);
+    // rows below 0 are the carried chunk (c is a multiple of the tile, so no
+    // tile straddles); scalar selects, one load sequence
+    const int row0 = kbeg + kt * kBN;
+    const bool carried = row0 < 0;
+    const int r = carried ? row0 + cl : row0;
+    const int lim = carried ? cl : n;
+    stage_rows(carried ? zpv : zbh, r, lim, D, kbuf + slot * T::KBYTES, NW, w, koff, T::KLOADS);
+    stage_rows(carried ? vpv : vbh, r, lim, DV, vbuf + slot * T::VBYTES, NW, w, voff, T::VLOADS);
   }
 
   __device__ __forceinline__ int k_addr(int mb, int ks) const { return ka[ks] + 32 * mb * (D * 2); }
@@ -509,12 +527,17 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   // the PV product with features in the role of keys).
   using T = ScaTile<D, DV, QB>;
   char* sbuf = reinterpret_cast<char*>(lds) + (kSca ? T::STAGE_BYTES : 0);
+  // chunk s reads the state holding the chunks before its previous one:
+  // snapshot slot s - 2 + 2 has_prev (with a carried chunk, slot 0 is the
+  // incoming state); the first two chunks of a sequence read nothing
+  const int rslot = s - 2 + 2 * a.has_prev;
+  const bool reads = s >= a.first_read;
   if constexpr (kRead) {
-    if (s >= 2) {
+    if (reads) {
       constexpr int RB = 64;  // rows per staging call
       constexpr int SLOADS = RB * DV * 2 / 16 / T::THREADS;
       constexpr int VCH = DV / 8;
-      const uint16_t* sn = a.snap + ((size_t)bh * a.nmem + (s - 2)) * (size_t)(D * DV);
+      const uint16_t* sn = a.snap + ((size_t)bh * a.nsnap + rslot) * (size_t)(D * DV);
       uint32_t soff[SLOADS];
 #pragma unroll
       for (int i = 0; i < SLOADS; ++i) {
@@ -542,7 +565,7 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   }
 
   if constexpr (kRead) {
-    if (s >= 2) {
+    if (reads) {
       // psi(Q_m) as the B operand: element e of lane (lq, g) in k-step
       // (fb, hh) is feature 32 fb + 16 hh + 8 (e >> 2) + 4 g + (e & 3). It is
       // packed unnormalised (2^(x - max)); the accumulators are scaled by the
@@ -701,11 +724,16 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   a.kappa_q = p.kappa_q; a.nu_q = p.nu_q; a.kappa_k = p.kappa_k;
   a.eta_q = p.eta_q; a.rho_q = p.rho_q;
   a.snap = static_cast<const uint16_t*>(w.snap);
+  a.zprev = static_cast<const uint16_t*>(p.zprev);
+  a.vprev = static_cast<const uint16_t*>(p.vprev);
+  a.has_prev = p.has_prev ? 1 : 0;
+  a.first_read = (int)p.first_read;
   a.n = p.n;
-  // the host validated n * max(d, dv) * 2 < 2^32 and the block count < 2^31
-  const int64_t cc = min(p.c, p.n);  // a chunk longer than the sequence is the sequence
-  a.c = (int)cc;
-  a.nchunks = (int)p.nchunks; a.nmem = (int)p.nmem; a.H = (int)p.H;
+  // the host validated n * max(d, dv) * 2 < 2^32 and the block count < 2^31;
+  // without a carried chunk, a chunk longer than the sequence is the sequence
+  const int64_t cc = min(p.c, p.n);
+  a.c = (int)(p.has_prev ? p.c : cc);
+  a.nchunks = (int)p.nchunks; a.nsnap = (int)p.nsnap; a.H = (int)p.H;
   a.qtiles = (int)((cc + kBM - 1) / kBM);
   const int64_t nblocks = p.B * p.H * p.nchunks * a.qtiles;
   a.nblocks = (int)nblocks;

@@ -22,6 +22,7 @@ EXPORTED = (
     "gecko_workspace_size", "gecko_sca_awm_forward", "gecko_sca_forward", "gecko_awm_forward",
     "gecko_timer_create", "gecko_timer_reset", "gecko_timer_read", "gecko_timer_destroy",
     "gecko_sca_awm_forward_timed", "gecko_status_string", "gecko_last_error", "gecko_version",
+    "gecko_stream_state_size", "gecko_stream_workspace_size", "gecko_sca_awm_forward_stream",
 )
 
 
@@ -62,6 +63,12 @@ def _load() -> ctypes.CDLL:
     lib.gecko_last_error.argtypes = []
     lib.gecko_version.restype = I
     lib.gecko_version.argtypes = []
+    lib.gecko_stream_state_size.restype = SZ
+    lib.gecko_stream_state_size.argtypes = [I64] * 5 + [I]
+    lib.gecko_stream_workspace_size.restype = SZ
+    lib.gecko_stream_workspace_size.argtypes = [I64] * 6 + [I]
+    lib.gecko_sca_awm_forward_stream.restype = I
+    lib.gecko_sca_awm_forward_stream.argtypes = [P] + [F] * 8 + [P, P] + [I64] * 7 + [I, I, U, P, SZ, P, SZ, P]
     return lib
 
 
@@ -191,6 +198,66 @@ def gecko_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, worksp
                                  B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags,
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def gecko_stream_state_size(B, H, d, dv, c, dtype_code) -> int:
+    r = lib.gecko_stream_state_size(B, H, d, dv, c, dtype_code)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_stream_state_size")
+    return r
+
+
+def gecko_stream_workspace_size(B, H, n, d, dv, c, dtype_code) -> int:
+    r = lib.gecko_stream_workspace_size(B, H, n, d, dv, c, dtype_code)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_stream_workspace_size")
+    return r
+
+
+def gecko_sca_awm_forward_stream(z, params, v, c, pos, state, out=None, out_dtype=None, flags=0, workspace=None,
+                                 stream=None):
+    """One call of a streamed sequence: rows pos .. pos + n of O = O_SCA + O_m.
+    ``state`` is a uint8 device tensor of gecko_stream_state_size() bytes."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    dt = _dtype_code(z)
+    if workspace is None:
+        nbytes = gecko_stream_workspace_size(B, H, n, d, dv, c, dt)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+    _check(lib.gecko_sca_awm_forward_stream(
+        _ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
+        B, H, n, d, dv, c, pos, dt, _dtype_code(out), flags, _ptr(state), state.numel(),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+class Stream:
+    """A sequence handed to the streaming forward in consecutive calls. Keeps
+    the device state and the token count; refuses a call after one that ended
+    inside a chunk."""
+
+    def __init__(self, B, H, d, dv, c, params, device="cuda", flags=0):
+        import torch
+
+        self.B, self.H, self.d, self.dv, self.c = B, H, d, dv, c
+        self.params, self.flags = params, flags
+        nbytes = gecko_stream_state_size(B, H, d, dv, c, GECKO_BF16)
+        self.state = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.pos = 0
+
+    def forward(self, z, v, out=None, out_dtype=None, workspace=None, stream=None):
+        if self.pos % self.c:
+            raise GeckoError(GECKO_EINVAL, "the previous call of this sequence ended inside a chunk")
+        if tuple(z.shape[:2]) != (self.B, self.H) or z.shape[3] != self.d or v.shape[3] != self.dv:
+            raise GeckoError(GECKO_EINVAL, "z and v do not match the stream's (B, H, d, dv)")
+        out = gecko_sca_awm_forward_stream(z, self.params, v, self.c, self.pos, self.state, out=out,
+                                           out_dtype=out_dtype, flags=self.flags, workspace=workspace,
+                                           stream=stream)
+        self.pos += z.shape[2]
+        return out
 
 
 class Timer:

@@ -106,6 +106,45 @@ gecko_status gecko_awm_forward(
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Streaming forward (bf16 inputs only): one sequence handed over in
+ * consecutive calls. The pages present Gecko as a model for sequences of
+ * arbitrary length whose memory is updated chunk by chunk and carries what
+ * the attention window no longer sees (chatpaper.ai abstract; paperlayer.ai
+ * summary, section 3.3). The output rows of each call are exactly the rows
+ * that one gecko_sca_awm_forward call over the whole sequence would give for
+ * the same tokens (chunks are counted from the start of the sequence).
+ *
+ * State: gecko_stream_state_size() bytes of caller-owned device memory,
+ * 256-byte aligned, one per sequence (all B*H heads of it). It holds the
+ * float32 memory state, the running per-feature denominator of the memory
+ * keys and the last chunk of Z' and V. Its contents are opaque; a call with
+ * pos == 0 ignores them, every call rewrites them. Sizes (B, H, d, dv, c)
+ * and the affine vectors must be the same on every call of a sequence.
+ *
+ * pos: tokens of this sequence given to earlier calls; 0 starts a new
+ * sequence. pos must be a multiple of c, and every call but the last of a
+ * sequence must hold a multiple of c tokens (a call with n % c != 0 ends the
+ * sequence; the library cannot detect a later call, whose result would then
+ * be undefined). c must be a multiple of 64. n >= 1 may be smaller than c.
+ *
+ * Workspace: gecko_stream_workspace_size() bytes (clobbered). The state must
+ * not alias z, v, out or the workspace. Errors as for gecko_sca_awm_forward
+ * (GECKO_EINVAL for a bad pos or a missing or small state). Calls of one
+ * sequence are ordered by the stream they are issued on.
+ */
+size_t gecko_stream_state_size(int64_t B, int64_t H, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype);
+size_t gecko_stream_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                   gecko_dtype in_dtype);
+gecko_status gecko_sca_awm_forward_stream(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, int64_t pos,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+    void* state, size_t state_bytes, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement helper: HIP events recorded between the kernels of a forward.
  * gecko_timer_create allocates the host object and `capacity` event sets;
  * each gecko_sca_awm_forward_timed call records one set (calls beyond the

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gecko_version() == 100
+    assert g.gecko_version() == 101
     for s in range(5):
         assert g.gecko_status_string(s).startswith("GECKO_")
     assert "unknown" in g.gecko_status_string(99)
@@ -122,3 +122,49 @@ def test_timer_argument_errors(g):
     assert g.lib.gecko_timer_create(0, ctypes.byref(h)) == g.GECKO_EINVAL
     assert g.lib.gecko_timer_reset(None) == g.GECKO_EINVAL
     assert g.lib.gecko_timer_destroy(None) == g.GECKO_OK
+
+
+def call_stream(g, **kw):
+    a = dict(z=FAKE, aff=[FAKE + 64 * i for i in range(8)], v=2 * FAKE, out=3 * FAKE, B=1, H=1, n=1000,
+             d=128, dv=256, c=128, pos=0, din=g.GECKO_BF16, dout=g.GECKO_BF16, flags=0, st=16 * FAKE,
+             stb=1 << 30, ws=32 * FAKE, wsb=1 << 30)
+    a.update(kw)
+    st = g.lib.gecko_sca_awm_forward_stream(a["z"], *a["aff"], a["v"], a["out"], a["B"], a["H"], a["n"], a["d"],
+                                            a["dv"], a["c"], a["pos"], a["din"], a["dout"], a["flags"], a["st"],
+                                            a["stb"], a["ws"], a["wsb"], None)
+    return st, g.lib.gecko_last_error().decode()
+
+
+def test_stream_validation_errors(g):
+    st, msg = call_stream(g, pos=64)
+    assert st == g.GECKO_EINVAL and "multiple of c" in msg
+    st, _ = call_stream(g, pos=-128)
+    assert st == g.GECKO_EINVAL
+    st, msg = call_stream(g, c=100)
+    assert st == g.GECKO_EUNSUPPORTED and "multiple of 64" in msg
+    st, msg = call_stream(g, din=g.GECKO_F32, dout=g.GECKO_F32, d=32, dv=32)
+    assert st == g.GECKO_EUNSUPPORTED and "bf16" in msg
+    st, msg = call_stream(g, st=0)
+    assert st == g.GECKO_EINVAL and "state" in msg
+    st, msg = call_stream(g, stb=1024)
+    assert st == g.GECKO_EINVAL and "too small" in msg
+    st, msg = call_stream(g, st=16 * FAKE + 16)
+    assert st == g.GECKO_EINVAL and "aligned" in msg
+    st, msg = call_stream(g, st=FAKE)  # overlaps z
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call_stream(g, wsb=1024)
+    assert st == g.GECKO_EWORKSPACE
+
+
+def test_stream_sizes(g):
+    s = g.gecko_stream_state_size(1, 8, 128, 256, 2048, g.GECKO_BF16)
+    expect = 8 * (128 * 256 * 4 + 128 * 2 * 4 + 2048 * 128 * 2 + 2048 * 256 * 2)
+    assert expect <= s <= expect + 4 * 256
+    with pytest.raises(g.GeckoError):
+        g.gecko_stream_state_size(1, 8, 128, 256, 2048, g.GECKO_F32)
+    # a call with a carried chunk stores one more memory step and one more snapshot
+    one = g.gecko_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16)
+    st = g.gecko_stream_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16)
+    per_step = 8 * (128 * 256 * 4 + 128 * 128 * 2 + 4 * 128 * 4 + 256 * 128 * 2)
+    extra = 8 * 128 * 256 * 2 + 8 * 128 * 2 * 4  # one more snapshot slot, the final denominator
+    assert one + 2 * per_step + extra <= st <= one + 2 * per_step + extra + 10 * 256
