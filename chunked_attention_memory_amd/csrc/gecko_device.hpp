@@ -93,6 +93,13 @@ __device__ __forceinline__ float other_half_sum(float x) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N vector-memory loads of this wave are in flight (they
+// complete in issue order, so the N most recent ones may still be pending)
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Copy rows [row0, row0 + rows_in_tile) of a row-major bf16 matrix with `width`
 // columns into LDS with buffer loads that write LDS directly (lane l of a

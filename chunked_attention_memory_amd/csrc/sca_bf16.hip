@@ -30,9 +30,12 @@
 // read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i
 // of a 4-row x 16-column block).
 //
-// Pipeline: tile kt+1 is loaded into the other LDS stage while tile kt is
-// computed; operand reads from LDS run a few MFMAs ahead of their use, and
-// the loop is unrolled by two tiles so every LDS address is a per-lane base
+// Pipeline: three LDS stages; tile kt+2 is loaded while tile kt is computed.
+// Each stage is a separate LDS variable, which lets the compiler see that
+// reads of one stage do not alias the loads still writing another (with one
+// LDS array it waits for every load in flight before the first V read of a
+// tile). Operand reads from LDS run a few MFMAs ahead of their use, and the
+// loop is unrolled by three tiles so every LDS address is a per-lane base
 // plus a constant offset.
 //
 // Softmax offset: the first pass uses none (P = 2^s; bf16 and fp32 share the
@@ -81,14 +84,20 @@ struct ScaTile {
   static constexpr int THREADS = 64 * NW;
   static constexpr int KBYTES = kBN * D * 2;   // dense rows, chunk-swizzled
   static constexpr int VBYTES = kBN * DV * 2;
-  static constexpr int NSTAGE = 2;  // (K, V) stages in LDS
-  static constexpr size_t STAGE_BYTES = NSTAGE * ((size_t)KBYTES + (size_t)VBYTES);
+  // (K, V) stages in LDS: tile k + 2 is loaded while tile k is computed
+  static constexpr int NSTAGE = 3;
+  static constexpr size_t STAGE1 = (size_t)KBYTES + (size_t)VBYTES;  // one stage: K tile, then V tile
+  static constexpr size_t STAGE_BYTES = NSTAGE * STAGE1;
   static constexpr size_t SNAP_BYTES = (size_t)D * DV * 2;  // the memory state for the readout
+  // The state goes to its own LDS region at kernel start when that fits
+  // beside the stages; otherwise into the stage memory after the loop.
+  static constexpr bool SNAP_EARLY = STAGE_BYTES + SNAP_BYTES <= 160 * 1024;
   static constexpr size_t lds_bytes(bool sca, bool read) {
-    return (sca ? STAGE_BYTES : 0) + (read ? SNAP_BYTES : 0);
+    return sca ? STAGE_BYTES + (read && SNAP_EARLY ? SNAP_BYTES : 0) : (read ? SNAP_BYTES : 0);
   }
   static constexpr int KLOADS = KBYTES / 16 / THREADS;  // 16-byte loads per thread per tile
   static constexpr int VLOADS = VBYTES / 16 / THREADS;
+  static constexpr int LOADS = KLOADS + VLOADS;  // staging loads per lane and tile
   static_assert(32 * QB * NW == kBM, "tile shape");
 };
 
@@ -141,8 +150,10 @@ struct ScaLoop {
   const uint16_t* zpv;  // carried chunk (keys at negative rows), streaming only
   const uint16_t* vpv;
   int cl;               // chunk length
-  char* kbuf;  // K stages
-  char* vbuf;  // V stages
+  // stage i: K tile at sb[i], V tile at sb[i] + KBYTES. Each stage is its
+  // own LDS variable, so the compiler can tell a stage being read from the
+  // stages the tile loads are still writing (and does not wait for them).
+  char* sb[T::NSTAGE];
   int n, kbeg, kend, ntiles, myq0, wave_q0, wave_last, w, g, lq;
   u32x4 qf[QB][KS];
   uint32_t koff[T::KLOADS], voff[T::VLOADS];
@@ -150,7 +161,8 @@ struct ScaLoop {
   int va[NMV];   // V transpose-read byte offset in a stage for value block mv, key row 0
 
   __device__ __forceinline__ void init(const ScaArgs& a, uint32_t bh, int h, int n_, int s, int c, int q0,
-                                       int qend, int w_, int lane, uint16_t* lds, const int (&va_)[NMV]) {
+                                       int qend, int w_, int lane, char* s0, char* s1, char* s2,
+                                       const int (&va_)[NMV]) {
     n = n_;
     w = w_;
     wave_q0 = q0 + 32 * QB * w;
@@ -162,8 +174,9 @@ struct ScaLoop {
     cl = c;
     zpv = a.has_prev ? a.zprev + (size_t)bh * (size_t)c * D : nullptr;
     vpv = a.has_prev ? a.vprev + (size_t)bh * (size_t)c * DV : nullptr;
-    kbuf = reinterpret_cast<char*>(lds);
-    vbuf = kbuf + T::NSTAGE * T::KBYTES;
+    sb[0] = s0;
+    sb[1] = s1;
+    sb[2] = s2;
 
     // query fragments: lane holds query 32 qb + lq of the wave, features
     // 16 ks + 8 g + [0, 8); rows past the tile repeat its last query
@@ -230,8 +243,8 @@ struct ScaLoop {
     const bool carried = row0 < 0;
     const int r = carried ? row0 + cl : row0;
     const int lim = carried ? cl : n;
-    stage_rows(carried ? zpv : zbh, r, lim, D, kbuf + slot * T::KBYTES, NW, w, koff, T::KLOADS);
-    stage_rows(carried ? vpv : vbh, r, lim, DV, vbuf + slot * T::VBYTES, NW, w, voff, T::VLOADS);
+    stage_rows(carried ? zpv : zbh, r, lim, D, sb[slot], NW, w, koff, T::KLOADS);
+    stage_rows(carried ? vpv : vbh, r, lim, DV, sb[slot] + T::KBYTES, NW, w, voff, T::VLOADS);
   }
 
   __device__ __forceinline__ int k_addr(int mb, int ks) const { return ka[ks] + 32 * mb * (D * 2); }
@@ -242,7 +255,7 @@ struct ScaLoop {
   // S^T for keys 32 mb + [0, 32) of the tile in `slot`, every query block:
   // register r holds key 32 mb + 8 (r >> 2) + 4 g + (r & 3)
   __device__ __forceinline__ void qk(int slot, int mb, f32x16 (&sc)[QB]) const {
-    const char* Kb = kbuf + slot * T::KBYTES;
+    const char* Kb = sb[slot];
     constexpr int AH = GECKO_SCA_KAHEAD;
     u32x4 op[AH + 1];
 #pragma unroll
@@ -276,7 +289,7 @@ struct ScaLoop {
   // O^T += V^T P^T for the 32 keys of half mb; the V operand of MFMA i + AH
   // is read from LDS before MFMA i is issued.
   __device__ __forceinline__ void pv(int slot, int mb, const u32x4 (&pf)[QB][2], f32x16 (&oacc)[QB][NMV]) const {
-    const char* Vb = vbuf + slot * T::VBYTES;
+    const char* Vb = sb[slot] + T::KBYTES;
     constexpr int NI = 2 * NMV;
     constexpr int AH = GECKO_SCA_VAHEAD;
     u32x4 op[AH + 1];
@@ -366,41 +379,54 @@ struct ScaLoop {
     pv(STG, mb, pf, oacc);
   }
 
-  // Tile k of a pass in stage STG = k mod 2 (a constant, so that operand
+  // Tile k of a pass in stage STG = k mod 3 (a constant, so that operand
   // addresses fold into the read offsets): stage this wave's share of tile
-  // k + 1 into the other stage (read last iteration), compute the halves of
-  // tile k that some query of the wave sees, end at the barrier.
+  // k + 2 into the stage tile k - 1 used (every wave is past it), compute the
+  // halves of tile k that some query of the wave sees, wait for this wave's
+  // share of tile k + 1 (tile k + 2's loads may stay in flight) and end at
+  // the barrier.
   template <int STG, bool kSub>
   __device__ __forceinline__ void tile(int k, const float (&msub)[QB], float (&lrun)[QB],
                                        f32x16 (&oacc)[QB][NMV]) const {
-    if (k + 1 < ntiles) stage(k + 1, STG ^ 1);
+    const bool ahead = k + 2 < ntiles;
+    if (ahead) stage(k + 2, (STG + 2) % T::NSTAGE);
     if (live(k, 0)) half<STG, kSub>(k, 0, msub, lrun, oacc);
     if (live(k, 1)) half<STG, kSub>(k, 1, msub, lrun, oacc);
-    wait_vmem();
+    if (ahead)
+      wait_vmem_leave<T::LOADS>();
+    else
+      wait_vmem();
     __syncthreads();
   }
 
   // full pass with fixed softmax offsets; returns the row exp-sums
   template <bool kSub>
   __device__ __forceinline__ void pass(const float (&msub)[QB], float (&ltot)[QB], f32x16 (&oacc)[QB][NMV]) const {
+    static_assert(T::NSTAGE == 3, "the tile loop is unrolled by the stage count");
     stage(0, 0);
-    wait_vmem();
+    if (ntiles > 1) {
+      stage(1, 1);
+      wait_vmem_leave<T::LOADS>();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
     float lrun[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
-    for (int k = 0; k < ntiles; k += 2) {
+    for (int k = 0; k < ntiles; k += 3) {
       tile<0, kSub>(k, msub, lrun, oacc);
       if (k + 1 < ntiles) tile<1, kSub>(k + 1, msub, lrun, oacc);
+      if (k + 2 < ntiles) tile<2, kSub>(k + 2, msub, lrun, oacc);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) ltot[qb] = other_half_sum(lrun[qb]);
   }
 
-  // OR of a per-lane flag over the workgroup, through a word of the K stage
+  // OR of a per-lane flag over the workgroup, through a word of the stage
   // memory (free between passes; every wave is past the pass's last barrier)
   __device__ __forceinline__ bool block_any(bool x) const {
-    volatile int* flag = reinterpret_cast<volatile int*>(kbuf);
+    volatile int* flag = reinterpret_cast<volatile int*>(sb[0]);
     if (threadIdx.x == 0) *flag = 0;
     __syncthreads();
     if (x) *flag = 1;
@@ -458,14 +484,38 @@ struct ScaLoop {
 // fb = (i / 2) % NFB, half hh = i % 2) from the staged state: the V^T
 // transpose reads of ScaLoop::v_addr with features in the role of keys.
 // A plain device function: a lambda in a kernel is compiled for the host too.
-template <int D, int DV>
-__device__ __forceinline__ u32x4 snap_operand(const char* sbuf, const int (&va)[DV / 32], int i) {
+// The staged state holds feature blocks [0, FB0) in region sa and the rest
+// in region sbk (32 rows of DV values per block).
+template <int D, int DV, int FB0>
+__device__ __forceinline__ u32x4 snap_operand(const char* sa, const char* sbk, const int (&va)[DV / 32], int i) {
   constexpr int NFB = D / 32;
   const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
-  const char* base = sbuf + va[mv];
-  const u32x2 l2 = lds_read_tr(base + (32 * fb + 16 * hh) * (DV * 2));
-  const u32x2 h2 = lds_read_tr(base + (32 * fb + 16 * hh + 8) * (DV * 2));
+  const char* base = (fb < FB0 ? sa + 32 * fb * (DV * 2) : sbk + 32 * (fb - FB0) * (DV * 2)) + va[mv];
+  const u32x2 l2 = lds_read_tr(base + (16 * hh) * (DV * 2));
+  const u32x2 h2 = lds_read_tr(base + (16 * hh + 8) * (DV * 2));
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Stage the memory state [D][DV] (bf16, feature rows) into LDS with the V
+// tiles' layout and swizzle: feature blocks [0, FB0) into sa, the rest into sbk.
+template <int D, int DV, int THREADS, int FB0>
+__device__ __forceinline__ void stage_snapshot(const uint16_t* sn, char* sa, char* sbk, int w, int lane) {
+  constexpr int NW = THREADS / 64;
+  constexpr int RB = 32;  // rows per staging call: one feature block
+  constexpr int SLOADS = RB * DV * 2 / 16 / THREADS;
+  static_assert(SLOADS >= 1 && SLOADS * 16 * THREADS == RB * DV * 2, "snapshot staging shape");
+  constexpr int VCH = DV / 8;
+  uint32_t soff[SLOADS];
+#pragma unroll
+  for (int i = 0; i < SLOADS; ++i) {
+    const int P = (NW * i + w) * 64 + lane;
+    const int r = P / VCH, p = P % VCH;
+    soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
+  }
+#pragma unroll
+  for (int rb = 0; rb < D / RB; ++rb)
+    stage_rows(sn, rb * RB, D, DV, rb < FB0 ? sa + rb * RB * DV * 2 : sbk + (rb - FB0) * RB * DV * 2, NW, w, soff,
+               SLOADS);
 }
 
 // Byte offset, in a staged V tile (rows of DV values), of the transpose read
@@ -490,7 +540,6 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   constexpr int QB = ScaShape<D, DV>::QB;
   constexpr int KS = D / 16;   // 16-feature k-steps of the readout
   constexpr int NMV = DV / 32; // 32-row blocks of O^T
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
   // run of logical blocks so the q-tiles of one chunk share an L2.
@@ -521,34 +570,39 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 #pragma unroll
     for (int i = 0; i < NMV; ++i) oacc[qb][i] = f32x16{};
 
-  // The memory state M'_{s-1} ([d][dv], feature rows) is final before this
-  // kernel starts: it goes to its own LDS region now, behind the attention
-  // loop, with the V tiles' layout and swizzle (the readout psi(Q_m) M' is
-  // the PV product with features in the role of keys).
+  // LDS: the three (K, V) stages, and the memory state M'_{s-1} ([d][dv],
+  // feature rows) with the V tiles' layout and swizzle (the readout
+  // psi(Q_m) M' is the PV product with features in the role of keys). The
+  // state is final before this kernel starts: where it fits beside the stages
+  // it is staged now, behind the attention loop; otherwise into the stage
+  // memory after the loop (feature blocks [0, FB0) in stage 0, the rest in
+  // stage 1).
   using T = ScaTile<D, DV, QB>;
-  char* sbuf = reinterpret_cast<char*>(lds) + (kSca ? T::STAGE_BYTES : 0);
+  constexpr int NFB = D / 32;
+  constexpr bool kEarly = !kSca || T::SNAP_EARLY;
+  constexpr int FB0 = kEarly ? NFB : (int)(T::STAGE1 / (32 * DV * 2)) < NFB ? (int)(T::STAGE1 / (32 * DV * 2)) : NFB;
+  static_assert(kEarly || (size_t)(NFB - FB0) * 32 * DV * 2 <= T::STAGE1, "state split over two stages");
+  __shared__ __attribute__((aligned(16))) char S0[kSca ? T::STAGE1 : 16];
+  __shared__ __attribute__((aligned(16))) char S1[kSca ? T::STAGE1 : 16];
+  __shared__ __attribute__((aligned(16))) char S2[kSca ? T::STAGE1 : 16];
+  __shared__ __attribute__((aligned(16))) char SN[kRead && kEarly ? T::SNAP_BYTES : 16];
+  char* snap_a;
+  char* snap_b;
+  if constexpr (kEarly) {
+    snap_a = SN;
+    snap_b = SN;
+  } else {
+    snap_a = S0;
+    snap_b = S1;
+  }
   // chunk s reads the state holding the chunks before its previous one:
   // snapshot slot s - 2 + 2 has_prev (with a carried chunk, slot 0 is the
   // incoming state); the first two chunks of a sequence read nothing
   const int rslot = s - 2 + 2 * a.has_prev;
   const bool reads = s >= a.first_read;
-  if constexpr (kRead) {
-    if (reads) {
-      constexpr int RB = 64;  // rows per staging call
-      constexpr int SLOADS = RB * DV * 2 / 16 / T::THREADS;
-      constexpr int VCH = DV / 8;
-      const uint16_t* sn = a.snap + ((size_t)bh * a.nsnap + rslot) * (size_t)(D * DV);
-      uint32_t soff[SLOADS];
-#pragma unroll
-      for (int i = 0; i < SLOADS; ++i) {
-        const int P = (T::NW * i + w) * 64 + lane;
-        const int r = P / VCH, p = P % VCH;
-        soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
-      }
-#pragma unroll
-      for (int rb = 0; rb < D / RB; ++rb)
-        stage_rows(sn, rb * RB, D, DV, sbuf + rb * RB * DV * 2, T::NW, w, soff, SLOADS);
-    }
+  const uint16_t* sn = a.snap + ((size_t)bh * a.nsnap + rslot) * (size_t)(D * DV);
+  if constexpr (kRead && kEarly) {
+    if (reads) stage_snapshot<D, DV, T::THREADS, FB0>(sn, snap_a, snap_b, w, lane);
   }
 
   // attention row sums: O = oacc / lsum (+ readout)
@@ -560,8 +614,11 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   for (int mv = 0; mv < NMV; ++mv) va[mv] = v_operand_base<DV>(lane, mv);
   if constexpr (kSca) {
     ScaLoop<D, DV, QB> L;
-    L.init(a, bh, h, n, s, c, q0, qend, w, lane, lds, va);
+    L.init(a, bh, h, n, s, c, q0, qend, w, lane, S0, S1, S2, va);
     L.run(oacc, lsum);
+  }
+  if constexpr (kRead && !kEarly) {  // every wave is past the loop's last barrier
+    if (reads) stage_snapshot<D, DV, T::THREADS, FB0>(sn, snap_a, snap_b, w, lane);
   }
 
   if constexpr (kRead) {
@@ -571,7 +628,6 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
       // packed unnormalised (2^(x - max)); the accumulators are scaled by the
       // psi row sum before the readout MFMAs and divided by it afterwards, so
       // that O = attention / lsum + psi M'.
-      constexpr int NFB = D / 32;
       const float* eq = a.eta_q + h * D;
       const float* rq = a.rho_q + h * D;
       u32x4 pf[QB][NFB][2];
@@ -624,10 +680,10 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
       constexpr int NI = NMV * NFB * 2, AH = 2;
       u32x4 op[AH + 1];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV>(sbuf, va, i);
+      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV, FB0>(snap_a, snap_b, va, i);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV>(sbuf, va, i + AH);
+        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV, FB0>(snap_a, snap_b, va, i + AH);
         const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(op[i % (AH + 1)], pf[qb][fb][hh], oacc[qb][mv]);
@@ -678,20 +734,10 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 hipError_t launch_one(const ScaArgs& a, hipStream_t stream) {
   using T = ScaTile<D, DV, ScaShape<D, DV>::QB>;
-  auto kern = sca_bf16_kernel<D, DV, kSca, kRead, kOutF32>;
-  constexpr size_t lds = T::lds_bytes(kSca, kRead);
-  static_assert(lds <= 160 * 1024, "LDS per workgroup");
-  if (lds > 65536) {
-    static bool attr_set = false;  // per instantiation
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-  }
+  // all LDS is static (per-stage variables, sized by lds_bytes)
+  static_assert(T::lds_bytes(kSca, kRead) <= 160 * 1024, "LDS per workgroup");
   const dim3 grid((unsigned)(8 * a.per_xcd));
-  hipLaunchKernelGGL(kern, grid, dim3(T::THREADS), lds, stream, a);
+  hipLaunchKernelGGL((sca_bf16_kernel<D, DV, kSca, kRead, kOutF32>), grid, dim3(T::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
