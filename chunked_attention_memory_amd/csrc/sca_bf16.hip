@@ -68,6 +68,10 @@ namespace {
 #ifndef GECKO_SCA_VAHEAD
 #define GECKO_SCA_VAHEAD 2
 #endif
+// (batch*head, chunk) pairs per group of the workgroup order (see the kernel)
+#ifndef GECKO_SCA_GROUP
+#define GECKO_SCA_GROUP 2
+#endif
 
 constexpr int kBM = 256;               // queries per workgroup
 constexpr int kBN = 64;                // keys per tile
@@ -546,9 +550,17 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   const uint32_t bid = blockIdx.x;
   const uint32_t lb = (bid & 7u) * (uint32_t)a.per_xcd + (bid >> 3);
   if (lb >= (uint32_t)a.nblocks) return;
+  // Within an XCD, groups of GECKO_SCA_GROUP consecutive (batch*head, chunk)
+  // pairs run their longest q-tiles first, so the workgroups left at the end
+  // of the grid are short ones.
   const uint32_t qtiles = (uint32_t)a.qtiles, nchunks = (uint32_t)a.nchunks;
-  const int qt = (int)(qtiles - 1 - lb % qtiles);  // longest q-tiles first
-  const uint32_t rest = lb / qtiles;
+  const uint32_t npairs = (uint32_t)a.nblocks / qtiles;
+  const uint32_t grp = lb / (GECKO_SCA_GROUP * qtiles);
+  const uint32_t base = grp * GECKO_SCA_GROUP;
+  const uint32_t gsize = min((uint32_t)GECKO_SCA_GROUP, npairs - base);
+  const uint32_t within = lb - base * qtiles;
+  const int qt = (int)(qtiles - 1 - within / gsize);
+  const uint32_t rest = base + within % gsize;
   const int s = (int)(rest % nchunks);
   const uint32_t bh = rest / nchunks;
   const int h = (int)(bh % (uint32_t)a.H);
