@@ -39,6 +39,12 @@ is used):
 * R7 z^0 = 0 (empty sum), so the ratio is 0 on the first update; M'_0 (read by
   chunk 1) is taken as 0 like M'_1.
 * R8 the output is exactly O_SCA + O_m (no gate, no projection).
+* R9 chunk-wise variant (the ablation the pages set SCA and AWM against:
+  Megalodon's chunk-wise attention, [paperlayer 2.3], and the memory without
+  sliding chunks, [paperlayer Appendix A]): attention stays inside the
+  current chunk (causal), and the memory is read one chunk earlier: with
+  M_0 = 0 and the same update, chunk s reads the state holding chunks
+  1..s-1 (the sliding form reads the one holding chunks 1..s-2).
 
 Everything is evaluated in float64 on the exact (already rounded) input values
 the GPU receives. Inputs may be float32 (bf16-exact values are exact in
@@ -111,28 +117,30 @@ def sca_chunk(q_rows: np.ndarray, k_win: np.ndarray, v_win: np.ndarray,
     return w @ np.asarray(v_win, np.float64)
 
 
-def _window(n: int, c: int, s: int) -> tuple[int, int, int]:
+def _window(n: int, c: int, s: int, sliding: bool = True) -> tuple[int, int, int]:
     """(first key, first query, end) of chunk s (0-based) and its window.
 
     R4: chunk 0 has no previous chunk; [paperlayer 3.2]: the window of chunk s
-    is the previous chunk plus the current one.
+    is the previous chunk plus the current one. R9: without sliding, the
+    current chunk only.
     """
     q0 = s * c
     q1 = min(q0 + c, n)
-    return max(0, q0 - c), q0, q1
+    return (max(0, q0 - c) if sliding else q0), q0, q1
 
 
-def sca_head(z, v, kappa_q, nu_q, kappa_k, nu_k, c: int, chunks=None) -> np.ndarray:
+def sca_head(z, v, kappa_q, nu_q, kappa_k, nu_k, c: int, chunks=None, sliding: bool = True) -> np.ndarray:
     """O_SCA for one head: z [n, d], v [n, dv], affine vectors [d].
 
     Returns float64 [n, dv]; or, if ``chunks`` (0-based chunk indices) is
-    given, a dict mapping each of those chunks to its rows.
+    given, a dict mapping each of those chunks to its rows. ``sliding=False``
+    is the chunk-wise attention of R9.
     """
     n = z.shape[0]
     out = np.empty((n, v.shape[1])) if chunks is None else {}
     nchunks = len(chunk_ranges(n, c))
     for s in (range(nchunks) if chunks is None else chunks):
-        k0, q0, q1 = _window(n, c, s)
+        k0, q0, q1 = _window(n, c, s, sliding)
         q = affine(z[q0:q1], kappa_q, nu_q)
         k = affine(z[k0:q1], kappa_k, nu_k)
         rows = sca_chunk(q, k, v[k0:q1], np.arange(q0, q1), np.arange(k0, q1))
@@ -144,7 +152,7 @@ def sca_head(z, v, kappa_q, nu_q, kappa_k, nu_k, c: int, chunks=None) -> np.ndar
 
 
 def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
-             trace=None, readout_chunks=None):
+             trace=None, readout_chunks=None, lag: int = 2):
     """O_m for one head: z [n, d], v [n, dv], affine vectors [d].
 
     Follows [rainbus "Method steps" (4)-(5)] and [rainbus "Core method"],
@@ -164,8 +172,11 @@ def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
       denominator, since the normaliser is identically one ("Core method",
       [paperlayer 3.3]).
 
+    ``lag=1`` is the memory without sliding chunks (R9): chunk s reads the
+    state holding chunks 1..s-1 (M_{s-1} with M_0 = 0) instead of M'_{s-1}.
+
     ``trace``, if a list, receives one dict per chunk s (1-based) with the
-    float64 z^s, phi^s(K_s) and M'_{s-1} used by the readout.
+    float64 z^s, phi^s(K_s) and the state used by the readout.
 
     Returns float64 [n, dv]; or, if ``readout_chunks`` (0-based chunk indices)
     is given, a dict mapping each of those chunks to its rows (the memory
@@ -180,10 +191,14 @@ def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
     z_prev = np.zeros(d)              # z^{s-1}
     mem_prev = np.zeros((d, dv))      # M'_{s-1}
     mem_cur = np.zeros((d, dv))       # M'_s
+    if lag not in (1, 2):
+        raise ValueError("lag is 2 (sliding chunks) or 1 (without)")
     for s, (a, b) in enumerate(ranges, start=1):
-        # readout of chunk s from M'_{s-1}
+        # readout of chunk s from M'_{s-1} (lag 2), or from the state holding
+        # chunks 1..s-1 (lag 1), which is M'_s of the same update
+        read = mem_prev if lag == 2 else mem_cur
         if wanted is None or s - 1 in wanted:
-            rows = feature_softmax(affine(z[a:b], eta_q, rho_q)) @ mem_prev
+            rows = feature_softmax(affine(z[a:b], eta_q, rho_q)) @ read
             if wanted is None:
                 out[a:b] = rows
             else:
@@ -199,36 +214,37 @@ def awm_head(z, v, eta_q, rho_q, eta_k, rho_k, c: int, no_delta: bool = False,
             resid = np.asarray(v[a:b], np.float64) - feature_softmax(km) @ mem_cur
         mem_next = (z_prev / z_cur)[:, None] * mem_cur + phi.T @ resid
         if trace is not None:
-            trace.append({"s": s, "z": z_cur.copy(), "phi": phi, "mem_read": mem_prev.copy()})
+            trace.append({"s": s, "z": z_cur.copy(), "phi": phi, "mem_read": read.copy()})
         mem_prev, mem_cur = mem_cur, mem_next
         z_prev = z_cur
     return out
 
 
 def forward_head(z, v, p: dict, h: int, c: int, no_delta: bool = False,
-                 sca_chunks=None) -> dict:
+                 sca_chunks=None, chunkwise: bool = False) -> dict:
     """O = O_SCA + O_m for head h of one batch row ([rainbus "Method steps" (5)], R8).
 
     ``p`` maps the eight affine-vector names to [H, d] arrays. With
     ``sca_chunks`` (0-based) every entry is a dict of those chunks' rows.
+    ``chunkwise`` selects the variant of R9.
     """
     o_sca = sca_head(z, v, p["kappa_q"][h], p["nu_q"][h], p["kappa_k"][h], p["nu_k"][h],
-                     c, chunks=sca_chunks)
+                     c, chunks=sca_chunks, sliding=not chunkwise)
     o_m = awm_head(z, v, p["eta_q"][h], p["rho_q"][h], p["eta_k"][h], p["rho_k"][h],
-                   c, no_delta=no_delta, readout_chunks=sca_chunks)
+                   c, no_delta=no_delta, readout_chunks=sca_chunks, lag=1 if chunkwise else 2)
     if sca_chunks is None:
         return {"o_sca": o_sca, "o_m": o_m, "o": o_sca + o_m}
     return {"o_sca": o_sca, "o_m": o_m, "o": {s: o_sca[s] + o_m[s] for s in sca_chunks}}
 
 
-def forward(z, v, p: dict, c: int, no_delta: bool = False) -> dict:
+def forward(z, v, p: dict, c: int, no_delta: bool = False, chunkwise: bool = False) -> dict:
     """Whole-tensor forward: z [B, H, n, d], v [B, H, n, dv]; float64 outputs [B, H, n, dv]."""
     B, H, n, _ = z.shape
     dv = v.shape[3]
     res = {key: np.empty((B, H, n, dv)) for key in ("o_sca", "o_m", "o")}
     for b in range(B):
         for h in range(H):
-            r = forward_head(z[b, h], v[b, h], p, h, c, no_delta=no_delta)
+            r = forward_head(z[b, h], v[b, h], p, h, c, no_delta=no_delta, chunkwise=chunkwise)
             for key in res:
                 res[key][b, h] = r[key]
     return res

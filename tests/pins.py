@@ -14,18 +14,19 @@ import numpy as np
 from scipy.special import softmax as sp_softmax
 
 
-def band_mask(n: int, c: int) -> np.ndarray:
-    """Visibility of key j to query i: causal, and key chunk >= query chunk - 1."""
+def band_mask(n: int, c: int, prev: int = 1) -> np.ndarray:
+    """Visibility of key j to query i: causal, and key chunk >= query chunk - prev
+    (prev = 1: sliding chunks; prev = 0: the chunk-wise variant)."""
     i = np.arange(n)[:, None]
     j = np.arange(n)[None, :]
-    return (j <= i) & (j // c >= i // c - 1)
+    return (j <= i) & (j // c >= i // c - prev)
 
 
-def brute_sca(q, k, v, c):
+def brute_sca(q, k, v, c, prev: int = 1):
     """Full n x n masked softmax attention (scale 1) with the band mask."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     logits = q @ k.T
-    logits[~band_mask(q.shape[0], c)] = -np.inf
+    logits[~band_mask(q.shape[0], c, prev)] = -np.inf
     return sp_softmax(logits, axis=1) @ v
 
 
@@ -39,16 +40,16 @@ def causal_attention_torch(q, k, v):
     return o[0, 0].numpy()
 
 
-def window_mean(v, c):
+def window_mean(v, c, prev: int = 1):
     """Closed form of SCA when every logit is equal: the mean of v over the window.
 
-    The window of token i is [max(0, (i//c - 1) c), i]; prefix sums give each mean.
+    The window of token i is [max(0, (i//c - prev) c), i]; prefix sums give each mean.
     """
     v = np.asarray(v, np.float64)
     n = v.shape[0]
     cs = np.vstack([np.zeros((1, v.shape[1])), np.cumsum(v, axis=0)])
     i = np.arange(n)
-    lo = np.maximum(0, (i // c - 1) * c)
+    lo = np.maximum(0, (i // c - prev) * c)
     return (cs[i + 1] - cs[lo]) / (i + 1 - lo)[:, None]
 
 
@@ -56,14 +57,15 @@ def _chunks(n, c):
     return [(a, min(a + c, n)) for a in range(0, n, c)]
 
 
-def awm_unrolled(qm, km, v, c):
+def awm_unrolled(qm, km, v, c, lag: int = 2):
     """O_m from the unrolled sum of transition-matrix products.
 
     With z^t the cumulative per-feature exp-sum through chunk t,
       T_t = diag(z^{t-1}/z^t) - diag(1/z^t) exp(K_t)^T psi(K_t)   (d x d)
       B_t = diag(1/z^t) exp(K_t)^T V_t                           (d x dv)
-    the memory is M'_s = sum_{t=1}^{s-1} T_{s-1} ... T_{t+1} B_t, and chunk s reads
-    psi(Q_m,s) M'_{s-1} (zero for s <= 2). Products are formed explicitly.
+    the memory is M'_s = sum_{t=1}^{s-1} T_{s-1} ... T_{t+1} B_t (it holds chunks
+    1..s-1), and chunk s reads the one holding chunks 1..s-lag: psi(Q_m,s)
+    M'_{s+1-lag} (zero for s <= lag). Products are formed explicitly.
     """
     qm, km, v = (np.asarray(a, np.float64) for a in (qm, km, v))
     n, d = km.shape
@@ -93,22 +95,23 @@ def awm_unrolled(qm, km, v, c):
         return total
 
     out = np.zeros((n, dv))
-    for s in range(3, N + 1):
+    for s in range(lag + 1, N + 1):
         a, b = ch[s - 1]
-        out[a:b] = sp_softmax(qm[a:b], axis=1) @ mem(s - 1)
+        out[a:b] = sp_softmax(qm[a:b], axis=1) @ mem(s + 1 - lag)
     return out
 
 
-def awm_no_delta_closed(qm, km, v, c):
+def awm_no_delta_closed(qm, km, v, c, lag: int = 2):
     """Closed form without the delta correction: linear attention with the
-    online-softmax kernel. M'_{s-1} = (sum over tokens of chunks 1..s-2 of
-    exp(k)^T v) / z^{s-2}, row f divided by z^{s-2}_f; chunk s reads psi(Q_m) M'_{s-1}."""
+    online-softmax kernel. The state holding chunks 1..u is (sum over their
+    tokens of exp(k)^T v) / z^u, row f divided by z^u_f; chunk s reads
+    psi(Q_m) times the one with u = s - lag."""
     qm, km, v = (np.asarray(a, np.float64) for a in (qm, km, v))
     n, d = km.shape
     out = np.zeros((n, v.shape[1]))
     ch = _chunks(n, c)
-    for s in range(3, len(ch) + 1):
-        end = ch[s - 3][1]  # last token of chunk s-2
+    for s in range(lag + 1, len(ch) + 1):
+        end = ch[s - lag - 1][1]  # last token of chunk s - lag
         e = np.exp(km[:end])
         mem = (e.T @ v[:end]) / e.sum(axis=0)[:, None]
         a, b = ch[s - 1]
@@ -116,13 +119,15 @@ def awm_no_delta_closed(qm, km, v, c):
     return out
 
 
-def awm_const_key_chunk_rows(v, c):
+def awm_const_key_chunk_rows(v, c, lag: int = 2):
     """Closed form when every memory key row is the same vector, one row per chunk.
 
-    Then every row of M' is the same vector m_s, psi(Q_m) M' = m_s for any
-    query, and with vbar_t the mean of V over chunk t (1-based):
-      chunk s <= 2 reads 0; chunk 3 reads vbar_1;
-      chunk s >= 4 reads sum_{t=2}^{s-2} (t-1) vbar_t / ((s-2)(s-3)).
+    Then every row of the state is the same vector, psi(Q_m) M' is that
+    vector for any query, and with vbar_t the mean of V over chunk t
+    (1-based) the state holding chunks 1..u is
+      f(0) = 0, f(1) = vbar_1, f(u) = sum_{t=2}^{u} (t-1) vbar_t / (u (u-1)).
+    Chunk s reads f(s - lag) (sliding chunks: lag 2, so chunk 3 reads vbar_1
+    and chunk s >= 4 reads sum_{t=2}^{s-2} (t-1) vbar_t / ((s-2)(s-3))).
     Returns [N, dv]: row s-1 is what every query of chunk s reads.
     """
     v = np.asarray(v, np.float64)
@@ -132,17 +137,16 @@ def awm_const_key_chunk_rows(v, c):
     t = np.arange(1, N + 1, dtype=np.float64)
     w = np.cumsum((t - 1.0)[:, None] * vbar, axis=0)              # row u-1 = sum_{t<=u} (t-1) vbar_t
     rows = np.zeros((N, v.shape[1]))
-    if N >= 3:
-        rows[2] = vbar[0]
-    for s in range(4, N + 1):
-        rows[s - 1] = w[s - 3] / ((s - 2) * (s - 3))
+    for s in range(lag + 1, N + 1):
+        u = s - lag
+        rows[s - 1] = vbar[0] if u == 1 else w[u - 1] / (u * (u - 1))
     return rows
 
 
-def awm_const_key_closed(v, c):
+def awm_const_key_closed(v, c, lag: int = 2):
     """awm_const_key_chunk_rows expanded to every token row."""
     v = np.asarray(v, np.float64)
-    rows = awm_const_key_chunk_rows(v, c)
+    rows = awm_const_key_chunk_rows(v, c, lag)
     out = np.zeros_like(v)
     for s, (a, b) in enumerate(_chunks(v.shape[0], c)):
         out[a:b] = rows[s]

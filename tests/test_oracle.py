@@ -324,3 +324,52 @@ def test_stream_rejects_a_push_after_a_partial_chunk():
     st.push(z[:20], v[:20])
     with pytest.raises(ValueError):
         st.push(z[20:], v[20:])
+
+
+# chunk-wise variant: attention inside the chunk, memory read one chunk earlier
+
+@pytest.mark.parametrize("n,c", SHAPES)
+def test_chunkwise_sca_matches_brute_force(n, c):
+    z, v, a = rand_head(n, 8, 5, seed=n * 13 + c, key_scale=3.0)
+    got = oracle.sca_head(z, v, a["kappa_q"], a["nu_q"], a["kappa_k"], a["nu_k"], c, sliding=False)
+    q = z * a["kappa_q"] + a["nu_q"]
+    k = z * a["kappa_k"] + a["nu_k"]
+    np.testing.assert_allclose(got, pins.brute_sca(q, k, v, c, prev=0), rtol=1e-12, atol=1e-12)
+    zero = np.zeros(8)
+    got = oracle.sca_head(z, v, zero, zero, a["kappa_k"], a["nu_k"], c, sliding=False)
+    np.testing.assert_allclose(got, pins.window_mean(v, c, prev=0), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,c,d,dv", AWM_SHAPES)
+def test_chunkwise_awm_matches_unrolled_and_no_delta_closed_form(n, c, d, dv):
+    z, v, a = rand_head(n, d, dv, seed=n * 5 + c * 7 + d, key_scale=2.0)
+    qm = z * a["eta_q"] + a["rho_q"]
+    km = z * a["eta_k"] + a["rho_k"]
+    got = oracle.awm_head(z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c, lag=1)
+    np.testing.assert_allclose(got, pins.awm_unrolled(qm, km, v, c, lag=1), rtol=1e-11, atol=1e-12)
+    got = oracle.awm_head(z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c, no_delta=True, lag=1)
+    np.testing.assert_allclose(got, pins.awm_no_delta_closed(qm, km, v, c, lag=1), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,c", [(10, 1), (64, 8), (70, 8), (33, 5)])
+def test_chunkwise_awm_constant_keys_closed_form(n, c):
+    d, dv = 5, 4
+    z, v, a = rand_head(n, d, dv, seed=n * c + 1)
+    zero = np.zeros(d)
+    got = oracle.awm_head(z, v, a["eta_q"], a["rho_q"], zero, a["rho_k"], c, lag=1)
+    np.testing.assert_allclose(got, pins.awm_const_key_closed(v, c, lag=1), rtol=1e-11, atol=1e-12)
+    # the first chunk reads nothing, the second reads the first chunk's mean
+    assert np.all(got[:c] == 0.0)
+    np.testing.assert_allclose(got[c:2 * c], np.broadcast_to(v[:c].mean(axis=0), got[c:2 * c].shape), rtol=1e-12)
+
+
+def test_chunkwise_is_the_sliding_memory_one_chunk_earlier():
+    # reading one chunk earlier: the variant's chunk s equals the sliding
+    # form's chunk s + 1 readout when both use the same state (same queries)
+    n, c, d, dv = 60, 6, 4, 3
+    z, v, a = rand_head(n, d, dv, seed=21, key_scale=2.0)
+    tr1, tr2 = [], []
+    oracle.awm_head(z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c, lag=1, trace=tr1)
+    oracle.awm_head(z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c, lag=2, trace=tr2)
+    for s in range(1, len(tr1)):
+        np.testing.assert_array_equal(tr1[s - 1]["mem_read"], tr2[s]["mem_read"])
