@@ -129,16 +129,19 @@ struct Call {
   void* state; size_t state_bytes;
 };
 
-// memory steps and snapshot slots of a call (see gecko::Problem)
-void mem_counts(int64_t N, bool stream, bool has_prev, int64_t& nmem, int64_t& nsnap) {
+// memory steps and snapshot slots of a call (see gecko::Problem); lag 2 with
+// sliding chunks, 1 for the chunk-wise variant (one call only)
+void mem_counts(int64_t N, bool stream, bool has_prev, int64_t lag, int64_t& nmem, int64_t& nsnap) {
   if (stream) {
     nmem = (has_prev ? 1 : 0) + N - 1;
     nsnap = nmem + (has_prev ? 1 : 0);
   } else {
-    nmem = N > 2 ? N - 2 : 0;
+    nmem = N > lag ? N - lag : 0;
     nsnap = nmem;
   }
 }
+
+int64_t lag_of(unsigned flags) { return (flags & GECKO_CHUNKWISE) ? 1 : 2; }
 
 gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   if (k.B < 1 || k.H < 1 || k.n < 1 || k.c < 1)
@@ -147,7 +150,10 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   if (k.d < 1 || k.dv < 1) return fail(GECKO_EINVAL, "d and dv must be >= 1");
   if (k.in_dtype != GECKO_F32 && k.in_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown input dtype %d", (int)k.in_dtype);
   if (k.out_dtype != GECKO_F32 && k.out_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown output dtype %d", (int)k.out_dtype);
-  if (k.flags & ~(unsigned)GECKO_AWM_NO_DELTA) return fail(GECKO_EINVAL, "unknown flag bits 0x%x", k.flags);
+  if (k.flags & ~(unsigned)(GECKO_AWM_NO_DELTA | GECKO_CHUNKWISE))
+    return fail(GECKO_EINVAL, "unknown flag bits 0x%x", k.flags);
+  if (k.streaming && (k.flags & GECKO_CHUNKWISE))
+    return fail(GECKO_EUNSUPPORTED, "the streaming forward is built for sliding chunks only");
   if (!k.z || !k.v || !k.out) return fail(GECKO_EINVAL, "z, v and out must be non-null");
   if (!aligned16(k.z) || !aligned16(k.v) || !aligned16(k.out))
     return fail(GECKO_EINVAL, "z, v and out must be 16-byte aligned");
@@ -170,7 +176,8 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   const int64_t N = nchunks_of(k.n, k.c);
   const bool has_prev = k.streaming && k.pos > 0;
   int64_t nmem = 0, nsnap = 0;
-  mem_counts(N, k.streaming, has_prev, nmem, nsnap);
+  const int64_t lag = lag_of(k.flags);
+  mem_counts(N, k.streaming, has_prev, lag, nmem, nsnap);
   if (k.streaming) {
     if (!bf16) return fail(GECKO_EUNSUPPORTED, "the streaming forward is built for bf16 inputs only");
     if (k.c % 64) return fail(GECKO_EUNSUPPORTED, "the streaming forward needs c to be a multiple of 64");
@@ -222,8 +229,10 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   p.nchunks = N; p.nmem = nmem; p.nsnap = nsnap; p.flags = k.flags;
   {
     const int64_t before = k.streaming ? k.pos / k.c : 0;  // chunks of the sequence before this call
-    p.first_read = before >= 2 ? 0 : 2 - before;
+    p.first_read = before >= lag ? 0 : lag - before;
   }
+  p.lag = lag;
+  p.prev = (k.flags & GECKO_CHUNKWISE) ? 0 : 1;
   p.out_f32 = k.out_dtype == GECKO_F32;
   p.stream = k.streaming;
   p.has_prev = has_prev;
@@ -301,8 +310,16 @@ extern "C" {
 size_t gecko_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
   if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv)) return (size_t)-1;
   if (in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) return (size_t)-1;
+  return gecko_workspace_size_for(B, H, n, d, dv, c, in_dtype, 0u);
+}
+
+size_t gecko_workspace_size_for(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                gecko_dtype in_dtype, unsigned flags) {
+  if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv)) return (size_t)-1;
+  if (in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) return (size_t)-1;
+  if (flags & ~(unsigned)(GECKO_AWM_NO_DELTA | GECKO_CHUNKWISE)) return (size_t)-1;
   int64_t nmem = 0, nsnap = 0;
-  mem_counts(nchunks_of(n, c), false, false, nmem, nsnap);
+  mem_counts(nchunks_of(n, c), false, false, lag_of(flags), nmem, nsnap);
   return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, in_dtype == GECKO_BF16, false).bytes;
 }
 
@@ -364,7 +381,7 @@ size_t gecko_stream_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, i
                                    gecko_dtype in_dtype) {
   if (B < 1 || H < 1 || n < 1 || c < 1 || !valid_d(d) || !valid_dv(dv) || in_dtype != GECKO_BF16) return (size_t)-1;
   int64_t nmem = 0, nsnap = 0;
-  mem_counts(nchunks_of(n, c), true, true, nmem, nsnap);  // the larger case: a carried chunk
+  mem_counts(nchunks_of(n, c), true, true, 2, nmem, nsnap);  // the larger case: a carried chunk
   return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, true, true).bytes;
 }
 

@@ -128,7 +128,7 @@ __global__ void f32_sca_kernel(Problem p, const float* snap, int mode) {
   if (mode & 1) {
     double q[128];
     for (int f = 0; f < d; ++f) q[f] = (double)p.kappa_q[h * d + f] * z[i * d + f] + p.nu_q[h * d + f];
-    const int64_t kbeg = s > 0 ? (s - 1) * p.c : 0;
+    const int64_t kbeg = (p.prev && s > 0) ? (s - 1) * p.c : s * p.c;  // previous chunk, if sliding
     double m = -__builtin_inf(), l = 0.0;
     for (int64_t j = kbeg; j <= i; ++j) {
       double logit = 0.0;
@@ -142,7 +142,7 @@ __global__ void f32_sca_kernel(Problem p, const float* snap, int mode) {
     }
     for (int k = 0; k < 32; ++k) acc[k] /= l;
   }
-  if ((mode & 2) && s >= 2) {
+  if ((mode & 2) && s >= p.first_read) {  // the state after chunks <= s - lag
     double qm[128];
     double mx = -__builtin_inf();
     for (int f = 0; f < d; ++f) {
@@ -154,7 +154,7 @@ __global__ void f32_sca_kernel(Problem p, const float* snap, int mode) {
       qm[f] = exp(qm[f] - mx);
       sm += qm[f];
     }
-    const float* sn = snap + (bh * p.nmem + (s - 2)) * (int64_t)dv * d;
+    const float* sn = snap + (bh * p.nmem + (s - p.lag)) * (int64_t)dv * d;
     for (int k = 0; k < 32; ++k) {
       double r = 0.0;
       for (int f = 0; f < d; ++f) r += qm[f] * sn[(int64_t)(x0 + k) * d + f];

@@ -7,8 +7,9 @@
 
 namespace gecko {
 
-// same bit as GECKO_AWM_NO_DELTA in gecko.h
+// same bits as GECKO_AWM_NO_DELTA and GECKO_CHUNKWISE in gecko.h
 constexpr unsigned GECKO_AWM_NO_DELTA_BIT = 1u << 0;
+constexpr unsigned GECKO_CHUNKWISE_BIT = 1u << 1;
 
 // Per-launch description of one forward. All pointers are device pointers.
 struct Problem {
@@ -20,7 +21,7 @@ struct Problem {
   int64_t B, H, n, d, dv, c;
   int64_t nchunks;      // N = ceil(n / c) chunks of this call
   int64_t nmem;         // chunks entered into the memory by this call (scan steps):
-                        //   one call: max(N - 2, 0); streaming: has_prev + N - 1
+                        //   one call: max(N - lag, 0); streaming: has_prev + N - 1
   unsigned flags;
   bool out_f32;         // output dtype (bf16 inputs may write float32 output)
   // Streaming (bf16 only). The memory pass and the scan see a virtual
@@ -30,7 +31,10 @@ struct Problem {
   // of a call with has_prev holds the incoming state (r = -1).
   int64_t nsnap;        // snapshot slots per (b, h): nmem + has_prev
   int64_t first_read;   // first chunk of the call that reads the memory: the
-                        //   sequence's first two chunks read none (2 - chunks before, at least 0)
+                        //   sequence's first lag chunks read none (lag - chunks before, at least 0)
+  int64_t lag;          // chunk s reads the state after chunks <= s - lag (one call: scan output s - lag);
+                        //   2 with sliding chunks, 1 for the chunk-wise variant
+  int64_t prev;         // attention window: 1 = previous chunk + current chunk, 0 = current chunk only
   bool stream;          // keep the memory state after this call (mstate, zfinal)
   bool has_prev;        // tokens were processed before: a carried chunk and an incoming state
   const void* zprev;    // [BH][c][d]  carried chunk (the last chunk of the previous call)

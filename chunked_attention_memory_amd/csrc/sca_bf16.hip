@@ -134,7 +134,9 @@ struct ScaArgs {
   const uint16_t* vprev;   // [bh][c][dv]
   int64_t n;
   int c, nchunks, nsnap, qtiles, nblocks, per_xcd, H, has_prev;
-  int first_read;  // chunks before it read no memory (the sequence's first two chunks)
+  int first_read;  // chunks before it read no memory (the sequence's first lag chunks)
+  int lag;         // chunk s reads the state after chunks <= s - lag (2, or 1 for the chunk-wise variant)
+  int prev;        // 1: the window holds the previous chunk; 0: the current chunk only
 };
 
 // The attention loop of one workgroup. Member functions rather than lambdas:
@@ -207,8 +209,9 @@ struct ScaLoop {
     }
 
     // key window: the previous chunk (rows -c .. -1 are the carried chunk of
-    // a streaming call) and this chunk up to its last query
-    kbeg = (s > 0 || a.has_prev) ? (s - 1) * c : 0;
+    // a streaming call; none in the chunk-wise variant) and this chunk up to
+    // its last query
+    kbeg = (a.prev && (s > 0 || a.has_prev)) ? (s - 1) * c : s * c;
     kend = qend;
     ntiles = (kend - kbeg + kBN - 1) / kBN;
     // last key any query of this wave can see; -1 (every key tile skipped)
@@ -607,10 +610,11 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
     snap_a = S0;
     snap_b = S1;
   }
-  // chunk s reads the state holding the chunks before its previous one:
-  // snapshot slot s - 2 + 2 has_prev (with a carried chunk, slot 0 is the
-  // incoming state); the first two chunks of a sequence read nothing
-  const int rslot = s - 2 + 2 * a.has_prev;
+  // chunk s reads the state holding the chunks before its previous one
+  // (chunk-wise variant: the chunks before it): snapshot slot
+  // s - lag + 2 has_prev (with a carried chunk, slot 0 is the incoming
+  // state); the first lag chunks of a sequence read nothing
+  const int rslot = s - a.lag + 2 * a.has_prev;
   const bool reads = s >= a.first_read;
   const uint16_t* sn = a.snap + ((size_t)bh * a.nsnap + rslot) * (size_t)(D * DV);
   if constexpr (kRead && kEarly) {
@@ -786,6 +790,8 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   a.vprev = static_cast<const uint16_t*>(p.vprev);
   a.has_prev = p.has_prev ? 1 : 0;
   a.first_read = (int)p.first_read;
+  a.lag = (int)p.lag;
+  a.prev = (int)p.prev;
   a.n = p.n;
   // the host validated n * max(d, dv) * 2 < 2^32 and the block count < 2^31;
   // without a carried chunk, a chunk longer than the sequence is the sequence

@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libgecko.so")
 GECKO_OK, GECKO_EINVAL, GECKO_EUNSUPPORTED, GECKO_EWORKSPACE, GECKO_EHIP = range(5)
 GECKO_F32, GECKO_BF16 = 0, 1
 GECKO_AWM_NO_DELTA = 1 << 0
+GECKO_CHUNKWISE = 1 << 1
 
 EXPORTED = (
     "gecko_workspace_size", "gecko_sca_awm_forward", "gecko_sca_forward", "gecko_awm_forward",
     "gecko_timer_create", "gecko_timer_reset", "gecko_timer_read", "gecko_timer_destroy",
     "gecko_sca_awm_forward_timed", "gecko_status_string", "gecko_last_error", "gecko_version",
     "gecko_stream_state_size", "gecko_stream_workspace_size", "gecko_sca_awm_forward_stream",
+    "gecko_workspace_size_for",
 )
 
 
@@ -35,11 +37,19 @@ class GeckoError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m chunked_attention_memory_amd.build`")
+    # torch first: its HIP runtime is then the one libgecko.so binds to (same
+    # soname), so the process has a single HIP runtime and torch's device
+    # memory and stream handles are valid in the library. Loading libgecko.so
+    # first would map a second HIP runtime beside torch's.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     P, F, I64, U, SZ = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
     I = ctypes.c_int
     lib.gecko_workspace_size.restype = SZ
     lib.gecko_workspace_size.argtypes = [I64] * 6 + [I]
+    lib.gecko_workspace_size_for.restype = SZ
+    lib.gecko_workspace_size_for.argtypes = [I64] * 6 + [I, U]
     fwd = [P] + [F] * 8 + [P, P] + [I64] * 6 + [I, I, U, P, SZ, P]
     lib.gecko_sca_awm_forward.restype = I
     lib.gecko_sca_awm_forward.argtypes = fwd
@@ -122,19 +132,19 @@ def gecko_status_string(status: int) -> str:
     return lib.gecko_status_string(status).decode()
 
 
-def gecko_workspace_size(B, H, n, d, dv, c, dtype_code) -> int:
-    r = lib.gecko_workspace_size(B, H, n, d, dv, c, dtype_code)
+def gecko_workspace_size(B, H, n, d, dv, c, dtype_code, flags=0) -> int:
+    r = lib.gecko_workspace_size_for(B, H, n, d, dv, c, dtype_code, flags)
     if r == ctypes.c_size_t(-1).value:
         raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_workspace_size")
     return r
 
 
-def alloc_workspace(z, v, c):
+def alloc_workspace(z, v, c, flags=0):
     """Device workspace (uint8 tensor, 256-byte aligned by torch) for a forward on z, v."""
     import torch
 
     B, H, n, d, dv = _shape(z, v)
-    nbytes = gecko_workspace_size(B, H, n, d, dv, c, _dtype_code(z))
+    nbytes = gecko_workspace_size(B, H, n, d, dv, c, _dtype_code(z), flags)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
 
 
@@ -162,7 +172,7 @@ def gecko_sca_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, wo
     if out is None:
         out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
     if workspace is None:
-        workspace = alloc_workspace(z, v, c)
+        workspace = alloc_workspace(z, v, c, flags)
     dt = _dtype_code(z)
     args = [_ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
             B, H, n, d, dv, c, dt, _dtype_code(out), flags, _ptr(workspace), workspace.numel(), _stream(stream)]
@@ -193,7 +203,7 @@ def gecko_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, worksp
     if out is None:
         out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
     if workspace is None:
-        workspace = alloc_workspace(z, v, c)
+        workspace = alloc_workspace(z, v, c, flags)
     _check(lib.gecko_awm_forward(_ptr(z), *_params(params, M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
                                  B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags,
                                  _ptr(workspace), workspace.numel(), _stream(stream)))

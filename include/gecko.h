@@ -55,7 +55,14 @@ typedef enum { GECKO_F32 = 0, GECKO_BF16 = 1 } gecko_dtype;
 enum {
     /* Test variant: drop the -psi(K_m) M' term of the update, leaving plain
      * linear attention with the online-softmax kernel. Not the method. */
-    GECKO_AWM_NO_DELTA = 1u << 0
+    GECKO_AWM_NO_DELTA = 1u << 0,
+    /* Ablation variant without sliding chunks: the chunk-wise attention
+     * Gecko replaces (paperlayer.ai summary, section 2.3: attention inside
+     * each chunk only, causal) and the memory without sliding chunks
+     * (Appendix A: M_0 = 0, the same update, and chunk s reads the state
+     * holding chunks 1..s-1, i.e. one chunk earlier than with sliding
+     * chunks). Not accepted by the streaming forward. */
+    GECKO_CHUNKWISE = 1u << 1
 };
 
 /*
@@ -76,6 +83,11 @@ enum {
  * memory-state snapshots that the readout uses. */
 size_t gecko_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
                             int64_t c, gecko_dtype in_dtype);
+
+/* The same for a given set of flags (GECKO_CHUNKWISE stores one more chunk
+ * per (batch, head)); gecko_workspace_size is this with flags = 0. */
+size_t gecko_workspace_size_for(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                int64_t c, gecko_dtype in_dtype, unsigned flags);
 
 /* O = O_SCA + O_m (the whole forward). Workspace: gecko_workspace_size()
  * bytes of caller-owned device memory; its contents on entry do not matter

@@ -168,3 +168,34 @@ def test_stream_sizes(g):
     per_step = 8 * (128 * 256 * 4 + 128 * 128 * 2 + 4 * 128 * 4 + 256 * 128 * 2)
     extra = 8 * 128 * 256 * 2 + 8 * 128 * 2 * 4  # one more snapshot slot, the final denominator
     assert one + 2 * per_step + extra <= st <= one + 2 * per_step + extra + 10 * 256
+
+
+def test_chunkwise_flag_host_checks(g):
+    # accepted by validation (fails later on the missing workspace), refused by the streaming entry
+    st, msg = call_full(g, flags=g.GECKO_CHUNKWISE)
+    assert st == g.GECKO_EWORKSPACE
+    st, msg = call_stream(g, flags=g.GECKO_CHUNKWISE)
+    assert st == g.GECKO_EUNSUPPORTED and "sliding" in msg
+    # one more memory chunk per (batch, head) than the sliding form
+    a = g.gecko_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16)
+    b = g.gecko_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_CHUNKWISE)
+    per_step = 8 * (128 * 256 * 4 + 128 * 128 * 2 + 4 * 128 * 4 + 256 * 128 * 2)
+    assert per_step <= b - a <= per_step + 8 * 256
+    # two chunks: the chunk-wise form already stores the first
+    assert g.gecko_workspace_size(1, 1, 100, 128, 256, 50, g.GECKO_BF16) == 0
+    assert g.gecko_workspace_size(1, 1, 100, 128, 256, 50, g.GECKO_BF16, g.GECKO_CHUNKWISE) > 0
+    assert g.lib.gecko_workspace_size_for(1, 1, 100, 128, 256, 50, g.GECKO_BF16, 1 << 7) == ctypes.c_size_t(-1).value
+
+
+def test_one_hip_runtime_per_process(g):
+    """Importing the binding before torch must still leave one HIP runtime
+    mapped (torch's), so torch's memory and streams are valid in the library."""
+    import subprocess
+    import sys
+
+    code = ("import chunked_attention_memory_amd.gecko\nimport torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    mapped = eval(out.stdout.strip().splitlines()[-1])
+    assert len(mapped) == 1, mapped
