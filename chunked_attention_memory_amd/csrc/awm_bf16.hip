@@ -109,7 +109,10 @@ struct ChunkLoop {
   static constexpr int NMF = D / 32;
   const uint16_t* zbh;
   const uint16_t* vbh;
-  char* st;  // stage s: Z' tile at st + s STAGE, V tile after it
+  // stage s: Z' tile at sb[s], V tile after it; psi tile at ps. Separate LDS
+  // variables, so that the compiler sees that the reads of one stage do not
+  // alias the loads filling the other (it would wait for them otherwise).
+  char* sb[2];
   char* ps;
   const float* e2s;  // eta_k * log2(e), in LDS
   const float* r2s;  // rho_k * log2(e), in LDS
@@ -121,7 +124,8 @@ struct ChunkLoop {
   int zb[2], vb[2][NMV], pb[2][NMF];
   int poff[T::FPT / 8];  // psi phase: this thread's 16-byte chunks of its token row
 
-  __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* lds) {
+  __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* s0, char* s1, char* psb,
+                                       float* ek) {
     const int h = (int)(bh % a.H);
     // chunk t of the virtual sequence [carried chunk (streaming)] + this
     // call's chunks; every chunk entered into the memory is full
@@ -143,10 +147,11 @@ struct ChunkLoop {
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     g = lane >> 5;
     lq = lane & 31;
-    st = lds;
-    ps = st + 2 * T::STAGE;
-    float* e2 = reinterpret_cast<float*>(ps + T::ZBYTES);
-    float* r2 = e2 + D;
+    sb[0] = s0;
+    sb[1] = s1;
+    ps = psb;
+    float* e2 = ek;
+    float* r2 = ek + D;
     if (tid < D) {
       e2[tid] = a.eta_k[h * D + tid] * kLog2e;
       r2[tid] = a.rho_k[h * D + tid] * kLog2e;
@@ -204,13 +209,13 @@ struct ChunkLoop {
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 
-  __device__ __forceinline__ const char* zs(int slot) const { return st + slot * T::STAGE; }
-  __device__ __forceinline__ const char* vs(int slot) const { return st + slot * T::STAGE + T::ZBYTES; }
+  __device__ __forceinline__ const char* zs(int slot) const { return sb[slot]; }
+  __device__ __forceinline__ const char* vs(int slot) const { return sb[slot] + T::ZBYTES; }
   __device__ __forceinline__ void stage_z(int it, int slot) const {
-    stage_rows(zbh, cbeg + it * kBT, n, D, st + slot * T::STAGE, T::NW, w, zoff, T::ZLOADS);
+    stage_rows(zbh, cbeg + it * kBT, n, D, sb[slot], T::NW, w, zoff, T::ZLOADS);
   }
   __device__ __forceinline__ void stage_v(int it, int slot) const {
-    stage_rows(vbh, cbeg + it * kBT, n, DV, st + slot * T::STAGE + T::ZBYTES, T::NW, w, voff, T::VLOADS);
+    stage_rows(vbh, cbeg + it * kBT, n, DV, sb[slot] + T::ZBYTES, T::NW, w, voff, T::VLOADS);
   }
 
   // K_m of this lane's feature (log2 units) for tokens 16 ks + 8 g + [0, 8) of the tile in `slot`
@@ -328,10 +333,10 @@ struct ChunkLoop {
       stage_v(it + 1, SLOT ^ 1);
     }
     psi_phase(SLOT);
-    __syncthreads();
+    barrier_lds();  // psi tile written (tile it + 1 keeps loading)
     mfma_phase(it, SLOT, msub, lsum, accg, acch);
     wait_vmem();
-    __syncthreads();
+    barrier_lds();  // tile it + 1 in LDS for every wave; tile it's reads done
   }
 
   __device__ __forceinline__ float pass(float msub, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF]) const {
@@ -349,11 +354,14 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
   using T = ChunkTile<D, DV>;
   constexpr int NMV = DV / 32;
   constexpr int NMF = D / 32;
-  extern __shared__ __attribute__((aligned(16))) char clds[];
+  __shared__ __attribute__((aligned(16))) char S0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char S1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char PS[T::ZBYTES];
+  __shared__ __attribute__((aligned(16))) float EK[2 * D];  // eta_k, rho_k (log2-scaled)
   const int64_t bh = blockIdx.x / a.nmem;
   const int64_t t = blockIdx.x % a.nmem;
   ChunkLoop<D, DV> L;
-  L.init(a, bh, t, clds);
+  L.init(a, bh, t, S0, S1, PS, EK);
 
   f32x16 accg[NMV], acch[NMF];
 #pragma unroll
@@ -683,18 +691,9 @@ __global__ void stream_finish_kernel(const uint16_t* __restrict__ z, const uint1
 
 template <int D, int DV>
 hipError_t launch_chunk(const ChunkArgs& a, int64_t BH, hipStream_t s) {
-  auto kern = awm_chunk_bf16_kernel<D, DV>;
-  const size_t lds = ChunkTile<D, DV>::LDS_BYTES;
-  if (lds > 65536) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(BH * a.nmem)), dim3(ChunkTile<D, DV>::THREADS), lds, s, a);
+  static_assert(ChunkTile<D, DV>::LDS_BYTES <= 160 * 1024, "LDS per workgroup");  // all static
+  hipLaunchKernelGGL((awm_chunk_bf16_kernel<D, DV>), dim3((unsigned)(BH * a.nmem)), dim3(ChunkTile<D, DV>::THREADS),
+                     0, s, a);
   return hipGetLastError();
 }
 

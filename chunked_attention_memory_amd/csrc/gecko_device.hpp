@@ -22,6 +22,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -92,31 +93,70 @@ __device__ __forceinline__ float other_half_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only:
+// vmcnt in bits 3:0 and 15:14, expcnt (bits 6:4) and lgkmcnt (bits 11:8) at
+// their maxima (no wait).
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// The waits use the builtin, not inline asm: the compiler's own wait
+// insertion then knows the loads are done and adds no wait of its own.
+// The empty asm with a memory clobber keeps memory accesses after the wait.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads, whose release
+// side waits for every outstanding global load of the wave (loads prefetching
+// later tiles included). The caller first makes what the other waves will
+// read complete: its LDS-writing loads with wait_vmem / wait_vmem_leave, its
+// LDS stores with the lgkmcnt wait here. The empty asm statements with a
+// memory clobber keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // wait until at most N vector-memory loads of this wave are in flight (they
 // complete in issue order, so the N most recent ones may still be pending)
 template <int N>
 __device__ __forceinline__ void wait_vmem_leave() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+  asm volatile("" ::: "memory");
 }
 
 // Copy rows [row0, row0 + rows_in_tile) of a row-major bf16 matrix with `width`
 // columns into LDS with buffer loads that write LDS directly (lane l of a
-// load lands at 16 l bytes past the load's LDS base); rows at or past n read
-// as zero. Load i of wave w fills the 1 KiB piece nwaves i + w of the tile;
-// off[i] is the byte offset, within the rows starting at row0, that this lane
-// fetches for load i. A plain __device__ function on purpose: the buffer
-// resource type may not appear in a lambda inside a kernel, which is also
-// compiled for the host.
+// load lands at 16 l bytes past the load's LDS base, held in M0); rows at or
+// past n read as zero (the buffer's size ends at row n). Load i of wave w
+// fills the 1 KiB piece nwaves i + w of the tile; off[i] is the byte offset,
+// within the rows starting at row0, that this lane fetches for load i.
+//
+// The loads are issued from inline asm so that the compiler does not track
+// them: it cannot tell which LDS variable they write and would otherwise wait
+// for all of them before LDS reads of other stages. Every caller waits for
+// them itself (wait_vmem / wait_vmem_leave, then a barrier) before any wave
+// reads what they wrote. They have no destination register; M0 is set by the
+// compiler through the input constraint, and the s_nop covers the M0 -> LDS
+// load hazard. A plain __device__ function on purpose: kernels' lambdas are
+// also compiled for the host.
 __device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile,
                                            int nwaves, int w, const uint32_t* off, int nloads) {
   const uint32_t rows = (uint32_t)(n > row0 ? n - row0 : 0);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + (size_t)row0 * width), (short)0, (int)(rows * (uint32_t)width * 2u), 0x00020000);
+  const uint64_t addr = (uint64_t)(uintptr_t)(base + (size_t)row0 * width);
+  i32x4 rs;  // buffer resource: base address, stride 0, size in bytes, raw-buffer flags
+  rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+  rs[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xFFFFu));
+  rs[2] = __builtin_amdgcn_readfirstlane((int)(rows * (uint32_t)width * 2u));
+  rs[3] = 0x00020000;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_tile;
 #pragma unroll
-  for (int i = 0; i < nloads; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + (nwaves * i + w) * 1024), 16, off[i], 0, 0, 0);
+  for (int i = 0; i < nloads; ++i) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((nwaves * i + w) * 1024));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rs), "{m0}"(m0)
+                 : "memory");
+  }
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16): in each 16-lane group,

@@ -403,7 +403,7 @@ struct ScaLoop {
       wait_vmem_leave<T::LOADS>();
     else
       wait_vmem();
-    __syncthreads();
+    barrier_lds();  // tile k + 1 is in LDS for every wave; tile k + 2 may still be loading
   }
 
   // full pass with fixed softmax offsets; returns the row exp-sums
@@ -417,7 +417,7 @@ struct ScaLoop {
     } else {
       wait_vmem();
     }
-    __syncthreads();
+    barrier_lds();
     float lrun[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrun[qb] = 0.f;
