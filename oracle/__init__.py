@@ -16,3 +16,4 @@ from .gecko_oracle import (  # noqa: F401
     sca_chunk,
     sca_head,
 )
+from .cema_oracle import cema, cema_multiplier  # noqa: F401
