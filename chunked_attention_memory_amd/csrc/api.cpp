@@ -372,6 +372,59 @@ gecko_status gecko_awm_forward(const void* z, const float* eta_q, const float* r
   }
 }
 
+size_t gecko_cema_workspace_size(int64_t B, int64_t n, int64_t D, int64_t h) {
+  if (B < 1 || n < 1 || D < 1 || !(h == 1 || h == 2 || h == 4 || h == 8 || h == 16)) return (size_t)-1;
+  return gecko::cema_plan(B, n, D, h).bytes;
+}
+
+gecko_status gecko_cema_forward(const void* x, const float* alpha, const float* delta, const float* theta,
+                                const float* beta, const float* eta, const uint8_t* reset, const float* h0, void* y,
+                                float* h_final, int64_t B, int64_t n, int64_t D, int64_t h, gecko_dtype in_dtype,
+                                gecko_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (B < 1 || n < 1 || D < 1) return fail(GECKO_EINVAL, "sizes must be >= 1");
+    if (!(h == 1 || h == 2 || h == 4 || h == 8 || h == 16))
+      return fail(GECKO_EUNSUPPORTED, "hidden dimensions per input dimension must be 1, 2, 4, 8 or 16 (got %lld)",
+                  (long long)h);
+    if ((in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) || (out_dtype != GECKO_F32 && out_dtype != GECKO_BF16))
+      return fail(GECKO_EINVAL, "unknown dtype");
+    if (!x || !y || !alpha || !delta || !theta || !beta || !eta)
+      return fail(GECKO_EINVAL, "x, y and the parameter vectors must be non-null");
+    const void* ptrs[] = {x, y, alpha, delta, theta, beta, eta, h0, h_final};
+    for (const void* q : ptrs)
+      if (reinterpret_cast<uintptr_t>(q) & 3u) return fail(GECKO_EINVAL, "pointers must be 4-byte aligned");
+    if (B > 65535 || n > (int64_t(1) << 40) || D > (1 << 24)) return fail(GECKO_EINVAL, "sizes out of range");
+    const size_t ib = in_dtype == GECKO_BF16 ? 2 : 4, ob = out_dtype == GECKO_BF16 ? 2 : 4;
+    const size_t xb = (size_t)B * n * D * ib, yb = (size_t)B * n * D * ob, sb = (size_t)B * D * h * 8;
+    if (overlaps(y, yb, x, xb)) return fail(GECKO_EINVAL, "y aliases x");
+    if (h_final && (overlaps(h_final, sb, y, yb) || overlaps(h_final, sb, x, xb) || (h0 && overlaps(h_final, sb, h0, sb))))
+      return fail(GECKO_EINVAL, "h_final aliases another buffer");
+    const gecko::CemaPlan plan = gecko::cema_plan(B, n, D, h);
+    if (B * plan.nwd * plan.C >= ((int64_t)1 << 31)) return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
+    if (plan.bytes > 0) {
+      if (!workspace) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", plan.bytes);
+      if (workspace_bytes < plan.bytes)
+        return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, plan.bytes);
+      if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
+      if (overlaps(workspace, plan.bytes, y, yb) || (h_final && overlaps(workspace, plan.bytes, h_final, sb)))
+        return fail(GECKO_EINVAL, "workspace aliases an output");
+    }
+    gecko::CemaProblem q;
+    q.x = x; q.y = y; q.alpha = alpha; q.delta = delta; q.theta = theta; q.beta = beta; q.eta = eta;
+    q.reset = reset; q.h0 = h0; q.hfin = h_final;
+    q.B = B; q.n = n; q.D = D; q.H = h;
+    q.in_bf16 = in_dtype == GECKO_BF16;
+    q.out_bf16 = out_dtype == GECKO_BF16;
+    const hipError_t e = gecko::launch_cema(q, plan, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "CEMA kernel launch");
+    g_last_error.clear();
+    return GECKO_OK;
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
 size_t gecko_stream_state_size(int64_t B, int64_t H, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
   if (B < 1 || H < 1 || c < 1 || !valid_d(d) || !valid_dv(dv) || in_dtype != GECKO_BF16) return (size_t)-1;
   return gecko::carve_state(nullptr, B * H, d, dv, c).bytes;

@@ -83,4 +83,27 @@ hipError_t launch_stream_finish(const Problem& p, const Workspace& w, void* zcar
 
 bool bf16_shape_built(int64_t d, int64_t dv);
 
+// CEMA (cema.hip). All pointers are device pointers.
+struct CemaProblem {
+  const void* x;        // [B][n][D], bf16 or float32
+  void* y;              // [B][n][D], bf16 or float32
+  const float* alpha; const float* delta; const float* theta; const float* beta;  // [D][H]
+  const float* eta;     // [D][H][2]
+  const uint8_t* reset; // [B][n] or null
+  const float* h0;      // [B][D][H][2] or null
+  float* hfin;          // [B][D][H][2] or null
+  int64_t B, n, D, H;
+  bool in_bf16, out_bf16;
+};
+
+// Chunking of the sequence and the workspace it needs: chunk end states and
+// entering states ([B][C][H][D] float2 each) and per-chunk reset flags.
+struct CemaPlan {
+  int64_t C, L, nwd;
+  size_t off_hin, off_flag, bytes;
+};
+
+CemaPlan cema_plan(int64_t B, int64_t n, int64_t D, int64_t H);
+hipError_t launch_cema(const CemaProblem& q, const CemaPlan& plan, void* ws, hipStream_t s);
+
 }  // namespace gecko

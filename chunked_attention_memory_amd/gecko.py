@@ -24,7 +24,7 @@ EXPORTED = (
     "gecko_timer_create", "gecko_timer_reset", "gecko_timer_read", "gecko_timer_destroy",
     "gecko_sca_awm_forward_timed", "gecko_status_string", "gecko_last_error", "gecko_version",
     "gecko_stream_state_size", "gecko_stream_workspace_size", "gecko_sca_awm_forward_stream",
-    "gecko_workspace_size_for",
+    "gecko_workspace_size_for", "gecko_cema_workspace_size", "gecko_cema_forward",
 )
 
 
@@ -73,6 +73,10 @@ def _load() -> ctypes.CDLL:
     lib.gecko_last_error.argtypes = []
     lib.gecko_version.restype = I
     lib.gecko_version.argtypes = []
+    lib.gecko_cema_workspace_size.restype = SZ
+    lib.gecko_cema_workspace_size.argtypes = [I64] * 4
+    lib.gecko_cema_forward.restype = I
+    lib.gecko_cema_forward.argtypes = [P] + [F] * 5 + [P, P, P, P] + [I64] * 4 + [I, I, P, SZ, P]
     lib.gecko_stream_state_size.restype = SZ
     lib.gecko_stream_state_size.argtypes = [I64] * 5 + [I]
     lib.gecko_stream_workspace_size.restype = SZ
@@ -242,6 +246,52 @@ def gecko_sca_awm_forward_stream(z, params, v, c, pos, state, out=None, out_dtyp
         B, H, n, d, dv, c, pos, dt, _dtype_code(out), flags, _ptr(state), state.numel(),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+CEMA_NAMES = ("alpha", "delta", "theta", "beta")
+
+
+def gecko_cema_workspace_size(B, n, D, h) -> int:
+    r = lib.gecko_cema_workspace_size(B, n, D, h)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_cema_workspace_size")
+    return r
+
+
+def gecko_cema_forward(x, params, reset=None, h0=None, out=None, out_dtype=None, want_state=False,
+                       workspace=None, stream=None):
+    """y = CEMA(x) for x [B, n, D]. ``params``: alpha, delta, theta, beta float32 [D, h] and
+    eta float32 [D, h, 2] (re, im). ``reset``: uint8 [B, n] or None; ``h0``: float32
+    [B, D, h, 2] or None. Returns y, or (y, h_final) with ``want_state``."""
+    import torch
+
+    if x.dim() != 3 or not x.is_cuda or not x.is_contiguous():
+        raise GeckoError(GECKO_EINVAL, "x must be a contiguous [B, n, D] device tensor")
+    B, n, D = x.shape
+    h = params["alpha"].shape[-1]
+    for k in CEMA_NAMES + ("eta",):
+        t = params[k]
+        shape = (D, h, 2) if k == "eta" else (D, h)
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or t.device != x.device:
+            raise GeckoError(GECKO_EINVAL, f"CEMA parameter {k} must be a contiguous float32 {shape} device tensor")
+    if out is None:
+        out = torch.empty((B, n, D), dtype=out_dtype or x.dtype, device=x.device)
+    hfin = torch.empty((B, D, h, 2), dtype=torch.float32, device=x.device) if want_state else None
+    for t, name in ((reset, "reset"), (h0, "h0")):
+        if t is not None and (not t.is_contiguous() or t.device != x.device):
+            raise GeckoError(GECKO_EINVAL, f"{name} must be a contiguous device tensor")
+    if reset is not None and (reset.dtype != torch.uint8 or tuple(reset.shape) != (B, n)):
+        raise GeckoError(GECKO_EINVAL, "reset must be uint8 [B, n]")
+    if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (B, D, h, 2)):
+        raise GeckoError(GECKO_EINVAL, "h0 must be float32 [B, D, h, 2]")
+    if workspace is None:
+        nbytes = gecko_cema_workspace_size(B, n, D, h)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.gecko_cema_forward(
+        _ptr(x), *[_ptr(params[k]) for k in CEMA_NAMES], _ptr(params["eta"]), _ptr(reset), _ptr(h0), _ptr(out),
+        _ptr(hfin), B, n, D, h, _dtype_code(x), _dtype_code(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return (out, hfin) if want_state else out
 
 
 class Stream:

@@ -102,3 +102,29 @@ def make_inputs_device(B: int, H: int, n: int, d: int, dv: int, dtype: str, seed
                 v[b, h, a:e] = (g * torch.sigmoid(g)).to(tdt)
     params = make_params(H, d, seed, tag)
     return {"z": z, "v": v, "params": params, "dtype": dtype}
+
+
+# ---------------------------------------------------------------- CEMA
+_CX, _CP, _CR = 10, 11, 12
+
+
+def make_cema_inputs(B: int, n: int, D: int, h: int, dtype: str, seed: int = 0, tag: int = 0,
+                     reset_rate: float = 0.0) -> dict:
+    """Seeded inputs for CEMA: x [B, n, D] iid N(0, 1) rounded to the run dtype;
+    per (dimension, hidden dimension) float32 parameters alpha ~ U(0.05, 0.5),
+    delta ~ U(0.1, 1) (so the damping factor stays at most 0.995), theta ~
+    U(-pi, pi), beta ~ N(0, 1), eta = N(0, 1) + i N(0, 1) as [D, h, 2]; reset
+    [B, n] uint8, each token a document boundary with probability reset_rate."""
+    x = np.empty((B, n, D), np.float32)
+    for b in range(B):
+        x[b] = _round(_rng(seed, tag, _CX, b, 0).standard_normal((n, D)), dtype)
+    rng = _rng(seed, tag, _CP, 0, 0)
+    params = {
+        "alpha": rng.uniform(0.05, 0.5, (D, h)).astype(np.float32),
+        "delta": rng.uniform(0.1, 1.0, (D, h)).astype(np.float32),
+        "theta": rng.uniform(-np.pi, np.pi, (D, h)).astype(np.float32),
+        "beta": rng.standard_normal((D, h)).astype(np.float32),
+        "eta": rng.standard_normal((D, h, 2)).astype(np.float32),
+    }
+    reset = (_rng(seed, tag, _CR, 0, 0).random((B, n)) < reset_rate).astype(np.uint8)
+    return {"x": x, "params": params, "reset": reset, "dtype": dtype}

@@ -157,6 +157,38 @@ gecko_status gecko_sca_awm_forward_stream(
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
     void* state, size_t state_bytes, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * CEMA: the complex multi-dimensional damped EMA that produces X' = CEMA(X)
+ * ahead of Z' (Gecko summary on paper.rainbus.top, "Prerequisites / EMA" and
+ * "Method steps" (1); paperlayer.ai summary, 2.1 and Appendix B.1). Per input
+ * dimension d and hidden dimension j < h:
+ *
+ *   h_t[d,j] = alpha[d,j] beta[d,j] x_t[d]
+ *              + M_t (1 - alpha[d,j] delta[d,j]) e^{i theta[d,j]} h_{t-1}[d,j]
+ *   y_t[d]   = Re(sum_j eta[d,j] h_t[d,j])
+ *
+ * with M_t = 0 where reset[t] != 0 (a document boundary: h_t restarts from
+ * the input) and h_0 = h0 (zero if h0 is NULL). Readings of what the pages
+ * leave open: the expansion of x into h dimensions is the real scale beta;
+ * the projection back to one output is Re(eta . h) with complex eta.
+ *
+ * Layout: x [B][n][D] (in_dtype), y [B][n][D] (out_dtype), dense row-major;
+ * alpha, delta, theta, beta [D][h] float32; eta [D][h][2] float32 (re, im);
+ * reset [B][n] bytes or NULL; h0 and h_final [B][D][h][2] float32 (re, im),
+ * each may be NULL. h in {1, 2, 4, 8, 16}. Pointers 4-byte aligned, the
+ * workspace 256-byte aligned (gecko_cema_workspace_size bytes; 0 when the
+ * sequence is short enough to run in one piece). h_final receives the state
+ * after the last token, so that a later call with h0 = h_final continues the
+ * sequence. Device pointers, caller-owned; asynchronous on `stream`.
+ */
+size_t gecko_cema_workspace_size(int64_t B, int64_t n, int64_t D, int64_t h);
+gecko_status gecko_cema_forward(
+    const void* x,
+    const float* alpha, const float* delta, const float* theta, const float* beta, const float* eta,
+    const uint8_t* reset, const float* h0, void* y, float* h_final,
+    int64_t B, int64_t n, int64_t D, int64_t h, gecko_dtype in_dtype, gecko_dtype out_dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement helper: HIP events recorded between the kernels of a forward.
  * gecko_timer_create allocates the host object and `capacity` event sets;
  * each gecko_sca_awm_forward_timed call records one set (calls beyond the

@@ -199,3 +199,16 @@ def test_one_hip_runtime_per_process(g):
     assert out.returncode == 0, out.stderr[-2000:]
     mapped = eval(out.stdout.strip().splitlines()[-1])
     assert len(mapped) == 1, mapped
+
+
+def test_cema_host_checks(g):
+    assert g.gecko_cema_workspace_size(1, 100, 64, 16) == 0          # one chunk: no workspace
+    assert g.gecko_cema_workspace_size(1, 131072, 4096, 16) > 0
+    assert g.lib.gecko_cema_workspace_size(1, 100, 64, 3) == ctypes.c_size_t(-1).value
+    aff = [FAKE + 256 * i for i in range(5)]
+    args = lambda **k: [k.get("x", FAKE * 8), *aff, 0, 0, k.get("y", FAKE * 16), 0, 1, k.get("n", 100), 64,
+                        k.get("h", 16), g.GECKO_BF16, g.GECKO_BF16, 0, 0, None]
+    assert g.lib.gecko_cema_forward(*args(h=3)) == g.GECKO_EUNSUPPORTED
+    assert g.lib.gecko_cema_forward(*args(x=0)) == g.GECKO_EINVAL
+    assert g.lib.gecko_cema_forward(*args(y=FAKE * 8 + 64)) == g.GECKO_EINVAL     # y aliases x
+    assert g.lib.gecko_cema_forward(*args(n=131072, y=FAKE * 64)) == g.GECKO_EWORKSPACE  # chunked, no workspace
