@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (published; counts packed FMA)
 METRIC = "SCA+AWM fwd tokens/s at 128K tokens, c=2048; % of bf16 MFMA peak"
 # committed counter summaries: (file, kernel sources it was measured on)
 PMC_SCA = (os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt"), ("sca_bf16.hip", "gecko_device.hpp"))
@@ -142,7 +143,32 @@ def time_variants(gecko, w, z, v, params, out, stream, args) -> dict:
     ms = timed(stream_step)
     res["stream_4_calls"] = {"ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3), "steps": steps,
                              "calls_per_step": 4, "tokens_per_call": q}
+    del parts, outs, ws_st
+    res["cema"] = time_cema(gecko, stream, timed)
     return res
+
+
+def time_cema(gecko, stream, timed) -> dict:
+    """CEMA at a 7B-scale layer: B1, 131072 tokens, D 4096, h 16, bf16 in and
+    out. The kernels are plain FMA arithmetic: 12 h flops per (token, input
+    dimension) for the method's one pass (input scale, complex multiply-add,
+    projection), against the fp32 vector peak."""
+    import torch
+
+    from chunked_attention_memory_amd import inputs
+
+    B, n, D, h = 1, 131072, 4096, 16
+    dev = inputs.make_cema_inputs_device(B, n, D, h, "bf16", seed=0, tag=60)
+    x, p = dev["x"], dev["params"]
+    y = torch.empty_like(x)
+    ws = torch.empty(max(gecko.gecko_cema_workspace_size(B, n, D, h), 256), dtype=torch.uint8, device=x.device)
+    ms = timed(lambda: gecko.gecko_cema_forward(x, p, out=y, workspace=ws, stream=stream))
+    flops = 12.0 * h * B * n * D
+    achieved = flops / (ms / 1e3) / 1e12
+    return {"workload": "cema_bf16_B1_n128k_D4096_h16", "ms_per_step": ms, "tokens_per_s": B * n / (ms / 1e3),
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_FP32_VECTOR_TFLOPS, "traffic": None,
+                         "flops_per_launch": flops, "algorithmic_bytes": 4.0 * B * n * D}}
 
 
 def main(argv=None) -> int:

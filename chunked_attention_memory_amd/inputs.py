@@ -128,3 +128,23 @@ def make_cema_inputs(B: int, n: int, D: int, h: int, dtype: str, seed: int = 0, 
     }
     reset = (_rng(seed, tag, _CR, 0, 0).random((B, n)) < reset_rate).astype(np.uint8)
     return {"x": x, "params": params, "reset": reset, "dtype": dtype}
+
+
+def make_cema_inputs_device(B: int, n: int, D: int, h: int, dtype: str, seed: int = 0, tag: int = 0,
+                            device: str = "cuda") -> dict:
+    """The CEMA recipe with x drawn by torch's device generator (sizes too large
+    to draw on the host quickly); parameters as in make_cema_inputs; no resets."""
+    import torch
+
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed((seed * 1000003 + tag * 10007 + 17) & 0x7FFFFFFF)
+    x = torch.empty((B, n, D), dtype=tdt, device=device)
+    step = 1 << 14
+    for b in range(B):
+        for a in range(0, n, step):
+            e = min(a + step, n)
+            x[b, a:e] = torch.randn((e - a, D), generator=gen, device=device, dtype=torch.float32).to(tdt)
+    host = make_cema_inputs(1, 1, D, h, dtype, seed, tag)
+    params = {k: torch.from_numpy(v).to(device).contiguous() for k, v in host["params"].items()}
+    return {"x": x, "params": params}
