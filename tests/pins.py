@@ -151,3 +151,44 @@ def awm_const_key_closed(v, c, lag: int = 2):
     for s, (a, b) in enumerate(_chunks(v.shape[0], c)):
         out[a:b] = rows[s]
     return out
+
+
+class ConstKeyStream:
+    """Both closed forms of a sequence handed over in segments of whole chunks,
+    with all attention logits equal and all memory keys equal: chunk s
+    (1-based) reads the window mean (pins.window_mean) plus the constant-key
+    state f(s - 2) of awm_const_key_chunk_rows, carried across segments.
+    push(v_segment) yields, chunk by chunk, the rows the segment must hold."""
+
+    def __init__(self, c: int):
+        self.c = c
+        self.prev = None        # the last chunk of v seen (float64)
+        self.u = 0              # chunks seen
+        self.vbar1 = None
+        self.w = {0: 0.0}       # u -> sum_{t<=u} (t-1) vbar_t
+
+    def state(self, u):
+        if u <= 0:
+            return 0.0
+        if u == 1:
+            return self.vbar1
+        return self.w[u] / (u * (u - 1))
+
+    def push(self, v):
+        c = self.c
+        n = v.shape[0]
+        for a in range(0, n, c):
+            cur = np.asarray(v[a:a + c], np.float64)
+            before = self.prev
+            win = cur if before is None else np.vstack([before, cur])
+            off = 0 if before is None else before.shape[0]
+            mean = np.cumsum(win, axis=0)[off:] / np.arange(off + 1, off + cur.shape[0] + 1)[:, None]
+            s = self.u + 1
+            yield mean + self.state(s - 2)
+            vbar = cur.mean(axis=0)
+            if s == 1:
+                self.vbar1 = vbar
+            self.w[s] = self.w[s - 1] + (s - 1) * vbar
+            self.w.pop(s - 3, None)
+            self.prev = cur
+            self.u = s

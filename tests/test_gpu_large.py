@@ -121,3 +121,41 @@ def test_4m_closed_forms_every_row():
         del vh, got
     del out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(1200)
+def test_stream_16m_tokens_in_four_calls_closed_forms_every_row():
+    """One head of 16,777,216 tokens (twice what one call can address) handed
+    to the streaming forward in four calls of 4M, with kappa_q = nu_q = 0 and
+    eta_k = 0: every row is the window mean plus the constant-key memory
+    state (pins.ConstKeyStream carries both closed forms across the calls)."""
+    import torch
+
+    g = gecko()
+    c, d, dv, calls, per = 2048, 128, 256, 4, 4194304
+    ref = pins.ConstKeyStream(c)
+    st = params = None
+    for k in range(calls):
+        dev = inputs.make_inputs_device(1, 1, per, d, dv, "bf16", seed=2, tag=40 + k)
+        if st is None:
+            p = dict(dev["params"])
+            for name in ("kappa_q", "nu_q", "eta_k"):
+                p[name] = np.zeros_like(p[name])
+            params = _device_params(p)
+            st = g.Stream(1, 1, d, dv, c, params)
+        announce(f"stream call {k}: tokens {k * per} .. {(k + 1) * per}")
+        out = st.forward(dev["z"], dev["v"])
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out.float()).all())
+        got = _host(out[0, 0])
+        vh = _host(dev["v"][0, 0])
+        del out, dev
+        worst, ss = 0.0, 0.0
+        for s, want in enumerate(ref.push(vh)):
+            err = np.abs(got[s * c:(s + 1) * c] - want)
+            worst = max(worst, float(err.max()))
+            ss += float((want * want).sum())
+        rms = np.sqrt(ss / (per * dv))
+        assert worst / rms <= BF16_TOL, (k, worst, rms)
+        del got, vh
+    torch.cuda.empty_cache()

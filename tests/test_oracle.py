@@ -373,3 +373,18 @@ def test_chunkwise_is_the_sliding_memory_one_chunk_earlier():
     oracle.awm_head(z, v, a["eta_q"], a["rho_q"], a["eta_k"], a["rho_k"], c, lag=2, trace=tr2)
     for s in range(1, len(tr1)):
         np.testing.assert_array_equal(tr1[s - 1]["mem_read"], tr2[s]["mem_read"])
+
+
+@pytest.mark.parametrize("splits", [[40], [8, 16, 16], [24, 8, 5]])
+def test_const_key_stream_closed_form_matches_one_shot(splits):
+    # the segment-by-segment closed forms (used at 16M tokens on the GPU) equal
+    # the one-shot ones over the whole sequence
+    c = 4
+    v = np.random.default_rng(9).standard_normal((sum(splits), 3))
+    want = pins.window_mean(v, c) + pins.awm_const_key_closed(v, c)
+    ref = pins.ConstKeyStream(c)
+    got, at = [], 0
+    for m in splits:
+        got += list(ref.push(v[at:at + m]))
+        at += m
+    np.testing.assert_allclose(np.concatenate(got), want, rtol=1e-12, atol=1e-13)
