@@ -17,3 +17,4 @@ from .gecko_oracle import (  # noqa: F401
     sca_head,
 )
 from .cema_oracle import cema, cema_multiplier  # noqa: F401
+from .tdn_oracle import tdn  # noqa: F401
