@@ -425,6 +425,58 @@ gecko_status gecko_cema_forward(const void* x, const float* alpha, const float* 
   }
 }
 
+size_t gecko_tdn_workspace_size(int64_t B, int64_t n, int64_t D, int64_t G) {
+  if (B < 1 || n < 1 || D < 1 || G < 1 || D % G || (D / G) % 8 || D > 8192) return (size_t)-1;
+  return gecko::tdn_plan(B, n, G).bytes;
+}
+
+gecko_status gecko_tdn_forward(const void* x, const float* gamma, const float* shift, const float* m0,
+                               const float* v0, int64_t t0, void* y, float* m_out, float* v_out, int64_t B,
+                               int64_t n, int64_t D, int64_t G, float beta1, float beta2, float eps,
+                               gecko_dtype in_dtype, gecko_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  try {
+    if (B < 1 || n < 1 || D < 1 || G < 1 || t0 < 0) return fail(GECKO_EINVAL, "sizes must be >= 1 and t0 >= 0");
+    if (D % G || (D / G) % 8)
+      return fail(GECKO_EUNSUPPORTED, "groups must split D into equal runs of a multiple of 8 features");
+    if (D > 8192) return fail(GECKO_EUNSUPPORTED, "D up to 8192");
+    if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f))
+      return fail(GECKO_EINVAL, "decay factors must lie in [0, 1) and eps must be > 0");
+    if ((in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) || (out_dtype != GECKO_F32 && out_dtype != GECKO_BF16))
+      return fail(GECKO_EINVAL, "unknown dtype");
+    if (!x || !y || !gamma || !shift) return fail(GECKO_EINVAL, "x, y, gamma and shift must be non-null");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(shift))
+      return fail(GECKO_EINVAL, "x, y, gamma and shift must be 16-byte aligned");
+    const void* small[] = {m0, v0, m_out, v_out};
+    for (const void* q : small)
+      if (reinterpret_cast<uintptr_t>(q) & 3u) return fail(GECKO_EINVAL, "state pointers must be 4-byte aligned");
+    if (B * n >= ((int64_t)1 << 31) || B > 65535) return fail(GECKO_EUNSUPPORTED, "B * n must stay below 2^31");
+    const size_t ib = in_dtype == GECKO_BF16 ? 2 : 4, ob = out_dtype == GECKO_BF16 ? 2 : 4;
+    const size_t xb = (size_t)B * n * D * ib, yb = (size_t)B * n * D * ob;
+    if (overlaps(y, yb, x, xb)) return fail(GECKO_EINVAL, "y aliases x");
+    const gecko::TdnPlan plan = gecko::tdn_plan(B, n, G);
+    if (!workspace) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", plan.bytes);
+    if (workspace_bytes < plan.bytes)
+      return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, plan.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+      return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
+    if (overlaps(workspace, plan.bytes, y, yb) || overlaps(workspace, plan.bytes, x, xb))
+      return fail(GECKO_EINVAL, "workspace aliases x or y");
+    gecko::TdnProblem p;
+    p.x = x; p.y = y; p.gamma = gamma; p.shift = shift; p.m0 = m0; p.v0 = v0; p.m_out = m_out; p.v_out = v_out;
+    p.B = B; p.n = n; p.D = D; p.G = G; p.t0 = t0;
+    p.beta1 = beta1; p.beta2 = beta2; p.eps = eps;
+    p.in_bf16 = in_dtype == GECKO_BF16;
+    p.out_bf16 = out_dtype == GECKO_BF16;
+    const hipError_t e = gecko::launch_tdn(p, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "TDN kernel launch");
+    g_last_error.clear();
+    return GECKO_OK;
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
 size_t gecko_stream_state_size(int64_t B, int64_t H, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype) {
   if (B < 1 || H < 1 || c < 1 || !valid_d(d) || !valid_dv(dv) || in_dtype != GECKO_BF16) return (size_t)-1;
   return gecko::carve_state(nullptr, B * H, d, dv, c).bytes;

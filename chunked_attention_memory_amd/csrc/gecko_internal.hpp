@@ -104,6 +104,26 @@ struct CemaPlan {
 };
 
 CemaPlan cema_plan(int64_t B, int64_t n, int64_t D, int64_t H);
+
+// Timestep decay normalisation (tdn.hip).
+struct TdnProblem {
+  const void* x;        // [B][n][D]
+  void* y;              // [B][n][D]
+  const float* gamma; const float* shift;  // [D]
+  const float* m0; const float* v0;        // [B][G] or null (zero)
+  float* m_out; float* v_out;              // [B][G] or null
+  int64_t B, n, D, G, t0;                  // t0: tokens of the sequence before this call
+  float beta1, beta2, eps;
+  bool in_bf16, out_bf16;
+};
+// workspace: per-token group statistics [B][n][G] float2, then the chunk
+// carries [B][NC][G] float2
+struct TdnPlan {
+  int64_t NC, L;
+  size_t off_carry, bytes;
+};
+TdnPlan tdn_plan(int64_t B, int64_t n, int64_t G);
+hipError_t launch_tdn(const TdnProblem& p, void* ws, hipStream_t s);
 hipError_t launch_cema(const CemaProblem& q, const CemaPlan& plan, void* ws, hipStream_t s);
 
 }  // namespace gecko

@@ -25,6 +25,7 @@ EXPORTED = (
     "gecko_sca_awm_forward_timed", "gecko_status_string", "gecko_last_error", "gecko_version",
     "gecko_stream_state_size", "gecko_stream_workspace_size", "gecko_sca_awm_forward_stream",
     "gecko_workspace_size_for", "gecko_cema_workspace_size", "gecko_cema_forward",
+    "gecko_tdn_workspace_size", "gecko_tdn_forward",
 )
 
 
@@ -77,6 +78,11 @@ def _load() -> ctypes.CDLL:
     lib.gecko_cema_workspace_size.argtypes = [I64] * 4
     lib.gecko_cema_forward.restype = I
     lib.gecko_cema_forward.argtypes = [P] + [F] * 5 + [P, P, P, P] + [I64] * 4 + [I, I, P, SZ, P]
+    lib.gecko_tdn_workspace_size.restype = SZ
+    lib.gecko_tdn_workspace_size.argtypes = [I64] * 4
+    lib.gecko_tdn_forward.restype = I
+    lib.gecko_tdn_forward.argtypes = ([P, F, F, F, F, I64, P, F, F] + [I64] * 4
+                                      + [ctypes.c_float] * 3 + [I, I, P, SZ, P])
     lib.gecko_stream_state_size.restype = SZ
     lib.gecko_stream_state_size.argtypes = [I64] * 5 + [I]
     lib.gecko_stream_workspace_size.restype = SZ
@@ -292,6 +298,43 @@ def gecko_cema_forward(x, params, reset=None, h0=None, out=None, out_dtype=None,
         _ptr(hfin), B, n, D, h, _dtype_code(x), _dtype_code(out), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return (out, hfin) if want_state else out
+
+
+def gecko_tdn_workspace_size(B, n, D, G) -> int:
+    r = lib.gecko_tdn_workspace_size(B, n, D, G)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid sizes for gecko_tdn_workspace_size")
+    return r
+
+
+def gecko_tdn_forward(x, gamma, shift, G, beta1, beta2, eps=1e-5, state=None, out=None, out_dtype=None,
+                      want_state=False, workspace=None, stream=None):
+    """Timestep decay normalisation of x [B, n, D] in G groups. ``state`` is
+    (m, v, t0) from an earlier call of the same sequence (m, v float32 [B, G]).
+    Returns y, or (y, (m, v, t)) with ``want_state``."""
+    import torch
+
+    if x.dim() != 3 or not x.is_cuda or not x.is_contiguous():
+        raise GeckoError(GECKO_EINVAL, "x must be a contiguous [B, n, D] device tensor")
+    B, n, D = x.shape
+    for t, name in ((gamma, "gamma"), (shift, "shift")):
+        if t.dtype != torch.float32 or t.numel() != D or not t.is_contiguous() or t.device != x.device:
+            raise GeckoError(GECKO_EINVAL, f"{name} must be a contiguous float32 [D] device tensor")
+    m0 = v0 = None
+    t0 = 0
+    if state is not None:
+        m0, v0, t0 = state
+    if out is None:
+        out = torch.empty((B, n, D), dtype=out_dtype or x.dtype, device=x.device)
+    m_out = torch.empty((B, G), dtype=torch.float32, device=x.device) if want_state else None
+    v_out = torch.empty((B, G), dtype=torch.float32, device=x.device) if want_state else None
+    if workspace is None:
+        workspace = torch.empty(max(gecko_tdn_workspace_size(B, n, D, G), 256), dtype=torch.uint8, device=x.device)
+    _check(lib.gecko_tdn_forward(_ptr(x), _ptr(gamma), _ptr(shift), _ptr(m0), _ptr(v0), int(t0), _ptr(out),
+                                 _ptr(m_out), _ptr(v_out), B, n, D, G, float(beta1), float(beta2), float(eps),
+                                 _dtype_code(x), _dtype_code(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return (out, (m_out, v_out, t0 + n)) if want_state else out
 
 
 class Stream:

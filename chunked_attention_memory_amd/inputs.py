@@ -148,3 +148,26 @@ def make_cema_inputs_device(B: int, n: int, D: int, h: int, dtype: str, seed: in
     host = make_cema_inputs(1, 1, D, h, dtype, seed, tag)
     params = {k: torch.from_numpy(v).to(device).contiguous() for k, v in host["params"].items()}
     return {"x": x, "params": params}
+
+
+# ---------------------------------------------------------------- TDN
+_TX, _TP = 20, 21
+
+
+def make_tdn_inputs(B: int, n: int, D: int, dtype: str, seed: int = 0, tag: int = 0) -> dict:
+    """Seeded inputs for timestep decay normalisation: x [B, n, D] =
+    s_t N(0, 1) + o_t + f_d, with a per-token scale s_t and offset o_t that
+    drift over the sequence (random walks, so the decayed statistics matter)
+    and a fixed per-feature offset f_d, rounded to the run dtype; gamma
+    ~ N(1, 0.1), shift ~ N(0, 0.1) per feature, float32."""
+    x = np.empty((B, n, D), np.float32)
+    for b in range(B):
+        rng = _rng(seed, tag, _TX, b, 0)
+        walk = np.cumsum(rng.standard_normal((n, 2)) * 0.05, axis=0)
+        scale = np.exp(0.5 * np.tanh(walk[:, :1]))
+        offset = 2.0 * np.tanh(walk[:, 1:])
+        feat = rng.standard_normal((1, D)) * 0.5
+        x[b] = _round(rng.standard_normal((n, D)) * scale + offset + feat, dtype)
+    rng = _rng(seed, tag, _TP, 0, 0)
+    return {"x": x, "gamma": (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32),
+            "shift": (0.1 * rng.standard_normal(D)).astype(np.float32), "dtype": dtype}

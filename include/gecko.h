@@ -189,6 +189,37 @@ gecko_status gecko_cema_forward(
     int64_t B, int64_t n, int64_t D, int64_t h, gecko_dtype in_dtype, gecko_dtype out_dtype,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Timestep decay normalisation (TDN), the normalisation Gecko uses in place
+ * of Megalodon's timestep normalisation (Gecko summary on paper.rainbus.top,
+ * "Novelty"; paperlayer.ai summary, 2.2 and 3.1). For each of G equal groups
+ * of the D features of token t (t counted from 1 over the whole sequence):
+ *
+ *   mu_t, s2_t = mean and variance of the group's values at token t
+ *   m_t = beta1 m_{t-1} + (1 - beta1) mu_t,  v_t = beta2 v_{t-1} + (1 - beta2) s2_t
+ *   y_t = gamma * (x_t - m_t / (1 - beta1^t)) / sqrt(v_t / (1 - beta2^t) + eps) + shift
+ *
+ * with m_0 = v_0 = 0 unless a call continues a sequence: then m0, v0 are the
+ * sums after the previous call (m_out, v_out of that call) and t0 the tokens
+ * before this call. Readings of what the pages leave open: the statistics are
+ * the current token's group mean and variance; the decayed sums start at 0
+ * and are bias-corrected as in Adam; the output is normalised per group and
+ * scaled and shifted per feature.
+ *
+ * Layout: x, y [B][n][D] (bf16 or float32, 16-byte aligned); gamma, shift [D]
+ * float32 (16-byte aligned); m0, v0, m_out, v_out [B][G] float32 or NULL.
+ * D % G == 0, D / G a multiple of 8, D <= 8192, 0 <= beta < 1, eps > 0.
+ * Workspace: gecko_tdn_workspace_size() bytes, 256-byte aligned (per-token
+ * group statistics). Device pointers, caller-owned; asynchronous on `stream`.
+ */
+size_t gecko_tdn_workspace_size(int64_t B, int64_t n, int64_t D, int64_t G);
+gecko_status gecko_tdn_forward(
+    const void* x, const float* gamma, const float* shift,
+    const float* m0, const float* v0, int64_t t0,
+    void* y, float* m_out, float* v_out,
+    int64_t B, int64_t n, int64_t D, int64_t G, float beta1, float beta2, float eps,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement helper: HIP events recorded between the kernels of a forward.
  * gecko_timer_create allocates the host object and `capacity` event sets;
  * each gecko_sca_awm_forward_timed call records one set (calls beyond the

@@ -212,3 +212,24 @@ def test_cema_host_checks(g):
     assert g.lib.gecko_cema_forward(*args(x=0)) == g.GECKO_EINVAL
     assert g.lib.gecko_cema_forward(*args(y=FAKE * 8 + 64)) == g.GECKO_EINVAL     # y aliases x
     assert g.lib.gecko_cema_forward(*args(n=131072, y=FAKE * 64)) == g.GECKO_EWORKSPACE  # chunked, no workspace
+
+
+def test_tdn_host_checks(g):
+    assert g.gecko_tdn_workspace_size(1, 100, 64, 8) > 0
+    assert g.lib.gecko_tdn_workspace_size(1, 100, 64, 3) == ctypes.c_size_t(-1).value   # uneven groups
+    assert g.lib.gecko_tdn_workspace_size(1, 100, 16384, 64) == ctypes.c_size_t(-1).value
+    F = ctypes.c_float
+    base = dict(x=FAKE * 8, gamma=FAKE, shift=FAKE + 4096, y=FAKE * 16, D=64, G=8, b1=0.9, b2=0.99, eps=1e-5,
+                ws=FAKE * 32, wsb=1 << 30)
+
+    def call(**k):
+        a = dict(base)
+        a.update(k)
+        return g.lib.gecko_tdn_forward(a["x"], a["gamma"], a["shift"], 0, 0, 0, a["y"], 0, 0, 1, 100, a["D"],
+                                       a["G"], F(a["b1"]), F(a["b2"]), F(a["eps"]), g.GECKO_BF16, g.GECKO_BF16,
+                                       a["ws"], a["wsb"], None)
+    assert call(G=3) == g.GECKO_EUNSUPPORTED
+    assert call(b1=1.0) == g.GECKO_EINVAL
+    assert call(eps=0.0) == g.GECKO_EINVAL
+    assert call(x=FAKE * 8 + 2) == g.GECKO_EINVAL
+    assert call(ws=0) == g.GECKO_EWORKSPACE
