@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (published; counts packed FMA)
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E (published)
 METRIC = "SCA+AWM fwd tokens/s at 128K tokens, c=2048; % of bf16 MFMA peak"
 # committed counter summaries: (file, kernel sources it was measured on)
 PMC_SCA = (os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt"), ("sca_bf16.hip", "gecko_device.hpp"))
@@ -145,7 +146,32 @@ def time_variants(gecko, w, z, v, params, out, stream, args) -> dict:
                              "calls_per_step": 4, "tokens_per_call": q}
     del parts, outs, ws_st
     res["cema"] = time_cema(gecko, stream, timed)
+    res["tdn"] = time_tdn(gecko, stream, timed)
     return res
+
+
+def time_tdn(gecko, stream, timed) -> dict:
+    """Timestep decay normalisation at a 7B-scale layer: B1, 131072 tokens,
+    D 4096 in 64 groups, bf16 in and out. HBM-bound: the algorithmic traffic
+    is x read once and y written once (the kernels read x twice: statistics,
+    then the normalisation)."""
+    import torch
+
+    B, n, D, G = 1, 131072, 4096, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(71)
+    x = torch.randn((B, n, D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gamma = torch.ones(D, dtype=torch.float32, device="cuda")
+    shift = torch.zeros(D, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(gecko.gecko_tdn_workspace_size(B, n, D, G), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: gecko.gecko_tdn_forward(x, gamma, shift, G, 0.99, 0.999, out=y, workspace=ws,
+                                               stream=stream))
+    alg = 4.0 * B * n * D
+    achieved = alg / (ms / 1e3) / 1e9
+    return {"workload": "tdn_bf16_B1_n128k_D4096_G64", "ms_per_step": ms, "tokens_per_s": B * n / (ms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "algorithmic_bytes": alg}}
 
 
 def time_cema(gecko, stream, timed) -> dict:

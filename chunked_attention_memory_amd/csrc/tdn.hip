@@ -115,14 +115,14 @@ __global__ __launch_bounds__(kT) void tdn_stats_kernel(const void* x, float2* st
 // replace each token's (mean, variance) by (m_hat, 1 / sqrt(v_hat + eps));
 // the last chunk also writes the final sums.
 template <bool kFinal>
-__global__ __launch_bounds__(kT) void tdn_chunk_kernel(float2* st, float2* carry, const float* m0, const float* v0,
+__global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* st, float2* carry, const float* m0, const float* v0,
                                                        float* m_out, float* v_out, int64_t n, int G, int64_t L,
                                                        int NC, int64_t t0, float b1, float b2, float eps) {
   const int64_t b = blockIdx.x / NC;
   const int c = (int)(blockIdx.x % NC);
   const int64_t ta = (int64_t)c * L, tb = std::min<int64_t>(ta + L, n);
   const float ln1 = logf(b1), ln2 = logf(b2);  // -inf for a zero factor
-  for (int g = threadIdx.x; g < G; g += kT) {
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
     float m = 0.f, v = 0.f;
     if constexpr (kFinal) {
       const float2 e = carry[(b * NC + c) * G + g];
@@ -130,13 +130,32 @@ __global__ __launch_bounds__(kT) void tdn_chunk_kernel(float2* st, float2* carry
       v = e.y;
     }
     float2* s = st + b * n * G + g;
-    for (int64_t t = ta; t < tb; ++t) {
+    // kB tokens per step: their loads are issued together, then the sums run
+    constexpr int kB = 16;
+    int64_t t = ta;
+    for (; t + kB <= tb; t += kB) {
+      float2 x[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) x[k] = s[(t + k) * G];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        m = fmaf(b1, m, (1.f - b1) * x[k].x);
+        v = fmaf(b2, v, (1.f - b2) * x[k].y);
+        if constexpr (kFinal) {
+          const float tt = (float)(t0 + t + k + 1);
+          const float mh = m / -expm1f(tt * ln1);  // 1 - b^t, accurate for b near 1
+          const float vh = v / -expm1f(tt * ln2);
+          s[(t + k) * G] = make_float2(mh, rsqrtf(vh + eps));
+        }
+      }
+    }
+    for (; t < tb; ++t) {
       const float2 x = s[t * G];
       m = fmaf(b1, m, (1.f - b1) * x.x);
       v = fmaf(b2, v, (1.f - b2) * x.y);
       if constexpr (kFinal) {
         const float tt = (float)(t0 + t + 1);
-        const float mh = m / -expm1f(tt * ln1);  // 1 - b^t, accurate for b near 1
+        const float mh = m / -expm1f(tt * ln1);
         const float vh = v / -expm1f(tt * ln2);
         s[t * G] = make_float2(mh, rsqrtf(vh + eps));
       }
@@ -163,40 +182,61 @@ __global__ void tdn_carry_kernel(float2* carry, const float* m0, const float* v0
   const double d1 = b1 > 0.f ? pow((double)b1, (double)L) : 0.0;
   const double d2 = b2 > 0.f ? pow((double)b2, (double)L) : 0.0;
   double m = m0 ? m0[i] : 0.0, v = v0 ? v0[i] : 0.0;
-  for (int c = 0; c < NC; ++c) {
-    float2* e = carry + (b * NC + c) * G + g;
-    if (c == NC - 1) {  // the last chunk's end sums are not needed (nor written)
-      *e = make_float2((float)m, (float)v);
-      break;
+  // the last chunk's end sums are not needed; the others are read 16 at a time
+  constexpr int kB = 16;
+  for (int c0 = 0; c0 < NC; c0 += kB) {
+    float2 end[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (c0 + k < NC - 1) end[k] = carry[(b * NC + c0 + k) * G + g];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      if (c0 + k < NC) {
+        carry[(b * NC + c0 + k) * G + g] = make_float2((float)m, (float)v);
+        if (c0 + k < NC - 1) {
+          m = d1 * m + end[k].x;
+          v = d2 * v + end[k].y;
+        }
+      }
     }
-    const float2 end = *e;
-    *e = make_float2((float)m, (float)v);
-    m = d1 * m + end.x;
-    v = d2 * v + end.y;
   }
 }
 
+constexpr int kRows = 8;  // token rows per apply block (gamma and shift stay in registers)
+
 template <bool kIn, bool kOut, int CPT>
 __global__ __launch_bounds__(kT) void tdn_apply_kernel(const void* x, const float2* nrm, const float* gamma,
-                                                       const float* shift, void* y, int D, int G) {
-  const int64_t row = blockIdx.x;
+                                                       const float* shift, void* y, int64_t rows, int D, int G) {
   const int nch = D / 8, cpg = (D / G) / 8;
+  float gm[CPT][8], sh[CPT][8];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const int c = threadIdx.x + k * kT;
-    if (c < nch) {
-      float v[8];
-      load8<kIn>(x, row * D + 8 * c, v);
-      const float2 q = nrm[row * G + c / cpg];  // (m_hat, 1 / sqrt(v_hat + eps))
-      const f32x4* gp = reinterpret_cast<const f32x4*>(gamma + 8 * c);
-      const f32x4* sp = reinterpret_cast<const f32x4*>(shift + 8 * c);
-      const f32x4 g0 = gp[0], g1 = gp[1], s0 = sp[0], s1 = sp[1];
+    const int c = min((int)threadIdx.x + k * kT, nch - 1);
+    const f32x4* gp = reinterpret_cast<const f32x4*>(gamma + 8 * c);
+    const f32x4* sp = reinterpret_cast<const f32x4*>(shift + 8 * c);
+    const f32x4 g0 = gp[0], g1 = gp[1], s0 = sp[0], s1 = sp[1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = fmaf(g0[j] * q.y, v[j] - q.x, s0[j]);
-        v[4 + j] = fmaf(g1[j] * q.y, v[4 + j] - q.x, s1[j]);
+    for (int j = 0; j < 4; ++j) {
+      gm[k][j] = g0[j];
+      gm[k][4 + j] = g1[j];
+      sh[k][j] = s0[j];
+      sh[k][4 + j] = s1[j];
+    }
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * kRows;
+  const int64_t r1 = min(r0 + kRows, rows);
+  for (int64_t row = r0; row < r1; ++row) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = threadIdx.x + k * kT;
+      if (c < nch) {
+        float v[8];
+        load8<kIn>(x, row * D + 8 * c, v);
+        const float2 q = nrm[row * G + c / cpg];  // (m_hat, 1 / sqrt(v_hat + eps))
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = fmaf(gm[k][j] * q.y, v[j] - q.x, sh[k][j]);
+        store8<kOut>(y, row * D + 8 * c, v);
       }
-      store8<kOut>(y, row * D + 8 * c, v);
     }
   }
 }
@@ -212,8 +252,9 @@ hipError_t launch_cpt(const TdnProblem& p, float2* st, hipStream_t s) {
   const TdnPlan pl = tdn_plan(p.B, p.n, p.G);
   float2* carry = reinterpret_cast<float2*>(reinterpret_cast<char*>(st) + pl.off_carry);
   const unsigned blocks = (unsigned)(p.B * pl.NC);
+  const unsigned cthreads = (unsigned)std::min<int64_t>(256, (p.G + 63) / 64 * 64);  // one thread per group
   if (pl.NC > 1) {
-    hipLaunchKernelGGL((tdn_chunk_kernel<false>), dim3(blocks), dim3(kT), 0, s, st, carry, p.m0, p.v0, p.m_out,
+    hipLaunchKernelGGL((tdn_chunk_kernel<false>), dim3(blocks), dim3(cthreads), 0, s, st, carry, p.m0, p.v0, p.m_out,
                        p.v_out, p.n, (int)p.G, pl.L, (int)pl.NC, p.t0, p.beta1, p.beta2, p.eps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -223,11 +264,11 @@ hipError_t launch_cpt(const TdnProblem& p, float2* st, hipStream_t s) {
                        p.B, (int)p.G, pl.L, (int)pl.NC, p.beta1, p.beta2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((tdn_chunk_kernel<true>), dim3(blocks), dim3(kT), 0, s, st, carry, p.m0, p.v0, p.m_out,
+  hipLaunchKernelGGL((tdn_chunk_kernel<true>), dim3(blocks), dim3(cthreads), 0, s, st, carry, p.m0, p.v0, p.m_out,
                      p.v_out, p.n, (int)p.G, pl.L, (int)pl.NC, p.t0, p.beta1, p.beta2, p.eps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((tdn_apply_kernel<kIn, kOut, CPT>), dim3(rows), dim3(kT), 0, s, p.x, st, p.gamma, p.shift,
-                     p.y, (int)p.D, (int)p.G);
+  hipLaunchKernelGGL((tdn_apply_kernel<kIn, kOut, CPT>), dim3((unsigned)((rows + kRows - 1) / kRows)), dim3(kT), 0,
+                     s, p.x, st, p.gamma, p.shift, p.y, (int64_t)rows, (int)p.D, (int)p.G);
   return hipGetLastError();
 }
 
