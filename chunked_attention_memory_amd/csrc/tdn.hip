@@ -14,9 +14,9 @@
 //     per-group mean then variance (two passes over registers) through LDS;
 //   scan: the tokens cut into chunks; one thread per (batch, chunk, group)
 //     computes the chunk's decayed sums from zero, the sums entering each
-//     chunk are carried across chunks (b^L per chunk, in double), and a second
-//     pass from the entering sums writes (m_hat, 1 / sqrt(v_hat + eps)) in
-//     place of the statistics;
+//     chunk are carried across chunks (b^L per chunk), and a second pass from
+//     the entering sums writes (m_hat, 1 / sqrt(v_hat + eps)) in place of the
+//     statistics; the sums run in double (1 - b^t by its own recurrence);
 //   apply: one block per token row, 16-byte loads and stores.
 #include <algorithm>
 
@@ -121,9 +121,15 @@ __global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* st, float2* carr
   const int64_t b = blockIdx.x / NC;
   const int c = (int)(blockIdx.x % NC);
   const int64_t ta = (int64_t)c * L, tb = std::min<int64_t>(ta + L, n);
-  const float ln1 = logf(b1), ln2 = logf(b2);  // -inf for a zero factor
+  // The sums run in double: with b near 1 a float32 sum settles about
+  // 2^-25 / (1 - b) away from its exact value (3e-4 relative at b = 0.9999).
+  // 1 - b^t follows u_t = b u_{t-1} + (1 - b) and runs beside them, from its
+  // value before the chunk.
+  const double d1 = b1, d2 = b2, e1 = 1.0 - d1, e2 = 1.0 - d2;
+  const double tp = (double)(t0 + ta);  // tokens of the sequence before the chunk
+  const double u1s = tp > 0.0 ? -expm1(tp * log(d1)) : 0.0, u2s = tp > 0.0 ? -expm1(tp * log(d2)) : 0.0;
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    float m = 0.f, v = 0.f;
+    double m = 0.0, v = 0.0, u1 = u1s, u2 = u2s;
     if constexpr (kFinal) {
       const float2 e = carry[(b * NC + c) * G + g];
       m = e.x;
@@ -139,34 +145,32 @@ __global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* st, float2* carr
       for (int k = 0; k < kB; ++k) x[k] = s[(t + k) * G];
 #pragma unroll
       for (int k = 0; k < kB; ++k) {
-        m = fmaf(b1, m, (1.f - b1) * x[k].x);
-        v = fmaf(b2, v, (1.f - b2) * x[k].y);
+        m = fma(d1, m, e1 * x[k].x);
+        v = fma(d2, v, e2 * x[k].y);
         if constexpr (kFinal) {
-          const float tt = (float)(t0 + t + k + 1);
-          const float mh = m / -expm1f(tt * ln1);  // 1 - b^t, accurate for b near 1
-          const float vh = v / -expm1f(tt * ln2);
-          s[(t + k) * G] = make_float2(mh, rsqrtf(vh + eps));
+          u1 = fma(d1, u1, e1);
+          u2 = fma(d2, u2, e2);
+          s[(t + k) * G] = make_float2((float)(m / u1), rsqrtf((float)(v / u2) + eps));
         }
       }
     }
     for (; t < tb; ++t) {
       const float2 x = s[t * G];
-      m = fmaf(b1, m, (1.f - b1) * x.x);
-      v = fmaf(b2, v, (1.f - b2) * x.y);
+      m = fma(d1, m, e1 * x.x);
+      v = fma(d2, v, e2 * x.y);
       if constexpr (kFinal) {
-        const float tt = (float)(t0 + t + 1);
-        const float mh = m / -expm1f(tt * ln1);
-        const float vh = v / -expm1f(tt * ln2);
-        s[t * G] = make_float2(mh, rsqrtf(vh + eps));
+        u1 = fma(d1, u1, e1);
+        u2 = fma(d2, u2, e2);
+        s[t * G] = make_float2((float)(m / u1), rsqrtf((float)(v / u2) + eps));
       }
     }
     if constexpr (kFinal) {
       if (c == NC - 1) {
-        if (m_out) m_out[b * G + g] = m;
-        if (v_out) v_out[b * G + g] = v;
+        if (m_out) m_out[b * G + g] = (float)m;
+        if (v_out) v_out[b * G + g] = (float)v;
       }
     } else {
-      carry[(b * NC + c) * G + g] = make_float2(m, v);
+      carry[(b * NC + c) * G + g] = make_float2((float)m, (float)v);
     }
   }
 }

@@ -4,8 +4,10 @@ float32). Statistics and sums are float32 on the GPU; the outputs are O(1)
 normalised values, so the bar is max |y - x| / rms(x) <= 1e-4 on float32
 output, and the carried sums match to 1e-4 relative. Cases: no decay (plain
 per-token group normalisation), typical and near-one decay factors (the bias
-correction at its most delicate), groups of 8 to 64, one token, the chunked
-scan, a sequence continued over two calls, and the bf16 output rounding."""
+correction at its most delicate, and a sequence long enough for the sums to
+reach their steady state, where float32 sums would drift by about
+2^-25 / (1 - beta)), groups of 8 to 64, one token, the chunked scan, a
+sequence continued over two calls, and the bf16 output rounding."""
 
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ def _dev(host):
     (1, 1, 16, 2, 0.9, 0.99, "bf16"),
     (1, 700, 256, 4, 0.0, 0.0, "f32"),          # no decay: group norm of each token
     (1, 5000, 4096, 64, 0.999, 0.9999, "bf16"),  # chunked scan, factors near one
+    (1, 65536, 256, 8, 0.999, 0.9999, "bf16"),   # long enough for the sums to settle
 ])
 def test_tdn_matches_oracle(B, n, D, G, b1, b2, dtype):
     import torch
