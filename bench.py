@@ -36,6 +36,8 @@ METRIC = "SCA+AWM fwd tokens/s at 128K tokens, c=2048; % of bf16 MFMA peak"
 # committed counter summaries: (file, kernel sources it was measured on)
 PMC_SCA = (os.path.join(ROOT, "profiles", "sca_bf16_128k_pmc.txt"), ("sca_bf16.hip", "gecko_device.hpp"))
 PMC_SCAN = (os.path.join(ROOT, "profiles", "awm_scan_128k_pmc.txt"), ("awm_bf16.hip", "gecko_device.hpp"))
+PMC_CEMA = (os.path.join(ROOT, "profiles", "cema_128k_pmc.txt"), ("cema.hip", "gecko_device.hpp"))
+PMC_TDN = (os.path.join(ROOT, "profiles", "tdn_128k_pmc.txt"), ("tdn.hip", "gecko_device.hpp"))
 
 
 def kernel_source_hash(sources) -> str:
@@ -171,7 +173,9 @@ def time_tdn(gecko, stream, timed) -> dict:
     achieved = alg / (ms / 1e3) / 1e9
     return {"workload": "tdn_bf16_B1_n128k_D4096_G64", "ms_per_step": ms, "tokens_per_s": B * n / (ms / 1e3),
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "algorithmic_bytes": alg}}
+                         "frac": achieved / PEAK_HBM_GBPS,
+                         "traffic": read_traffic(PMC_TDN, "tdn_bf16_B1_n128k_D4096_G64:bf16"),
+                         "algorithmic_bytes": alg}}
 
 
 def time_cema(gecko, stream, timed) -> dict:
@@ -193,7 +197,8 @@ def time_cema(gecko, stream, timed) -> dict:
     achieved = flops / (ms / 1e3) / 1e12
     return {"workload": "cema_bf16_B1_n128k_D4096_h16", "ms_per_step": ms, "tokens_per_s": B * n / (ms / 1e3),
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                         "frac": achieved / PEAK_FP32_VECTOR_TFLOPS, "traffic": None,
+                         "frac": achieved / PEAK_FP32_VECTOR_TFLOPS,
+                         "traffic": read_traffic(PMC_CEMA, "cema_bf16_B1_n128k_D4096_h16:bf16"),
                          "flops_per_launch": flops, "algorithmic_bytes": 4.0 * B * n * D}}
 
 
