@@ -18,3 +18,4 @@ from .gecko_oracle import (  # noqa: F401
 )
 from .cema_oracle import cema, cema_multiplier  # noqa: F401
 from .tdn_oracle import tdn  # noqa: F401
+from .gecko_grad_oracle import AFFINE, forward_torch_head, grad, grad_head, lse_head  # noqa: F401
