@@ -127,6 +127,8 @@ struct Call {
   bool streaming;
   int64_t pos;
   void* state; size_t state_bytes;
+  // gecko_forward_lse: per-query attention log-sum-exp output (bf16 only)
+  float* lse;
 };
 
 // memory steps and snapshot slots of a call (see gecko::Problem); lag 2 with
@@ -239,6 +241,7 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   p.zprev = p.vprev = nullptr;
   p.mstate = nullptr;
   p.zstate = nullptr;
+  p.lse = k.lse;
   if (k.streaming) {
     const gecko::StreamState t = gecko::carve_state(k.state, BH, k.d, k.dv, k.c);
     p.mstate = t.mstate;
@@ -507,6 +510,215 @@ gecko_status gecko_sca_awm_forward_stream(const void* z, const float* kappa_q, c
   }
 }
 
+gecko_status gecko_forward_lse(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                               const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
+                               const float* rho_k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                               int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
+                               gecko_dtype out_dtype, unsigned flags, unsigned parts, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  try {
+    if (!(parts & GECKO_PART_SCA) || (parts & ~3u))
+      return fail(GECKO_EINVAL, "parts must hold GECKO_PART_SCA (and may hold GECKO_PART_AWM)");
+    if (in_dtype != GECKO_BF16) return fail(GECKO_EUNSUPPORTED, "the log-sum-exp output is built for bf16 inputs only");
+    if (!lse) return fail(GECKO_EINVAL, "lse must be non-null");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(GECKO_EINVAL, "lse must be 4-byte aligned");
+    if (B >= 1 && H >= 1 && n >= 1 && dv >= 1 && out && B <= (1 << 20) && H <= (1 << 20) && n <= (int64_t(1) << 40)) {
+      const size_t lb = (size_t)B * H * n * 4;
+      const size_t ob = (size_t)B * H * n * dv * (out_dtype == GECKO_BF16 ? 2 : 4);
+      if (overlaps(lse, lb, out, ob) || (workspace && overlaps(lse, lb, workspace, workspace_bytes)))
+        return fail(GECKO_EINVAL, "lse aliases the output or the workspace");
+    }
+    const int mode = (parts & GECKO_PART_SCA ? kModeSca : 0) | (parts & GECKO_PART_AWM ? kModeAwm : 0);
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, mode, nullptr};
+    k.lse = lse;
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+// the forward description the backward kernels share (one call, no stream)
+gecko_status bwd_problem(const void* z, const float* const (&aff)[8], const void* v, const void* dout, float* dz,
+                         float* dv_out, float* daff, int64_t B,
+                         int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
+                         gecko_dtype out_dtype, unsigned flags, unsigned parts, bool check_ptrs,
+                         gecko::BwdProblem& p) {
+  if (B < 1 || H < 1 || n < 1 || c < 1 || d < 1 || dv < 1)
+    return fail(GECKO_EINVAL, "sizes must be >= 1");
+  if (B > (1 << 20) || H > (1 << 20) || n > (int64_t(1) << 40)) return fail(GECKO_EINVAL, "sizes out of range");
+  if (in_dtype != GECKO_F32 && in_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown input dtype %d", (int)in_dtype);
+  if (out_dtype != GECKO_F32 && out_dtype != GECKO_BF16) return fail(GECKO_EINVAL, "unknown output dtype %d", (int)out_dtype);
+  if (flags & ~(unsigned)(GECKO_AWM_NO_DELTA | GECKO_CHUNKWISE)) return fail(GECKO_EINVAL, "unknown flag bits 0x%x", flags);
+  if (parts < 1 || parts > 3) return fail(GECKO_EINVAL, "parts must be GECKO_PART_SCA, GECKO_PART_AWM or both");
+  if (in_dtype != GECKO_BF16) return fail(GECKO_EUNSUPPORTED, "the backward is built for bf16 inputs only");
+  if (!gecko::bwd_shape_built(d, dv))
+    return fail(GECKO_EUNSUPPORTED, "the backward is built for (d, dv) in {(128, 256), (128, 128)}");
+  if ((n + 512) * (d > dv ? d : dv) * 2 > (int64_t)0xFFFFFFFF)
+    return fail(GECKO_EUNSUPPORTED, "the backward needs n * max(d, dv) * 2 < 4 GiB per (batch, head) slab");
+  const int64_t BH = B * H;
+  const int64_t N = nchunks_of(n, c);
+  const int64_t cc = c < n ? c : n;
+  if (BH * N * ((cc + 255) / 256) >= ((int64_t)1 << 31) || BH * ((n + 255) / 256) >= ((int64_t)1 << 31))
+    return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
+  const bool sca = parts & GECKO_PART_SCA, awm = parts & GECKO_PART_AWM;
+  if (check_ptrs) {
+    if (!z || !v || !dout || !dz || !dv_out || !daff) return fail(GECKO_EINVAL, "z, v, dout, dz, dv and daff must be non-null");
+    const void* a16[] = {z, v, dout, dz, dv_out};
+    for (const void* q : a16)
+      if (reinterpret_cast<uintptr_t>(q) & 15u) return fail(GECKO_EINVAL, "z, v, dout, dz and dv must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(daff) & 3u) return fail(GECKO_EINVAL, "daff must be 4-byte aligned");
+    for (int i = 0; i < 8; ++i) {
+      const bool needed = i < 4 ? sca : awm;
+      if (needed && !aff[i]) return fail(GECKO_EINVAL, "affine vector %d is null", i);
+      if (needed && (reinterpret_cast<uintptr_t>(aff[i]) & 15u))
+        return fail(GECKO_EINVAL, "affine vector %d must be 16-byte aligned", i);
+    }
+    const size_t osz = out_dtype == GECKO_BF16 ? 2 : 4;
+    const size_t zb = (size_t)BH * n * d * 2, vb = (size_t)BH * n * dv * 2, ob = (size_t)BH * n * dv * osz;
+    const size_t dzb = (size_t)BH * n * d * 4, dvb = (size_t)BH * n * dv * 4, ab = (size_t)8 * H * d * 4;
+    struct R { const void* p; size_t b; } outs[] = {{dz, dzb}, {dv_out, dvb}, {daff, ab}};
+    struct R ins[] = {{z, zb}, {v, vb}, {dout, ob}};
+    for (int i = 0; i < 3; ++i) {
+      for (const R& r : ins)
+        if (r.p && overlaps(outs[i].p, outs[i].b, r.p, r.b)) return fail(GECKO_EINVAL, "a gradient output aliases an input");
+      for (int j = i + 1; j < 3; ++j)
+        if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return fail(GECKO_EINVAL, "gradient outputs overlap");
+    }
+  }
+  gecko::Problem& f = p.f;
+  f = gecko::Problem{};
+  f.z = z; f.v = v; f.out = nullptr;
+  f.kappa_q = aff[0]; f.nu_q = aff[1]; f.kappa_k = aff[2]; f.nu_k = aff[3];
+  f.eta_q = aff[4]; f.rho_q = aff[5]; f.eta_k = aff[6]; f.rho_k = aff[7];
+  f.B = B; f.H = H; f.n = n; f.d = d; f.dv = dv; f.c = c;
+  f.nchunks = N;
+  const int64_t lag = lag_of(flags);
+  int64_t nmem = 0, nsnap = 0;
+  mem_counts(N, false, false, lag, nmem, nsnap);
+  f.nmem = nmem; f.nsnap = nsnap; f.flags = flags;
+  f.first_read = lag; f.lag = lag; f.prev = (flags & GECKO_CHUNKWISE) ? 0 : 1;
+  f.out_f32 = out_dtype == GECKO_F32;
+  f.stream = false; f.has_prev = false;
+  p.dout = dout; p.dz = dz; p.dv = dv_out; p.daff = daff;
+  p.sca = sca; p.awm = awm; p.out_f32 = out_dtype == GECKO_F32;
+  return GECKO_OK;
+}
+
+}  // namespace
+
+namespace gecko {
+
+BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p) {
+  BwdWorkspace w{};
+  const Problem& f = p.f;
+  const size_t BH = (size_t)(f.B * f.H), n = (size_t)f.n, d = (size_t)f.d, dv = (size_t)f.dv;
+  const size_t nm = (size_t)f.nmem;
+  size_t off = 0;
+  const bool mem = p.awm && f.nmem > 0;
+  if (mem) {
+    w.fw = carve_workspace(base, f.B * f.H, f.n, f.d, f.dv, f.nmem, f.nsnap, true, false);
+    off = align_up(w.fw.bytes);
+  }
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return static_cast<char*>(base) + at;
+  };
+  if (p.sca) {
+    w.qp = reinterpret_cast<uint16_t*>(take(BH * n * d * 2));
+    w.ld = reinterpret_cast<float*>(take(BH * n * 8));
+    w.dq = reinterpret_cast<float*>(take(BH * n * d * 4));
+    w.dk = reinterpret_cast<float*>(take(BH * n * d * 4));
+  }
+  if (p.out_f32) w.do16 = reinterpret_cast<uint16_t*>(take(BH * n * dv * 2));
+  if (p.awm) {
+    w.dqm = reinterpret_cast<float*>(take(BH * n * d * 4));
+    w.dkm = reinterpret_cast<float*>(take(BH * n * d * 4));
+  }
+  if (mem) {
+    w.r = reinterpret_cast<float*>(take(BH * nm * d * dv * 4));
+    w.ht = reinterpret_cast<uint16_t*>(take(BH * nm * d * d * 2));
+    w.ds = reinterpret_cast<uint16_t*>(take(BH * nm * d * dv * 2));
+    w.part = reinterpret_cast<float*>(take(BH * nm * (dv / 32) * d * 2 * 4));
+    w.zeta = reinterpret_cast<float*>(take(BH * nm * d * 4));
+    w.x = reinterpret_cast<uint16_t*>(take(BH * nm * d * d * 2));
+    w.s32 = reinterpret_cast<float*>(take(BH * nm * d * dv * 4));
+    w.fw.snap32 = w.s32;
+  }
+  w.rows_per_blk = 256;
+  w.nblk = (f.n + w.rows_per_blk - 1) / w.rows_per_blk;
+  w.apart = reinterpret_cast<float*>(take(BH * (size_t)w.nblk * 8 * d * 4));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace gecko
+
+extern "C" {
+
+size_t gecko_backward_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts) {
+  const float* none[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  gecko::BwdProblem p;
+  const std::string saved = g_last_error;
+  if (bwd_problem(nullptr, none, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, n, d, dv, c, in_dtype, out_dtype,
+                  flags, parts, false, p) != GECKO_OK) {
+    g_last_error = saved;
+    return (size_t)-1;
+  }
+  return gecko::carve_bwd_workspace(nullptr, p).bytes;
+}
+
+gecko_status gecko_backward(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                            const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
+                            const float* rho_k, const void* v, const void* dout, float* dz, float* dv_out,
+                            float* daff, int64_t B, int64_t H, int64_t n, int64_t d,
+                            int64_t dv, int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                            unsigned parts, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    const float* aff[8] = {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k};
+    gecko::BwdProblem p;
+    gecko_status st = bwd_problem(z, aff, v, dout, dz, dv_out, daff, B, H, n, d, dv, c, in_dtype, out_dtype, flags,
+                                  parts, true, p);
+    if (st != GECKO_OK) return st;
+    const gecko::BwdWorkspace need = gecko::carve_bwd_workspace(nullptr, p);
+    if (!workspace) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", need.bytes);
+    if (workspace_bytes < need.bytes)
+      return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+      return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
+    {
+      const size_t BH = (size_t)(B * H);
+      const void* o[] = {z, v, dout, dz, dv_out, daff};
+      const size_t ob = BH * n * dv * (out_dtype == GECKO_BF16 ? 2 : 4);
+      const size_t b[] = {BH * n * d * 2, BH * n * dv * 2, ob, BH * n * d * 4, BH * n * dv * 4, (size_t)8 * H * d * 4};
+      for (int i = 0; i < 6; ++i)
+        if (o[i] && overlaps(workspace, need.bytes, o[i], b[i]))
+          return fail(GECKO_EINVAL, "the workspace aliases an input or an output");
+    }
+    const gecko::BwdWorkspace w = gecko::carve_bwd_workspace(workspace, p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p.out_f32 && (e = gecko::launch_bwd_dout16(p, w, s)) != hipSuccess) return hip_fail(e, "dO conversion launch");
+    if (p.awm && (e = gecko::launch_bwd_awm(p, w, s)) != hipSuccess) return hip_fail(e, "memory backward launch");
+    if (p.sca) {
+      if ((e = gecko::launch_bwd_prep(p, w, s)) != hipSuccess) return hip_fail(e, "attention backward prep launch");
+      if ((e = gecko::launch_bwd_dq(p, w, s)) != hipSuccess) return hip_fail(e, "attention dQ launch");
+      if ((e = gecko::launch_bwd_dkdv(p, w, p.awm, s)) != hipSuccess) return hip_fail(e, "attention dK dV launch");
+    }
+    if ((e = gecko::launch_bwd_combine(p, w, s)) != hipSuccess) return hip_fail(e, "gradient combine launch");
+    g_last_error.clear();
+    return GECKO_OK;
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
 gecko_status gecko_timer_create(int capacity, gecko_timer** timer) {
   if (!timer || capacity < 1 || capacity > (1 << 20)) return fail(GECKO_EINVAL, "bad timer arguments");
   gecko_timer* t = new (std::nothrow) gecko_timer;
@@ -569,6 +781,6 @@ const char* gecko_status_string(gecko_status status) {
 
 const char* gecko_last_error(void) { return g_last_error.c_str(); }
 
-int gecko_version(void) { return 101; }
+int gecko_version(void) { return 102; }
 
 }  // extern "C"

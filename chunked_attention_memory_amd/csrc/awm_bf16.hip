@@ -483,6 +483,7 @@ struct ScanArgs {
                        //   [bh][dv/32][d/32][64 lanes][16]; read if has_prev, written if stream
   const float* zstate; // streaming: (M, L) per feature before the call [bh][d][2], read if has_prev
   float* zfinal;       // streaming: (M, L) per feature after the call [bh][d][2], written if stream
+  float* snap32;       // optional: every snapshot again in float32 [bh][nsnap][d][dv]
   int64_t nmem, nsnap;
   int no_delta;        // drop the H_t M' term (test variant)
   int has_prev, stream;
@@ -594,6 +595,12 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
     // snapshot rows f of the state after step t, values 32 j .. 32 j + 31:
     // 64 bytes per row
     write_snap(t + hp, mt[buf ^ 1]);
+    if (a.snap32) {  // float32 copy: row f, values 32 j + 8 qq + 4 g + [0, 4)
+      float* s32 = a.snap32 + (bh * a.nsnap + t + hp) * (int64_t)D * DV + (int64_t)f * DV + 32 * j + 4 * g;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<f32x4*>(s32 + 8 * qq) = f32x4{mst[4 * qq], mst[4 * qq + 1], mst[4 * qq + 2], mst[4 * qq + 3]};
+    }
     buf ^= 1;
   };
 
@@ -738,7 +745,7 @@ hipError_t launch_awm_scan_bf16(const Problem& p, const Workspace& w, hipStream_
   a.g = w.g; a.hm = static_cast<const uint16_t*>(w.h); a.cmax = w.cmax; a.csum = w.csum;
   a.snap = static_cast<uint16_t*>(w.snap); a.nmem = p.nmem; a.nsnap = p.nsnap;
   a.no_delta = (p.flags & GECKO_AWM_NO_DELTA_BIT) ? 1 : 0;
-  a.mstate = p.mstate; a.zstate = p.zstate; a.zfinal = w.zfinal;
+  a.mstate = p.mstate; a.zstate = p.zstate; a.zfinal = w.zfinal; a.snap32 = w.snap32;
   a.has_prev = p.has_prev ? 1 : 0; a.stream = p.stream ? 1 : 0;
   const int64_t BH = p.B * p.H;
   if (p.d == 128 && p.dv == 256) return launch_scan<128, 256>(a, BH, s);

@@ -41,6 +41,7 @@ struct Problem {
   const void* vprev;    // [BH][c][dv]
   float* mstate;        // [BH][dv/32][d/32][64][16] fp32 state M'^T (scan accumulator layout), in/out
   const float* zstate;  // [BH][d][2] running (M, L) per feature (log2 max, scaled sum) before this call
+  float* lse;           // bf16 attention only, may be null: [BH][n] natural log-sum-exp of each query's logits
 };
 
 // Workspace carve-up (byte offsets from the workspace base). Every array is
@@ -56,6 +57,7 @@ struct Workspace {
   void* snap;      // state read by chunk t+2: bf16 [bh][nsnap][d][dv], fp32 [bh][t][dv][d]
   float* rowstat;  // fp32 path only: per-token (max, sum) of K_m rows  [bh][n][2]
   float* zfinal;   // streaming: running (M, L) per feature after the call  [bh][d][2]
+  float* snap32;   // optional (bf16 scan): the snapshots again in float32 [bh][nsnap][d][dv] (set by the backward)
   size_t bytes;
 };
 
@@ -82,6 +84,50 @@ hipError_t launch_stream_finish(const Problem& p, const Workspace& w, void* zcar
                                 int64_t row0, int64_t rows, hipStream_t s);
 
 bool bf16_shape_built(int64_t d, int64_t dv);
+
+// ---------------------------------------------------------------- backward
+// Gradients of L = sum(dO * O) (bf16 inputs, d = 128, dv in {128, 256}).
+struct BwdProblem {
+  Problem f;            // the forward (z, v, affine vectors, sizes, nmem, lag, prev)
+  const void* dout;     // [BH][n][dv], bf16 or float32
+  float* dz;            // [BH][n][d]
+  float* dv;            // [BH][n][dv]
+  float* daff;          // [8][H][d]: kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k
+  bool sca, awm, out_f32;
+};
+
+// Backward workspace. Arrays indexed [bh][t] have t = 0..nmem-1, the chunk
+// entering the memory (scan step t).
+struct BwdWorkspace {
+  Workspace fw;         // forward memory pass and scan, recomputed
+  uint16_t* qp;         // scaled queries (kappa_q z + nu_q) kappa_k log2(e), bf16 [BH][n][d]
+  float* ld;            // per query: (log2-sum-exp of the scaled logits, sum_j P_ij dP_ij) [BH][n][2]
+  uint16_t* do16;       // dO in bf16 [BH][n][dv] when dO is float32 (else null: dO itself)
+  float* dq;            // dL/dQ, dL/dK, dL/dQ_m, dL/dK_m, each [BH][n][d]
+  float* dk;
+  float* dqm;
+  float* dkm;
+  float* r;             // readout gradient reaching state t: psi(Q_m)^T dO of the chunk that reads it,
+                        //   transposed, in the scan's accumulator layout [BH][t][dv/32][d/32][64][16]
+  uint16_t* ht;         // H_t transposed, scan B-operand order [BH][t][d/16][d/32][64][8]
+  uint16_t* ds;         // dL/dS_t (state after step t), bf16 [BH][t][d][dv]
+  float* part;          // per 32-value slice: rowsum(R_t * S_t), rowsum(C_t * S_t) [BH][t][dv/32][d][2]
+  float* zeta;          // z^t * dL/dz^t per feature [BH][t][d]
+  uint16_t* x;          // dS_t S_{t-1}^T, bf16 [BH][t][d][d]
+  float* s32;           // the states S_t in float32 [BH][t][d][dv] (forward scan, backward mode)
+  float* apart;         // affine-gradient partial sums [BH][nblk][8][d]
+  int64_t nblk, rows_per_blk;
+  size_t bytes;
+};
+
+BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p);
+bool bwd_shape_built(int64_t d, int64_t dv);
+hipError_t launch_bwd_prep(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_bwd_dout16(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdProblem& p, const BwdWorkspace& w, bool accumulate_dv, hipStream_t s);
+hipError_t launch_bwd_awm(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_bwd_combine(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
 
 // CEMA (cema.hip). All pointers are device pointers.
 struct CemaProblem {

@@ -126,6 +126,8 @@ struct ScaArgs {
   const float* kappa_q;
   const float* nu_q;
   const float* kappa_k;
+  const float* nu_k;   // read only when lse is set
+  float* lse;          // optional [bh][n]: natural log-sum-exp of each query's logits
   const float* eta_q;
   const float* rho_q;
   const uint16_t* snap;  // [bh][nsnap][d][dv]; chunk s reads slot s - 2 + 2 has_prev (0-based)
@@ -443,8 +445,9 @@ struct ScaLoop {
     return any;
   }
 
-  // O^T for the wave's queries, not yet divided by the row sums (lsum)
-  __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV], float (&lsum)[QB]) const {
+  // O^T for the wave's queries, not yet divided by the row sums (lsum); the
+  // row sums hold 2^(s - mout) summed over the visible keys
+  __device__ __forceinline__ void run(f32x16 (&oacc)[QB][NMV], float (&lsum)[QB], float (&mout)[QB]) const {
     // First pass without an offset: P = 2^s. The row sums show whether that
     // was safe: if a valid query's sum lies outside [2^-60, 2^63] (some 2^s
     // overflowed, or every term is tiny), the workgroup finds the exact row
@@ -483,7 +486,10 @@ struct ScaLoop {
       pass<true>(msub, ltot, oacc);
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] = ltot[qb];
+    for (int qb = 0; qb < QB; ++qb) {
+      lsum[qb] = ltot[qb];
+      mout[qb] = msub[qb];
+    }
   }
 };
 
@@ -631,7 +637,37 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   if constexpr (kSca) {
     ScaLoop<D, DV, QB> L;
     L.init(a, bh, h, n, s, c, q0, qend, w, lane, S0, S1, S2, va);
-    L.run(oacc, lsum);
+    float msub[QB];
+    L.run(oacc, lsum, msub);
+    if (a.lse) {
+      // the kernel's logits are log2(e) (q_i . k_j - q_i . nu_k) (see the
+      // header), so log sum_j exp(q_i . k_j) = ln 2 (msub + log2 lsum) + q_i . nu_k
+      const float* kq = a.kappa_q + h * D;
+      const float* nq = a.nu_q + h * D;
+      const float* nk = a.nu_k + h * D;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int myq = myq0 + 32 * qb;
+        const uint16_t* zq = zbh + (size_t)min(myq, qend - 1) * D;
+        float qn = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int f0 = 16 * ks + 8 * g;
+          float x[8];
+          const u32x4 raw = ld16(zq + f0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf_lo(raw[j]);
+            x[2 * j + 1] = bf_hi(raw[j]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qn += (kq[f0 + i] * x[i] + nq[f0 + i]) * nk[f0 + i];
+        }
+        qn = other_half_sum(qn);
+        if (g == 0 && myq < qend)
+          a.lse[(size_t)bh * n + myq] = 0.6931471805599453f * (msub[qb] + log2f(lsum[qb])) + qn;
+      }
+    }
   }
   if constexpr (kRead && !kEarly) {  // every wave is past the loop's last barrier
     if (reads) stage_snapshot<D, DV, T::THREADS, FB0>(sn, snap_a, snap_b, w, lane);
@@ -784,6 +820,7 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   a.v = static_cast<const uint16_t*>(p.v);
   a.out = p.out;
   a.kappa_q = p.kappa_q; a.nu_q = p.nu_q; a.kappa_k = p.kappa_k;
+  a.nu_k = p.nu_k; a.lse = p.lse;
   a.eta_q = p.eta_q; a.rho_q = p.rho_q;
   a.snap = static_cast<const uint16_t*>(w.snap);
   a.zprev = static_cast<const uint16_t*>(p.zprev);

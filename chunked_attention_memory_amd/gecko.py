@@ -18,6 +18,7 @@ GECKO_OK, GECKO_EINVAL, GECKO_EUNSUPPORTED, GECKO_EWORKSPACE, GECKO_EHIP = range
 GECKO_F32, GECKO_BF16 = 0, 1
 GECKO_AWM_NO_DELTA = 1 << 0
 GECKO_CHUNKWISE = 1 << 1
+GECKO_PART_SCA, GECKO_PART_AWM = 1, 2
 
 EXPORTED = (
     "gecko_workspace_size", "gecko_sca_awm_forward", "gecko_sca_forward", "gecko_awm_forward",
@@ -26,6 +27,7 @@ EXPORTED = (
     "gecko_stream_state_size", "gecko_stream_workspace_size", "gecko_sca_awm_forward_stream",
     "gecko_workspace_size_for", "gecko_cema_workspace_size", "gecko_cema_forward",
     "gecko_tdn_workspace_size", "gecko_tdn_forward",
+    "gecko_forward_lse", "gecko_backward_workspace_size", "gecko_backward",
 )
 
 
@@ -89,6 +91,12 @@ def _load() -> ctypes.CDLL:
     lib.gecko_stream_workspace_size.argtypes = [I64] * 6 + [I]
     lib.gecko_sca_awm_forward_stream.restype = I
     lib.gecko_sca_awm_forward_stream.argtypes = [P] + [F] * 8 + [P, P] + [I64] * 7 + [I, I, U, P, SZ, P, SZ, P]
+    lib.gecko_forward_lse.restype = I
+    lib.gecko_forward_lse.argtypes = [P] + [F] * 8 + [P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_backward_workspace_size.restype = SZ
+    lib.gecko_backward_workspace_size.argtypes = [I64] * 6 + [I, I, U, U]
+    lib.gecko_backward.restype = I
+    lib.gecko_backward.argtypes = [P] + [F] * 8 + [P, P, P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
     return lib
 
 
@@ -404,3 +412,62 @@ def to_device_inputs(host: dict, device="cuda"):
     params = {k: torch.from_numpy(a).to(device=device, dtype=torch.float32).contiguous()
               for k, a in host["params"].items()}
     return z, v, params
+
+
+def _part_params(params, parts, device, H, d):
+    q = _params(params, Q_NAMES, device, H, d) if parts & GECKO_PART_SCA else [None] * 4
+    m = _params(params, M_NAMES, device, H, d) if parts & GECKO_PART_AWM else [None] * 4
+    return q + m
+
+
+def gecko_forward_lse(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, out=None, lse=None, out_dtype=None,
+                      flags=0, workspace=None, stream=None):
+    """O of the selected parts and the attention log-sum-exp per query ([B, H, n] float32)."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=z.device)
+    if workspace is None and parts & GECKO_PART_AWM:
+        workspace = alloc_workspace(z, v, c, flags)
+    _check(lib.gecko_forward_lse(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(out), _ptr(lse),
+                                 B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags, parts,
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def gecko_backward_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags=0,
+                                  parts=GECKO_PART_SCA | GECKO_PART_AWM) -> int:
+    r = lib.gecko_backward_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags, parts)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid or unsupported arguments for gecko_backward_workspace_size")
+    return r
+
+
+def gecko_backward(z, params, v, dout, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, flags=0, dz=None, dv=None,
+                   daff=None, workspace=None, stream=None):
+    """Gradients of sum(dout * O): dict with ``dz`` [B, H, n, d], ``dv`` [B, H, n, dv] (float32) and one
+    float32 [H, d] tensor per affine name (views of ``daff`` [8, H, d])."""
+    import torch
+
+    B, H, n, d, dvs = _shape(z, v)
+    if tuple(dout.shape) != (B, H, n, dvs) or not dout.is_contiguous():
+        raise GeckoError(GECKO_EINVAL, "dout must be a contiguous [B, H, n, dv] tensor")
+    if dz is None:
+        dz = torch.empty((B, H, n, d), dtype=torch.float32, device=z.device)
+    if dv is None:
+        dv = torch.empty((B, H, n, dvs), dtype=torch.float32, device=z.device)
+    if daff is None:
+        daff = torch.empty((8, H, d), dtype=torch.float32, device=z.device)
+    if workspace is None:
+        nbytes = gecko_backward_workspace_size(B, H, n, d, dvs, c, _dtype_code(z), _dtype_code(dout), flags, parts)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+    _check(lib.gecko_backward(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
+                              _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c, _dtype_code(z),
+                              _dtype_code(dout), flags, parts, _ptr(workspace), workspace.numel(), _stream(stream)))
+    res = {"dz": dz, "dv": dv}
+    for i, k in enumerate(Q_NAMES + M_NAMES):
+        res["d" + k] = daff[i]
+    return res

@@ -104,6 +104,26 @@ def make_inputs_device(B: int, H: int, n: int, d: int, dv: int, dtype: str, seed
     return {"z": z, "v": v, "params": params, "dtype": dtype}
 
 
+# ---------------------------------------------------------------- backward
+_DO = 3
+
+
+def make_dout(B: int, H: int, n: int, dv: int, dtype: str, seed: int = 0, tag: int = 0) -> np.ndarray:
+    """Upstream gradient dL/dO for the backward: iid N(0, 1), rounded to the run
+    dtype, float32 [B, H, n, dv] (drawn per (batch, head) slab like Z' and V)."""
+    out = np.empty((B, H, n, dv), np.float32)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = _round(_rng(seed, tag, _DO, b, h).standard_normal((n, dv)), dtype)
+    return out
+
+
+def sharpen(params: dict, factor: float) -> dict:
+    """The same affine vectors with the scales (kappa, eta) multiplied by
+    ``factor``: larger logits, peakier attention and feature softmaxes."""
+    return {k: (v * np.float32(factor) if k[0] in ("k", "e") else v).astype(np.float32) for k, v in params.items()}
+
+
 # ---------------------------------------------------------------- CEMA
 _CX, _CP, _CR = 10, 11, 12
 

@@ -243,6 +243,68 @@ gecko_status gecko_sca_awm_forward_timed(
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
     void* workspace, size_t workspace_bytes, void* stream, gecko_timer* timer);
 
+/*
+ * Training: the backward (bf16 inputs only; (d, dv) in {(128, 256),
+ * (128, 128)}) and a forward that also returns the attention normaliser.
+ *
+ * The pages define the forward only; the backward computes the derivatives
+ * of L = sum(dO * O) with respect to Z', V and the eight affine vectors, O
+ * being the output of the same parts of the layer (O_SCA, O_m or both) with
+ * the same flags. Following the training setup the pages describe
+ * (paperlayer.ai summary, Appendix B.1: what the backward needs is recomputed
+ * from chunk-boundary states instead of being stored), the backward keeps
+ * nothing from the forward: it reruns the memory's chunk pass and scan and
+ * the attention's row statistics itself.
+ *
+ * parts: GECKO_PART_SCA, GECKO_PART_AWM or both (O = O_SCA + O_m).
+ */
+enum { GECKO_PART_SCA = 1, GECKO_PART_AWM = 2 };
+
+/* gecko_sca_awm_forward (parts = SCA | AWM) or gecko_sca_forward (parts =
+ * SCA) that also writes lse [B][H][n] float32: for each query i,
+ * log sum_j exp(q_i . k_j) over its attention window (natural log), the
+ * softmax normaliser (e.g. for a caller's own attention backward). parts
+ * must hold GECKO_PART_SCA; the workspace is needed with GECKO_PART_AWM
+ * (gecko_workspace_size_for bytes). bf16 inputs only (GECKO_EUNSUPPORTED
+ * otherwise). lse must be 4-byte aligned and alias nothing else. */
+gecko_status gecko_forward_lse(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out, float* lse,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gecko_backward needs ((size_t)-1 if the
+ * arguments are invalid or not built). It holds the recomputed memory pass
+ * and scan, the scaled queries and their row statistics, per-token
+ * gradients with respect to Q, K, Q_m and K_m (float32), the state gradients
+ * per chunk and partial sums. out_dtype is the dtype of dout. */
+size_t gecko_backward_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts);
+
+/* Gradients of L = sum(dout * O), O the output of `parts` with `flags`.
+ *   z, v, affine vectors: the forward's inputs (z, v bf16, 16-byte aligned;
+ *       the affine vectors of the parts used, 16-byte aligned).
+ *   dout: dL/dO, [B][H][n][dv] in out_dtype (bf16 or float32; float32 is
+ *       rounded to bf16, the operand precision of every product).
+ *   dz [B][H][n][d], dv_out [B][H][n][dv], daff [8][H][d] (float32, fully
+ *       overwritten): daff holds, in this order, the gradients of kappa_q,
+ *       nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k summed over the batch
+ *       (zero for the vectors of a part not selected).
+ * The outputs must not alias each other, an input or the workspace. flags:
+ * GECKO_AWM_NO_DELTA and GECKO_CHUNKWISE as in the forward. */
+gecko_status gecko_backward(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, const void* dout,
+    float* dz, float* dv_out, float* daff,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gecko_status_string(gecko_status status);
 

@@ -46,10 +46,11 @@ def _t(x):
 
 
 def forward_torch_head(z, v, p, c: int, parts=("sca", "awm"), chunkwise: bool = False,
-                       no_delta: bool = False):
+                       no_delta: bool = False, keep=None):
     """O of one head as torch float64 tensors: z [n, d], v [n, dv], p maps the
     eight names to [d] tensors. ``parts`` selects O_SCA, O_m or their sum
-    ([rainbus "Method steps" (5)], R8)."""
+    ([rainbus "Method steps" (5)], R8). If ``keep`` is a dict it receives the
+    derived Q, K, Q_m, K_m tensors (keys "q", "k", "qm", "km")."""
     n, _ = z.shape
     dv = v.shape[1]
     out = torch.zeros((n, dv), dtype=torch.float64)
@@ -58,6 +59,8 @@ def forward_torch_head(z, v, p, c: int, parts=("sca", "awm"), chunkwise: bool = 
         # [rainbus "Method steps" (2)]: Q and K by the per-feature affine maps
         q = p["kappa_q"] * z + p["nu_q"]
         k = p["kappa_k"] * z + p["nu_k"]
+        if keep is not None:
+            keep["q"], keep["k"] = q, k
         rows = []
         for a in starts:
             b = min(a + c, n)
@@ -72,6 +75,8 @@ def forward_torch_head(z, v, p, c: int, parts=("sca", "awm"), chunkwise: bool = 
         # [rainbus "Method steps" (4)-(5)], "Core method"; R1, R5-R7, R9
         qm = p["eta_q"] * z + p["rho_q"]
         km = p["eta_k"] * z + p["rho_k"]
+        if keep is not None:
+            keep["qm"], keep["km"] = qm, km
         d = z.shape[1]
         z_prev = torch.zeros(d, dtype=torch.float64)
         mem_prev = torch.zeros((d, dv), dtype=torch.float64)  # M'_{s-1}
@@ -95,18 +100,32 @@ def grad_head(z, v, p: dict, h: int, c: int, dout, parts=("sca", "awm"), chunkwi
               no_delta: bool = False) -> dict:
     """Gradients of L = sum(dout * O) for head h of one batch row.
 
-    Returns float64 numpy arrays: ``dz`` [n, d], ``dv`` [n, dv] and one [d]
-    vector per affine name ("d" + name)."""
+    Returns float64 numpy arrays: ``dz`` [n, d], ``dv`` [n, dv], one [d]
+    vector per affine name ("d" + name), and the per-token gradients with
+    respect to the derived Q, K, Q_m, K_m ("dq", "dk", "dqm", "dkm", [n, d];
+    zero for a part not selected). The affine gradients are the sums over
+    tokens of Z' times (or just) these; dz is their combination through the
+    scales."""
     zt = _t(z).requires_grad_(True)
     vt = _t(v).requires_grad_(True)
     pt = {k: _t(p[k][h]).requires_grad_(True) for k in AFFINE}
-    o = forward_torch_head(zt, vt, pt, c, parts=parts, chunkwise=chunkwise, no_delta=no_delta)
+    keep = {}
+    o = forward_torch_head(zt, vt, pt, c, parts=parts, chunkwise=chunkwise, no_delta=no_delta, keep=keep)
     loss = (o * _t(dout)).sum()
-    leaves = [zt, vt] + [pt[k] for k in AFFINE]
+    names = [k for k in ("q", "k", "qm", "km") if k in keep]
+    leaves = [zt, vt] + [pt[k] for k in AFFINE] + [keep[k] for k in names]
     grads = torch.autograd.grad(loss, leaves, allow_unused=True)
-    res = {"dz": grads[0].numpy(), "dv": grads[1].numpy()}
-    for k, gk in zip(AFFINE, grads[2:]):
+    # a part that never reaches the output (the memory of a sequence of at
+    # most lag chunks) leaves its inputs unused: their gradient is zero
+    res = {"dz": np.zeros(z.shape) if grads[0] is None else grads[0].numpy(),
+           "dv": np.zeros(v.shape) if grads[1] is None else grads[1].numpy()}
+    for k, gk in zip(AFFINE, grads[2:2 + len(AFFINE)]):
         res["d" + k] = np.zeros(z.shape[1]) if gk is None else gk.numpy()
+    for k in ("q", "k", "qm", "km"):
+        res["d" + k] = np.zeros(z.shape)
+    for k, gk in zip(names, grads[2 + len(AFFINE):]):
+        if gk is not None:
+            res["d" + k] = gk.numpy()
     return res
 
 
@@ -114,19 +133,22 @@ def grad(z, v, p: dict, c: int, dout, parts=("sca", "awm"), chunkwise: bool = Fa
          no_delta: bool = False) -> dict:
     """Whole-tensor gradients: z [B, H, n, d], v and dout [B, H, n, dv].
 
-    ``dz`` [B, H, n, d] and ``dv`` [B, H, n, dv]; each affine gradient
-    [H, d] is summed over the batch (the vectors are shared by the rows)."""
+    ``dz`` [B, H, n, d], ``dv`` [B, H, n, dv] and the per-token ``dq``,
+    ``dk``, ``dqm``, ``dkm`` [B, H, n, d]; each affine gradient [H, d] is
+    summed over the batch (the vectors are shared by the rows)."""
     B, H, n, d = z.shape
     dv = v.shape[3]
     res = {"dz": np.empty((B, H, n, d)), "dv": np.empty((B, H, n, dv))}
+    for k in ("q", "k", "qm", "km"):
+        res["d" + k] = np.empty((B, H, n, d))
     for k in AFFINE:
         res["d" + k] = np.zeros((H, d))
     for b in range(B):
         for h in range(H):
             r = grad_head(z[b, h], v[b, h], p, h, c, dout[b, h], parts=parts, chunkwise=chunkwise,
                           no_delta=no_delta)
-            res["dz"][b, h] = r["dz"]
-            res["dv"][b, h] = r["dv"]
+            for k in ("dz", "dv", "dq", "dk", "dqm", "dkm"):
+                res[k][b, h] = r[k]
             for k in AFFINE:
                 res["d" + k][h] += r["d" + k]
     return res

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gecko_version() == 101
+    assert g.gecko_version() == 102
     for s in range(5):
         assert g.gecko_status_string(s).startswith("GECKO_")
     assert "unknown" in g.gecko_status_string(99)
@@ -233,3 +233,83 @@ def test_tdn_host_checks(g):
     assert call(eps=0.0) == g.GECKO_EINVAL
     assert call(x=FAKE * 8 + 2) == g.GECKO_EINVAL
     assert call(ws=0) == g.GECKO_EWORKSPACE
+
+
+def call_bwd(g, **kw):
+    a = dict(z=FAKE, aff=[FAKE + 64 * i for i in range(8)], v=2 * FAKE, dout=5 * FAKE, dz=6 * FAKE, dv=7 * FAKE,
+             daff=8 * FAKE, B=1, H=1, n=1000, d=128, dvs=256, c=128, din=g.GECKO_BF16, dtype=g.GECKO_BF16, flags=0,
+             parts=3, ws=0, wsb=0)
+    a.update(kw)
+    st = g.lib.gecko_backward(a["z"], *a["aff"], a["v"], a["dout"], a["dz"], a["dv"], a["daff"],
+                              a["B"], a["H"], a["n"], a["d"], a["dvs"], a["c"], a["din"], a["dtype"], a["flags"],
+                              a["parts"], a["ws"], a["wsb"], None)
+    return st, g.lib.gecko_last_error().decode()
+
+
+def test_backward_host_checks(g):
+    st, msg = call_bwd(g)
+    assert st == g.GECKO_EWORKSPACE and "workspace" in msg
+    st, msg = call_bwd(g, din=g.GECKO_F32)
+    assert st == g.GECKO_EUNSUPPORTED and "bf16" in msg
+    st, msg = call_bwd(g, d=64, dvs=128)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, msg = call_bwd(g, parts=0)
+    assert st == g.GECKO_EINVAL and "parts" in msg
+    st, msg = call_bwd(g, flags=8)
+    assert st == g.GECKO_EINVAL
+    st, msg = call_bwd(g, dout=0)
+    assert st == g.GECKO_EINVAL and "non-null" in msg
+    # without the memory part its vectors may be null (the workspace is still needed)
+    st, msg = call_bwd(g, aff=[FAKE + 64 * i for i in range(4)] + [0] * 4, parts=g.GECKO_PART_SCA)
+    assert st == g.GECKO_EWORKSPACE
+    st, msg = call_bwd(g, aff=[FAKE + 64 * i for i in range(4)] + [0] * 4)
+    assert st == g.GECKO_EINVAL and "affine" in msg
+    st, msg = call_bwd(g, dz=FAKE + 8)
+    assert st == g.GECKO_EINVAL and "aligned" in msg
+    st, msg = call_bwd(g, dz=FAKE)  # dz on top of z
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call_bwd(g, dv=6 * FAKE + 4096)  # dv inside dz
+    assert st == g.GECKO_EINVAL and ("overlap" in msg or "alias" in msg)
+    st, msg = call_bwd(g, n=0)
+    assert st == g.GECKO_EINVAL
+
+
+def test_backward_workspace_size(g):
+    full = g.gecko_backward_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16)
+    sca = g.gecko_backward_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16,
+                                          parts=g.GECKO_PART_SCA)
+    awm = g.gecko_backward_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16,
+                                          parts=g.GECKO_PART_AWM)
+    rows = 8 * 131072
+    # attention: q' (bf16), row statistics, dQ and dK (fp32) per token
+    assert sca >= rows * (128 * 2 + 8 + 2 * 128 * 4)
+    # memory: dQ_m, dK_m per token plus per-chunk state gradients
+    assert awm >= rows * 2 * 128 * 4 + 8 * 62 * (128 * 256 * (4 + 2) + 2 * 128 * 128 * 2)
+    assert full >= max(sca, awm)
+    f32 = g.gecko_backward_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_F32)
+    assert f32 >= full + rows * 256 * 2  # a bf16 copy of a float32 dO
+    with pytest.raises(g.GeckoError):
+        g.gecko_backward_workspace_size(1, 1, 100, 64, 64, 32, g.GECKO_BF16, g.GECKO_BF16)
+    with pytest.raises(g.GeckoError):
+        g.gecko_backward_workspace_size(1, 1, 100, 128, 256, 32, g.GECKO_F32, g.GECKO_F32)
+
+
+def test_forward_lse_host_checks(g):
+    def call(**kw):
+        a = dict(parts=3, lse=4 * FAKE, din=g.GECKO_BF16, ws=0, wsb=0)
+        a.update(kw)
+        st = g.lib.gecko_forward_lse(FAKE, *[FAKE + 64 * i for i in range(8)], 2 * FAKE, 3 * FAKE, a["lse"], 1, 1,
+                                     1000, 128, 256, 100, a["din"], g.GECKO_BF16, 0, a["parts"], a["ws"], a["wsb"],
+                                     None)
+        return st, g.lib.gecko_last_error().decode()
+
+    st, msg = call(parts=g.GECKO_PART_AWM)
+    assert st == g.GECKO_EINVAL and "GECKO_PART_SCA" in msg
+    st, msg = call(din=g.GECKO_F32)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, msg = call(lse=0)
+    assert st == g.GECKO_EINVAL
+    st, msg = call(lse=3 * FAKE + 64)  # inside out
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call()  # the memory part needs the workspace
+    assert st == g.GECKO_EWORKSPACE

@@ -137,3 +137,19 @@ def test_lse_reproduces_attention(chunkwise):
     want = oracle.sca_head(z[0, 0], v[0, 0], p["kappa_q"][0], p["nu_q"][0], p["kappa_k"][0], p["nu_k"][0], 16,
                            sliding=not chunkwise)
     np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("parts,chunkwise,no_delta", VARIANTS)
+def test_per_token_gradients_compose(parts, chunkwise, no_delta):
+    """The per-token gradients with respect to Q, K, Q_m, K_m give back, by
+    the chain rule through the affine maps, the finite-difference-pinned dZ'
+    and affine gradients."""
+    z, v, p, dout = rand_problem(60, 8, 5, 2, seed=21, scale=1.5)
+    g = go.grad(z, v, p, 16, dout, parts=parts, chunkwise=chunkwise, no_delta=no_delta)
+    dz = (p["kappa_q"][None, :, None] * g["dq"] + p["kappa_k"][None, :, None] * g["dk"]
+          + p["eta_q"][None, :, None] * g["dqm"] + p["eta_k"][None, :, None] * g["dkm"])
+    np.testing.assert_allclose(dz, g["dz"], rtol=1e-10, atol=1e-12)
+    for scale, shift, key in (("kappa_q", "nu_q", "dq"), ("kappa_k", "nu_k", "dk"),
+                              ("eta_q", "rho_q", "dqm"), ("eta_k", "rho_k", "dkm")):
+        np.testing.assert_allclose((z * g[key]).sum(axis=(0, 2)), g["d" + scale], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g[key].sum(axis=(0, 2)), g["d" + shift], rtol=1e-10, atol=1e-12)
