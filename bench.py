@@ -147,9 +147,39 @@ def time_variants(gecko, w, z, v, params, out, stream, args) -> dict:
     res["stream_4_calls"] = {"ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3), "steps": steps,
                              "calls_per_step": 4, "tokens_per_call": q}
     del parts, outs, ws_st
+    res["backward"] = time_backward(gecko, w, z, v, params, stream, timed)
     res["cema"] = time_cema(gecko, stream, timed)
     res["tdn"] = time_tdn(gecko, stream, timed)
     return res
+
+
+def time_backward(gecko, w, z, v, params, stream, timed) -> dict:
+    """The backward of the headline layer (both parts) on its resident inputs
+    and a resident N(0, 1) bf16 dL/dO: one gecko_backward call per step (it
+    recomputes the memory scan and the attention row statistics itself). The
+    roofline counts each product of the backward once
+    (configs.backward_flop_count) against the bf16 MFMA peak."""
+    import torch
+
+    from chunked_attention_memory_amd import configs
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(91)
+    do = torch.randn((w.B, w.H, w.n, w.dv), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dz = torch.empty((w.B, w.H, w.n, w.d), dtype=torch.float32, device="cuda")
+    dvt = torch.empty((w.B, w.H, w.n, w.dv), dtype=torch.float32, device="cuda")
+    daff = torch.empty((8, w.H, w.d), dtype=torch.float32, device="cuda")
+    nbytes = gecko.gecko_backward_workspace_size(w.B, w.H, w.n, w.d, w.dv, w.c, gecko.GECKO_BF16, gecko.GECKO_BF16)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: gecko.gecko_backward(z, params, v, do, w.c, dz=dz, dv=dvt, daff=daff, workspace=ws,
+                                            stream=stream))
+    flops = configs.backward_flop_count(w.n, w.c, w.d, w.dv)["total"] * w.B * w.H
+    achieved = flops / (ms / 1e3) / 1e12
+    del do, dz, dvt, daff, ws
+    return {"workload": "bwd_" + w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.n / (ms / 1e3),
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "flops_per_call": flops},
+            "workspace_bytes": nbytes}
 
 
 def time_tdn(gecko, stream, timed) -> dict:

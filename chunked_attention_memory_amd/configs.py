@@ -72,6 +72,31 @@ def flop_count(n: int, c: int, d: int, dv: int) -> dict:
             "total": sca + write + corr + scan + read}
 
 
+def backward_flop_count(n: int, c: int, d: int, dv: int) -> dict:
+    """Multiply-add FLOPs of the backward of one head, each product counted
+    once (recomputation that an implementation chooses is not counted).
+
+    * SCA: per unmasked pair the logits q.k (2d), dP = dO.v (2dv), the dV
+      (2dv), dQ (2d) and dK (2d) contributions;
+    * memory, chunks 3..N that read the state: psi(Q)^T dO into the state
+      gradient and dO S^T into dpsi(Q) (2 c_s d dv each);
+    * the reverse scan's transposed correction product, N-3 steps of 2 d^2 dv;
+    * per chunk t entering the memory (1..N-2): Phi dS_t into dV and
+      V dS_t^T into dPhi (2 c_t d dv each); for t >= 2, X_t = dS_t S_{t-1}^T
+      (2 d^2 dv) and psi X^T, Phi X (2 c_t d^2 each).
+    """
+    sizes = chunk_sizes(n, c)
+    N = len(sizes)
+    pairs = flop_count(n, c, d, dv)["pairs"]
+    sca = 2 * (3 * d + 2 * dv) * pairs
+    read = sum(2 * 2 * sizes[s] * d * dv for s in range(2, N))
+    scan = max(N - 3, 0) * 2 * d * d * dv
+    keys = sum(2 * 2 * sizes[t] * d * dv for t in range(0, max(N - 2, 0)))
+    corr = sum(2 * d * d * dv + 2 * 2 * sizes[t] * d * d for t in range(1, max(N - 2, 0)))
+    return {"pairs": pairs, "sca": sca, "awm_read": read, "awm_scan": scan, "awm_keys": keys, "awm_corr": corr,
+            "total": sca + read + scan + keys + corr}
+
+
 def workload_flops(w: Workload) -> dict:
     per = flop_count(w.n, w.c, w.d, w.dv)
     return {k: v * w.B * w.H for k, v in per.items()}

@@ -17,16 +17,19 @@
 //
 // Kernels:
 //  * prep: q' (bf16); dO in bf16 when it comes as float32.
-//  * dq: one workgroup = 128 queries of one chunk (4 waves x 32), streaming
+//  * dq: one workgroup = 256 queries of one chunk (8 waves x 32), streaming
 //    the key window in 64-key tiles twice. Per 32-key half and wave,
 //      S^T = Z_keys q'^T, dP^T = V dO^T,
 //    then (first pass) the row statistics lse2_i and D_i = sum_j P_ij dP_ij,
 //    or (second pass) dS^T and U^T += Z_keys^T dS^T; dL/dq = kappa_k * U.
-//  * dkdv: one workgroup = 128 keys of one chunk (4 waves x 32), streaming
-//    the queries that see them (the rest of their chunk, the next chunk) in
+//  * dkdv: one workgroup = 32 keys per wave of one chunk, streaming the
+//    queries that see them (the rest of their chunk, the next chunk) in
 //    64-query tiles; per 32-query half and wave,
 //      S = q' Z_keys^T, dP = dO V^T, dV^T += dO^T P, Y^T += Z_q^T dS
-//    and dL/dk = kappa_q * Y + nu_q * colsum(dS) at the end.
+//    and dL/dk = kappa_q * Y + nu_q * colsum(dS) at the end. With dv = 256
+//    the dV and dK accumulators of one wave do not fit its registers at two
+//    waves per SIMD, so dV (S, P, dV) and dK (S, dP, dS, Y) run as two
+//    kernels of 8 waves; with dv = 128 one kernel of 4 waves does both.
 // Key (query) tiles go from HBM straight into LDS (buffer loads writing LDS),
 // two stages; all operands come from LDS through lds_row / lds_tr.
 #include <algorithm>
@@ -37,10 +40,27 @@
 namespace gecko {
 namespace {
 
-constexpr int kNW = 4;  // one wave per SIMD: the accumulators need more than half the register file
-constexpr int kThreads = 64 * kNW;
-constexpr int kBlk = 32 * kNW;  // queries (dq) or keys (dkdv) per workgroup
-constexpr int kT = 64;          // rows per staged tile
+constexpr int kT = 64;  // rows per staged tile
+
+// Waves per workgroup of the dq kernel, and the dk dv layout at dv = 256:
+// 0 one kernel for both accumulators, 4 waves of one key block; 1 separate
+// dV and dK kernels of 4 waves of GECKO_BWD_QB key blocks; 2 separate
+// kernels of 8 waves of one block. Eight waves (two per SIMD, so that one
+// wave's exponentials overlap the other's MFMAs) fit the registers only with
+// the two 32-row halves of a tile processed in a loop rather than unrolled.
+#ifndef GECKO_BWD_DQ_NW
+#define GECKO_BWD_DQ_NW 8
+#endif
+#ifndef GECKO_BWD_KV256
+#define GECKO_BWD_KV256 2
+#endif
+// 32-row blocks per wave: queries in dq, keys in the split dk dv kernels
+#ifndef GECKO_BWD_DQ_QB
+#define GECKO_BWD_DQ_QB 1
+#endif
+#ifndef GECKO_BWD_QB
+#define GECKO_BWD_QB 1
+#endif
 
 // ---------------------------------------------------------------- prep
 struct PrepArgs {
@@ -90,7 +110,7 @@ struct DqArgs {
   const uint16_t* v;
   const uint16_t* dO;
   const float* kk;
-  float* ld;   // written: (lse2, D) per query, for the dk dv kernel
+  float* ld;   // written: (lse2, D) per query, for the dk dv kernels
   float* dq;
   int64_t n;
   int c, nchunks, qtiles, H, prev;
@@ -102,90 +122,128 @@ struct RowStats {
   float m, l, a;
 };
 
-template <int D, int DV>
+// NW waves, QB 32-query blocks per wave: each K / V operand read from LDS
+// serves QB MFMAs, and a workgroup of 32 NW QB queries reuses every staged
+// key tile that many times (the staging, not the MFMAs, bounds a workgroup of
+// fewer queries).
+template <int D, int DV, int NW, int QB>
 struct DqLoop {
+  static constexpr int THREADS = 64 * NW;
   static constexpr int ZB = kT * D * 2, VB = kT * DV * 2;
   static constexpr int STAGE = ZB + VB;
-  static constexpr int ZL = ZB / 16 / kThreads, VL = VB / 16 / kThreads;
+  static constexpr int ZL = ZB / 16 / THREADS, VL = VB / 16 / THREADS;
   static constexpr int KS = D / 16, VS = DV / 16, NF = D / 32;
+  // LDS stages: three where they fit (tile k + 2 loads while tile k is
+  // computed), else two
+  static constexpr int NS = 3 * STAGE <= 160 * 1024 ? 3 : 2;
+  static constexpr int LOADS = ZL + VL;  // staging loads per lane and tile
   const uint16_t* zbh;
   const uint16_t* vbh;
-  char* sb[2];
-  int n, kbeg, ntiles, myq, wave_last, w, lane, g, lq;
-  float lse2, dd;
+  char* sb[3];
+  int n, kbeg, ntiles, wave_last, w, lane, g, lq;
+  int myq[QB];
+  float lse2[QB], dd[QB];
   uint32_t zoff[ZL], voff[VL];
-  u32x4 qf[KS], df[VS];
+  u32x4 qf[QB][KS], df[QB][VS];
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
     const int row0 = kbeg + kt * kT;
-    stage_rows(zbh, row0, n, D, sb[slot], kNW, w, zoff, ZL);
-    stage_rows(vbh, row0, n, DV, sb[slot] + ZB, kNW, w, voff, VL);
+    stage_rows(zbh, row0, n, D, sb[slot], NW, w, zoff, ZL);
+    stage_rows(vbh, row0, n, DV, sb[slot] + ZB, NW, w, voff, VL);
   }
 
-  // S^T and dP^T of one 32-key half of the tile in `slot`
-  __device__ __forceinline__ void scores(int mb, int slot, f32x16& sc, f32x16& dp) const {
+  // S^T and dP^T of one 32-key half of the tile in `slot`, every query block
+  __device__ __forceinline__ void scores(int mb, int slot, f32x16 (&sc)[QB], f32x16 (&dp)[QB]) const {
     const char* Zs = sb[slot];
     const char* Vs = sb[slot] + ZB;
     const int arow = 32 * mb + perm_row(lq);
-    sc = f32x16{};
-    dp = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = mfma_bf16(lds_row<D>(Zs, arow, 2 * ks + g), qf[ks], sc);
+    for (int qb = 0; qb < QB; ++qb) {
+      sc[qb] = f32x16{};
+      dp[qb] = f32x16{};
+    }
 #pragma unroll
-    for (int ks = 0; ks < VS; ++ks) dp = mfma_bf16(lds_row<DV>(Vs, arow, 2 * ks + g), df[ks], dp);
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = lds_row<D>(Zs, arow, 2 * ks + g);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = mfma_bf16(a, qf[qb][ks], sc[qb]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < VS; ++ks) {
+      const u32x4 a = lds_row<DV>(Vs, arow, 2 * ks + g);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) dp[qb] = mfma_bf16(a, df[qb][ks], dp[qb]);
+    }
   }
 
   // statistics pass: fold this half's visible keys into (m, l, a)
-  __device__ __forceinline__ void stats_half(int kt, int mb, int slot, RowStats& st) const {
-    f32x16 sc, dp;
+  __device__ __forceinline__ void stats_half(int kt, int mb, int slot, RowStats (&st)[QB]) const {
+    f32x16 sc[QB], dp[QB];
     scores(mb, slot, sc, dp);
     const int kb = kbeg + kt * kT + 32 * mb;
-    float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-      mx = fmaxf(mx, key <= myq ? sc[r] : kNegInf);
-    }
-    if (mx > st.m) {  // rescale to the new maximum (a first finite maximum scales 0 by 0)
-      const float f = st.m == kNegInf ? 0.f : exp2_fast(st.m - mx);
-      st.l *= f;
-      st.a *= f;
-      st.m = mx;
-    }
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-      const float e = key <= myq ? exp2_fast(sc[r] - st.m) : 0.f;
-      st.l += e;
-      st.a += e * dp[r];
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
+        mx = fmaxf(mx, key <= myq[qb] ? sc[qb][r] : kNegInf);
+      }
+      if (mx > st[qb].m) {  // rescale to the new maximum (a first finite maximum scales 0 by 0)
+        const float f = st[qb].m == kNegInf ? 0.f : exp2_fast(st[qb].m - mx);
+        st[qb].l *= f;
+        st[qb].a *= f;
+        st[qb].m = mx;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
+        const float e = key <= myq[qb] ? exp2_fast(sc[qb][r] - st[qb].m) : 0.f;
+        st[qb].l += e;
+        st[qb].a += e * dp[qb][r];
+      }
     }
   }
 
   // gradient pass: dS and U^T += Z^T dS^T for one half
-  __device__ __forceinline__ void grad_half(int kt, int mb, int slot, f32x16 (&U)[NF]) const {
-    f32x16 sc, dp;
+  __device__ __forceinline__ void grad_half(int kt, int mb, int slot, f32x16 (&U)[QB][NF]) const {
+    f32x16 sc[QB], dp[QB];
     scores(mb, slot, sc, dp);
     const char* Zs = sb[slot];
     const int kb = kbeg + kt * kT + 32 * mb;
-    float ds[16];
+    u32x4 d0[QB], d1[QB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-      const float p = key <= myq ? exp2_fast(sc[r] - lse2) : 0.f;
-      ds[r] = p * (dp[r] - dd);
+    for (int qb = 0; qb < QB; ++qb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
+        const float p = key <= myq[qb] ? exp2_fast(sc[qb][r] - lse2[qb]) : 0.f;
+        ds[r] = p * (dp[qb][r] - dd[qb]);
+      }
+      d0[qb] = pack8(ds);
+      d1[qb] = pack8(ds + 8);
     }
-    const u32x4 d0 = pack8(ds), d1 = pack8(ds + 8);
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb) {
-      U[fb] = mfma_bf16(lds_tr<D>(Zs, 32 * mb, 32 * fb, lane), d0, U[fb]);
-      U[fb] = mfma_bf16(lds_tr<D>(Zs, 32 * mb + 16, 32 * fb, lane), d1, U[fb]);
+      const u32x4 a0 = lds_tr<D>(Zs, 32 * mb, 32 * fb, lane);
+      const u32x4 a1 = lds_tr<D>(Zs, 32 * mb + 16, 32 * fb, lane);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        U[qb][fb] = mfma_bf16(a0, d0[qb], U[qb][fb]);
+        U[qb][fb] = mfma_bf16(a1, d1[qb], U[qb][fb]);
+      }
     }
   }
 
+  // Tile kt in stage SLOT: stage tile kt + NS - 1 into the stage tile kt - 1
+  // used (every wave is past it), compute, wait for this wave's share of
+  // tile kt + 1 (tile kt + 2's loads may stay in flight) and end at the barrier.
   template <int SLOT, bool kStats>
-  __device__ __forceinline__ void tile(int kt, RowStats& st, f32x16 (&U)[NF]) const {
-    if (kt + 1 < ntiles) stage(kt + 1, SLOT ^ 1);  // every wave is past tile kt - 1
-#pragma unroll
+  __device__ __forceinline__ void tile(int kt, RowStats (&st)[QB], f32x16 (&U)[QB][NF]) const {
+    const bool ahead = kt + NS - 1 < ntiles;
+    if (ahead) stage(kt + NS - 1, (SLOT + NS - 1) % NS);
+#pragma unroll 1
     for (int mb = 0; mb < 2; ++mb) {
       if (kbeg + kt * kT + 32 * mb <= wave_last) {
         if constexpr (kStats)
@@ -194,18 +252,27 @@ struct DqLoop {
           grad_half(kt, mb, SLOT, U);
       }
     }
-    wait_vmem();
+    if (NS == 3 && ahead)
+      wait_vmem_leave<LOADS>();
+    else
+      wait_vmem();
     barrier_lds();
   }
 
   template <bool kStats>
-  __device__ __forceinline__ void pass(RowStats& st, f32x16 (&U)[NF]) const {
+  __device__ __forceinline__ void pass(RowStats (&st)[QB], f32x16 (&U)[QB][NF]) const {
     stage(0, 0);
-    wait_vmem();
+    if (NS == 3 && ntiles > 1) {
+      stage(1, 1);
+      wait_vmem_leave<LOADS>();
+    } else {
+      wait_vmem();
+    }
     barrier_lds();
-    for (int kt = 0; kt < ntiles; kt += 2) {
+    for (int kt = 0; kt < ntiles; kt += NS) {
       tile<0, kStats>(kt, st, U);
       if (kt + 1 < ntiles) tile<1, kStats>(kt + 1, st, U);
+      if (NS == 3 && kt + 2 < ntiles) tile<2 % NS, kStats>(kt + 2, st, U);
     }
   }
 };
@@ -217,12 +284,14 @@ struct DqLoop {
 // forward's bf16-rounded weights, would be off by 2^-9 of dP; under a peaked
 // softmax, where dS_ii = P_ii (dP_ii - D_i) is a small difference of large
 // terms, that error exceeds dS itself.) The second pass forms dS and U.
-template <int D, int DV>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(DqArgs a) {
-  using L = DqLoop<D, DV>;
+template <int D, int DV, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
+  using L = DqLoop<D, DV, NW, QB>;
   constexpr int NF = L::NF;
+  constexpr int kBlk = 32 * NW * QB;
   __shared__ __attribute__((aligned(16))) char S0[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S1[L::STAGE];
+  __shared__ __attribute__((aligned(16))) char S2[L::NS == 3 ? L::STAGE : 16];
   const int qt = (int)(blockIdx.x % (unsigned)a.qtiles);
   const int rest = (int)(blockIdx.x / (unsigned)a.qtiles);
   const int s = rest % a.nchunks;
@@ -241,36 +310,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(DqArgs a) {
   l.lq = l.lane & 31;
   l.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   l.n = n;
-  const int wq0 = q0 + 32 * l.w;
-  l.myq = wq0 + l.lq;
-  l.wave_last = wq0 < qend ? min(wq0 + 32, qend) - 1 : -1;
+  const int wq0 = q0 + 32 * QB * l.w;
+  l.wave_last = wq0 < qend ? min(wq0 + 32 * QB, qend) - 1 : -1;
   const size_t base = (size_t)bh * (size_t)n;
   l.zbh = a.z + base * D;
   l.vbh = a.v + base * DV;
   l.sb[0] = S0;
   l.sb[1] = S1;
-  const size_t qrow = base + (size_t)min(l.myq, qend - 1);
+  l.sb[2] = S2;
 #pragma unroll
-  for (int ks = 0; ks < L::KS; ++ks) l.qf[ks] = ld16(a.qp + qrow * D + 16 * ks + 8 * l.g);
+  for (int qb = 0; qb < QB; ++qb) {
+    l.myq[qb] = wq0 + 32 * qb + l.lq;
+    const size_t qrow = base + (size_t)min(l.myq[qb], qend - 1);
 #pragma unroll
-  for (int ks = 0; ks < L::VS; ++ks) l.df[ks] = ld16(a.dO + qrow * DV + 16 * ks + 8 * l.g);
+    for (int ks = 0; ks < L::KS; ++ks) l.qf[qb][ks] = ld16(a.qp + qrow * D + 16 * ks + 8 * l.g);
+#pragma unroll
+    for (int ks = 0; ks < L::VS; ++ks) l.df[qb][ks] = ld16(a.dO + qrow * DV + 16 * ks + 8 * l.g);
+  }
   l.kbeg = (a.prev && s > 0) ? (s - 1) * c : s * c;
   l.ntiles = (qend - l.kbeg + kT - 1) / kT;
-  stage_offsets<D>(l.zoff, kNW, l.w, l.lane);
-  stage_offsets<DV>(l.voff, kNW, l.w, l.lane);
+  stage_offsets<D>(l.zoff, NW, l.w, l.lane);
+  stage_offsets<DV>(l.voff, NW, l.w, l.lane);
 
-  f32x16 U[NF];
+  f32x16 U[QB][NF];
+  RowStats st[QB];
 #pragma unroll
-  for (int fb = 0; fb < NF; ++fb) U[fb] = f32x16{};
-  RowStats st{kNegInf, 0.f, 0.f};
+  for (int qb = 0; qb < QB; ++qb) {
+    st[qb] = RowStats{kNegInf, 0.f, 0.f};
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb) U[qb][fb] = f32x16{};
+  }
   l.template pass<true>(st, U);
-  {
-    // merge the two lane halves (each saw half of every 32-key block)
-    const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);
-    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l), __float_as_uint(st.l), false, false);
-    const auto sa = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.a), __float_as_uint(st.a), false, false);
-    // each swap result holds this lane's value and the other half's, in the
-    // same order for the three; the merge is symmetric in the two
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    // merge the two lane halves (each saw half of every 32-key block); each
+    // swap result holds this lane's value and the other half's, in the same
+    // order for the three, and the merge is symmetric in the two
+    const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].m), __float_as_uint(st[qb].m), false, false);
+    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].l), __float_as_uint(st[qb].l), false, false);
+    const auto sa = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].a), __float_as_uint(st[qb].a), false, false);
     const float m0 = __uint_as_float(sm[0]), m1 = __uint_as_float(sm[1]);
     const float l0 = __uint_as_float(sl[0]), l1 = __uint_as_float(sl[1]);
     const float a0 = __uint_as_float(sa[0]), a1 = __uint_as_float(sa[1]);
@@ -279,18 +357,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(DqArgs a) {
     const float f1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - m);
     const float lt = l0 * f0 + l1 * f1, at = a0 * f0 + a1 * f1;
     const bool any = m != kNegInf && lt > 0.f;
-    l.lse2 = any ? m + log2f(lt) : 0.f;
-    l.dd = any ? at / lt : 0.f;
+    l.lse2[qb] = any ? m + log2f(lt) : 0.f;
+    l.dd[qb] = any ? at / lt : 0.f;
+    if (l.g == 0 && l.myq[qb] < qend)
+      *reinterpret_cast<float2*>(a.ld + 2 * (base + (size_t)l.myq[qb])) = make_float2(l.lse2[qb], l.dd[qb]);
   }
-  if (l.g == 0 && l.myq < qend)
-    *reinterpret_cast<float2*>(a.ld + 2 * (base + (size_t)l.myq)) = make_float2(l.lse2, l.dd);
   // every wave is past the statistics pass's last barrier: its stages are free
   l.template pass<false>(st, U);
 
-  if (l.myq < qend) {
+  const float* kk = a.kk + h * D;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (l.myq[qb] >= qend) continue;
     // register r of block fb holds feature 32 fb + 16 (r >> 3) + 8 g + (r & 7)
-    const float* kk = a.kk + h * D;
-    float* dst = a.dq + (base + (size_t)l.myq) * D;
+    float* dst = a.dq + (base + (size_t)l.myq[qb]) * D;
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
@@ -301,7 +381,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(DqArgs a) {
           const f32x4 k4 = *reinterpret_cast<const f32x4*>(kk + f + 4 * q);
           const int r = 8 * hh + 4 * q;
           *reinterpret_cast<f32x4*>(dst + f + 4 * q) =
-              f32x4{k4[0] * U[fb][r], k4[1] * U[fb][r + 1], k4[2] * U[fb][r + 2], k4[3] * U[fb][r + 3]};
+              f32x4{k4[0] * U[qb][fb][r], k4[1] * U[qb][fb][r + 1], k4[2] * U[qb][fb][r + 2],
+                    k4[3] * U[qb][fb][r + 3]};
         }
       }
   }
@@ -322,104 +403,179 @@ struct KvArgs {
   int c, nchunks, ktiles, H, prev, accum;
 };
 
-template <int D, int DV>
+// NW waves, KB 32-key blocks per wave. MODE 0: dK and dV; 1: dV only (P
+// alone, no dP); 2: dK only.
+template <int D, int DV, int NW, int KB, int MODE>
 struct KvLoop {
+  static constexpr bool kDV = MODE != 2, kDK = MODE != 1;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int QB_ = kT * D * 2, VB = kT * DV * 2, LB = 1024;
-  static constexpr int STAGE = 2 * QB_ + VB + LB;  // q' tile, z tile, dO tile, (lse2, D) of 128 rows
-  static constexpr int QL = QB_ / 16 / kThreads, VL = VB / 16 / kThreads;
+  // q' tile, z tile (dK only), dO tile, (lse2, D) of 128 rows
+  static constexpr int ZOFF = QB_, DOFF = kDK ? 2 * QB_ : QB_, LOFF = DOFF + VB;
+  static constexpr int STAGE = LOFF + LB;
+  static constexpr int QL = QB_ / 16 / THREADS, VL = VB / 16 / THREADS;
   static constexpr int KS = D / 16, VS = DV / 16, NF = D / 32, NMV = DV / 32;
+  static constexpr int NY = kDK ? NF : 1, NV = kDV ? NMV : 1;
+  static constexpr int NS = 3 * STAGE <= 160 * 1024 ? 3 : 2;
+  static constexpr int LOADS = QL * (kDK ? 2 : 1) + VL;  // staging loads per lane and tile (wave 0: one more)
   const uint16_t* qbh;
   const uint16_t* zbh;
   const uint16_t* dbh;
   const uint16_t* lbh;  // (lse2, D) pairs as 4 bf16-sized units per row
-  char* sb[2];
-  int n, ta, nb0, ntiles, j0, myk, wj0, has, w, lane, g, lq;
+  char* sb[3];
+  int n, ta, nb0, ntiles, j0, wj0, has, w, lane, g, lq;
   int own_end, next_end;  // ends of the two query ranges (a tile may reach past them)
+  int myk[KB];
   uint32_t qoff[QL], doff[VL];
-  u32x4 kf[KS], vf[VS];
+  u32x4 kf[KB][KS], vf[KB][kDK ? VS : 1];
 
   __device__ __forceinline__ int qbase(int kt) const { return kt < ta ? j0 + kt * kT : nb0 + (kt - ta) * kT; }
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
     const int row0 = qbase(kt);
-    stage_rows(qbh, row0, n, D, sb[slot], kNW, w, qoff, QL);
-    stage_rows(zbh, row0, n, D, sb[slot] + QB_, kNW, w, qoff, QL);
-    stage_rows(dbh, row0, n, DV, sb[slot] + 2 * QB_, kNW, w, doff, VL);
+    stage_rows(qbh, row0, n, D, sb[slot], NW, w, qoff, QL);
+    if constexpr (kDK) stage_rows(zbh, row0, n, D, sb[slot] + ZOFF, NW, w, qoff, QL);
+    stage_rows(dbh, row0, n, DV, sb[slot] + DOFF, NW, w, doff, VL);
     if (w == 0) {
       const uint32_t lo[1] = {(uint32_t)lane * 16u};
-      stage_rows(lbh, row0, n, 4, sb[slot] + 2 * QB_ + VB, 1, 0, lo, 1);
+      stage_rows(lbh, row0, n, 4, sb[slot] + LOFF, 1, 0, lo, 1);
     }
   }
 
-  // one 32-query half of the tile in `slot`
-  __device__ __forceinline__ void half(int kt, int mq, int slot, f32x16 (&Y)[NF], f32x16 (&dV)[NMV],
-                                       float& sig) const {
+  // one 32-query half of the tile in `slot`, every key block
+  __device__ __forceinline__ void half(int kt, int mq, int slot, f32x16 (&Y)[KB][NY], f32x16 (&dV)[KB][NV],
+                                       float (&sig)[KB]) const {
     const char* Qs = sb[slot];
-    const char* Zq = sb[slot] + QB_;
-    const char* Ds = sb[slot] + 2 * QB_;
-    const float* Ls = reinterpret_cast<const float*>(sb[slot] + 2 * QB_ + VB);
+    const char* Zq = sb[slot] + ZOFF;
+    const char* Ds = sb[slot] + DOFF;
+    const float* Ls = reinterpret_cast<const float*>(sb[slot] + LOFF);
     const bool own = kt < ta;
     const int qb = qbase(kt) + 32 * mq;
     const int arow = 32 * mq + perm_row(lq);
-    f32x16 sc = f32x16{}, dp = f32x16{};
+    f32x16 sc[KB], dp[KB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = mfma_bf16(lds_row<D>(Qs, arow, 2 * ks + g), kf[ks], sc);
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
 #pragma unroll
-    for (int ks = 0; ks < VS; ++ks) dp = mfma_bf16(lds_row<DV>(Ds, arow, 2 * ks + g), vf[ks], dp);
-    u32x4 pk[2], dk[2];
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = lds_row<D>(Qs, arow, 2 * ks + g);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sc[kb] = mfma_bf16(a, kf[kb][ks], sc[kb]);
+    }
+    if constexpr (kDK) {
+#pragma unroll
+      for (int ks = 0; ks < VS; ++ks) {
+        const u32x4 a = lds_row<DV>(Ds, arow, 2 * ks + g);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dp[kb] = mfma_bf16(a, vf[kb][ks], dp[kb]);
+      }
+    }
+    u32x4 pk[KB][2], dk[KB][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       // queries 32 mq + 16 hh + 8 g + [0, 8): (lse2, D) pairs, 64 bytes
       const float* lp = Ls + 2 * (32 * mq + 16 * hh + 8 * g);
-      float p[8], ds[8];
+      float2 st[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * hh + j;
-        const int q = qb + 16 * hh + 8 * g + j;
-        const float2 st = *reinterpret_cast<const float2*>(lp + 2 * j);
-        const bool vis = own ? (q < own_end && q >= myk) : q < next_end;
-        p[j] = vis ? exp2_fast(sc[r] - st.x) : 0.f;
-        ds[j] = p[j] * (dp[r] - st.y);
+      for (int j = 0; j < 8; ++j) st[j] = *reinterpret_cast<const float2*>(lp + 2 * j);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float p[8], ds[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * hh + j;
+          const int q = qb + 16 * hh + 8 * g + j;
+          const bool vis = own ? (q < own_end && q >= myk[kb]) : q < next_end;
+          p[j] = vis ? exp2_fast(sc[kb][r] - st[j].x) : 0.f;
+          ds[j] = p[j] * (dp[kb][r] - st[j].y);
+        }
+        pk[kb][hh] = pack8(p);
+        dk[kb][hh] = pack8(ds);
       }
-      pk[hh] = pack8(p);
-      dk[hh] = pack8(ds);
     }
-    const u32x4 p0 = pk[0], p1 = pk[1], d0 = dk[0], d1 = dk[1];
+    if constexpr (kDV) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sig = sum2_bf16(d0[i], sum2_bf16(d1[i], sig));
+      for (int mv = 0; mv < NMV; ++mv) {
+        const u32x4 a0 = lds_tr<DV>(Ds, 32 * mq, 32 * mv, lane);
+        const u32x4 a1 = lds_tr<DV>(Ds, 32 * mq + 16, 32 * mv, lane);
 #pragma unroll
-    for (int mv = 0; mv < NMV; ++mv) {
-      dV[mv] = mfma_bf16(lds_tr<DV>(Ds, 32 * mq, 32 * mv, lane), p0, dV[mv]);
-      dV[mv] = mfma_bf16(lds_tr<DV>(Ds, 32 * mq + 16, 32 * mv, lane), p1, dV[mv]);
+        for (int kb = 0; kb < KB; ++kb) {
+          dV[kb][mv] = mfma_bf16(a0, pk[kb][0], dV[kb][mv]);
+          dV[kb][mv] = mfma_bf16(a1, pk[kb][1], dV[kb][mv]);
+        }
+      }
     }
+    if constexpr (kDK) {
 #pragma unroll
-    for (int fb = 0; fb < NF; ++fb) {
-      Y[fb] = mfma_bf16(lds_tr<D>(Zq, 32 * mq, 32 * fb, lane), d0, Y[fb]);
-      Y[fb] = mfma_bf16(lds_tr<D>(Zq, 32 * mq + 16, 32 * fb, lane), d1, Y[fb]);
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sig[kb] = sum2_bf16(dk[kb][0][i], sum2_bf16(dk[kb][1][i], sig[kb]));
+#pragma unroll
+      for (int fb = 0; fb < NF; ++fb) {
+        const u32x4 a0 = lds_tr<D>(Zq, 32 * mq, 32 * fb, lane);
+        const u32x4 a1 = lds_tr<D>(Zq, 32 * mq + 16, 32 * fb, lane);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          Y[kb][fb] = mfma_bf16(a0, dk[kb][0], Y[kb][fb]);
+          Y[kb][fb] = mfma_bf16(a1, dk[kb][1], Y[kb][fb]);
+        }
+      }
     }
   }
 
+  // wait until only the newest tile's loads may be in flight
+  __device__ __forceinline__ void wait_all_but_one_tile() const {
+    if (w == 0)
+      wait_vmem_leave<LOADS + 1>();
+    else
+      wait_vmem_leave<LOADS>();
+  }
+
   template <int SLOT>
-  __device__ __forceinline__ void tile(int kt, f32x16 (&Y)[NF], f32x16 (&dV)[NMV], float& sig) const {
-    if (kt + 1 < ntiles) stage(kt + 1, SLOT ^ 1);
+  __device__ __forceinline__ void tile(int kt, f32x16 (&Y)[KB][NY], f32x16 (&dV)[KB][NV], float (&sig)[KB]) const {
+    const bool ahead = kt + NS - 1 < ntiles;
+    if (ahead) stage(kt + NS - 1, (SLOT + NS - 1) % NS);
     const int qb0 = qbase(kt);
-#pragma unroll
+#pragma unroll 1
     for (int mq = 0; mq < 2; ++mq) {
       const int qb = qb0 + 32 * mq;
       // skip halves past the sequence, or (own chunk) wholly before the wave's keys
       if (has && qb < n && !(kt < ta && qb + 31 < wj0)) half(kt, mq, SLOT, Y, dV, sig);
     }
-    wait_vmem();
+    if (NS == 3 && ahead)
+      wait_all_but_one_tile();
+    else
+      wait_vmem();
     barrier_lds();
+  }
+
+  __device__ __forceinline__ void run(f32x16 (&Y)[KB][NY], f32x16 (&dV)[KB][NV], float (&sig)[KB]) const {
+    stage(0, 0);
+    if (NS == 3 && ntiles > 1) {
+      stage(1, 1);
+      wait_all_but_one_tile();
+    } else {
+      wait_vmem();
+    }
+    barrier_lds();
+    for (int kt = 0; kt < ntiles; kt += NS) {
+      tile<0>(kt, Y, dV, sig);
+      if (kt + 1 < ntiles) tile<1>(kt + 1, Y, dV, sig);
+      if (NS == 3 && kt + 2 < ntiles) tile<2 % NS>(kt + 2, Y, dV, sig);
+    }
   }
 };
 
-template <int D, int DV>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(KvArgs a) {
-  using L = KvLoop<D, DV>;
-  constexpr int NF = L::NF, NMV = L::NMV;
+template <int D, int DV, int NW, int KB, int MODE>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(KvArgs a) {
+  using L = KvLoop<D, DV, NW, KB, MODE>;
+  constexpr int NF = L::NF, NMV = L::NMV, NY = L::NY, NV = L::NV;
+  constexpr int kBlk = 32 * NW * KB;
   __shared__ __attribute__((aligned(16))) char S0[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S1[L::STAGE];
+  __shared__ __attribute__((aligned(16))) char S2[L::NS == 3 ? L::STAGE : 16];
   const int kt_ = (int)(blockIdx.x % (unsigned)a.ktiles);
   const int rest = (int)(blockIdx.x / (unsigned)a.ktiles);
   const int s = rest % a.nchunks;
@@ -439,8 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(KvArgs a) {
   l.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   l.n = n;
   l.j0 = j0;
-  l.wj0 = j0 + 32 * l.w;
-  l.myk = l.wj0 + l.lq;
+  l.wj0 = j0 + 32 * KB * l.w;
   l.has = l.wj0 < jend;
   const size_t base = (size_t)bh * (size_t)n;
   l.qbh = a.qp + base * D;
@@ -449,11 +604,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(KvArgs a) {
   l.lbh = reinterpret_cast<const uint16_t*>(a.ld + 2 * base);
   l.sb[0] = S0;
   l.sb[1] = S1;
-  const size_t krow = base + (size_t)min(l.myk, jend - 1);
+  l.sb[2] = S2;
 #pragma unroll
-  for (int ks = 0; ks < L::KS; ++ks) l.kf[ks] = ld16(a.z + krow * D + 16 * ks + 8 * l.g);
+  for (int kb = 0; kb < KB; ++kb) {
+    l.myk[kb] = l.wj0 + 32 * kb + l.lq;
+    const size_t krow = base + (size_t)min(l.myk[kb], jend - 1);
 #pragma unroll
-  for (int ks = 0; ks < L::VS; ++ks) l.vf[ks] = ld16(a.v + krow * DV + 16 * ks + 8 * l.g);
+    for (int ks = 0; ks < L::KS; ++ks) l.kf[kb][ks] = ld16(a.z + krow * D + 16 * ks + 8 * l.g);
+    if constexpr (L::kDK) {
+#pragma unroll
+      for (int ks = 0; ks < L::VS; ++ks) l.vf[kb][ks] = ld16(a.v + krow * DV + 16 * ks + 8 * l.g);
+    }
+  }
   // queries that see these keys: the rest of chunk s, then all of chunk s + 1
   l.ta = (cend - j0 + kT - 1) / kT;
   l.nb0 = (s + 1) * c;
@@ -461,59 +623,64 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(KvArgs a) {
   l.own_end = cend;
   l.next_end = l.nb0 + nbq;
   l.ntiles = l.ta + (nbq + kT - 1) / kT;
-  stage_offsets<D>(l.qoff, kNW, l.w, l.lane);
-  stage_offsets<DV>(l.doff, kNW, l.w, l.lane);
+  stage_offsets<D>(l.qoff, NW, l.w, l.lane);
+  stage_offsets<DV>(l.doff, NW, l.w, l.lane);
 
-  f32x16 Y[NF], dV[NMV];
+  f32x16 Y[KB][NY], dV[KB][NV];
+  float sig[KB];
 #pragma unroll
-  for (int fb = 0; fb < NF; ++fb) Y[fb] = f32x16{};
+  for (int kb = 0; kb < KB; ++kb) {
+    sig[kb] = 0.f;
 #pragma unroll
-  for (int mv = 0; mv < NMV; ++mv) dV[mv] = f32x16{};
-  float sig = 0.f;
-  l.stage(0, 0);
-  wait_vmem();
-  barrier_lds();
-  for (int kt = 0; kt < l.ntiles; kt += 2) {
-    l.template tile<0>(kt, Y, dV, sig);
-    if (kt + 1 < l.ntiles) l.template tile<1>(kt + 1, Y, dV, sig);
+    for (int fb = 0; fb < NY; ++fb) Y[kb][fb] = f32x16{};
+#pragma unroll
+    for (int mv = 0; mv < NV; ++mv) dV[kb][mv] = f32x16{};
   }
-  sig = other_half_sum(sig);
+  l.run(Y, dV, sig);
 
-  if (l.myk < jend) {
-    const float* kq = a.kq + h * D;
-    const float* nq = a.nq + h * D;
-    float* dk = a.dk + (base + (size_t)l.myk) * D;
+  const float* kq = a.kq + h * D;
+  const float* nq = a.nq + h * D;
 #pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
+  for (int kb = 0; kb < KB; ++kb) {
+    const float sg = other_half_sum(sig[kb]);
+    const int myk = l.myk[kb];
+    if (myk >= jend) continue;
+    if constexpr (L::kDK) {
+      float* dk = a.dk + (base + (size_t)myk) * D;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int f = 32 * fb + 16 * hh + 8 * l.g;
+      for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const f32x4 k4 = *reinterpret_cast<const f32x4*>(kq + f + 4 * q);
-          const f32x4 n4 = *reinterpret_cast<const f32x4*>(nq + f + 4 * q);
-          const int r = 8 * hh + 4 * q;
-          f32x4 o;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int f = 32 * fb + 16 * hh + 8 * l.g;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = k4[i] * Y[fb][r + i] + n4[i] * sig;
-          *reinterpret_cast<f32x4*>(dk + f + 4 * q) = o;
+          for (int q = 0; q < 2; ++q) {
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(kq + f + 4 * q);
+            const f32x4 n4 = *reinterpret_cast<const f32x4*>(nq + f + 4 * q);
+            const int r = 8 * hh + 4 * q;
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = k4[i] * Y[kb][fb][r + i] + n4[i] * sg;
+            *reinterpret_cast<f32x4*>(dk + f + 4 * q) = o;
+          }
         }
-      }
-    float* dv = a.dv + (base + (size_t)l.myk) * DV;
+    }
+    if constexpr (L::kDV) {
+      float* dv = a.dv + (base + (size_t)myk) * DV;
 #pragma unroll
-    for (int mv = 0; mv < NMV; ++mv)
+      for (int mv = 0; mv < NMV; ++mv)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int col = 32 * mv + 16 * hh + 8 * l.g;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int col = 32 * mv + 16 * hh + 8 * l.g;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int r = 8 * hh + 4 * q;
-          f32x4 o{dV[mv][r], dV[mv][r + 1], dV[mv][r + 2], dV[mv][r + 3]};
-          f32x4* p = reinterpret_cast<f32x4*>(dv + col + 4 * q);
-          if (a.accum) o += *p;
-          *p = o;
+          for (int q = 0; q < 2; ++q) {
+            const int r = 8 * hh + 4 * q;
+            f32x4 o{dV[kb][mv][r], dV[kb][mv][r + 1], dV[kb][mv][r + 2], dV[kb][mv][r + 3]};
+            f32x4* p = reinterpret_cast<f32x4*>(dv + col + 4 * q);
+            if (a.accum) o += *p;
+            *p = o;
+          }
         }
-      }
+    }
   }
 }
 
@@ -545,6 +712,7 @@ hipError_t launch_bwd_dout16(const BwdProblem& p, const BwdWorkspace& w, hipStre
 }
 
 hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s) {
+  constexpr int NW = GECKO_BWD_DQ_NW, QB = GECKO_BWD_DQ_QB;
   DqArgs a;
   a.qp = w.qp;
   a.z = static_cast<const uint16_t*>(p.f.z);
@@ -554,12 +722,21 @@ hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t
   a.n = p.f.n;
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
   a.c = (int)cc; a.nchunks = (int)p.f.nchunks; a.H = (int)p.f.H; a.prev = (int)p.f.prev;
-  a.qtiles = (int)((cc + kBlk - 1) / kBlk);
+  a.qtiles = (int)((cc + 32 * NW * QB - 1) / (32 * NW * QB));
   const dim3 grid((unsigned)(p.f.B * p.f.H * p.f.nchunks * a.qtiles));
   if (p.f.dv == 256)
-    hipLaunchKernelGGL((bwd_dq_kernel<128, 256>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 256, NW, QB>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<128, 128>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 128, NW, QB>), grid, dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DV, int NW, int KB, int MODE>
+hipError_t launch_kv(KvArgs a, const BwdProblem& p, hipStream_t s) {
+  const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
+  a.ktiles = (int)((cc + 32 * NW * KB - 1) / (32 * NW * KB));
+  const dim3 grid((unsigned)(p.f.B * p.f.H * p.f.nchunks * a.ktiles));
+  hipLaunchKernelGGL((bwd_dkdv_kernel<128, DV, NW, KB, MODE>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -573,14 +750,19 @@ hipError_t launch_bwd_dkdv(const BwdProblem& p, const BwdWorkspace& w, bool accu
   a.n = p.f.n;
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
   a.c = (int)cc; a.nchunks = (int)p.f.nchunks; a.H = (int)p.f.H; a.prev = (int)p.f.prev;
-  a.ktiles = (int)((cc + kBlk - 1) / kBlk);
   a.accum = accumulate_dv ? 1 : 0;
-  const dim3 grid((unsigned)(p.f.B * p.f.H * p.f.nchunks * a.ktiles));
-  if (p.f.dv == 256)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 256>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 128>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  a.ktiles = 0;
+  if (p.f.dv == 128) return launch_kv<128, 4, 1, 0>(a, p, s);
+#if GECKO_BWD_KV256 == 0
+  return launch_kv<256, 4, 1, 0>(a, p, s);
+#else
+  // dv = 256: the dV and dK accumulators of the wave's key blocks together
+  // exceed the register file, so dV and dK run as two kernels
+  constexpr int NW = GECKO_BWD_KV256 == 2 ? 8 : 4, KB = GECKO_BWD_KV256 == 2 ? 1 : GECKO_BWD_QB;
+  hipError_t e = launch_kv<256, NW, KB, 1>(a, p, s);
+  if (e != hipSuccess) return e;
+  return launch_kv<256, NW, KB, 2>(a, p, s);
+#endif
 }
 
 }  // namespace gecko
