@@ -53,6 +53,50 @@ __device__ __forceinline__ u32x4 lds_tr(const char* t, int r0, int col0, int lan
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// The same reads with the lane-dependent part of the address computed once.
+// For a block of rows starting at a multiple of 16, sw16 of a row depends on
+// the lane only, and the swizzle splits into a constant XOR on the high chunk
+// bits and a fixed low part, so a read costs one XOR and one add.
+//
+// RowReader: lds_row(t, row0 + perm_row(l & 31), 2 ks + g) for row0 = 0 mod 16.
+template <int W>
+struct RowReader {
+  int base;  // perm_row(lq) W 2 + 16 ((g ^ sw) & 1)
+  int swh;   // sw16(perm_row(lq)) & 14
+  __device__ __forceinline__ void init(int lane) {
+    const int r = perm_row(lane & 31), g = lane >> 5, sw = sw16(r);
+    base = r * (W * 2) + 16 * ((g ^ sw) & 1);
+    swh = sw & 14;
+  }
+  __device__ __forceinline__ u32x4 read(const char* t, int row0, int ks) const {
+    return *reinterpret_cast<const u32x4*>(t + row0 * (W * 2) + base + 16 * ((2 * ks) ^ swh));
+  }
+};
+
+// TrReader: lds_tr<W, kPerm>(t, r0, 32 blk, lane) for r0 = 0 mod 16.
+template <int W, bool kPerm = true>
+struct TrReader {
+  int base0, base1;  // rows 8 g + s / 4 (+ 4): row offset, low chunk bits, byte within the chunk
+  int swh0, swh1;    // high chunk bits of the two rows' swizzles
+  __device__ __forceinline__ void init(int lane) {
+    const int s = lane & 15, grp = (lane >> 4) & 1, g = lane >> 5, a = s & 3;
+    const int p2 = kPerm ? (((a & 1) << 1) | (a >> 1)) : a;
+    const int cl = 2 * grp + (p2 >> 1), eoff = 8 * (p2 & 1);
+    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
+    const int sw0 = sw16(r0), sw1 = sw16(r1);
+    base0 = r0 * (W * 2) + 16 * (cl ^ (sw0 & 3)) + eoff;
+    base1 = r1 * (W * 2) + 16 * (cl ^ (sw1 & 3)) + eoff;
+    swh0 = sw0 & 12;
+    swh1 = sw1 & 12;
+  }
+  __device__ __forceinline__ u32x4 read(const char* t, int r0, int blk) const {
+    const char* p = t + r0 * (W * 2);
+    const u32x2 lo = lds_read_tr(p + base0 + 16 * ((4 * blk) ^ swh0));
+    const u32x2 hi = lds_read_tr(p + base1 + 16 * ((4 * blk) ^ swh1));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
 // Source byte offsets for stage_rows: LDS chunk P = (nw i + w) 64 + lane of
 // load i is physical chunk P % (W / 8) of tile row P / (W / 8), which holds
 // logical chunk (P % (W / 8)) ^ sw16(row).

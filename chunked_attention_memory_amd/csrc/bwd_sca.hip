@@ -54,6 +54,30 @@ constexpr int kT = 64;  // rows per staged tile
 #ifndef GECKO_BWD_KV256
 #define GECKO_BWD_KV256 2
 #endif
+// Operand reads from LDS run GECKO_BWD_AHEAD MFMAs ahead of their use;
+// GECKO_BWD_SCHED pins that interleave with scheduling group barriers.
+#ifndef GECKO_BWD_SCHED
+#define GECKO_BWD_SCHED 1
+#endif
+#ifndef GECKO_BWD_AHEAD
+#define GECKO_BWD_AHEAD 2
+#endif
+
+// Pin `n` MFMAs each preceded by `per` LDS reads, after `ahead` leading
+// reads (the chains below read their operands that far ahead).
+template <int N, int PER, int AH, int MF>
+__device__ __forceinline__ void sched_chain() {
+#if GECKO_BWD_SCHED
+  __builtin_amdgcn_sched_group_barrier(0x100, PER * AH, 0);
+#pragma unroll
+  for (int i = 0; i < N - AH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MF * AH, 0);
+#endif
+}
+
 // 32-row blocks per wave: queries in dq, keys in the split dk dv kernels
 #ifndef GECKO_BWD_DQ_QB
 #define GECKO_BWD_DQ_QB 1
@@ -140,11 +164,14 @@ struct DqLoop {
   const uint16_t* zbh;
   const uint16_t* vbh;
   char* sb[3];
-  int n, kbeg, ntiles, wave_last, w, lane, g, lq;
+  int n, kbeg, ntiles, wave_first, wave_last, w, lane, g, lq;
   int myq[QB];
   float lse2[QB], dd[QB];
   uint32_t zoff[ZL], voff[VL];
   u32x4 qf[QB][KS], df[QB][VS];
+  RowReader<D> zr;
+  RowReader<DV> vr;
+  TrReader<D> zt;
 
   __device__ __forceinline__ void stage(int kt, int slot) const {
     const int row0 = kbeg + kt * kT;
@@ -156,33 +183,62 @@ struct DqLoop {
   __device__ __forceinline__ void scores(int mb, int slot, f32x16 (&sc)[QB], f32x16 (&dp)[QB]) const {
     const char* Zs = sb[slot];
     const char* Vs = sb[slot] + ZB;
-    const int arow = 32 * mb + perm_row(lq);
+    const int row0 = 32 * mb;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       sc[qb] = f32x16{};
       dp[qb] = f32x16{};
     }
+    // one stream of KS K-row and VS V-row operands, read AH ahead
+    constexpr int NI = KS + VS, AH = GECKO_BWD_AHEAD;
+    u32x4 op[AH + 1];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 a = lds_row<D>(Zs, arow, 2 * ks + g);
+    for (int i = 0; i < AH; ++i) op[i] = i < KS ? zr.read(Zs, row0, i) : vr.read(Vs, row0, i - KS);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = mfma_bf16(a, qf[qb][ks], sc[qb]);
+    for (int i = 0; i < NI; ++i) {
+      const int j = i + AH;
+      if (j < NI) op[j % (AH + 1)] = j < KS ? zr.read(Zs, row0, j) : vr.read(Vs, row0, j - KS);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (i < KS)
+          sc[qb] = mfma_bf16(op[i % (AH + 1)], qf[qb][i], sc[qb]);
+        else
+          dp[qb] = mfma_bf16(op[i % (AH + 1)], df[qb][i - KS], dp[qb]);
+      }
     }
-#pragma unroll
-    for (int ks = 0; ks < VS; ++ks) {
-      const u32x4 a = lds_row<DV>(Vs, arow, 2 * ks + g);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) dp[qb] = mfma_bf16(a, df[qb][ks], dp[qb]);
-    }
+    sched_chain<NI, 1, AH, QB>();
   }
+
+  // whether every key of the half at kb is visible to every query of the
+  // wave (its last key at or before the wave's first query): no mask
+  __device__ __forceinline__ bool all_visible(int kb) const { return kb + 31 <= wave_first; }
 
   // statistics pass: fold this half's visible keys into (m, l, a)
   __device__ __forceinline__ void stats_half(int kt, int mb, int slot, RowStats (&st)[QB]) const {
     f32x16 sc[QB], dp[QB];
     scores(mb, slot, sc, dp);
     const int kb = kbeg + kt * kT + 32 * mb;
+    const bool full = all_visible(kb);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      if (full) {
+        float mx = sc[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qb][r]);
+        if (mx > st[qb].m) {
+          const float f = st[qb].m == kNegInf ? 0.f : exp2_fast(st[qb].m - mx);
+          st[qb].l *= f;
+          st[qb].a *= f;
+          st[qb].m = mx;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_fast(sc[qb][r] - st[qb].m);
+          st[qb].l += e;
+          st[qb].a += e * dp[qb][r];
+        }
+        continue;
+      }
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -211,29 +267,39 @@ struct DqLoop {
     scores(mb, slot, sc, dp);
     const char* Zs = sb[slot];
     const int kb = kbeg + kt * kT + 32 * mb;
+    const bool full = all_visible(kb);
     u32x4 d0[QB], d1[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float ds[16];
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-        const float p = key <= myq[qb] ? exp2_fast(sc[qb][r] - lse2[qb]) : 0.f;
-        ds[r] = p * (dp[qb][r] - dd[qb]);
+        for (int r = 0; r < 16; ++r) ds[r] = exp2_fast(sc[qb][r] - lse2[qb]) * (dp[qb][r] - dd[qb]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
+          const float p = key <= myq[qb] ? exp2_fast(sc[qb][r] - lse2[qb]) : 0.f;
+          ds[r] = p * (dp[qb][r] - dd[qb]);
+        }
       }
       d0[qb] = pack8(ds);
       d1[qb] = pack8(ds + 8);
     }
+    // operand i = (fb, k-half) of Z^T, read AH ahead
+    constexpr int NI = 2 * NF, AH = GECKO_BWD_AHEAD;
+    u32x4 op[AH + 1];
 #pragma unroll
-    for (int fb = 0; fb < NF; ++fb) {
-      const u32x4 a0 = lds_tr<D>(Zs, 32 * mb, 32 * fb, lane);
-      const u32x4 a1 = lds_tr<D>(Zs, 32 * mb + 16, 32 * fb, lane);
+    for (int i = 0; i < AH; ++i) op[i] = zt.read(Zs, 32 * mb + 16 * (i & 1), i >> 1);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        U[qb][fb] = mfma_bf16(a0, d0[qb], U[qb][fb]);
-        U[qb][fb] = mfma_bf16(a1, d1[qb], U[qb][fb]);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int j = i + AH;
+      if (j < NI) op[j % (AH + 1)] = zt.read(Zs, 32 * mb + 16 * (j & 1), j >> 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        U[qb][i >> 1] = mfma_bf16(op[i % (AH + 1)], (i & 1) ? d1[qb] : d0[qb], U[qb][i >> 1]);
     }
+    sched_chain<NI, 2, AH, QB>();
   }
 
   // Tile kt in stage SLOT: stage tile kt + NS - 1 into the stage tile kt - 1
@@ -311,6 +377,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
   l.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   l.n = n;
   const int wq0 = q0 + 32 * QB * l.w;
+  l.wave_first = wq0;
   l.wave_last = wq0 < qend ? min(wq0 + 32 * QB, qend) - 1 : -1;
   const size_t base = (size_t)bh * (size_t)n;
   l.zbh = a.z + base * D;
@@ -331,6 +398,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
   l.ntiles = (qend - l.kbeg + kT - 1) / kT;
   stage_offsets<D>(l.zoff, NW, l.w, l.lane);
   stage_offsets<DV>(l.voff, NW, l.w, l.lane);
+  l.zr.init(l.lane);
+  l.vr.init(l.lane);
+  l.zt.init(l.lane);
 
   f32x16 U[QB][NF];
   RowStats st[QB];
@@ -428,6 +498,10 @@ struct KvLoop {
   int myk[KB];
   uint32_t qoff[QL], doff[VL];
   u32x4 kf[KB][KS], vf[KB][kDK ? VS : 1];
+  RowReader<D> qr;
+  RowReader<DV> dr;
+  TrReader<DV> dt;
+  TrReader<D> zt;
 
   __device__ __forceinline__ int qbase(int kt) const { return kt < ta ? j0 + kt * kT : nb0 + (kt - ta) * kT; }
 
@@ -451,27 +525,36 @@ struct KvLoop {
     const float* Ls = reinterpret_cast<const float*>(sb[slot] + LOFF);
     const bool own = kt < ta;
     const int qb = qbase(kt) + 32 * mq;
-    const int arow = 32 * mq + perm_row(lq);
+    const int row0 = 32 * mq;
     f32x16 sc[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       sc[kb] = f32x16{};
       dp[kb] = f32x16{};
     }
+    {
+      // one stream of KS q'-row and (dK) VS dO-row operands, read AH ahead
+      constexpr int NI = KS + (kDK ? VS : 0), AH = GECKO_BWD_AHEAD;
+      u32x4 op[AH + 1];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 a = lds_row<D>(Qs, arow, 2 * ks + g);
+      for (int i = 0; i < AH; ++i) op[i] = i < KS ? qr.read(Qs, row0, i) : dr.read(Ds, row0, i - KS);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sc[kb] = mfma_bf16(a, kf[kb][ks], sc[kb]);
-    }
-    if constexpr (kDK) {
+      for (int i = 0; i < NI; ++i) {
+        const int j = i + AH;
+        if (j < NI) op[j % (AH + 1)] = j < KS ? qr.read(Qs, row0, j) : dr.read(Ds, row0, j - KS);
 #pragma unroll
-      for (int ks = 0; ks < VS; ++ks) {
-        const u32x4 a = lds_row<DV>(Ds, arow, 2 * ks + g);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dp[kb] = mfma_bf16(a, vf[kb][ks], dp[kb]);
+        for (int kb = 0; kb < KB; ++kb) {
+          if (i < KS)
+            sc[kb] = mfma_bf16(op[i % (AH + 1)], kf[kb][i], sc[kb]);
+          else if constexpr (kDK)
+            dp[kb] = mfma_bf16(op[i % (AH + 1)], vf[kb][i - KS], dp[kb]);
+        }
       }
+      sched_chain<NI, 1, AH, KB>();
     }
+    // no mask when every query of the half sees every key of the wave:
+    // the half lies inside its range and (own chunk) after the wave's keys
+    const bool full = own ? (qb >= wj0 + 32 * KB - 1 && qb + 31 < own_end) : qb + 31 < next_end;
     u32x4 pk[KB][2], dk[KB][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -483,45 +566,59 @@ struct KvLoop {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float p[8], ds[8];
+        if (full) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * hh + j;
-          const int q = qb + 16 * hh + 8 * g + j;
-          const bool vis = own ? (q < own_end && q >= myk[kb]) : q < next_end;
-          p[j] = vis ? exp2_fast(sc[kb][r] - st[j].x) : 0.f;
-          ds[j] = p[j] * (dp[kb][r] - st[j].y);
+          for (int j = 0; j < 8; ++j) {
+            p[j] = exp2_fast(sc[kb][8 * hh + j] - st[j].x);
+            ds[j] = p[j] * (dp[kb][8 * hh + j] - st[j].y);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * hh + j;
+            const int q = qb + 16 * hh + 8 * g + j;
+            const bool vis = own ? (q < own_end && q >= myk[kb]) : q < next_end;
+            p[j] = vis ? exp2_fast(sc[kb][r] - st[j].x) : 0.f;
+            ds[j] = p[j] * (dp[kb][r] - st[j].y);
+          }
         }
         pk[kb][hh] = pack8(p);
         dk[kb][hh] = pack8(ds);
       }
     }
     if constexpr (kDV) {
+      // operand i = (mv, k-half) of dO^T, read AH ahead
+      constexpr int NI = 2 * NMV, AH = GECKO_BWD_AHEAD;
+      u32x4 op[AH + 1];
 #pragma unroll
-      for (int mv = 0; mv < NMV; ++mv) {
-        const u32x4 a0 = lds_tr<DV>(Ds, 32 * mq, 32 * mv, lane);
-        const u32x4 a1 = lds_tr<DV>(Ds, 32 * mq + 16, 32 * mv, lane);
+      for (int i = 0; i < AH; ++i) op[i] = dt.read(Ds, 32 * mq + 16 * (i & 1), i >> 1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          dV[kb][mv] = mfma_bf16(a0, pk[kb][0], dV[kb][mv]);
-          dV[kb][mv] = mfma_bf16(a1, pk[kb][1], dV[kb][mv]);
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int j = i + AH;
+        if (j < NI) op[j % (AH + 1)] = dt.read(Ds, 32 * mq + 16 * (j & 1), j >> 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dV[kb][i >> 1] = mfma_bf16(op[i % (AH + 1)], pk[kb][i & 1], dV[kb][i >> 1]);
       }
+      sched_chain<NI, 2, AH, KB>();
     }
     if constexpr (kDK) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sig[kb] = sum2_bf16(dk[kb][0][i], sum2_bf16(dk[kb][1][i], sig[kb]));
+      // operand i = (fb, k-half) of Z_q^T, read AH ahead
+      constexpr int NI = 2 * NF, AH = GECKO_BWD_AHEAD;
+      u32x4 op[AH + 1];
 #pragma unroll
-      for (int fb = 0; fb < NF; ++fb) {
-        const u32x4 a0 = lds_tr<D>(Zq, 32 * mq, 32 * fb, lane);
-        const u32x4 a1 = lds_tr<D>(Zq, 32 * mq + 16, 32 * fb, lane);
+      for (int i = 0; i < AH; ++i) op[i] = zt.read(Zq, 32 * mq + 16 * (i & 1), i >> 1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          Y[kb][fb] = mfma_bf16(a0, dk[kb][0], Y[kb][fb]);
-          Y[kb][fb] = mfma_bf16(a1, dk[kb][1], Y[kb][fb]);
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int j = i + AH;
+        if (j < NI) op[j % (AH + 1)] = zt.read(Zq, 32 * mq + 16 * (j & 1), j >> 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Y[kb][i >> 1] = mfma_bf16(op[i % (AH + 1)], dk[kb][i & 1], Y[kb][i >> 1]);
       }
+      sched_chain<NI, 2, AH, KB>();
     }
   }
 
@@ -625,6 +722,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(KvArgs a) {
   l.ntiles = l.ta + (nbq + kT - 1) / kT;
   stage_offsets<D>(l.qoff, NW, l.w, l.lane);
   stage_offsets<DV>(l.doff, NW, l.w, l.lane);
+  l.qr.init(l.lane);
+  l.dr.init(l.lane);
+  l.dt.init(l.lane);
+  l.zt.init(l.lane);
 
   f32x16 Y[KB][NY], dV[KB][NV];
   float sig[KB];
