@@ -213,7 +213,11 @@ struct DqLoop {
   // wave (its last key at or before the wave's first query): no mask
   __device__ __forceinline__ bool all_visible(int kb) const { return kb + 31 <= wave_first; }
 
-  // statistics pass: fold this half's visible keys into (m, l, a)
+  // statistics pass: fold this half's visible keys into (m, l, a). Without
+  // kMax the offset is fixed at 0 (2^s summed directly: bf16 and fp32 share
+  // the exponent range, so only the final sums need checking); with kMax it
+  // follows the running maximum.
+  template <bool kMax>
   __device__ __forceinline__ void stats_half(int kt, int mb, int slot, RowStats (&st)[QB]) const {
     f32x16 sc[QB], dp[QB];
     scores(mb, slot, sc, dp);
@@ -221,48 +225,45 @@ struct DqLoop {
     const bool full = all_visible(kb);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      float e[16];
       if (full) {
-        float mx = sc[qb][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qb][r]);
-        if (mx > st[qb].m) {
+        for (int r = 0; r < 16; ++r) e[r] = sc[qb][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
+          e[r] = key <= myq[qb] ? sc[qb][r] : kNegInf;
+        }
+      }
+      if constexpr (kMax) {
+        float mx = e[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, e[r]);
+        if (mx > st[qb].m) {  // rescale to the new maximum (a first finite maximum scales 0 by 0)
           const float f = st[qb].m == kNegInf ? 0.f : exp2_fast(st[qb].m - mx);
           st[qb].l *= f;
           st[qb].a *= f;
           st[qb].m = mx;
         }
+        // a lane half with no visible key yet keeps m = -inf: offset 0 (its
+        // exponentials are all 0), not -inf - (-inf)
+        const float ms = st[qb].m == kNegInf ? 0.f : st[qb].m;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(sc[qb][r] - st[qb].m);
-          st[qb].l += e;
-          st[qb].a += e * dp[qb][r];
-        }
-        continue;
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-        mx = fmaxf(mx, key <= myq[qb] ? sc[qb][r] : kNegInf);
-      }
-      if (mx > st[qb].m) {  // rescale to the new maximum (a first finite maximum scales 0 by 0)
-        const float f = st[qb].m == kNegInf ? 0.f : exp2_fast(st[qb].m - mx);
-        st[qb].l *= f;
-        st[qb].a *= f;
-        st[qb].m = mx;
+        for (int r = 0; r < 16; ++r) e[r] -= ms;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb + (r & 7) + 8 * g + 16 * (r >> 3);
-        const float e = key <= myq[qb] ? exp2_fast(sc[qb][r] - st[qb].m) : 0.f;
-        st[qb].l += e;
-        st[qb].a += e * dp[qb][r];
+        const float x = exp2_fast(e[r]);
+        st[qb].l += x;
+        st[qb].a += x * dp[qb][r];
       }
     }
   }
 
-  // gradient pass: dS and U^T += Z^T dS^T for one half
-  __device__ __forceinline__ void grad_half(int kt, int mb, int slot, f32x16 (&U)[QB][NF]) const {
+  // gradient pass: dS and U^T += Z^T dS^T for one half; sig gathers the row
+  // sums of the bf16 dS that the products use
+  __device__ __forceinline__ void grad_half(int kt, int mb, int slot, f32x16 (&U)[QB][NF], float (&sig)[QB]) const {
     f32x16 sc[QB], dp[QB];
     scores(mb, slot, sc, dp);
     const char* Zs = sb[slot];
@@ -285,6 +286,8 @@ struct DqLoop {
       }
       d0[qb] = pack8(ds);
       d1[qb] = pack8(ds + 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sig[qb] = sum2_bf16(d0[qb][i], sum2_bf16(d1[qb][i], sig[qb]));
     }
     // operand i = (fb, k-half) of Z^T, read AH ahead
     constexpr int NI = 2 * NF, AH = GECKO_BWD_AHEAD;
@@ -305,17 +308,19 @@ struct DqLoop {
   // Tile kt in stage SLOT: stage tile kt + NS - 1 into the stage tile kt - 1
   // used (every wave is past it), compute, wait for this wave's share of
   // tile kt + 1 (tile kt + 2's loads may stay in flight) and end at the barrier.
-  template <int SLOT, bool kStats>
-  __device__ __forceinline__ void tile(int kt, RowStats (&st)[QB], f32x16 (&U)[QB][NF]) const {
+  // kPass: 0 statistics with a fixed offset, 1 statistics with the running
+  // maximum, 2 gradients
+  template <int SLOT, int kPass>
+  __device__ __forceinline__ void tile(int kt, RowStats (&st)[QB], f32x16 (&U)[QB][NF], float (&sig)[QB]) const {
     const bool ahead = kt + NS - 1 < ntiles;
     if (ahead) stage(kt + NS - 1, (SLOT + NS - 1) % NS);
 #pragma unroll 1
     for (int mb = 0; mb < 2; ++mb) {
       if (kbeg + kt * kT + 32 * mb <= wave_last) {
-        if constexpr (kStats)
-          stats_half(kt, mb, SLOT, st);
+        if constexpr (kPass < 2)
+          stats_half<kPass == 1>(kt, mb, SLOT, st);
         else
-          grad_half(kt, mb, SLOT, U);
+          grad_half(kt, mb, SLOT, U, sig);
       }
     }
     if (NS == 3 && ahead)
@@ -325,8 +330,8 @@ struct DqLoop {
     barrier_lds();
   }
 
-  template <bool kStats>
-  __device__ __forceinline__ void pass(RowStats (&st)[QB], f32x16 (&U)[QB][NF]) const {
+  template <int kPass>
+  __device__ __forceinline__ void pass(RowStats (&st)[QB], f32x16 (&U)[QB][NF], float (&sig)[QB]) const {
     stage(0, 0);
     if (NS == 3 && ntiles > 1) {
       stage(1, 1);
@@ -336,9 +341,9 @@ struct DqLoop {
     }
     barrier_lds();
     for (int kt = 0; kt < ntiles; kt += NS) {
-      tile<0, kStats>(kt, st, U);
-      if (kt + 1 < ntiles) tile<1, kStats>(kt + 1, st, U);
-      if (NS == 3 && kt + 2 < ntiles) tile<2 % NS, kStats>(kt + 2, st, U);
+      tile<0, kPass>(kt, st, U, sig);
+      if (kt + 1 < ntiles) tile<1, kPass>(kt + 1, st, U, sig);
+      if (NS == 3 && kt + 2 < ntiles) tile<2 % NS, kPass>(kt + 2, st, U, sig);
     }
   }
 };
@@ -404,13 +409,29 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
 
   f32x16 U[QB][NF];
   RowStats st[QB];
+  float sig[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    st[qb] = RowStats{kNegInf, 0.f, 0.f};
+    st[qb] = RowStats{0.f, 0.f, 0.f};
+    sig[qb] = 0.f;
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb) U[qb][fb] = f32x16{};
   }
-  l.template pass<true>(st, U);
+  // First without an offset; if a valid query's sum lies outside
+  // [2^-60, 2^63] (some 2^s overflowed, or every term is tiny), the workgroup
+  // redoes the statistics with the running maximum.
+  l.template pass<0>(st, U, sig);
+  bool redo = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = other_half_sum(st[qb].l);
+    redo = redo || (l.myq[qb] < qend && !(lt >= 0x1p-60f && lt <= 0x1p63f));
+  }
+  if (__syncthreads_or(redo)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st[qb] = RowStats{kNegInf, 0.f, 0.f};
+    l.template pass<1>(st, U, sig);
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     // merge the two lane halves (each saw half of every 32-key block); each
@@ -433,12 +454,19 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
       *reinterpret_cast<float2*>(a.ld + 2 * (base + (size_t)l.myq[qb])) = make_float2(l.lse2[qb], l.dd[qb]);
   }
   // every wave is past the statistics pass's last barrier: its stages are free
-  l.template pass<false>(st, U);
+  l.template pass<2>(st, U, sig);
 
+  // dq = kappa_k * sum_j dS_ij z_j relies on sum_j dS_ij = 0; the bf16 dS
+  // that the products use sum to a rounding residue sigma, which a component
+  // shared by all keys would multiply. Moving the residue onto the diagonal
+  // key (U - sigma z_i) makes the sum exactly zero, so shared components
+  // cancel as they do in exact arithmetic.
   const float* kk = a.kk + h * D;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    const float sg = other_half_sum(sig[qb]);
     if (l.myq[qb] >= qend) continue;
+    const uint16_t* zq = a.z + (base + (size_t)l.myq[qb]) * D;
     // register r of block fb holds feature 32 fb + 16 (r >> 3) + 8 g + (r & 7)
     float* dst = a.dq + (base + (size_t)l.myq[qb]) * D;
 #pragma unroll
@@ -446,13 +474,16 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int f = 32 * fb + 16 * hh + 8 * l.g;
+        float zf[8];
+        unpack8(ld16(zq + f), zf);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const f32x4 k4 = *reinterpret_cast<const f32x4*>(kk + f + 4 * q);
           const int r = 8 * hh + 4 * q;
-          *reinterpret_cast<f32x4*>(dst + f + 4 * q) =
-              f32x4{k4[0] * U[qb][fb][r], k4[1] * U[qb][fb][r + 1], k4[2] * U[qb][fb][r + 2],
-                    k4[3] * U[qb][fb][r + 3]};
+          f32x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = k4[i] * (U[qb][fb][r + i] - sg * zf[4 * q + i]);
+          *reinterpret_cast<f32x4*>(dst + f + 4 * q) = o;
         }
       }
   }

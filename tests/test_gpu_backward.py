@@ -12,10 +12,12 @@ the size of the typical one. Each product rounds its operands to bf16
 (2^-9 relative) and accumulates in fp32; the observed errors are 0.2-0.5% of
 the largest entry. Each affine-vector gradient is a sum over (batch, token)
 of a per-token term (Z' dQ, dQ, ..., Z' dK_m, dK_m); its bar is the error
-bound of such a sum, |y - x| <= 2e-2 * sum of |term| per entry (several of
-these sums nearly cancel: d nu_k vanishes exactly and d rho_k does without
-the delta term, so a bar relative to the sum itself could not be met by any
-rounding of the terms).
+bound of such a sum, |y - x| <= 2e-2 * (sum of |term| + 1e-3 * its largest
+value over the vector) per entry (several of these sums nearly cancel: d nu_k
+vanishes exactly and d rho_k does without the delta term, so a bar relative
+to the sum itself could not be met by any rounding of the terms; the floor
+covers entries whose every term vanishes, such as a feature that shifts all
+logits of a row alike).
 The saved log-sum-exp is checked against the oracle's to 2e-2 absolute (the
 logits themselves are formed from bf16-rounded scaled queries), and the
 forward output of gecko_forward_lse is bit-identical to gecko_sca_awm_forward.
@@ -73,6 +75,7 @@ def _errors(got, want):
 SUMMAND = {"kappa_q": ("dq", True), "nu_q": ("dq", False), "kappa_k": ("dk", True), "nu_k": ("dk", False),
            "eta_q": ("dqm", True), "rho_q": ("dqm", False), "eta_k": ("dkm", True), "rho_k": ("dkm", False)}
 SUM_TOL = 2e-2
+SUM_FLOOR = 1e-3
 
 
 def _check(got, want, parts_names, z):
@@ -84,6 +87,7 @@ def _check(got, want, parts_names, z):
             src, with_z = SUMMAND[k]
             term = want[src] * (z if with_z else 1.0)
             bound = np.abs(term).sum(axis=(0, 2))  # [H, d]
+            bound = bound + SUM_FLOOR * bound.max()
             ratio = float(np.max(np.abs(got["d" + k] - want["d" + k]) / (bound + 1e-30)))
             assert ratio <= SUM_TOL, ("d" + k, ratio)
 
@@ -205,3 +209,20 @@ def test_value_gradient_identity_at_scale():
     scale = float(v.double().abs().mul(res["dv"].double().abs()).sum())
     assert abs(lhs - rhs) <= 1e-2 * scale, (lhs, rhs, scale)
     assert torch.isfinite(res["dz"]).all() and torch.isfinite(res["dv"]).all()
+
+
+def test_backward_logits_past_the_exponent_range():
+    """Every logit carries a large part shared by all keys (Z' feature 0 set
+    to 3 and kappa_q, kappa_k = 8 there: about 830 in log2 units), so 2^s
+    overflows float32 and the attention statistics take the running-maximum
+    path, while the softmax over the varying parts stays unsaturated."""
+    g = gecko()
+    host = inputs.make_inputs(1, 1, 300, 128, 256, "bf16", seed=0, tag=310)
+    host["z"][..., 0] = 3.0
+    for k in ("kappa_q", "kappa_k"):
+        host["params"][k][:, 0] = 8.0
+    dout = inputs.make_dout(1, 1, 300, 256, "bf16", seed=0, tag=310)
+    got = _run(host, dout, 128, g.GECKO_PART_SCA)
+    want = go.grad(host["z"].astype(np.float64), host["v"].astype(np.float64), host["params"], 128,
+                   dout.astype(np.float64), parts=("sca",))
+    _check(got, want, ("sca",), host["z"].astype(np.float64))
