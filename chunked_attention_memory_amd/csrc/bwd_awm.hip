@@ -305,9 +305,12 @@ __global__ void bwd_zeta_kernel(const float* __restrict__ part, const float* __r
   if (f >= D) return;
   const int64_t bh = blockIdx.x;
   float z = 0.f;
+  // the loads do not depend on the recurrence: unrolled, they run ahead of it
+#pragma unroll 4
   for (int64_t t = nmem - 1; t >= 0; --t) {
     const int64_t row = bh * nmem + t;
     float pr = 0.f, pc = 0.f;
+#pragma unroll 8
     for (int j = 0; j < nsl; ++j) {
       const float2 pp = *reinterpret_cast<const float2*>(part + ((row * nsl + j) * D + f) * 2);
       pr += pp.x;

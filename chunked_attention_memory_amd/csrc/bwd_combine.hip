@@ -67,7 +67,15 @@ __global__ __launch_bounds__(128) void bwd_affine_reduce_kernel(const float* __r
   float s = 0.f;
   for (int64_t b = 0; b < B; ++b) {
     const float* p = apart + (((b * H + h) * nblk) * 8 + i) * (int64_t)D + f;
-    for (int k = 0; k < nblk; ++k) s += p[(int64_t)k * 8 * D];
+    // four independent partial sums keep several loads in flight; they are
+    // combined in a fixed order, so the result does not depend on timing
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    for (; k + 4 <= nblk; k += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s4[u] += p[(int64_t)(k + u) * 8 * D];
+    for (; k < nblk; ++k) s4[0] += p[(int64_t)k * 8 * D];
+    s += (s4[0] + s4[1]) + (s4[2] + s4[3]);
   }
   daff[((int64_t)i * H + h) * D + f] = s;
 }
