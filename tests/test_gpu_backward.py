@@ -226,3 +226,59 @@ def test_backward_logits_past_the_exponent_range():
     want = go.grad(host["z"].astype(np.float64), host["v"].astype(np.float64), host["params"], 128,
                    dout.astype(np.float64), parts=("sca",))
     _check(got, want, ("sca",), host["z"].astype(np.float64))
+
+
+def test_full_size_attention_gradients_on_sampled_chunks():
+    """The bench configuration (B1 H8, 131072 tokens, c 2048). The attention
+    gradients of chunk s depend on chunks s-1, s, s+1 only (its queries see
+    chunks s-1 and s, its keys are seen by chunks s and s+1), so the oracle
+    differentiates that three-chunk stretch alone and its dZ' and dV rows of
+    chunk s are compared, for chunks 1 and 40 of two heads."""
+    import torch
+
+    g = gecko()
+    B, H, n, c, d, dv = 1, 8, 131072, 2048, 128, 256
+    dev = inputs.make_inputs_device(B, H, n, d, dv, "bf16", seed=3, tag=311)
+    z, v = dev["z"], dev["v"]
+    p = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(311)
+    do = torch.randn((B, H, n, dv), generator=gen, device="cuda").to(torch.bfloat16)
+    announce(f"full-size attention backward n={n} c={c} H={H}")
+    res = g.gecko_backward(z, p, v, do, c, parts=g.GECKO_PART_SCA)
+    torch.cuda.synchronize()
+    for s, h in ((1, 0), (40, 5)):
+        a, b = (s - 1) * c, (s + 2) * c
+        zs = z[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        vs = v[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ds = do[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ph = {k: dev["params"][k][h:h + 1] for k in dev["params"]}
+        want = go.grad(zs, vs, ph, c, ds, parts=("sca",))
+        for key in ("dz", "dv"):
+            got = to_numpy(res[key][0, h, s * c:(s + 1) * c])
+            fro, mx = _errors(got, want[key][0, 0, c:2 * c])
+            assert fro <= GRAD_TOL and mx <= GRAD_TOL, (s, h, key, fro, mx)
+
+
+def test_full_size_value_gradient_identity():
+    """Both parts at the bench configuration: <V, dL/dV> = <dO, O> (O is
+    linear in V) to 1e-2 of the sum of |terms|."""
+    import torch
+
+    g = gecko()
+    B, H, n, c, d, dv = 1, 8, 131072, 2048, 128, 256
+    dev = inputs.make_inputs_device(B, H, n, d, dv, "bf16", seed=4, tag=312)
+    z, v = dev["z"], dev["v"]
+    p = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(312)
+    do = torch.randn((B, H, n, dv), generator=gen, device="cuda").to(torch.bfloat16)
+    announce(f"full-size value-gradient identity n={n} c={c} H={H}")
+    out = g.gecko_sca_awm_forward(z, p, v, c, out_dtype=torch.float32)
+    res = g.gecko_backward(z, p, v, do, c)
+    torch.cuda.synchronize()
+    for h in range(H):
+        lhs = float((v[0, h].double() * res["dv"][0, h].double()).sum())
+        rhs = float((do[0, h].double() * out[0, h].double()).sum())
+        scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
+        assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
