@@ -292,6 +292,19 @@ def main(argv=None) -> int:
     stages, calls = timer.read()
     timer.close()
 
+    # per-call durations (an event pair around each call, after the timed
+    # region): median and minimum, beside the timed region's mean
+    per_call = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        per_call.append((e0, e1))
+    torch.cuda.synchronize()
+    call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in per_call)
+    del per_call
+
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -337,6 +350,7 @@ def main(argv=None) -> int:
         "flops_per_step": flops["total"],
         "peak_tflops_used": PEAK_BF16_TFLOPS,
         "ms_per_step_events": ev_ms / args.steps,
+        "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)},
         "stage_ms": stage_ms,
         "roofline": {"kernel": "sca_bf16_kernel (attention + readout)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
