@@ -282,3 +282,48 @@ def test_full_size_value_gradient_identity():
         rhs = float((do[0, h].double() * out[0, h].double()).sum())
         scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
         assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
+
+
+def test_backward_one_million_tokens():
+    """1,048,576 tokens (512 chunks of 2048, B1 H2): the reverse state scan
+    runs 510 steps; one (batch, head) slab of Z' spans 256 MiB and of V 512 MiB.
+    Every gradient is finite; <V, dV> = <dO, O> for the whole layer; the
+    attention gradients of sampled chunks (first, middle, last) match the
+    oracle on their three-chunk stretches."""
+    import torch
+
+    g = gecko()
+    B, H, n, c, d, dv = 1, 2, 1 << 20, 2048, 128, 256
+    dev = inputs.make_inputs_device(B, H, n, d, dv, "bf16", seed=5, tag=313)
+    z, v = dev["z"], dev["v"]
+    p = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(313)
+    do = torch.randn((B, H, n, dv), generator=gen, device="cuda").to(torch.bfloat16)
+    announce(f"backward n={n} c={c} H={H}")
+    out = g.gecko_sca_awm_forward(z, p, v, c, out_dtype=torch.float32)
+    res = g.gecko_backward(z, p, v, do, c)
+    torch.cuda.synchronize()
+    for k in ("dz", "dv"):
+        assert torch.isfinite(res[k]).all(), k
+    assert all(torch.isfinite(res["d" + k]).all() for k in NAMES)
+    for h in range(H):
+        lhs = float((v[0, h].double() * res["dv"][0, h].double()).sum())
+        rhs = float((do[0, h].double() * out[0, h].double()).sum())
+        scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
+        assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
+    del out, res
+    sca = g.gecko_backward(z, p, v, do, c, parts=g.GECKO_PART_SCA)
+    torch.cuda.synchronize()
+    N = n // c
+    for s, h in ((1, 0), (N // 2, 1), (N - 2, 0)):
+        a, b = (s - 1) * c, (s + 2) * c
+        zs = z[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        vs = v[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ds = do[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ph = {k: dev["params"][k][h:h + 1] for k in dev["params"]}
+        want = go.grad(zs, vs, ph, c, ds, parts=("sca",))
+        for key in ("dz", "dv"):
+            got = to_numpy(sca[key][0, h, s * c:(s + 1) * c])
+            fro, mx = _errors(got, want[key][0, 0, c:2 * c])
+            assert fro <= GRAD_TOL and mx <= GRAD_TOL, (s, h, key, fro, mx)
