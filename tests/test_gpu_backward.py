@@ -117,6 +117,9 @@ def _case(B, H, n, dv, c, parts, flags=0, out_dtype="bf16", sharp=1.0, tag=300):
     (1, 1, 600, 256, 96),    # chunk length not a multiple of the 64-row tiles
     (1, 1, 300, 256, 1000),  # one chunk (c > n): causal attention, no memory read
     (1, 1, 65, 256, 64),     # two chunks, one-token tail
+    (1, 1, 1, 256, 64),      # a single token
+    (2, 2, 256, 256, 128),   # exactly two chunks: the memory never reaches the output
+    (2, 3, 333, 128, 64),    # batch and heads together, ragged tail
 ])
 def test_backward_both_parts(B, H, n, dv, c):
     g = gecko()
@@ -140,6 +143,8 @@ def test_backward_variants():
     _case(1, 1, 700, 256, 128, g.GECKO_PART_SCA | g.GECKO_PART_AWM, flags=g.GECKO_AWM_NO_DELTA, tag=303)
     _case(1, 1, 700, 256, 128, g.GECKO_PART_SCA | g.GECKO_PART_AWM, flags=g.GECKO_CHUNKWISE, tag=304)
     _case(1, 1, 500, 128, 64, g.GECKO_PART_AWM, flags=g.GECKO_CHUNKWISE | g.GECKO_AWM_NO_DELTA, tag=305)
+    # chunkwise over one chunk: no memory read, attention within the chunk only
+    _case(1, 2, 128, 256, 128, g.GECKO_PART_SCA | g.GECKO_PART_AWM, flags=g.GECKO_CHUNKWISE, tag=310)
 
 
 def test_backward_sharp_logits():
