@@ -127,6 +127,33 @@ __global__ __launch_bounds__(256) void bwd_dout_bf16_kernel(const float* __restr
   }
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b mod 8),
+// and each XCD has its own L2. Logical block (b mod 8) per_xcd + b / 8 gives
+// every XCD a contiguous run of (batch*head, chunk) pairs, so the tiles that
+// read the same key window meet in one L2 instead of each XCD streaming the
+// whole window from HBM.
+#ifndef GECKO_BWD_XCD
+#define GECKO_BWD_XCD 1
+#endif
+__device__ __forceinline__ uint32_t logical_block(uint32_t per_xcd) {
+#if GECKO_BWD_XCD
+  return (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+#else
+  (void)per_xcd;
+  return blockIdx.x;
+#endif
+}
+
+inline unsigned xcd_grid(int64_t nblocks, int64_t* per_xcd) {
+#if GECKO_BWD_XCD
+  *per_xcd = (nblocks + 7) / 8;
+  return (unsigned)(8 * *per_xcd);
+#else
+  *per_xcd = nblocks;
+  return (unsigned)nblocks;
+#endif
+}
+
 // ---------------------------------------------------------------- dq
 struct DqArgs {
   const uint16_t* qp;
@@ -138,6 +165,7 @@ struct DqArgs {
   float* dq;
   int64_t n;
   int c, nchunks, qtiles, H, prev;
+  uint32_t nblocks, per_xcd;
 };
 
 // Running softmax statistics of one lane's keys for its query: max m (log2
@@ -363,8 +391,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(16))) char S0[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S1[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S2[L::NS == 3 ? L::STAGE : 16];
-  const int qt = (int)(blockIdx.x % (unsigned)a.qtiles);
-  const int rest = (int)(blockIdx.x / (unsigned)a.qtiles);
+  // within a chunk the last query tiles have the longest key windows: they
+  // start first, so the workgroups left at the end of the grid are short
+  const uint32_t lb = logical_block(a.per_xcd);
+  if (lb >= a.nblocks) return;
+  const int qt = a.qtiles - 1 - (int)(lb % (unsigned)a.qtiles);
+  const int rest = (int)(lb / (unsigned)a.qtiles);
   const int s = rest % a.nchunks;
   const int bh = rest / a.nchunks;
   const int n = (int)a.n, c = a.c;
@@ -502,6 +534,7 @@ struct KvArgs {
   float* dv;
   int64_t n;
   int c, nchunks, ktiles, H, prev, accum;
+  uint32_t nblocks, per_xcd;
 };
 
 // NW waves, KB 32-key blocks per wave. MODE 0: dK and dV; 1: dV only (P
@@ -704,8 +737,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(KvArgs a) {
   __shared__ __attribute__((aligned(16))) char S0[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S1[L::STAGE];
   __shared__ __attribute__((aligned(16))) char S2[L::NS == 3 ? L::STAGE : 16];
-  const int kt_ = (int)(blockIdx.x % (unsigned)a.ktiles);
-  const int rest = (int)(blockIdx.x / (unsigned)a.ktiles);
+  // the first key tiles of a chunk have the most queries: they start first
+  const uint32_t lb = logical_block(a.per_xcd);
+  if (lb >= a.nblocks) return;
+  const int kt_ = (int)(lb % (unsigned)a.ktiles);
+  const int rest = (int)(lb / (unsigned)a.ktiles);
   const int s = rest % a.nchunks;
   const int bh = rest / a.nchunks;
   const int n = (int)a.n, c = a.c;
@@ -855,7 +891,11 @@ hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
   a.c = (int)cc; a.nchunks = (int)p.f.nchunks; a.H = (int)p.f.H; a.prev = (int)p.f.prev;
   a.qtiles = (int)((cc + 32 * NW * QB - 1) / (32 * NW * QB));
-  const dim3 grid((unsigned)(p.f.B * p.f.H * p.f.nchunks * a.qtiles));
+  const int64_t nblocks = p.f.B * p.f.H * p.f.nchunks * a.qtiles;
+  int64_t per_xcd = 0;
+  const dim3 grid(xcd_grid(nblocks, &per_xcd));
+  a.nblocks = (uint32_t)nblocks;
+  a.per_xcd = (uint32_t)per_xcd;
   if (p.f.dv == 256)
     hipLaunchKernelGGL((bwd_dq_kernel<128, 256, NW, QB>), grid, dim3(64 * NW), 0, s, a);
   else
@@ -867,7 +907,11 @@ template <int DV, int NW, int KB, int MODE>
 hipError_t launch_kv(KvArgs a, const BwdProblem& p, hipStream_t s) {
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
   a.ktiles = (int)((cc + 32 * NW * KB - 1) / (32 * NW * KB));
-  const dim3 grid((unsigned)(p.f.B * p.f.H * p.f.nchunks * a.ktiles));
+  const int64_t nblocks = p.f.B * p.f.H * p.f.nchunks * a.ktiles;
+  int64_t per_xcd = 0;
+  const dim3 grid(xcd_grid(nblocks, &per_xcd));
+  a.nblocks = (uint32_t)nblocks;
+  a.per_xcd = (uint32_t)per_xcd;
   hipLaunchKernelGGL((bwd_dkdv_kernel<128, DV, NW, KB, MODE>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
