@@ -25,7 +25,21 @@
 namespace gecko {
 namespace {
 
-constexpr int kBT = 64;                 // tokens per tile of the chunk pass
+// Chunk pass: tokens per tile and LDS stages (tile i + kNS - 1 loads while
+// tile i is computed)
+#ifndef GECKO_CHUNK_BT
+#define GECKO_CHUNK_BT 32
+#endif
+#ifndef GECKO_CHUNK_NS
+#define GECKO_CHUNK_NS 4
+#endif
+constexpr int kBT = GECKO_CHUNK_BT;
+constexpr int kNS = GECKO_CHUNK_NS;
+static_assert(kNS >= 4 && kNS <= 6 && kNS % 2 == 0, "chunk pass stages");
+// operands of the chunk pass's MFMAs read from LDS this many MFMAs ahead
+#ifndef GECKO_CHUNK_AH
+#define GECKO_CHUNK_AH 2
+#endif
 constexpr float kOverflow = 0x1p63f;
 
 template <int CTRL>
@@ -70,10 +84,11 @@ struct ChunkTile {
   static constexpr int PARTS = THREADS / kBT;  // threads per token row in the psi phase
   static constexpr int FPT = D / PARTS;        // features per thread in the psi phase
   static constexpr int KT = kBT / 16;          // 16-token k-steps per tile
-  static_assert(FPT % 8 == 0 && (PARTS == 2 || PARTS == 4 || PARTS == 8), "psi phase split");
+  static_assert(FPT % 8 == 0 && FPT <= 16 && (PARTS == 2 || PARTS == 4 || PARTS == 8), "psi phase split");
   static constexpr int STAGE = ZBYTES + VBYTES;
-  // two (Z', V) stages, the psi tile, then the (log2-scaled) eta_k and rho_k vectors
-  static constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + ZBYTES + 2 * D * sizeof(float);
+  static constexpr int LOADS = ZLOADS + VLOADS;  // staging loads per lane and tile
+  // kNS (Z', V) stages, then two psi tiles
+  static constexpr size_t LDS_BYTES = kNS * (size_t)STAGE + 2 * (size_t)ZBYTES;
 };
 
 struct ChunkArgs {
@@ -109,23 +124,23 @@ struct ChunkLoop {
   static constexpr int NMF = D / 32;
   const uint16_t* zbh;
   const uint16_t* vbh;
-  // stage s: Z' tile at sb[s], V tile after it; psi tile at ps. Separate LDS
+  // stage s: Z' tile at sb[s], V tile after it; psi tiles at psb. Separate LDS
   // variables, so that the compiler sees that the reads of one stage do not
   // alias the loads filling the other (it would wait for them otherwise).
-  char* sb[2];
-  char* ps;
-  const float* e2s;  // eta_k * log2(e), in LDS
-  const float* r2s;  // rho_k * log2(e), in LDS
+  char* sb[kNS];
+  char* psb[2];  // psi of tiles with even / odd index
   int n, cbeg, cend, ntiles, w, lane, g, lq;
   float ekf, rkf;  // this lane's feature
+  // eta_k, rho_k (log2-scaled) of this thread's features in the psi phase
+  float pe[T::FPT], pr[T::FPT];
   uint32_t zoff[T::ZLOADS], voff[T::VLOADS];
   // Transpose-read bases (byte offsets within a stage / the psi tile) for
   // read jj of block blk at k-step 0; k-step ks adds 16 ks rows. See tr_base.
   int zb[2], vb[2][NMV], pb[2][NMF];
   int poff[T::FPT / 8];  // psi phase: this thread's 16-byte chunks of its token row
 
-  __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* s0, char* s1, char* psb,
-                                       float* ek) {
+  __device__ __forceinline__ void init(const ChunkArgs& a, int64_t bh, int64_t t, char* const (&stages)[kNS],
+                                       char* ps0, char* ps1) {
     const int h = (int)(bh % a.H);
     // chunk t of the virtual sequence [carried chunk (streaming)] + this
     // call's chunks; every chunk entered into the memory is full
@@ -147,17 +162,18 @@ struct ChunkLoop {
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     g = lane >> 5;
     lq = lane & 31;
-    sb[0] = s0;
-    sb[1] = s1;
-    ps = psb;
-    float* e2 = ek;
-    float* r2 = ek + D;
-    if (tid < D) {
-      e2[tid] = a.eta_k[h * D + tid] * kLog2e;
-      r2[tid] = a.rho_k[h * D + tid] * kLog2e;
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) sb[i] = stages[i];
+    psb[0] = ps0;
+    psb[1] = ps1;
+    {
+      const int f0 = T::FPT * (tid % T::PARTS);
+#pragma unroll
+      for (int i = 0; i < T::FPT; ++i) {
+        pe[i] = a.eta_k[h * D + f0 + i] * kLog2e;
+        pr[i] = a.rho_k[h * D + f0 + i] * kLog2e;
+      }
     }
-    e2s = e2;
-    r2s = r2;
     const int f = 32 * w + lq;
     ekf = a.eta_k[h * D + f] * kLog2e;
     rkf = a.rho_k[h * D + f] * kLog2e;
@@ -218,13 +234,15 @@ struct ChunkLoop {
     stage_rows(vbh, cbeg + it * kBT, n, DV, sb[slot] + T::ZBYTES, T::NW, w, voff, T::VLOADS);
   }
 
-  // K_m of this lane's feature (log2 units) for tokens 16 ks + 8 g + [0, 8) of the tile in `slot`
-  __device__ __forceinline__ void keys(int slot, int ks, float (&k)[8]) const {
+  // eta_k z + shift for this lane's feature (log2 units) and tokens
+  // 16 ks + 8 g + [0, 8) of the tile in `slot`: K_m itself for
+  // shift = rho_k log2(e), K_m less an offset m for shift = rho_k log2(e) - m
+  __device__ __forceinline__ void keys(int slot, int ks, float shift, float (&k)[8]) const {
     const u32x4 zr = tr_operand<D>(zs(slot), zb[0], zb[1], ks);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      k[2 * j] = ekf * bf_lo(zr[j]) + rkf;
-      k[2 * j + 1] = ekf * bf_hi(zr[j]) + rkf;
+      k[2 * j] = ekf * bf_lo(zr[j]) + shift;
+      k[2 * j + 1] = ekf * bf_hi(zr[j]) + shift;
     }
   }
 
@@ -235,83 +253,93 @@ struct ChunkLoop {
 #pragma unroll
     for (int ks = 0; ks < T::KT; ++ks) {
       float k[8];
-      keys(slot, ks, k);
+      keys(slot, ks, rkf, k);
 #pragma unroll
       for (int j = 0; j < 8; ++j) mx = fmaxf(mx, 16 * ks + 8 * g + j < valid ? k[j] : kNegInf);
     }
     return mx;
   }
 
-  // psi(K_m) for the tile's tokens into LDS: thread -> token tid / PARTS,
-  // features FPT (tid % PARTS) + [0, FPT)
-  __device__ __forceinline__ void psi_phase(int slot) const {
+  // psi(K_m) for the tokens of the tile in `slot` into the psi buffer `pd`:
+  // thread -> token tid / PARTS, features FPT (tid % PARTS) + [0, FPT). psi
+  // is a softmax over the row, so any per-row offset gives the same result:
+  // without kMax the offset is 0 and a valid row whose exp-sum leaves
+  // [2^-60, 2^63] sets `bad` (the workgroup then redoes the pass with kMax,
+  // offset = the row maximum).
+  template <bool kMax>
+  __device__ __forceinline__ void psi_phase(int slot, char* pd, int valid, bool& bad) const {
     constexpr int FPT = T::FPT, CH = FPT / 8;
-    const int q = threadIdx.x % T::PARTS;
     float x[FPT];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(zs(slot) + poff[k]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[8 * k + 2 * j] = bf_lo(raw[j]);
-        x[8 * k + 2 * j + 1] = bf_hi(raw[j]);
+        x[8 * k + 2 * j] = pe[8 * k + 2 * j] * bf_lo(raw[j]) + pr[8 * k + 2 * j];
+        x[8 * k + 2 * j + 1] = pe[8 * k + 2 * j + 1] * bf_hi(raw[j]) + pr[8 * k + 2 * j + 1];
       }
     }
-    float mx = kNegInf;
+    if constexpr (kMax) {
+      float mx = x[0];
 #pragma unroll
-    for (int f4 = 0; f4 < FPT / 4; ++f4) {
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(e2s + FPT * q + 4 * f4);
-      const f32x4 r4 = *reinterpret_cast<const f32x4*>(r2s + FPT * q + 4 * f4);
+      for (int f = 1; f < FPT; ++f) mx = fmaxf(mx, x[f]);
+      mx = group_max<T::PARTS>(mx);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[4 * f4 + i] = e4[i] * x[4 * f4 + i] + r4[i];
-        mx = fmaxf(mx, x[4 * f4 + i]);
-      }
+      for (int f = 0; f < FPT; ++f) x[f] -= mx;
     }
-    mx = group_max<T::PARTS>(mx);
     float sm = 0.f;
 #pragma unroll
     for (int f = 0; f < FPT; ++f) {
-      x[f] = exp2_fast(x[f] - mx);
+      x[f] = exp2_fast(x[f]);
       sm += x[f];
     }
     sm = group_sum<T::PARTS>(sm);
+    if constexpr (!kMax) {
+      if ((int)threadIdx.x / T::PARTS < valid && !(sm >= 0x1p-60f && sm <= kOverflow)) bad = true;
+    }
     const float inv = 1.f / sm;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const float* y = x + 8 * k;
       const u32x4 pk{pack2(y[0] * inv, y[1] * inv), pack2(y[2] * inv, y[3] * inv), pack2(y[4] * inv, y[5] * inv),
                      pack2(y[6] * inv, y[7] * inv)};
-      *reinterpret_cast<u32x4*>(ps + poff[k]) = pk;
+      *reinterpret_cast<u32x4*>(pd + poff[k]) = pk;
     }
   }
 
-  // E for every k-step of the tile (its sum accumulated), then the two
-  // products; the operand of MFMA i + AH is read from LDS before MFMA i.
-  __device__ __forceinline__ void mfma_phase(int it, int slot, float msub, float& lsum, f32x16 (&accg)[NMV],
-                                             f32x16 (&acch)[NMF]) const {
-    const int valid = cend - (cbeg + it * kBT);
-    u32x4 ef[T::KT];
+  // E of this lane's feature for every k-step of the tile in `slot` (its sum
+  // accumulated into lsum), as the MFMA B operands. rkm = rho_k log2(e) less
+  // the feature's offset; tokens from `valid` on belong to no chunk entry:
+  // E = 0 there.
+  __device__ __forceinline__ void e_phase(int slot, int valid, float rkm, float& lsum, u32x4 (&ef)[T::KT]) const {
+    const bool full = valid >= kBT;
 #pragma unroll
     for (int ks = 0; ks < T::KT; ++ks) {
-      float k[8];
-      keys(slot, ks, k);
       float e[8];
+      keys(slot, ks, rkm, e);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e[j] = 16 * ks + 8 * g + j < valid ? exp2_fast(k[j] - msub) : 0.f;
+        e[j] = full || 16 * ks + 8 * g + j < valid ? exp2_fast(e[j]) : 0.f;
         lsum += e[j];
       }
       ef[ks] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
     }
-    constexpr int NB = NMV + NMF, NI = T::KT * NB, AH = 2;
+  }
+
+  // the two products of the tile in `slot` with psi from `psr`: G^T += V^T E
+  // and H^T += psi^T E; the operand of MFMA i + AH is read from LDS before
+  // MFMA i
+  __device__ __forceinline__ void products(int slot, const char* psr, const u32x4 (&ef)[T::KT],
+                                           f32x16 (&accg)[NMV], f32x16 (&acch)[NMF]) const {
+    constexpr int NB = NMV + NMF, NI = T::KT * NB, AH = GECKO_CHUNK_AH;
     const char* vsb = vs(slot);
     u32x4 op[AH + 1];
 #pragma unroll
     for (int i = 0; i < NI + AH; ++i) {
       if (i < NI) {
         const int ks = i / NB, b = i % NB;
-        op[i % (AH + 1)] = b < NMV ? tr_operand<DV>(vsb, vb[0][b] , vb[1][b], ks) : tr_operand<D>(ps, pb[0][b - NMV], pb[1][b - NMV], ks);
+        op[i % (AH + 1)] = b < NMV ? tr_operand<DV>(vsb, vb[0][b], vb[1][b], ks)
+                                   : tr_operand<D>(psr, pb[0][b - NMV], pb[1][b - NMV], ks);
       }
       if (i >= AH) {
         const int m = i - AH, ks = m / NB, b = m % NB;
@@ -321,30 +349,74 @@ struct ChunkLoop {
     }
   }
 
-  // one pass over the chunk with a fixed per-feature offset; returns the
-  // exp-sum. Expects tile 0 staged in slot 0; tile it+1 loads while tile it
-  // is computed.
-  // one tile in LDS stage SLOT (a constant, so LDS offsets fold into the reads)
-  template <int SLOT>
-  __device__ __forceinline__ void tile(int it, float msub, float& lsum, f32x16 (&accg)[NMV],
-                                       f32x16 (&acch)[NMF]) const {
-    if (it + 1 < ntiles) {
-      stage_z(it + 1, SLOT ^ 1);  // replaces tile it-1, whose reads are done
-      stage_v(it + 1, SLOT ^ 1);
-    }
-    psi_phase(SLOT);
-    barrier_lds();  // psi tile written (tile it + 1 keeps loading)
-    mfma_phase(it, SLOT, msub, lsum, accg, acch);
+  // wait until this lane's staging loads have landed except those of the
+  // last k tiles issued (k >= 0, uniform)
+  __device__ __forceinline__ void wait_leaving(int k) const {
+    if constexpr (kNS >= 6) if (k >= 3) { wait_vmem_leave<3 * T::LOADS>(); return; }
+    if constexpr (kNS >= 5) if (k >= 2) { wait_vmem_leave<2 * T::LOADS>(); return; }
+    if constexpr (kNS >= 4) if (k >= 1) { wait_vmem_leave<T::LOADS>(); return; }
     wait_vmem();
-    barrier_lds();  // tile it + 1 in LDS for every wave; tile it's reads done
   }
 
-  __device__ __forceinline__ float pass(float msub, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF]) const {
-    float lsum = 0.f;
-    for (int it = 0; it < ntiles; it += 2) {
-      tile<0>(it, msub, lsum, accg, acch);
-      if (it + 1 < ntiles) tile<1>(it + 1, msub, lsum, accg, acch);
+  // Tile it in LDS stage SLOT (a constant, so LDS offsets fold into the
+  // reads), psi(it) in buffer SLOT & 1 (kNS is even, so that is it & 1) and
+  // E(it) in ef: stage tile it + kNS - 1 into the stage of tile it - 1; the
+  // products of tile it, and in the same stretch of code (no barrier
+  // between, so that the VALU work runs under the MFMAs) psi and E of tile
+  // it + 1 (landed), into the other psi buffer and ef. Past the last tile
+  // that second part reads a stale stage with every token outside the chunk
+  // (E = 0, no range check), and its psi is never read. Then wait for tile
+  // it + 2 and end at the barrier.
+  template <int SLOT, bool kMax>
+  __device__ __forceinline__ void tile(int it, float rkm, float& lsum, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF],
+                                       u32x4 (&ef)[T::KT], bool& bad) const {
+    if (it + kNS - 1 < ntiles) {
+      stage_z(it + kNS - 1, (SLOT + kNS - 1) % kNS);
+      stage_v(it + kNS - 1, (SLOT + kNS - 1) % kNS);
     }
+    u32x4 efn[T::KT];
+    const int valid1 = cend - (cbeg + (it + 1) * kBT);
+    products(SLOT, psb[SLOT & 1], ef, accg, acch);
+    psi_phase<kMax>((SLOT + 1) % kNS, psb[(SLOT + 1) & 1], valid1, bad);
+    e_phase((SLOT + 1) % kNS, valid1, rkm, lsum, efn);
+    // tiles issued after tile it + 2: it + 3 .. min(it + kNS - 1, ntiles - 1)
+    wait_leaving(min(kNS - 3, ntiles - 3 - it));
+    barrier_lds();  // psi(it + 1) written; tile it + 2 landed; stage of tile it free
+#pragma unroll
+    for (int ks = 0; ks < T::KT; ++ks) ef[ks] = efn[ks];
+  }
+
+  template <int S, bool kMax>
+  __device__ __forceinline__ void tiles_from(int it, float rkm, float& lsum, f32x16 (&accg)[NMV],
+                                             f32x16 (&acch)[NMF], u32x4 (&ef)[T::KT], bool& bad) const {
+    if (it + S < ntiles) {
+      tile<S, kMax>(it + S, rkm, lsum, accg, acch, ef, bad);
+      if constexpr (S + 1 < kNS) tiles_from<S + 1, kMax>(it, rkm, lsum, accg, acch, ef, bad);
+    }
+  }
+
+  // one pass over the chunk with a fixed per-feature offset msub for E and
+  // (kMax) the row maximum or (otherwise) no offset for psi; returns the
+  // exp-sum of E and sets `bad` as psi_phase does. Expects tile 0 staged in
+  // stage 0 and landed (every wave past a barrier); stages tiles
+  // 1 .. kNS - 2 itself.
+  template <bool kMax>
+  __device__ __forceinline__ float pass(float msub, f32x16 (&accg)[NMV], f32x16 (&acch)[NMF], bool& bad) const {
+#pragma unroll
+    for (int i = 1; i < kNS - 1; ++i)
+      if (i < ntiles) {
+        stage_z(i, i);
+        stage_v(i, i);
+      }
+    const float rkm = rkf - msub;
+    float lsum = 0.f;
+    u32x4 ef[T::KT];
+    psi_phase<kMax>(0, psb[0], cend - cbeg, bad);
+    e_phase(0, cend - cbeg, rkm, lsum, ef);
+    // tiles issued after tile 1: 2 .. min(kNS - 2, ntiles - 1)
+    wait_leaving(min(kNS - 3, ntiles - 2));
+    barrier_lds();  // psi(0) written; tile 1 landed
+    for (int it = 0; it < ntiles; it += kNS) tiles_from<0, kMax>(it, rkm, lsum, accg, acch, ef, bad);
     return other_half_sum(lsum);
   }
 };
@@ -354,14 +426,23 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
   using T = ChunkTile<D, DV>;
   constexpr int NMV = DV / 32;
   constexpr int NMF = D / 32;
+  // each stage its own LDS variable (see ChunkLoop::sb)
   __shared__ __attribute__((aligned(16))) char S0[T::STAGE];
   __shared__ __attribute__((aligned(16))) char S1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char PS[T::ZBYTES];
-  __shared__ __attribute__((aligned(16))) float EK[2 * D];  // eta_k, rho_k (log2-scaled)
+  __shared__ __attribute__((aligned(16))) char S2[kNS > 2 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char S3[kNS > 3 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char S4[kNS > 4 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char S5[kNS > 5 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char PS0[T::ZBYTES];
+  __shared__ __attribute__((aligned(16))) char PS1[T::ZBYTES];
   const int64_t bh = blockIdx.x / a.nmem;
   const int64_t t = blockIdx.x % a.nmem;
   ChunkLoop<D, DV> L;
-  L.init(a, bh, t, S0, S1, PS, EK);
+  char* const all[6] = {S0, S1, S2, S3, S4, S5};
+  char* stages[kNS];
+#pragma unroll
+  for (int i = 0; i < kNS; ++i) stages[i] = all[i];
+  L.init(a, bh, t, stages, PS0, PS1);
 
   f32x16 accg[NMV], acch[NMF];
 #pragma unroll
@@ -374,18 +455,24 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
   wait_vmem();
   __syncthreads();
   float m = other_half_max(L.tile_max(0, 0));  // the first token is always valid
-  float ltot = L.pass(m, accg, acch);
-  if (__syncthreads_or(!(ltot <= kOverflow))) {
-    // a key exceeded the first tile's maximum by 2^63: exact maximum, then redo
-    float mx = kNegInf;
-    for (int it = 0; it < L.ntiles; ++it) {
-      L.stage_z(it, 0);
-      wait_vmem();
-      __syncthreads();
-      mx = fmaxf(mx, L.tile_max(it, 0));
-      __syncthreads();
+  bool psi_bad = false;
+  float ltot = L.template pass<false>(m, accg, acch, psi_bad);
+  const bool e_bad = !(ltot <= kOverflow);
+  if (__syncthreads_or(e_bad || psi_bad)) {
+    // the offset-free psi left its range, or a key exceeded the first tile's
+    // maximum by 2^63: redo with the row maxima in psi and (for the latter)
+    // the exact per-feature maximum in E
+    if (__syncthreads_or(e_bad)) {
+      float mx = kNegInf;
+      for (int it = 0; it < L.ntiles; ++it) {
+        L.stage_z(it, 0);
+        wait_vmem();
+        __syncthreads();
+        mx = fmaxf(mx, L.tile_max(it, 0));
+        __syncthreads();
+      }
+      m = other_half_max(mx);
     }
-    m = other_half_max(mx);
 #pragma unroll
     for (int i = 0; i < NMV; ++i) accg[i] = f32x16{};
 #pragma unroll
@@ -394,7 +481,7 @@ __global__ __launch_bounds__(2 * D, 1) void awm_chunk_bf16_kernel(ChunkArgs a) {
     L.stage_v(0, 0);
     wait_vmem();
     __syncthreads();
-    ltot = L.pass(m, accg, acch);
+    ltot = L.template pass<true>(m, accg, acch, psi_bad);
   }
 
   const int f = 32 * L.w + L.lq;
