@@ -148,6 +148,7 @@ def time_variants(gecko, w, z, v, params, out, stream, args) -> dict:
                              "calls_per_step": 4, "tokens_per_call": q}
     del parts, outs, ws_st
     res["backward"] = time_backward(gecko, w, z, v, params, stream, timed)
+    res.update(time_backward_saved(gecko, w, z, v, params, stream, timed))
     res["cema"] = time_cema(gecko, stream, timed)
     res["tdn"] = time_tdn(gecko, stream, timed)
     return res
@@ -180,6 +181,57 @@ def time_backward(gecko, w, z, v, params, stream, timed) -> dict:
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / PEAK_BF16_TFLOPS, "flops_per_call": flops},
             "workspace_bytes": nbytes}
+
+
+def time_backward_saved(gecko, w, z, v, params, stream, timed) -> dict:
+    """The training path of the headline layer (both parts): gecko_forward_train
+    (the forward output plus the float32 attention output and per-query
+    weight statistics) and gecko_backward_saved, which reuses them in place of
+    the attention statistics pass. Timed alone ("backward_saved", the
+    statistics made once before timing) and as a forward + backward pair
+    ("train_step_saved"). Same resident dL/dO and flop accounting as the
+    recomputing backward (the forward's algorithmic flops added for the pair)."""
+    import torch
+
+    from chunked_attention_memory_amd import configs
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(91)
+    do = torch.randn((w.B, w.H, w.n, w.dv), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dz = torch.empty((w.B, w.H, w.n, w.d), dtype=torch.float32, device="cuda")
+    dvt = torch.empty((w.B, w.H, w.n, w.dv), dtype=torch.float32, device="cuda")
+    daff = torch.empty((8, w.H, w.d), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.B, w.H, w.n, w.dv), dtype=torch.bfloat16, device="cuda")
+    o_sca = torch.empty((w.B, w.H, w.n, w.dv), dtype=torch.float32, device="cuda")
+    stats = torch.empty((w.B, w.H, w.n, 2), dtype=torch.float32, device="cuda")
+    ws_f = gecko.alloc_workspace(z, v, w.c, 0)
+    nbytes = gecko.gecko_backward_saved_workspace_size(w.B, w.H, w.n, w.d, w.dv, w.c, gecko.GECKO_BF16,
+                                                       gecko.GECKO_BF16)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        gecko.gecko_forward_train(z, params, v, w.c, out=out, o_sca=o_sca, stats=stats, workspace=ws_f,
+                                  stream=stream)
+
+    def bwd():
+        gecko.gecko_backward_saved(z, params, v, do, o_sca, stats, w.c, dz=dz, dv=dvt, daff=daff, workspace=ws,
+                                   stream=stream)
+
+    fwd()
+    ms_b = timed(bwd)
+    ms_t = timed(lambda: (fwd(), bwd()))
+    fl_b = configs.backward_flop_count(w.n, w.c, w.d, w.dv)["total"] * w.B * w.H
+    fl_f = configs.workload_flops(w)["total"]
+    del do, dz, dvt, daff, out, o_sca, stats, ws_f, ws
+    res = {}
+    for key, ms, fl in (("backward_saved", ms_b, fl_b), ("train_step_saved", ms_t, fl_b + fl_f)):
+        achieved = fl / (ms / 1e3) / 1e12
+        res[key] = {"workload": ("bwd_" if key == "backward_saved" else "fwd_bwd_") + w.name, "ms_per_step": ms,
+                    "tokens_per_s": w.B * w.n / (ms / 1e3),
+                    "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "flops_per_call": fl}}
+    res["backward_saved"]["workspace_bytes"] = nbytes
+    return res
 
 
 def time_tdn(gecko, stream, timed) -> dict:

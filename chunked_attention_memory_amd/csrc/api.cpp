@@ -129,6 +129,9 @@ struct Call {
   void* state; size_t state_bytes;
   // gecko_forward_lse: per-query attention log-sum-exp output (bf16 only)
   float* lse;
+  // gecko_forward_train: float32 attention output and per-query (m, l) (bf16 only)
+  float* o_sca;
+  float* stats;
 };
 
 // memory steps and snapshot slots of a call (see gecko::Problem); lag 2 with
@@ -242,6 +245,8 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   p.mstate = nullptr;
   p.zstate = nullptr;
   p.lse = k.lse;
+  p.o_sca = k.o_sca;
+  p.stats = k.stats;
   if (k.streaming) {
     const gecko::StreamState t = gecko::carve_state(k.state, BH, k.d, k.dv, k.c);
     p.mstate = t.mstate;
@@ -538,6 +543,46 @@ gecko_status gecko_forward_lse(const void* z, const float* kappa_q, const float*
   }
 }
 
+gecko_status gecko_forward_train(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                                 const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
+                                 const float* rho_k, const void* v, void* out, float* o_sca, float* stats, int64_t B,
+                                 int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
+                                 gecko_dtype out_dtype, unsigned flags, unsigned parts, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    if (!(parts & GECKO_PART_SCA) || (parts & ~3u))
+      return fail(GECKO_EINVAL, "parts must hold GECKO_PART_SCA (and may hold GECKO_PART_AWM)");
+    if (in_dtype != GECKO_BF16) return fail(GECKO_EUNSUPPORTED, "the training forward is built for bf16 inputs only");
+    if (!gecko::bwd_shape_built(d, dv))
+      return fail(GECKO_EUNSUPPORTED, "the training forward is built for (d, dv) in {(128, 256), (128, 128)}");
+    if (!o_sca || !stats) return fail(GECKO_EINVAL, "o_sca and stats must be non-null");
+    if (!aligned16(o_sca) || (reinterpret_cast<uintptr_t>(stats) & 7u))
+      return fail(GECKO_EINVAL, "o_sca must be 16-byte and stats 8-byte aligned");
+    if (B >= 1 && H >= 1 && n >= 1 && out && B <= (1 << 20) && H <= (1 << 20) && n <= (int64_t(1) << 40)) {
+      const size_t BH = (size_t)B * H;
+      const size_t sb = BH * n * 8, ab = BH * n * dv * 4;
+      const size_t ob = BH * n * dv * (out_dtype == GECKO_BF16 ? 2 : 4);
+      const void* in[] = {z, v};
+      const size_t ib[] = {BH * n * d * 2, BH * n * dv * 2};
+      if (overlaps(o_sca, ab, stats, sb) || overlaps(o_sca, ab, out, ob) || overlaps(stats, sb, out, ob) ||
+          (workspace && (overlaps(o_sca, ab, workspace, workspace_bytes) ||
+                         overlaps(stats, sb, workspace, workspace_bytes))))
+        return fail(GECKO_EINVAL, "o_sca and stats must not alias each other, the output or the workspace");
+      for (int i = 0; i < 2; ++i)
+        if (in[i] && (overlaps(o_sca, ab, in[i], ib[i]) || overlaps(stats, sb, in[i], ib[i])))
+          return fail(GECKO_EINVAL, "o_sca and stats must not alias an input");
+    }
+    const int mode = (parts & GECKO_PART_SCA ? kModeSca : 0) | (parts & GECKO_PART_AWM ? kModeAwm : 0);
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, mode, nullptr};
+    k.o_sca = o_sca;
+    k.stats = stats;
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
 }  // extern "C"
 
 namespace {
@@ -606,6 +651,7 @@ gecko_status bwd_problem(const void* z, const float* const (&aff)[8], const void
   f.stream = false; f.has_prev = false;
   p.dout = dout; p.dz = dz; p.dv = dv_out; p.daff = daff;
   p.sca = sca; p.awm = awm; p.out_f32 = out_dtype == GECKO_F32;
+  p.saved = false; p.o_sca = nullptr; p.stats = nullptr;
   return GECKO_OK;
 }
 
@@ -636,6 +682,7 @@ BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p) {
     w.dk = reinterpret_cast<float*>(take(BH * n * d * 4));
   }
   if (p.out_f32) w.do16 = reinterpret_cast<uint16_t*>(take(BH * n * dv * 2));
+  if (p.saved && p.sca) w.dos = reinterpret_cast<uint16_t*>(take(BH * n * dv * 2));
   if (p.awm) {
     w.dqm = reinterpret_cast<float*>(take(BH * n * d * 4));
     w.dkm = reinterpret_cast<float*>(take(BH * n * d * 4));
@@ -674,6 +721,70 @@ size_t gecko_backward_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d,
   return gecko::carve_bwd_workspace(nullptr, p).bytes;
 }
 
+size_t gecko_backward_saved_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                           gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                                           unsigned parts) {
+  const float* none[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  gecko::BwdProblem p;
+  const std::string saved = g_last_error;
+  if (bwd_problem(nullptr, none, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, n, d, dv, c, in_dtype, out_dtype,
+                  flags, parts, false, p) != GECKO_OK || !p.sca) {
+    g_last_error = saved;
+    return (size_t)-1;
+  }
+  p.saved = true;
+  return gecko::carve_bwd_workspace(nullptr, p).bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// workspace and alias checks, then the launch sequence of both backward entry points
+gecko_status run_backward(const gecko::BwdProblem& p, void* workspace, size_t workspace_bytes, void* stream) {
+  const gecko::BwdWorkspace need = gecko::carve_bwd_workspace(nullptr, p);
+  if (!workspace) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", need.bytes);
+  if (workspace_bytes < need.bytes)
+    return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+    return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
+  {
+    const gecko::Problem& f = p.f;
+    const size_t BH = (size_t)(f.B * f.H), n = (size_t)f.n, d = (size_t)f.d, dv = (size_t)f.dv;
+    const void* o[] = {f.z, f.v, p.dout, p.dz, p.dv, p.daff, p.o_sca, p.stats};
+    const size_t ob = BH * n * dv * (p.out_f32 ? 4 : 2);
+    const size_t b[] = {BH * n * d * 2, BH * n * dv * 2, ob, BH * n * d * 4, BH * n * dv * 4,
+                        (size_t)8 * f.H * d * 4, BH * n * dv * 4, BH * n * 8};
+    for (int i = 0; i < 8; ++i)
+      if (o[i] && overlaps(workspace, need.bytes, o[i], b[i]))
+        return fail(GECKO_EINVAL, "the workspace aliases an input or an output");
+    if (p.saved)
+      for (int i = 6; i < 8; ++i)
+        for (int j = 3; j < 6; ++j)
+          if (o[j] && overlaps(o[i], b[i], o[j], b[j]))
+            return fail(GECKO_EINVAL, "o_sca and stats must not alias an output");
+  }
+  const gecko::BwdWorkspace w = gecko::carve_bwd_workspace(workspace, p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p.out_f32 && (e = gecko::launch_bwd_dout16(p, w, s)) != hipSuccess) return hip_fail(e, "dO conversion launch");
+  if (p.awm && (e = gecko::launch_bwd_awm(p, w, s)) != hipSuccess) return hip_fail(e, "memory backward launch");
+  if (p.sca) {
+    if ((e = gecko::launch_bwd_prep(p, w, s)) != hipSuccess) return hip_fail(e, "attention backward prep launch");
+    if (p.saved && (e = gecko::launch_bwd_saved_prep(p, w, s)) != hipSuccess)
+      return hip_fail(e, "saved statistics launch");
+    if ((e = gecko::launch_bwd_dq(p, w, s)) != hipSuccess) return hip_fail(e, "attention dQ launch");
+    if ((e = gecko::launch_bwd_dkdv(p, w, p.awm, s)) != hipSuccess) return hip_fail(e, "attention dK dV launch");
+  }
+  if ((e = gecko::launch_bwd_combine(p, w, s)) != hipSuccess) return hip_fail(e, "gradient combine launch");
+  g_last_error.clear();
+  return GECKO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gecko_status gecko_backward(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
                             const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
                             const float* rho_k, const void* v, const void* dout, float* dz, float* dv_out,
@@ -686,34 +797,33 @@ gecko_status gecko_backward(const void* z, const float* kappa_q, const float* nu
     gecko_status st = bwd_problem(z, aff, v, dout, dz, dv_out, daff, B, H, n, d, dv, c, in_dtype, out_dtype, flags,
                                   parts, true, p);
     if (st != GECKO_OK) return st;
-    const gecko::BwdWorkspace need = gecko::carve_bwd_workspace(nullptr, p);
-    if (!workspace) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", need.bytes);
-    if (workspace_bytes < need.bytes)
-      return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need.bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
-      return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
-    {
-      const size_t BH = (size_t)(B * H);
-      const void* o[] = {z, v, dout, dz, dv_out, daff};
-      const size_t ob = BH * n * dv * (out_dtype == GECKO_BF16 ? 2 : 4);
-      const size_t b[] = {BH * n * d * 2, BH * n * dv * 2, ob, BH * n * d * 4, BH * n * dv * 4, (size_t)8 * H * d * 4};
-      for (int i = 0; i < 6; ++i)
-        if (o[i] && overlaps(workspace, need.bytes, o[i], b[i]))
-          return fail(GECKO_EINVAL, "the workspace aliases an input or an output");
-    }
-    const gecko::BwdWorkspace w = gecko::carve_bwd_workspace(workspace, p);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (p.out_f32 && (e = gecko::launch_bwd_dout16(p, w, s)) != hipSuccess) return hip_fail(e, "dO conversion launch");
-    if (p.awm && (e = gecko::launch_bwd_awm(p, w, s)) != hipSuccess) return hip_fail(e, "memory backward launch");
-    if (p.sca) {
-      if ((e = gecko::launch_bwd_prep(p, w, s)) != hipSuccess) return hip_fail(e, "attention backward prep launch");
-      if ((e = gecko::launch_bwd_dq(p, w, s)) != hipSuccess) return hip_fail(e, "attention dQ launch");
-      if ((e = gecko::launch_bwd_dkdv(p, w, p.awm, s)) != hipSuccess) return hip_fail(e, "attention dK dV launch");
-    }
-    if ((e = gecko::launch_bwd_combine(p, w, s)) != hipSuccess) return hip_fail(e, "gradient combine launch");
-    g_last_error.clear();
-    return GECKO_OK;
+    return run_backward(p, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
+}
+
+gecko_status gecko_backward_saved(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
+                                  const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
+                                  const float* rho_k, const void* v, const void* dout, const float* o_sca,
+                                  const float* stats, float* dz, float* dv_out, float* daff, int64_t B, int64_t H,
+                                  int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
+                                  gecko_dtype out_dtype, unsigned flags, unsigned parts, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  try {
+    const float* aff[8] = {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k};
+    gecko::BwdProblem p;
+    gecko_status st = bwd_problem(z, aff, v, dout, dz, dv_out, daff, B, H, n, d, dv, c, in_dtype, out_dtype, flags,
+                                  parts, true, p);
+    if (st != GECKO_OK) return st;
+    if (!p.sca) return fail(GECKO_EINVAL, "saved statistics belong to the attention part: parts must hold it");
+    if (!o_sca || !stats) return fail(GECKO_EINVAL, "o_sca and stats must be non-null");
+    if (!aligned16(o_sca) || (reinterpret_cast<uintptr_t>(stats) & 7u))
+      return fail(GECKO_EINVAL, "o_sca must be 16-byte and stats 8-byte aligned");
+    p.saved = true;
+    p.o_sca = o_sca;
+    p.stats = stats;
+    return run_backward(p, workspace, workspace_bytes, stream);
   } catch (...) {
     return fail(GECKO_EHIP, "internal error");
   }
@@ -781,6 +891,6 @@ const char* gecko_status_string(gecko_status status) {
 
 const char* gecko_last_error(void) { return g_last_error.c_str(); }
 
-int gecko_version(void) { return 102; }
+int gecko_version(void) { return 103; }
 
 }  // extern "C"

@@ -154,6 +154,68 @@ inline unsigned xcd_grid(int64_t nblocks, int64_t* per_xcd) {
 #endif
 }
 
+// ---------------------------------------------------------------- saved statistics
+// From the forward's per-query offset m and sum l of its bf16 weights
+// 2^(s - m) (log2 units, as the PV product used them) and its float32
+// attention output O: the attention kernels' dO operand dO' = bf16(dO / l)
+// and, per query, (m, D') with D' = dO' . O. Then
+//   2^(s_ij - m_i) (dO'_i . v_j - D'_i) = P_ij (dP_ij - D_i)
+// for the forward's own weights P_ij = bf16(2^(s_ij - m_i)) / l_i (up to the
+// bf16 rounding of dO / l), and sum_j P_ij dP_ij = D_i holds to float32
+// rounding because O is the forward's product of those same weights: the
+// kernels use (m, D') where they would use their own (lse2, D).
+struct SavedArgs {
+  const void* dout;     // bf16 or float32 [rows][dv]
+  const float* o;       // [rows][dv]
+  const float* stats;   // [rows][2]: (m, l)
+  uint16_t* dos;        // [rows][dv]
+  float* ld;            // [rows][2]: (m, D')
+  int64_t rows;
+  int out_f32;
+};
+
+// DV / 8 threads per row, 8 values each; a row's threads are consecutive
+// lanes of one wave (DV / 8 divides 64)
+template <int DV>
+__global__ __launch_bounds__(256) void bwd_saved_prep_kernel(SavedArgs a) {
+  constexpr int TPR = DV / 8, RPB = 256 / TPR;
+  static_assert(64 % TPR == 0, "a row's threads within one wave");
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int t = threadIdx.x % TPR;
+  // rows past the end repeat the last row (every lane takes part in the
+  // shuffles) and store nothing
+  const int64_t r = row < a.rows ? row : a.rows - 1;
+  const float2 st = *reinterpret_cast<const float2*>(a.stats + 2 * r);
+  const float inv = 1.f / st.y;
+  float x[8];
+  if (a.out_f32) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dout) + r * DV + 8 * t);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = x0[i];
+      x[4 + i] = x1[i];
+    }
+  } else {
+    unpack8(ld16(static_cast<const uint16_t*>(a.dout) + r * DV + 8 * t), x);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] *= inv;
+  const u32x4 pk = pack8(x);
+  unpack8(pk, x);  // the rounded values the products use
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.o + r * DV + 8 * t);
+  const f32x4 o0 = orow[0], o1 = orow[1];
+  float dsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dsum += x[i] * o0[i] + x[4 + i] * o1[i];
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+  if (row < a.rows) {
+    st16(a.dos + row * DV + 8 * t, pk);
+    if (t == 0) *reinterpret_cast<float2*>(a.ld + 2 * row) = make_float2(st.x, dsum);
+  }
+}
+
 // ---------------------------------------------------------------- dq
 struct DqArgs {
   const uint16_t* qp;
@@ -161,10 +223,11 @@ struct DqArgs {
   const uint16_t* v;
   const uint16_t* dO;
   const float* kk;
-  float* ld;   // written: (lse2, D) per query, for the dk dv kernels
+  float* ld;   // written: (lse2, D) per query, for the dk dv kernels (read instead when saved)
   float* dq;
   int64_t n;
   int c, nchunks, qtiles, H, prev;
+  int saved;   // (m, D') of the forward's statistics already in ld: no statistics pass
   uint32_t nblocks, per_xcd;
 };
 
@@ -449,43 +512,52 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb) U[qb][fb] = f32x16{};
   }
-  // First without an offset; if a valid query's sum lies outside
-  // [2^-60, 2^63] (some 2^s overflowed, or every term is tiny), the workgroup
-  // redoes the statistics with the running maximum.
-  l.template pass<0>(st, U, sig);
-  bool redo = false;
+  if (a.saved) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = other_half_sum(st[qb].l);
-    redo = redo || (l.myq[qb] < qend && !(lt >= 0x1p-60f && lt <= 0x1p63f));
-  }
-  if (__syncthreads_or(redo)) {
+    for (int qb = 0; qb < QB; ++qb) {
+      const float2 v = *reinterpret_cast<const float2*>(a.ld + 2 * (base + (size_t)min(l.myq[qb], qend - 1)));
+      l.lse2[qb] = v.x;
+      l.dd[qb] = v.y;
+    }
+  } else {
+    // First without an offset; if a valid query's sum lies outside
+    // [2^-60, 2^63] (some 2^s overflowed, or every term is tiny), the workgroup
+    // redoes the statistics with the running maximum.
+    l.template pass<0>(st, U, sig);
+    bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st[qb] = RowStats{kNegInf, 0.f, 0.f};
-    l.template pass<1>(st, U, sig);
-  }
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = other_half_sum(st[qb].l);
+      redo = redo || (l.myq[qb] < qend && !(lt >= 0x1p-60f && lt <= 0x1p63f));
+    }
+    if (__syncthreads_or(redo)) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    // merge the two lane halves (each saw half of every 32-key block); each
-    // swap result holds this lane's value and the other half's, in the same
-    // order for the three, and the merge is symmetric in the two
-    const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].m), __float_as_uint(st[qb].m), false, false);
-    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].l), __float_as_uint(st[qb].l), false, false);
-    const auto sa = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].a), __float_as_uint(st[qb].a), false, false);
-    const float m0 = __uint_as_float(sm[0]), m1 = __uint_as_float(sm[1]);
-    const float l0 = __uint_as_float(sl[0]), l1 = __uint_as_float(sl[1]);
-    const float a0 = __uint_as_float(sa[0]), a1 = __uint_as_float(sa[1]);
-    const float m = fmaxf(m0, m1);
-    const float f0 = m0 == kNegInf ? 0.f : exp2_fast(m0 - m);
-    const float f1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - m);
-    const float lt = l0 * f0 + l1 * f1, at = a0 * f0 + a1 * f1;
-    const bool any = m != kNegInf && lt > 0.f;
-    l.lse2[qb] = any ? m + log2f(lt) : 0.f;
-    l.dd[qb] = any ? at / lt : 0.f;
-    if (l.g == 0 && l.myq[qb] < qend)
-      *reinterpret_cast<float2*>(a.ld + 2 * (base + (size_t)l.myq[qb])) = make_float2(l.lse2[qb], l.dd[qb]);
+      for (int qb = 0; qb < QB; ++qb) st[qb] = RowStats{kNegInf, 0.f, 0.f};
+      l.template pass<1>(st, U, sig);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // merge the two lane halves (each saw half of every 32-key block); each
+      // swap result holds this lane's value and the other half's, in the same
+      // order for the three, and the merge is symmetric in the two
+      const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].m), __float_as_uint(st[qb].m), false, false);
+      const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].l), __float_as_uint(st[qb].l), false, false);
+      const auto sa = __builtin_amdgcn_permlane32_swap(__float_as_uint(st[qb].a), __float_as_uint(st[qb].a), false, false);
+      const float m0 = __uint_as_float(sm[0]), m1 = __uint_as_float(sm[1]);
+      const float l0 = __uint_as_float(sl[0]), l1 = __uint_as_float(sl[1]);
+      const float a0 = __uint_as_float(sa[0]), a1 = __uint_as_float(sa[1]);
+      const float m = fmaxf(m0, m1);
+      const float f0 = m0 == kNegInf ? 0.f : exp2_fast(m0 - m);
+      const float f1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - m);
+      const float lt = l0 * f0 + l1 * f1, at = a0 * f0 + a1 * f1;
+      const bool any = m != kNegInf && lt > 0.f;
+      l.lse2[qb] = any ? m + log2f(lt) : 0.f;
+      l.dd[qb] = any ? at / lt : 0.f;
+      if (l.g == 0 && l.myq[qb] < qend)
+        *reinterpret_cast<float2*>(a.ld + 2 * (base + (size_t)l.myq[qb])) = make_float2(l.lse2[qb], l.dd[qb]);
+    }
   }
-  // every wave is past the statistics pass's last barrier: its stages are free
+  // after a statistics pass every wave is past its last barrier: the stages are free
   l.template pass<2>(st, U, sig);
 
   // dq = kappa_k * sum_j dS_ij z_j relies on sum_j dS_ij = 0; the bf16 dS
@@ -856,6 +928,9 @@ const uint16_t* dout16(const BwdProblem& p, const BwdWorkspace& w) {
   return w.do16 ? w.do16 : static_cast<const uint16_t*>(p.dout);
 }
 
+// the attention kernels' dO operand: dO / l per query with saved statistics
+const uint16_t* attn_dout(const BwdProblem& p, const BwdWorkspace& w) { return p.saved ? w.dos : dout16(p, w); }
+
 }  // namespace
 
 bool bwd_shape_built(int64_t d, int64_t dv) { return d == 128 && (dv == 256 || dv == 128); }
@@ -879,14 +954,32 @@ hipError_t launch_bwd_dout16(const BwdProblem& p, const BwdWorkspace& w, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_saved_prep(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s) {
+  SavedArgs a;
+  a.dout = p.dout;
+  a.o = p.o_sca;
+  a.stats = p.stats;
+  a.dos = w.dos;
+  a.ld = w.ld;
+  a.rows = p.f.B * p.f.H * p.f.n;
+  a.out_f32 = p.out_f32 ? 1 : 0;
+  if (p.f.dv == 256) {
+    hipLaunchKernelGGL((bwd_saved_prep_kernel<256>), dim3((unsigned)((a.rows + 7) / 8)), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_saved_prep_kernel<128>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s) {
   constexpr int NW = GECKO_BWD_DQ_NW, QB = GECKO_BWD_DQ_QB;
   DqArgs a;
   a.qp = w.qp;
   a.z = static_cast<const uint16_t*>(p.f.z);
   a.v = static_cast<const uint16_t*>(p.f.v);
-  a.dO = dout16(p, w);
+  a.dO = attn_dout(p, w);
   a.ld = w.ld; a.kk = p.f.kappa_k; a.dq = w.dq;
+  a.saved = p.saved ? 1 : 0;
   a.n = p.f.n;
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;
   a.c = (int)cc; a.nchunks = (int)p.f.nchunks; a.H = (int)p.f.H; a.prev = (int)p.f.prev;
@@ -921,7 +1014,7 @@ hipError_t launch_bwd_dkdv(const BwdProblem& p, const BwdWorkspace& w, bool accu
   a.qp = w.qp;
   a.z = static_cast<const uint16_t*>(p.f.z);
   a.v = static_cast<const uint16_t*>(p.f.v);
-  a.dO = dout16(p, w);
+  a.dO = attn_dout(p, w);
   a.ld = w.ld; a.kq = p.f.kappa_q; a.nq = p.f.nu_q; a.dk = w.dk; a.dv = p.dv;
   a.n = p.f.n;
   const int64_t cc = p.f.c < p.f.n ? p.f.c : p.f.n;

@@ -42,6 +42,8 @@ struct Problem {
   float* mstate;        // [BH][dv/32][d/32][64][16] fp32 state M'^T (scan accumulator layout), in/out
   const float* zstate;  // [BH][d][2] running (M, L) per feature (log2 max, scaled sum) before this call
   float* lse;           // bf16 attention only, may be null: [BH][n] natural log-sum-exp of each query's logits
+  float* o_sca;         // bf16 attention only, may be null: [BH][n][dv] float32 attention output alone
+  float* stats;         // bf16 attention only, may be null: [BH][n][2] offset and sum of the bf16 weights
 };
 
 // Workspace carve-up (byte offsets from the workspace base). Every array is
@@ -94,6 +96,10 @@ struct BwdProblem {
   float* dv;            // [BH][n][dv]
   float* daff;          // [8][H][d]: kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k
   bool sca, awm, out_f32;
+  // saved attention statistics of the forward (gecko_backward_saved), else null
+  bool saved;
+  const float* o_sca;   // [BH][n][dv] float32 attention output
+  const float* stats;   // [BH][n][2] offset m and sum l of the bf16 weights 2^(s - m)
 };
 
 // Backward workspace. Arrays indexed [bh][t] have t = 0..nmem-1, the chunk
@@ -103,6 +109,7 @@ struct BwdWorkspace {
   uint16_t* qp;         // scaled queries (kappa_q z + nu_q) kappa_k log2(e), bf16 [BH][n][d]
   float* ld;            // per query: (log2-sum-exp of the scaled logits, sum_j P_ij dP_ij) [BH][n][2]
   uint16_t* do16;       // dO in bf16 [BH][n][dv] when dO is float32 (else null: dO itself)
+  uint16_t* dos;        // saved statistics: bf16(dO / l) per query, the attention kernels' dO [BH][n][dv]
   float* dq;            // dL/dQ, dL/dK, dL/dQ_m, dL/dK_m, each [BH][n][d]
   float* dk;
   float* dqm;
@@ -124,6 +131,7 @@ BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p);
 bool bwd_shape_built(int64_t d, int64_t dv);
 hipError_t launch_bwd_prep(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
 hipError_t launch_bwd_dout16(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_bwd_saved_prep(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdProblem& p, const BwdWorkspace& w, bool accumulate_dv, hipStream_t s);
 hipError_t launch_bwd_awm(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s);

@@ -128,6 +128,8 @@ struct ScaArgs {
   const float* kappa_k;
   const float* nu_k;   // read only when lse is set
   float* lse;          // optional [bh][n]: natural log-sum-exp of each query's logits
+  float* o_sca;        // optional [bh][n][dv] float32: the attention output alone
+  float* stats;        // optional [bh][n][2]: offset m and sum l of the bf16 weights 2^(s - m)
   const float* eta_q;
   const float* rho_q;
   const uint16_t* snap;  // [bh][nsnap][d][dv]; chunk s reads slot s - 2 + 2 has_prev (0-based)
@@ -639,6 +641,32 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
     L.init(a, bh, h, n, s, c, q0, qend, w, lane, S0, S1, S2, va);
     float msub[QB];
     L.run(oacc, lsum, msub);
+    // training outputs: O_SCA = oacc / lsum in float32 (accumulator register
+    // r of block mv holds value column 32 mv + 16 (r >> 3) + 8 g + (r & 7)),
+    // and per query the offset and the sum of the bf16 weights the PV product
+    // used, from which a backward pass rebuilds exactly those weights
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int myq = myq0 + 32 * qb;
+      if (myq >= qend) continue;
+      if (a.stats && g == 0)
+        *reinterpret_cast<float2*>(a.stats + 2 * ((size_t)bh * n + myq)) = make_float2(msub[qb], lsum[qb]);
+      if (a.o_sca) {
+        const float inv = 1.f / lsum[qb];
+        float* orow = a.o_sca + ((size_t)bh * n + myq) * DV;
+#pragma unroll
+        for (int mv = 0; mv < NMV; ++mv)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const f32x16& o = oacc[qb][mv];
+            float* dst = orow + 32 * mv + 16 * hh + 8 * g;
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{o[8 * hh + 0] * inv, o[8 * hh + 1] * inv, o[8 * hh + 2] * inv, o[8 * hh + 3] * inv};
+            *reinterpret_cast<f32x4*>(dst + 4) =
+                f32x4{o[8 * hh + 4] * inv, o[8 * hh + 5] * inv, o[8 * hh + 6] * inv, o[8 * hh + 7] * inv};
+          }
+      }
+    }
     if (a.lse) {
       // the kernel's logits are log2(e) (q_i . k_j - q_i . nu_k) (see the
       // header), so log sum_j exp(q_i . k_j) = ln 2 (msub + log2 lsum) + q_i . nu_k
@@ -821,6 +849,7 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   a.out = p.out;
   a.kappa_q = p.kappa_q; a.nu_q = p.nu_q; a.kappa_k = p.kappa_k;
   a.nu_k = p.nu_k; a.lse = p.lse;
+  a.o_sca = p.o_sca; a.stats = p.stats;
   a.eta_q = p.eta_q; a.rho_q = p.rho_q;
   a.snap = static_cast<const uint16_t*>(w.snap);
   a.zprev = static_cast<const uint16_t*>(p.zprev);

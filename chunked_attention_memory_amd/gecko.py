@@ -28,6 +28,7 @@ EXPORTED = (
     "gecko_workspace_size_for", "gecko_cema_workspace_size", "gecko_cema_forward",
     "gecko_tdn_workspace_size", "gecko_tdn_forward",
     "gecko_forward_lse", "gecko_backward_workspace_size", "gecko_backward",
+    "gecko_forward_train", "gecko_backward_saved_workspace_size", "gecko_backward_saved",
 )
 
 
@@ -97,6 +98,12 @@ def _load() -> ctypes.CDLL:
     lib.gecko_backward_workspace_size.argtypes = [I64] * 6 + [I, I, U, U]
     lib.gecko_backward.restype = I
     lib.gecko_backward.argtypes = [P] + [F] * 8 + [P, P, P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_forward_train.restype = I
+    lib.gecko_forward_train.argtypes = [P] + [F] * 8 + [P, P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_backward_saved_workspace_size.restype = SZ
+    lib.gecko_backward_saved_workspace_size.argtypes = [I64] * 6 + [I, I, U, U]
+    lib.gecko_backward_saved.restype = I
+    lib.gecko_backward_saved.argtypes = [P] + [F] * 8 + [P] * 7 + [I64] * 6 + [I, I, U, U, P, SZ, P]
     return lib
 
 
@@ -438,6 +445,28 @@ def gecko_forward_lse(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, ou
     return out, lse
 
 
+def gecko_forward_train(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, out=None, o_sca=None, stats=None,
+                        out_dtype=None, flags=0, workspace=None, stream=None):
+    """O of the selected parts, the attention output alone (``o_sca`` [B, H, n, dv] float32) and the per-query
+    offset and bf16-weight sum (``stats`` [B, H, n, 2] float32) that gecko_backward_saved reuses."""
+    import torch
+
+    B, H, n, d, dv = _shape(z, v)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+    if o_sca is None:
+        o_sca = torch.empty((B, H, n, dv), dtype=torch.float32, device=z.device)
+    if stats is None:
+        stats = torch.empty((B, H, n, 2), dtype=torch.float32, device=z.device)
+    if workspace is None and parts & GECKO_PART_AWM:
+        workspace = alloc_workspace(z, v, c, flags)
+    _check(lib.gecko_forward_train(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(out),
+                                   _ptr(o_sca), _ptr(stats), B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out),
+                                   flags, parts, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   _stream(stream)))
+    return out, o_sca, stats
+
+
 def gecko_backward_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags=0,
                                   parts=GECKO_PART_SCA | GECKO_PART_AWM) -> int:
     r = lib.gecko_backward_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags, parts)
@@ -467,6 +496,45 @@ def gecko_backward(z, params, v, dout, c, parts=GECKO_PART_SCA | GECKO_PART_AWM,
     _check(lib.gecko_backward(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
                               _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c, _dtype_code(z),
                               _dtype_code(dout), flags, parts, _ptr(workspace), workspace.numel(), _stream(stream)))
+    res = {"dz": dz, "dv": dv}
+    for i, k in enumerate(Q_NAMES + M_NAMES):
+        res["d" + k] = daff[i]
+    return res
+
+
+def gecko_backward_saved_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags=0,
+                                        parts=GECKO_PART_SCA | GECKO_PART_AWM) -> int:
+    r = lib.gecko_backward_saved_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags, parts)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid or unsupported arguments for gecko_backward_saved_workspace_size")
+    return r
+
+
+def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, flags=0,
+                         dz=None, dv=None, daff=None, workspace=None, stream=None):
+    """gecko_backward with the attention statistics of gecko_forward_train (same inputs, parts and flags)."""
+    import torch
+
+    B, H, n, d, dvs = _shape(z, v)
+    if tuple(dout.shape) != (B, H, n, dvs) or not dout.is_contiguous():
+        raise GeckoError(GECKO_EINVAL, "dout must be a contiguous [B, H, n, dv] tensor")
+    if (tuple(o_sca.shape) != (B, H, n, dvs) or o_sca.dtype != torch.float32 or not o_sca.is_contiguous()
+            or tuple(stats.shape) != (B, H, n, 2) or stats.dtype != torch.float32 or not stats.is_contiguous()):
+        raise GeckoError(GECKO_EINVAL, "o_sca must be float32 [B, H, n, dv] and stats float32 [B, H, n, 2]")
+    if dz is None:
+        dz = torch.empty((B, H, n, d), dtype=torch.float32, device=z.device)
+    if dv is None:
+        dv = torch.empty((B, H, n, dvs), dtype=torch.float32, device=z.device)
+    if daff is None:
+        daff = torch.empty((8, H, d), dtype=torch.float32, device=z.device)
+    if workspace is None:
+        nbytes = gecko_backward_saved_workspace_size(B, H, n, d, dvs, c, _dtype_code(z), _dtype_code(dout), flags,
+                                                     parts)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+    _check(lib.gecko_backward_saved(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
+                                    _ptr(o_sca), _ptr(stats), _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c,
+                                    _dtype_code(z), _dtype_code(dout), flags, parts, _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
     res = {"dz": dz, "dv": dv}
     for i, k in enumerate(Q_NAMES + M_NAMES):
         res["d" + k] = daff[i]

@@ -305,6 +305,53 @@ gecko_status gecko_backward(
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training forward: out exactly as gecko_forward_lse / gecko_sca_awm_forward
+ * with the same arguments, plus what gecko_backward_saved reuses in place of
+ * its statistics pass (training, per the paperlayer.ai summary, Appendix B.1:
+ * keep what the backward needs rather than recompute it; the quantities are
+ * those of the attention step, paper.rainbus.top, "Method steps" (3)):
+ *   o_sca: [B][H][n][dv] float32, 16-byte aligned, caller-owned, fully
+ *       overwritten: the attention output O_SCA alone.
+ *   stats: [B][H][n][2] float32, 8-byte aligned, fully overwritten: per query
+ *       the offset m and the sum l of the weights 2^(s - m) rounded to bf16,
+ *       as the attention's value product used them; s is the query's logit
+ *       less q . nu_k, times log2(e) (a shift shared by the query's keys).
+ *       O_SCA = (sum_j bf16(2^(s_j - m)) v_j) / l.
+ * bf16 inputs, (d, dv) in {(128, 256), (128, 128)}; parts must include
+ * GECKO_PART_SCA. o_sca and stats must not alias each other, an input, the
+ * output or the workspace (GECKO_EINVAL). Workspace as gecko_workspace_size. */
+gecko_status gecko_forward_train(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out, float* o_sca, float* stats,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gecko_backward_saved needs: gecko_backward's
+ * plus the per-query scaled copy of dO ((size_t)-1 if the arguments are
+ * invalid, not built, or parts lacks GECKO_PART_SCA). */
+size_t gecko_backward_saved_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                                           gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                                           unsigned parts);
+
+/* gecko_backward with the attention statistics of gecko_forward_train of the
+ * same inputs, parts and flags (o_sca, stats as written there; read only,
+ * not aliasing an output or the workspace): the same gradients, with the
+ * attention weights taken as the forward's own bf16-rounded ones, and no
+ * statistics pass over the key window. parts must include GECKO_PART_SCA;
+ * other arguments and errors as gecko_backward. */
+gecko_status gecko_backward_saved(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, const void* dout, const float* o_sca, const float* stats,
+    float* dz, float* dv_out, float* daff,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gecko_status_string(gecko_status status);
 

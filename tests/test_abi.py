@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gecko_version() == 102
+    assert g.gecko_version() == 103
     for s in range(5):
         assert g.gecko_status_string(s).startswith("GECKO_")
     assert "unknown" in g.gecko_status_string(99)
@@ -313,3 +313,69 @@ def test_forward_lse_host_checks(g):
     assert st == g.GECKO_EINVAL and "alias" in msg
     st, msg = call()  # the memory part needs the workspace
     assert st == g.GECKO_EWORKSPACE
+
+
+def test_forward_train_host_checks(g):
+    def call(**kw):
+        a = dict(parts=3, o=4 * FAKE, stats=5 * FAKE, din=g.GECKO_BF16, d=128, dvs=256, ws=0, wsb=0)
+        a.update(kw)
+        st = g.lib.gecko_forward_train(FAKE, *[FAKE + 64 * i for i in range(8)], 2 * FAKE, 3 * FAKE, a["o"],
+                                       a["stats"], 1, 1, 1000, a["d"], a["dvs"], 100, a["din"], g.GECKO_BF16, 0,
+                                       a["parts"], a["ws"], a["wsb"], None)
+        return st, g.lib.gecko_last_error().decode()
+
+    st, msg = call(parts=g.GECKO_PART_AWM)
+    assert st == g.GECKO_EINVAL and "GECKO_PART_SCA" in msg
+    st, msg = call(din=g.GECKO_F32)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, msg = call(d=64, dvs=128)
+    assert st == g.GECKO_EUNSUPPORTED
+    st, msg = call(o=0)
+    assert st == g.GECKO_EINVAL and "non-null" in msg
+    st, msg = call(stats=5 * FAKE + 4)
+    assert st == g.GECKO_EINVAL and "aligned" in msg
+    st, msg = call(o=3 * FAKE + 64)  # inside out
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call(stats=FAKE + 256)  # inside z
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call()  # the memory part needs the workspace
+    assert st == g.GECKO_EWORKSPACE
+
+
+def call_bwd_saved(g, **kw):
+    a = dict(z=FAKE, aff=[FAKE + 64 * i for i in range(8)], v=2 * FAKE, dout=5 * FAKE, o=3 * FAKE, stats=4 * FAKE,
+             dz=6 * FAKE, dv=7 * FAKE, daff=8 * FAKE, parts=3, ws=0, wsb=0)
+    a.update(kw)
+    st = g.lib.gecko_backward_saved(a["z"], *a["aff"], a["v"], a["dout"], a["o"], a["stats"], a["dz"], a["dv"],
+                                    a["daff"], 1, 1, 1000, 128, 256, 128, g.GECKO_BF16, g.GECKO_BF16, 0, a["parts"],
+                                    a["ws"], a["wsb"], None)
+    return st, g.lib.gecko_last_error().decode()
+
+
+def test_backward_saved_host_checks(g):
+    st, msg = call_bwd_saved(g)
+    assert st == g.GECKO_EWORKSPACE and "workspace" in msg
+    st, msg = call_bwd_saved(g, parts=g.GECKO_PART_AWM)
+    assert st == g.GECKO_EINVAL and "attention" in msg
+    st, msg = call_bwd_saved(g, o=0)
+    assert st == g.GECKO_EINVAL and "non-null" in msg
+    st, msg = call_bwd_saved(g, stats=4 * FAKE + 4)
+    assert st == g.GECKO_EINVAL and "aligned" in msg
+    st, msg = call_bwd_saved(g, o=FAKE + 8)
+    assert st == g.GECKO_EINVAL and "aligned" in msg
+    # with a workspace, the alias checks (every case below fails before any launch)
+    ws = 16 * FAKE
+    st, msg = call_bwd_saved(g, o=6 * FAKE, ws=ws, wsb=1 << 40)  # o_sca on top of dz
+    assert st == g.GECKO_EINVAL and "alias" in msg
+    st, msg = call_bwd_saved(g, stats=ws + 4096, ws=ws, wsb=1 << 40)  # stats inside the workspace
+    assert st == g.GECKO_EINVAL and "alias" in msg
+
+
+def test_backward_saved_workspace_size(g):
+    rows = 8 * 131072
+    plain = g.gecko_backward_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16)
+    saved = g.gecko_backward_saved_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16)
+    assert saved >= plain + rows * 256 * 2  # the per-query scaled dO (bf16)
+    with pytest.raises(g.GeckoError):
+        g.gecko_backward_saved_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16,
+                                              parts=g.GECKO_PART_AWM)
