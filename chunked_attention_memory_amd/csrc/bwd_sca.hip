@@ -18,7 +18,8 @@
 // Kernels:
 //  * prep: q' (bf16); dO in bf16 when it comes as float32.
 //  * dq: one workgroup = 256 queries of one chunk (8 waves x 32), streaming
-//    the key window in 64-key tiles twice. Per 32-key half and wave,
+//    the key window in 64-key tiles twice (once with saved statistics). Per
+//    32-key half and wave,
 //      S^T = Z_keys q'^T, dP^T = V dO^T,
 //    then (first pass) the row statistics lse2_i and D_i = sum_j P_ij dP_ij,
 //    or (second pass) dS^T and U^T += Z_keys^T dS^T; dL/dq = kappa_k * U.
@@ -26,10 +27,10 @@
 //    queries that see them (the rest of their chunk, the next chunk) in
 //    64-query tiles; per 32-query half and wave,
 //      S = q' Z_keys^T, dP = dO V^T, dV^T += dO^T P, Y^T += Z_q^T dS
-//    and dL/dk = kappa_q * Y + nu_q * colsum(dS) at the end. With dv = 256
-//    the dV and dK accumulators of one wave do not fit its registers at two
-//    waves per SIMD, so dV (S, P, dV) and dK (S, dP, dS, Y) run as two
-//    kernels of 8 waves; with dv = 128 one kernel of 4 waves does both.
+//    and dL/dk = kappa_q * Y + nu_q * colsum(dS) at the end: one kernel of 4
+//    waves (one per SIMD: with dv = 256 the dV and dK accumulators take a
+//    wave's whole register file), or as a build option dV (S, P, dV) and dK
+//    (S, dP, dS, Y) as two kernels of 8 waves.
 // Key (query) tiles go from HBM straight into LDS (buffer loads writing LDS),
 // two stages; all operands come from LDS through lds_row / lds_tr.
 #include <algorithm>
@@ -43,16 +44,20 @@ namespace {
 constexpr int kT = 64;  // rows per staged tile
 
 // Waves per workgroup of the dq kernel, and the dk dv layout at dv = 256:
-// 0 one kernel for both accumulators, 4 waves of one key block; 1 separate
-// dV and dK kernels of 4 waves of GECKO_BWD_QB key blocks; 2 separate
-// kernels of 8 waves of one block. Eight waves (two per SIMD, so that one
-// wave's exponentials overlap the other's MFMAs) fit the registers only with
-// the two 32-row halves of a tile processed in a loop rather than unrolled.
+// 0 one kernel for both accumulators, 4 waves of one key block (one wave per
+// SIMD: the dV and dK accumulators together need its whole register file);
+// 1 separate dV and dK kernels of 4 waves of GECKO_BWD_QB key blocks; 2
+// separate kernels of 8 waves of one block (two waves per SIMD, so that one
+// wave's exponentials overlap the other's MFMAs). Eight waves fit the
+// registers only with the two 32-row halves of a tile processed in a loop
+// rather than unrolled. With the XCD-aware workgroup order, 0 is the fastest
+// at 128K tokens (5.9 ms against 6.3 ms for 2): it forms S and reads each
+// query tile once for both products.
 #ifndef GECKO_BWD_DQ_NW
 #define GECKO_BWD_DQ_NW 8
 #endif
 #ifndef GECKO_BWD_KV256
-#define GECKO_BWD_KV256 2
+#define GECKO_BWD_KV256 0
 #endif
 // Operand reads from LDS run GECKO_BWD_AHEAD MFMAs ahead of their use;
 // GECKO_BWD_SCHED pins that interleave with scheduling group barriers.
@@ -1025,8 +1030,7 @@ hipError_t launch_bwd_dkdv(const BwdProblem& p, const BwdWorkspace& w, bool accu
 #if GECKO_BWD_KV256 == 0
   return launch_kv<256, 4, 1, 0>(a, p, s);
 #else
-  // dv = 256: the dV and dK accumulators of the wave's key blocks together
-  // exceed the register file, so dV and dK run as two kernels
+  // dv = 256 as two kernels (GECKO_BWD_KV256 1 or 2, see above)
   constexpr int NW = GECKO_BWD_KV256 == 2 ? 8 : 4, KB = GECKO_BWD_KV256 == 2 ? 1 : GECKO_BWD_QB;
   hipError_t e = launch_kv<256, NW, KB, 1>(a, p, s);
   if (e != hipSuccess) return e;
