@@ -209,3 +209,40 @@ def test_backward_saved_full_size():
             got = to_numpy(sca[key][0, h, s * c:(s + 1) * c])
             fro, mx = _errors(got, want[key][0, 0, c:2 * c])
             assert fro <= GRAD_TOL and mx <= GRAD_TOL, (s, h, key, fro, mx)
+
+
+def test_backward_saved_one_million_tokens():
+    """1,048,576 tokens (512 chunks of 2048, B1 H2; o_sca alone is 2 GiB):
+    finite gradients, <V, dV> = <dO, O>, and the saved backward within the
+    bar of the recomputing one on sampled rows of every 64th chunk."""
+    import torch
+
+    g = gecko()
+    B, H, n, c, d, dv = 1, 2, 1 << 20, 2048, 128, 256
+    dev = inputs.make_inputs_device(B, H, n, d, dv, "bf16", seed=5, tag=413)
+    z, v = dev["z"], dev["v"]
+    p = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(413)
+    do = torch.randn((B, H, n, dv), generator=gen, device="cuda").to(torch.bfloat16)
+    announce(f"saved backward n={n} c={c} H={H}")
+    out, o_sca, stats = g.gecko_forward_train(z, p, v, c, out_dtype=torch.float32)
+    res = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(res["dz"]).all() and torch.isfinite(res["dv"]).all()
+    assert all(torch.isfinite(res["d" + k]).all() for k in NAMES)
+    for h in range(H):
+        lhs = float((v[0, h].double() * res["dv"][0, h].double()).sum())
+        rhs = float((do[0, h].double() * out[0, h].double()).sum())
+        scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
+        assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
+    del out, o_sca, stats
+    ref = g.gecko_backward(z, p, v, do, c)
+    torch.cuda.synchronize()
+    rows = torch.cat([torch.arange(s * c, s * c + 256) for s in range(0, n // c, 64)]).cuda()
+    for key in ("dz", "dv"):
+        for h in range(H):
+            got = to_numpy(res[key][0, h].index_select(0, rows))
+            want = to_numpy(ref[key][0, h].index_select(0, rows))
+            fro, mx = _errors(got, want)
+            assert fro <= GRAD_TOL and mx <= GRAD_TOL, (key, h, fro, mx)
