@@ -378,7 +378,15 @@ struct SideArgs {
   float* dv;              // [bh][n][dv]
   int64_t n, c, nmem;
   int nchunks, blocks_per_chunk, H, lag;
+  uint32_t nblocks, per_xcd;
 };
+
+// Workgroups go to the 8 XCDs round-robin, each with its own L2; logical
+// block (b mod 8) per_xcd + b / 8 keeps the blocks of one chunk (which all
+// stage that chunk's state-sized operands) on one XCD.
+__device__ __forceinline__ uint32_t side_block(const SideArgs& a) {
+  return (blockIdx.x & 7u) * a.per_xcd + (blockIdx.x >> 3);
+}
 
 // features of lane half g in B-operand order: k-step ks, element e -> 16 ks + 8 g + e
 template <int D>
@@ -420,8 +428,10 @@ __global__ __launch_bounds__(512, 1) void bwd_qside_kernel(SideArgs a) {
   constexpr int MB = D * DV * 2;
   __shared__ __attribute__((aligned(16))) char Ms[MB];
   __shared__ float CS[512];
-  const int blk = (int)(blockIdx.x % (unsigned)a.blocks_per_chunk);
-  const int rest = (int)(blockIdx.x / (unsigned)a.blocks_per_chunk);
+  const uint32_t lb = side_block(a);
+  if (lb >= a.nblocks) return;
+  const int blk = (int)(lb % (unsigned)a.blocks_per_chunk);
+  const int rest = (int)(lb / (unsigned)a.blocks_per_chunk);
   const int s = rest % a.nchunks;
   const int64_t bh = rest / a.nchunks;
   const int h = (int)(bh % a.H);
@@ -529,8 +539,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kside_kernel(SideArgs a) {
   __shared__ __attribute__((aligned(16))) char DSs[DSB];
   __shared__ __attribute__((aligned(16))) char Xs[kNoDelta ? 16 : XB];
   __shared__ __attribute__((aligned(16))) float FV[2 * D];  // log2 z_t, zeta_t
-  const int blk = (int)(blockIdx.x % (unsigned)a.blocks_per_chunk);
-  const int rest = (int)(blockIdx.x / (unsigned)a.blocks_per_chunk);
+  const uint32_t lb = side_block(a);
+  if (lb >= a.nblocks) return;
+  const int blk = (int)(lb % (unsigned)a.blocks_per_chunk);
+  const int rest = (int)(lb / (unsigned)a.blocks_per_chunk);
   const int t = rest % a.nchunks;
   const int64_t bh = rest / a.nchunks;
   const int h = (int)(bh % a.H);
@@ -727,7 +739,10 @@ hipError_t launch_all(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s)
   sa.nchunks = (int)f.nchunks;
   sa.blocks_per_chunk = (int)((cc + 255) / 256);
   sa.H = (int)f.H; sa.lag = (int)f.lag;
-  const dim3 grid((unsigned)(BH * f.nchunks * sa.blocks_per_chunk));
+  const int64_t nblocks = BH * f.nchunks * sa.blocks_per_chunk;
+  sa.nblocks = (uint32_t)nblocks;
+  sa.per_xcd = (uint32_t)((nblocks + 7) / 8);
+  const dim3 grid((unsigned)(8 * sa.per_xcd));
   hipLaunchKernelGGL((bwd_qside_kernel<D, DV>), grid, dim3(512), 0, s, sa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (no_delta)
