@@ -1,6 +1,7 @@
 """ctypes binding of libgecko.so (declared in include/gecko.h).
 
-Argument marshalling only: every step of the forward runs in the HIP library.
+Argument marshalling only: every step of the forward and the backward runs in
+the HIP library.
 Tensors are torch tensors on the GPU (torch provides device memory and the
 stream); shapes are taken from them. Importing this module loads the library
 and raises if it has not been built (``python -m chunked_attention_memory_amd.build``).
