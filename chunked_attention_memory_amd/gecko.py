@@ -513,7 +513,7 @@ def gecko_backward_saved_workspace_size(B, H, n, d, dv, c, in_code, out_code, fl
 
 def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, flags=0,
                          dz=None, dv=None, daff=None, workspace=None, stream=None):
-    """gecko_backward with the attention statistics of gecko_forward_train (same inputs, parts and flags)."""
+    """gecko_backward with the attention statistics of gecko_forward_train (same inputs, c, parts and flags)."""
     import torch
 
     B, H, n, d, dvs = _shape(z, v)

@@ -337,7 +337,7 @@ size_t gecko_backward_saved_workspace_size(int64_t B, int64_t H, int64_t n, int6
                                            unsigned parts);
 
 /* gecko_backward with the attention statistics of gecko_forward_train of the
- * same inputs, parts and flags (o_sca, stats as written there; read only,
+ * same inputs, c, parts and flags (o_sca, stats as written there; read only,
  * not aliasing an output or the workspace): the same gradients, with the
  * attention weights taken as the forward's own bf16-rounded ones, and no
  * statistics pass over the key window. parts must include GECKO_PART_SCA;
