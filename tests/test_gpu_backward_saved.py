@@ -171,9 +171,10 @@ def test_backward_saved_agrees_with_recompute_and_repeats():
 
 def test_backward_saved_full_size():
     """The bench configuration (B1 H8, 131072 tokens, c 2048), both parts:
-    finite gradients; <V, dV> = <dO, O>; the attention gradients of chunks 1
-    and 40 of two heads against the oracle on their three-chunk stretches
-    (attention-only call)."""
+    finite gradients; <V, dV> = <dO, O>; the training forward's O_SCA of
+    chunks 1, 40 and 63 against the oracle on their two-chunk stretches; the
+    attention gradients of chunks 1 and 40 of two heads against the oracle on
+    their three-chunk stretches (attention-only call)."""
     import torch
 
     g = gecko()
@@ -194,6 +195,16 @@ def test_backward_saved_full_size():
         rhs = float((do[0, h].double() * out[0, h].double()).sum())
         scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
         assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
+    # the training forward's attention output on sampled chunks: the oracle's
+    # O_SCA of chunk s needs chunks s-1 and s only
+    for s, h in ((1, 0), (40, 5), (63, 7)):
+        a, b = (s - 1) * c, (s + 1) * c
+        zs = z[0, h, a:b].float().cpu().numpy().astype(np.float64)
+        vs = v[0, h, a:b].float().cpu().numpy().astype(np.float64)
+        pr = dev["params"]
+        want = oracle.sca_head(zs, vs, pr["kappa_q"][h], pr["nu_q"][h], pr["kappa_k"][h], pr["nu_k"][h], c)
+        fro, mx = _errors(to_numpy(o_sca[0, h, s * c:(s + 1) * c]), want[c:])
+        assert fro <= GRAD_TOL and mx <= GRAD_TOL, (s, h, fro, mx)
     del out, res
     _, o_sca, stats = g.gecko_forward_train(z, p, v, c, parts=g.GECKO_PART_SCA)
     sca = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c, parts=g.GECKO_PART_SCA)
