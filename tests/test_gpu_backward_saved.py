@@ -257,3 +257,53 @@ def test_backward_saved_one_million_tokens():
             want = to_numpy(ref[key][0, h].index_select(0, rows))
             fro, mx = _errors(got, want)
             assert fro <= GRAD_TOL and mx <= GRAD_TOL, (key, h, fro, mx)
+
+
+def test_training_pair_four_million_tokens():
+    """The largest configuration (B1 H4, 4,194,304 tokens, c 2048): each (batch,
+    head) slab of V and its gradients holds 2^30 values and the arrays 2^32,
+    so every offset past a slab is 64-bit. The training forward and the
+    saved-statistics backward run to completion with finite gradients,
+    <V, dV> = <dO, O> per head, and the attention gradients of the first and
+    the last chunk of a head against the oracle on their three-chunk
+    stretches (attention-only call)."""
+    import torch
+
+    g = gecko()
+    B, H, n, c, d, dv = 1, 4, 1 << 22, 2048, 128, 256
+    dev = inputs.make_inputs_device(B, H, n, d, dv, "bf16", seed=7, tag=414)
+    z, v = dev["z"], dev["v"]
+    p = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(414)
+    do = torch.empty((B, H, n, dv), dtype=torch.bfloat16, device="cuda")
+    for h in range(H):  # drawn per head to bound the float32 temporary
+        do[0, h] = torch.randn((n, dv), generator=gen, device="cuda").to(torch.bfloat16)
+    announce(f"training pair n={n} c={c} H={H}")
+    out, o_sca, stats = g.gecko_forward_train(z, p, v, c)
+    res = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(res["dz"]).all() and torch.isfinite(res["dv"]).all()
+    assert all(torch.isfinite(res["d" + k]).all() for k in NAMES)
+    for h in range(H):
+        lhs = float((v[0, h].double() * res["dv"][0, h].double()).sum())
+        rhs = float((do[0, h].double() * out[0, h].float().double()).sum())
+        scale = float((v[0, h].double() * res["dv"][0, h].double()).abs().sum())
+        assert abs(lhs - rhs) <= 1e-2 * scale, (h, lhs, rhs, scale)
+    del out, o_sca, stats, res
+    torch.cuda.empty_cache()
+    _, o_sca, stats = g.gecko_forward_train(z, p, v, c, parts=g.GECKO_PART_SCA)
+    sca = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c, parts=g.GECKO_PART_SCA)
+    torch.cuda.synchronize()
+    N = n // c
+    for s, h in ((1, 3), (N - 2, 3)):
+        a, b = (s - 1) * c, (s + 2) * c
+        zs = z[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        vs = v[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ds = do[0, h, a:b].float().cpu().numpy().astype(np.float64)[None, None]
+        ph = {k: dev["params"][k][h:h + 1] for k in dev["params"]}
+        want = go.grad(zs, vs, ph, c, ds, parts=("sca",))
+        for key in ("dz", "dv"):
+            got = to_numpy(sca[key][0, h, s * c:(s + 1) * c])
+            fro, mx = _errors(got, want[key][0, 0, c:2 * c])
+            assert fro <= GRAD_TOL and mx <= GRAD_TOL, (s, h, key, fro, mx)
