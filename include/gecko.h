@@ -307,9 +307,11 @@ gecko_status gecko_backward(
 
 /* Training forward: out exactly as gecko_forward_lse / gecko_sca_awm_forward
  * with the same arguments, plus what gecko_backward_saved reuses in place of
- * its statistics pass (training, per the paperlayer.ai summary, Appendix B.1:
- * keep what the backward needs rather than recompute it; the quantities are
- * those of the attention step, paper.rainbus.top, "Method steps" (3)):
+ * its statistics pass over the attention window (the quantities are those of
+ * the attention step, paper.rainbus.top, "Method steps" (3); the pages'
+ * training recomputes the memory from chunk-boundary states, paperlayer.ai
+ * summary, Appendix B.1, which gecko_backward_saved still does; keeping the
+ * attention's per-query statistics instead is this library's choice):
  *   o_sca: [B][H][n][dv] float32, 16-byte aligned, caller-owned, fully
  *       overwritten: the attention output O_SCA alone.
  *   stats: [B][H][n][2] float32, 8-byte aligned, fully overwritten: per query
