@@ -170,11 +170,12 @@ struct TdnProblem {
   float beta1, beta2, eps;
   bool in_bf16, out_bf16;
 };
-// workspace: per-token group statistics [B][n][G] float2, then the chunk
-// carries [B][NC][G] float2
+// workspace: per-token decayed sums within each sub-chunk [B][n][G] float2,
+// the sums of each sub-chunk (then the sums entering it) [B][nsub][G] float2,
+// then the chunk carries [B][NC][G] float2 (chunks of Ls sub-chunks)
 struct TdnPlan {
-  int64_t NC, L;
-  size_t off_carry, bytes;
+  int64_t nsub, NC, Ls;
+  size_t off_sub, off_carry, bytes;
 };
 TdnPlan tdn_plan(int64_t B, int64_t n, int64_t G);
 hipError_t launch_tdn(const TdnProblem& p, void* ws, hipStream_t s);

@@ -9,15 +9,20 @@
 // t counts tokens of the sequence from 1; (m, v, t) may continue an earlier
 // call.
 //
-// Three kernels, each bound by HBM traffic or latency, none by arithmetic:
-//   stats: one 256-thread block per token row; 16-byte loads of 8 features,
-//     per-group mean then variance (two passes over registers) through LDS;
-//   scan: the tokens cut into chunks; one thread per (batch, chunk, group)
-//     computes the chunk's decayed sums from zero, the sums entering each
-//     chunk are carried across chunks (b^L per chunk), and a second pass from
-//     the entering sums writes (m_hat, 1 / sqrt(v_hat + eps)) in place of the
-//     statistics; the sums run in double (1 - b^t by its own recurrence);
-//   apply: one block per token row, 16-byte loads and stores.
+// Four kernels, each bound by HBM traffic or latency, none by arithmetic:
+//   stats: one 256-thread block per sub-chunk of 16 tokens; per token the
+//     group mean and variance (two passes over registers, reduced across
+//     lanes, or through LDS where a group does not fit one wave's lanes), and
+//     per group the decayed sums from zero at the sub-chunk's first token,
+//     written per token, with the sub-chunk's end sums;
+//   chunk / carry: the same recurrence over the sub-chunk sums (decay b^16
+//     per sub-chunk): chunks of them from zero in parallel, the sums entering
+//     each chunk carried across chunks, then the sums entering every
+//     sub-chunk, all in double;
+//   apply: 8 token rows per block; each token's sums are its within-sub-chunk
+//     sums plus the entering ones decayed to it, then bias correction and the
+//     affine output, 16-byte loads and stores.
+// x is read twice (stats, apply) and y written once.
 #include <algorithm>
 
 #include "gecko_device.hpp"
@@ -25,26 +30,6 @@
 
 namespace gecko {
 namespace {
-
-template <bool kBf16>
-__device__ __forceinline__ void load8(const void* base, int64_t i, float (&v)[8]) {
-  if constexpr (kBf16) {
-    const u32x4 r = ld16(static_cast<const uint16_t*>(base) + i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = bf_lo(r[j]);
-      v[2 * j + 1] = bf_hi(r[j]);
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
-    const f32x4 a = p[0], b = p[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = a[j];
-      v[4 + j] = b[j];
-    }
-  }
-}
 
 template <bool kBf16>
 __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8]) {
@@ -58,110 +43,215 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8
   }
 }
 
-constexpr int kT = 256;  // threads per row block
+constexpr int kT = 256;   // threads per row block
+constexpr int kR = 16;    // tokens per statistics block (one sub-chunk of the sequence)
+constexpr int kGPT = 4;   // groups per thread at most (G <= D / 8 <= 1024 = kGPT kT)
 
-// stats[(b n + t) G + g] = (mean, variance) of the group. CPT 8-feature
-// chunks per thread (D <= 8 CPT kT); part holds one partial per chunk.
-template <bool kBf16, int CPT>
-__global__ __launch_bounds__(kT) void tdn_stats_kernel(const void* x, float2* stats, int D, int G) {
+// One block per sub-chunk of kR tokens of a batch row. Per token: the group
+// (mean, variance) from 16-byte loads, mean then variance (two passes over
+// registers); then, per group, the decayed sums from a zero start at the
+// sub-chunk's first token,
+//   m = b1 m + (1 - b1) mu,  v = b2 v + (1 - b2) s2   (double),
+// written per token to st, and the sums after its last token to agg. Rows
+// r + 1 .. r + kRing - 1 are loading while row r is reduced. kShfl: a group
+// is a power-of-two run of at most 64 lanes of one wave (cpg lanes), reduced
+// with lane exchanges, and its first lane keeps the group's sums: no
+// barriers. Otherwise the partials go through LDS, alternating between two
+// buffers by row so that three barriers per row suffice, and thread g keeps
+// the sums of groups g + j kT.
+constexpr int kRing = 4;
+
+template <bool kBf16, int CPT, bool kShfl>
+__global__ __launch_bounds__(kT) void tdn_stats_kernel(const void* x, float2* st, float2* agg, int64_t n,
+                                                       int64_t nsub, int D, int G, float b1, float b2) {
   extern __shared__ float sm[];
-  float* part = sm;              // [D / 8]
-  float* gmean = sm + D / 8;     // [G]
-  const int64_t row = blockIdx.x;
   const int nch = D / 8, cpg = (D / G) / 8;  // chunks per row, per group
+  const int64_t b = blockIdx.x / nsub;
+  const int64_t k = blockIdx.x % nsub;
+  const int64_t row0 = b * n + k * kR;  // first token row of the sub-chunk
+  const int rows = (int)min((int64_t)kR, n - k * kR);
   const float invF = 1.f / (float)(D / G);
-  float v[CPT][8];
+  const double d1 = b1, d2 = b2, e1 = 1.0 - d1, e2 = 1.0 - d2;
+  constexpr int NS = kShfl ? CPT : kGPT;  // sums kept per thread
+  double m[NS], v[NS];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int c = threadIdx.x + k * kT;
-    if (c < nch) {
-      load8<kBf16>(x, row * D + 8 * c, v[k]);
-      float s = 0.f;
+  for (int j = 0; j < NS; ++j) m[j] = v[j] = 0.0;
+
+  // raw rows in flight: loads are unconditional (lanes past the row re-read
+  // its last chunk, unused) and converted where used, so the compiler keeps
+  // them in flight instead of waiting inside a branch
+  constexpr int RW = kBf16 ? 1 : 2;  // 16-byte words per 8-feature chunk
+  auto load_row = [&](int r, u32x4 (&dst)[CPT][RW]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += v[k][j];
-      part[c] = s;
+    for (int q = 0; q < CPT; ++q) {
+      const int c = min((int)threadIdx.x + q * kT, nch - 1);
+      const int64_t e = (row0 + r) * D + 8 * c;
+      if constexpr (kBf16) {
+        dst[q][0] = ld16(static_cast<const uint16_t*>(x) + e);
+      } else {
+        const u32x4* pw = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e);
+        dst[q][0] = pw[0];
+        dst[q][1] = pw[1];
+      }
+    }
+  };
+  // one token row from its raw words: statistics, then the sums
+  auto do_row = [&](int r, const u32x4 (&raw)[CPT][RW]) {
+    float cur[CPT][8];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (kBf16) {
+          const uint32_t wd = raw[q][0][j / 2];
+          cur[q][j] = (j & 1) ? bf_hi(wd) : bf_lo(wd);
+        } else {
+          cur[q][j] = __uint_as_float(raw[q][j / 4][j % 4]);
+        }
+      }
+    if constexpr (kShfl) {
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = threadIdx.x + q * kT;
+        const bool on = c < nch;
+        float s = 0.f;
+        if (on) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s += cur[q][j];
+        }
+        for (int o = 1; o < cpg; o <<= 1) s += __shfl_xor(s, o);
+        const float mu = s * invF;
+        float sq = 0.f;
+        if (on) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sq = fmaf(cur[q][j] - mu, cur[q][j] - mu, sq);
+        }
+        for (int o = 1; o < cpg; o <<= 1) sq += __shfl_xor(sq, o);
+        if (on && c % cpg == 0) {
+          m[q] = fma(d1, m[q], e1 * (double)mu);
+          v[q] = fma(d2, v[q], e2 * (double)(sq * invF));
+          st[(row0 + r) * G + c / cpg] = make_float2((float)m[q], (float)v[q]);
+        }
+      }
+    } else {
+      float* part = sm + (r & 1) * nch;
+      float* gmean = sm + 2 * nch + (r & 1) * G;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = threadIdx.x + q * kT;
+        if (c < nch) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s += cur[q][j];
+          part[c] = s;
+        }
+      }
+      __syncthreads();
+      for (int g = threadIdx.x; g < G; g += kT) {
+        float s = 0.f;
+        for (int i = 0; i < cpg; ++i) s += part[g * cpg + i];
+        gmean[g] = s * invF;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = threadIdx.x + q * kT;
+        if (c < nch) {
+          const float mu = gmean[c / cpg];
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s = fmaf(cur[q][j] - mu, cur[q][j] - mu, s);
+          part[c] = s;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kGPT; ++j) {
+        const int g = threadIdx.x + j * kT;
+        if (g < G) {
+          float s = 0.f;
+          for (int i = 0; i < cpg; ++i) s += part[g * cpg + i];
+          m[j] = fma(d1, m[j], e1 * (double)gmean[g]);
+          v[j] = fma(d2, v[j], e2 * (double)(s * invF));
+          st[(row0 + r) * G + g] = make_float2((float)m[j], (float)v[j]);
+        }
+      }
+    }
+  };
+  if (rows == kR) {
+    // a whole sub-chunk: straight-line code with constant ring slots, so
+    // the compiler's memory-counter waits leave kRing - 1 rows in flight
+    u32x4 xr[kRing][CPT][RW];
+#pragma unroll
+    for (int u = 0; u + 1 < kRing; ++u) load_row(u, xr[u]);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      if (r + kRing - 1 < kR) load_row(r + kRing - 1, xr[(r + kRing - 1) % kRing]);
+      do_row(r, xr[r % kRing]);
+    }
+  } else {
+    for (int r = 0; r < rows; ++r) {
+      u32x4 one[CPT][RW];
+      load_row(r, one);
+      do_row(r, one);
     }
   }
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kT) {
-    float s = 0.f;
-    for (int i = 0; i < cpg; ++i) s += part[g * cpg + i];
-    gmean[g] = s * invF;
-  }
-  __syncthreads();
+  float2* ag = agg + (b * nsub + k) * G;
+  if constexpr (kShfl) {
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int c = threadIdx.x + k * kT;
-    if (c < nch) {
-      const float mu = gmean[c / cpg];
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s = fmaf(v[k][j] - mu, v[k][j] - mu, s);
-      part[c] = s;
+    for (int q = 0; q < CPT; ++q) {
+      const int c = threadIdx.x + q * kT;
+      if (c < nch && c % cpg == 0) ag[c / cpg] = make_float2((float)m[q], (float)v[q]);
     }
-  }
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kT) {
-    float s = 0.f;
-    for (int i = 0; i < cpg; ++i) s += part[g * cpg + i];
-    stats[row * G + g] = make_float2(gmean[g], s * invF);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kGPT; ++j) {
+      const int g = threadIdx.x + j * kT;
+      if (g < G) ag[g] = make_float2((float)m[j], (float)v[j]);
+    }
   }
 }
 
-// Decayed statistics over the tokens of chunk c of row b, one thread per
-// group (consecutive threads read consecutive groups of a token). kFinal = 0
-// (phase A): from zero, write the chunk's end sums to carry[b][c][g].
-// kFinal = 1 (phase C): from the entering sums in carry[b][c][g] (phase B),
-// replace each token's (mean, variance) by (m_hat, 1 / sqrt(v_hat + eps));
-// the last chunk also writes the final sums.
+// Decayed sums over the sub-chunks [c Ls, (c + 1) Ls) of row b, one thread
+// per group (consecutive threads read consecutive groups). The sums after
+// sub-chunk k are S_k = b^len_k S_{k-1} + agg_k, len_k its token count (kR
+// but for the sequence's last). kFinal = 0 (phase A): from zero, write the
+// chunk's end sums to carry[b][c][g]. kFinal = 1 (phase C): from the entering
+// sums in carry[b][c][g] (phase B), replace each agg_k by the sums entering
+// sub-chunk k; the last chunk also writes the final sums. In double.
 template <bool kFinal>
-__global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* st, float2* carry, const float* m0, const float* v0,
-                                                       float* m_out, float* v_out, int64_t n, int G, int64_t L,
-                                                       int NC, int64_t t0, float b1, float b2, float eps) {
+__global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* ag, float2* carry, float* m_out, float* v_out,
+                                                       int64_t n, int64_t nsub, int G, int64_t Ls, int NC, float b1,
+                                                       float b2) {
   const int64_t b = blockIdx.x / NC;
   const int c = (int)(blockIdx.x % NC);
-  const int64_t ta = (int64_t)c * L, tb = std::min<int64_t>(ta + L, n);
-  // The sums run in double: with b near 1 a float32 sum settles about
-  // 2^-25 / (1 - b) away from its exact value (3e-4 relative at b = 0.9999).
-  // 1 - b^t follows u_t = b u_{t-1} + (1 - b) and runs beside them, from its
-  // value before the chunk.
-  const double d1 = b1, d2 = b2, e1 = 1.0 - d1, e2 = 1.0 - d2;
-  const double tp = (double)(t0 + ta);  // tokens of the sequence before the chunk
-  const double u1s = tp > 0.0 ? -expm1(tp * log(d1)) : 0.0, u2s = tp > 0.0 ? -expm1(tp * log(d2)) : 0.0;
+  const int64_t ka = (int64_t)c * Ls, kb = std::min<int64_t>(ka + Ls, nsub);
+  const double f1 = pow((double)b1, (double)kR), f2 = pow((double)b2, (double)kR);
+  const double lastlen = (double)(n - (nsub - 1) * kR);
+  const double l1 = pow((double)b1, lastlen), l2 = pow((double)b2, lastlen);
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    double m = 0.0, v = 0.0, u1 = u1s, u2 = u2s;
+    double m = 0.0, v = 0.0;
     if constexpr (kFinal) {
       const float2 e = carry[(b * NC + c) * G + g];
       m = e.x;
       v = e.y;
     }
-    float2* s = st + b * n * G + g;
-    // kB tokens per step: their loads are issued together, then the sums run
+    float2* s = ag + b * nsub * G + g;
+    // kB sub-chunks per step: their loads are issued together, then the sums run
     constexpr int kB = 16;
-    int64_t t = ta;
-    for (; t + kB <= tb; t += kB) {
-      float2 x[kB];
+    for (int64_t k0 = ka; k0 < kb; k0 += kB) {
+      float2 a[kB];
 #pragma unroll
-      for (int k = 0; k < kB; ++k) x[k] = s[(t + k) * G];
+      for (int u = 0; u < kB; ++u)
+        if (k0 + u < kb) a[u] = s[(k0 + u) * G];
 #pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        m = fma(d1, m, e1 * x[k].x);
-        v = fma(d2, v, e2 * x[k].y);
-        if constexpr (kFinal) {
-          u1 = fma(d1, u1, e1);
-          u2 = fma(d2, u2, e2);
-          s[(t + k) * G] = make_float2((float)(m / u1), rsqrtf((float)(v / u2) + eps));
+      for (int u = 0; u < kB; ++u) {
+        if (k0 + u < kb) {
+          if constexpr (kFinal) s[(k0 + u) * G] = make_float2((float)m, (float)v);
+          const bool last = k0 + u == nsub - 1;
+          m = fma(last ? l1 : f1, m, (double)a[u].x);
+          v = fma(last ? l2 : f2, v, (double)a[u].y);
         }
-      }
-    }
-    for (; t < tb; ++t) {
-      const float2 x = s[t * G];
-      m = fma(d1, m, e1 * x.x);
-      v = fma(d2, v, e2 * x.y);
-      if constexpr (kFinal) {
-        u1 = fma(d1, u1, e1);
-        u2 = fma(d2, u2, e2);
-        s[t * G] = make_float2((float)(m / u1), rsqrtf((float)(v / u2) + eps));
       }
     }
     if constexpr (kFinal) {
@@ -176,7 +266,8 @@ __global__ __launch_bounds__(256) void tdn_chunk_kernel(float2* st, float2* carr
 }
 
 // Phase B: one thread per (b, g); the sums entering each chunk, in double,
-// written over the chunk end sums: enter(c + 1) = b^L enter(c) + end(c).
+// written over the chunk end sums: enter(c + 1) = b^L enter(c) + end(c),
+// L the tokens of a chunk.
 __global__ void tdn_carry_kernel(float2* carry, const float* m0, const float* v0, int64_t B, int G, int64_t L,
                                  int NC, float b1, float b2) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -208,9 +299,16 @@ __global__ void tdn_carry_kernel(float2* carry, const float* m0, const float* v0
 
 constexpr int kRows = 8;  // token rows per apply block (gamma and shift stay in registers)
 
+// y for kRows token rows. Token t of row b, i = t mod kR tokens into its
+// sub-chunk k: the sums are m = st_t + b1^(i+1) enter_k (v alike), and with
+// tau = t0 + t + 1 tokens of the sequence so far, m_hat = m / (1 - b1^tau),
+// v_hat = v / (1 - b2^tau); 1 - b^tau is -expm1(tau ln b), accurate for b
+// near 1.
 template <bool kIn, bool kOut, int CPT>
-__global__ __launch_bounds__(kT) void tdn_apply_kernel(const void* x, const float2* nrm, const float* gamma,
-                                                       const float* shift, void* y, int64_t rows, int D, int G) {
+__global__ __launch_bounds__(kT) void tdn_apply_kernel(const void* x, const float2* st, const float2* ent,
+                                                       const float* gamma, const float* shift, void* y, int64_t n,
+                                                       int64_t nsub, int64_t rows, int D, int G, int64_t t0,
+                                                       float b1, float b2, float eps) {
   const int nch = D / 8, cpg = (D / G) / 8;
   float gm[CPT][8], sh[CPT][8];
 #pragma unroll
@@ -227,82 +325,148 @@ __global__ __launch_bounds__(kT) void tdn_apply_kernel(const void* x, const floa
       sh[k][4 + j] = s1[j];
     }
   }
+  const float lg1 = log2f(b1), lg2 = log2f(b2);  // -inf at b = 0
+  const float ln1 = logf(b1), ln2 = logf(b2);
+  constexpr int RW = kIn ? 1 : 2;  // 16-byte words per 8-feature chunk
+  // kA rows at a time: every load of the batch is issued before the first
+  // is used (unconditional loads: lanes past the row re-read its last chunk,
+  // unused), so the compiler's memory-counter waits keep them in flight
+  constexpr int kA = 4;
   const int64_t r0 = (int64_t)blockIdx.x * kRows;
   const int64_t r1 = min(r0 + kRows, rows);
-  for (int64_t row = r0; row < r1; ++row) {
+  for (int64_t ra = r0; ra < r1; ra += kA) {
+    const int na = (int)min((int64_t)kA, r1 - ra);
+    u32x4 raw[kA][CPT][RW];
+    float2 sv[kA][CPT], ev[kA][CPT];
+    int64_t tok[kA];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int c = threadIdx.x + k * kT;
-      if (c < nch) {
-        float v[8];
-        load8<kIn>(x, row * D + 8 * c, v);
-        const float2 q = nrm[row * G + c / cpg];  // (m_hat, 1 / sqrt(v_hat + eps))
+    for (int u = 0; u < kA; ++u) {
+      const int64_t row = ra + min(u, na - 1);
+      const int64_t b = row / n, t = row - b * n;
+      tok[u] = t;
+      const float2* ek = ent + (b * nsub + t / kR) * G;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = fmaf(gm[k][j] * q.y, v[j] - q.x, sh[k][j]);
-        store8<kOut>(y, row * D + 8 * c, v);
+      for (int q = 0; q < CPT; ++q) {
+        const int c = min((int)threadIdx.x + q * kT, nch - 1);
+        const int64_t e = row * D + 8 * c;
+        if constexpr (kIn) {
+          raw[u][q][0] = ld16(static_cast<const uint16_t*>(x) + e);
+        } else {
+          const u32x4* pw = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e);
+          raw[u][q][0] = pw[0];
+          raw[u][q][1] = pw[1];
+        }
+        sv[u][q] = st[row * G + c / cpg];
+        ev[u][q] = ek[c / cpg];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kA; ++u) {
+      if (u >= na) break;
+      const int64_t row = ra + u, t = tok[u];
+      const float i1 = (float)(t % kR + 1);
+      const float p1 = exp2f(lg1 * i1), p2 = exp2f(lg2 * i1);
+      const float tau = (float)(t0 + t + 1);
+      const float iu1 = 1.f / -expm1f(tau * ln1), iu2 = 1.f / -expm1f(tau * ln2);
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = threadIdx.x + q * kT;
+        if (c < nch) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (kIn) {
+              const uint32_t wd = raw[u][q][0][j / 2];
+              v[j] = (j & 1) ? bf_hi(wd) : bf_lo(wd);
+            } else {
+              v[j] = __uint_as_float(raw[u][q][j / 4][j % 4]);
+            }
+          }
+          const float mh = fmaf(p1, ev[u][q].x, sv[u][q].x) * iu1;
+          const float rs = rsqrtf(fmaf(p2, ev[u][q].y, sv[u][q].y) * iu2 + eps);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = fmaf(gm[q][j] * rs, v[j] - mh, sh[q][j]);
+          store8<kOut>(y, row * D + 8 * c, v);
+        }
       }
     }
   }
 }
 
 template <bool kIn, bool kOut, int CPT>
-hipError_t launch_cpt(const TdnProblem& p, float2* st, hipStream_t s) {
-  const unsigned rows = (unsigned)(p.B * p.n);
-  const size_t lds = (size_t)(p.D / 8 + p.G) * sizeof(float);
-  hipLaunchKernelGGL((tdn_stats_kernel<kIn, CPT>), dim3(rows), dim3(kT), lds, s, p.x, st, (int)p.D, (int)p.G);
+hipError_t launch_cpt(const TdnProblem& p, char* ws, hipStream_t s) {
+  const TdnPlan pl = tdn_plan(p.B, p.n, p.G);
+  float2* st = reinterpret_cast<float2*>(ws);
+  float2* sub = reinterpret_cast<float2*>(ws + pl.off_sub);
+  float2* carry = reinterpret_cast<float2*>(ws + pl.off_carry);
+  const int64_t cpg = p.D / p.G / 8;
+  const dim3 sgrid((unsigned)(p.B * pl.nsub));
+  if (cpg <= 64 && (cpg & (cpg - 1)) == 0) {
+    hipLaunchKernelGGL((tdn_stats_kernel<kIn, CPT, true>), sgrid, dim3(kT), 0, s, p.x, st, sub, p.n, pl.nsub,
+                       (int)p.D, (int)p.G, p.beta1, p.beta2);
+  } else {
+    const size_t lds = (size_t)(2 * (p.D / 8) + 2 * p.G) * sizeof(float);
+    hipLaunchKernelGGL((tdn_stats_kernel<kIn, CPT, false>), sgrid, dim3(kT), lds, s, p.x, st, sub, p.n, pl.nsub,
+                       (int)p.D, (int)p.G, p.beta1, p.beta2);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // statistics scan: chunks of L tokens in parallel, carries across chunks
-  const TdnPlan pl = tdn_plan(p.B, p.n, p.G);
-  float2* carry = reinterpret_cast<float2*>(reinterpret_cast<char*>(st) + pl.off_carry);
+  // scan over the sub-chunk sums: chunks of Ls sub-chunks in parallel,
+  // carries across chunks
   const unsigned blocks = (unsigned)(p.B * pl.NC);
   const unsigned cthreads = (unsigned)std::min<int64_t>(256, (p.G + 63) / 64 * 64);  // one thread per group
   if (pl.NC > 1) {
-    hipLaunchKernelGGL((tdn_chunk_kernel<false>), dim3(blocks), dim3(cthreads), 0, s, st, carry, p.m0, p.v0, p.m_out,
-                       p.v_out, p.n, (int)p.G, pl.L, (int)pl.NC, p.t0, p.beta1, p.beta2, p.eps);
+    hipLaunchKernelGGL((tdn_chunk_kernel<false>), dim3(blocks), dim3(cthreads), 0, s, sub, carry, p.m_out, p.v_out,
+                       p.n, pl.nsub, (int)p.G, pl.Ls, (int)pl.NC, p.beta1, p.beta2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {  // with one chunk this only writes the given (or zero) sums as its entering ones
     const int64_t th = p.B * p.G;
     hipLaunchKernelGGL(tdn_carry_kernel, dim3((unsigned)((th + 255) / 256)), dim3(256), 0, s, carry, p.m0, p.v0,
-                       p.B, (int)p.G, pl.L, (int)pl.NC, p.beta1, p.beta2);
+                       p.B, (int)p.G, pl.Ls * kR, (int)pl.NC, p.beta1, p.beta2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((tdn_chunk_kernel<true>), dim3(blocks), dim3(cthreads), 0, s, st, carry, p.m0, p.v0, p.m_out,
-                     p.v_out, p.n, (int)p.G, pl.L, (int)pl.NC, p.t0, p.beta1, p.beta2, p.eps);
+  hipLaunchKernelGGL((tdn_chunk_kernel<true>), dim3(blocks), dim3(cthreads), 0, s, sub, carry, p.m_out, p.v_out, p.n,
+                     pl.nsub, (int)p.G, pl.Ls, (int)pl.NC, p.beta1, p.beta2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = p.B * p.n;
   hipLaunchKernelGGL((tdn_apply_kernel<kIn, kOut, CPT>), dim3((unsigned)((rows + kRows - 1) / kRows)), dim3(kT), 0,
-                     s, p.x, st, p.gamma, p.shift, p.y, (int64_t)rows, (int)p.D, (int)p.G);
+                     s, p.x, st, sub, p.gamma, p.shift, p.y, p.n, pl.nsub, rows, (int)p.D, (int)p.G, p.t0, p.beta1,
+                     p.beta2, p.eps);
   return hipGetLastError();
 }
 
 template <bool kIn, bool kOut>
-hipError_t launch_io(const TdnProblem& p, float2* st, hipStream_t s) {
+hipError_t launch_io(const TdnProblem& p, char* ws, hipStream_t s) {
   const int64_t cpt = (p.D / 8 + kT - 1) / kT;
-  if (cpt <= 1) return launch_cpt<kIn, kOut, 1>(p, st, s);
-  if (cpt <= 2) return launch_cpt<kIn, kOut, 2>(p, st, s);
-  return launch_cpt<kIn, kOut, 4>(p, st, s);
+  if (cpt <= 1) return launch_cpt<kIn, kOut, 1>(p, ws, s);
+  if (cpt <= 2) return launch_cpt<kIn, kOut, 2>(p, ws, s);
+  return launch_cpt<kIn, kOut, 4>(p, ws, s);
 }
 
 }  // namespace
 
 TdnPlan tdn_plan(int64_t B, int64_t n, int64_t G) {
   TdnPlan p{};
-  // chunks of at least 512 tokens; up to 2048 blocks in all
-  const int64_t want = std::max<int64_t>(1, 2048 / B);
-  p.NC = std::max<int64_t>(1, std::min(want, n / 512));
-  p.L = (n + p.NC - 1) / p.NC;
-  p.NC = (n + p.L - 1) / p.L;
+  p.nsub = (n + kR - 1) / kR;
+  // about sqrt(nsub) chunks of as many sub-chunks: the two chunk passes and
+  // the carry each run that many dependent steps
+  int64_t nc = 1;
+  while ((nc + 1) * (nc + 1) <= p.nsub) ++nc;
+  p.Ls = (p.nsub + nc - 1) / nc;
+  p.NC = (p.nsub + p.Ls - 1) / p.Ls;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t stats = (size_t)B * (size_t)n * (size_t)G * sizeof(float2);
-  p.off_carry = (stats + 255) / 256 * 256;
+  p.off_sub = up(stats);
+  p.off_carry = up(p.off_sub + (size_t)B * (size_t)p.nsub * (size_t)G * sizeof(float2));
   p.bytes = p.off_carry + (size_t)B * (size_t)p.NC * (size_t)G * sizeof(float2);
   return p;
 }
 
 hipError_t launch_tdn(const TdnProblem& p, void* ws, hipStream_t s) {
-  float2* st = static_cast<float2*>(ws);
-  if (p.in_bf16) return p.out_bf16 ? launch_io<true, true>(p, st, s) : launch_io<true, false>(p, st, s);
-  return p.out_bf16 ? launch_io<false, true>(p, st, s) : launch_io<false, false>(p, st, s);
+  char* w = static_cast<char*>(ws);
+  if (p.in_bf16) return p.out_bf16 ? launch_io<true, true>(p, w, s) : launch_io<true, false>(p, w, s);
+  return p.out_bf16 ? launch_io<false, true>(p, w, s) : launch_io<false, false>(p, w, s);
 }
 
 }  // namespace gecko

@@ -6,7 +6,9 @@ output, and the carried sums match to 1e-4 relative. Cases: no decay (plain
 per-token group normalisation), typical and near-one decay factors (the bias
 correction at its most delicate, and a sequence long enough for the sums to
 reach their steady state, where float32 sums would drift by about
-2^-25 / (1 - beta)), groups of 8 to 64, one token, the chunked scan, a
+2^-25 / (1 - beta)), groups of 8 to 1024 features (reduced across lanes, or
+through LDS where a group is not a power-of-two run of at most 64 lanes), one
+token, the chunked scan, a
 sequence continued over two calls, and the bf16 output rounding."""
 
 from __future__ import annotations
@@ -42,6 +44,9 @@ def _dev(host):
     (1, 700, 256, 4, 0.0, 0.0, "f32"),          # no decay: group norm of each token
     (1, 5000, 4096, 64, 0.999, 0.9999, "bf16"),  # chunked scan, factors near one
     (1, 65536, 256, 8, 0.999, 0.9999, "bf16"),   # long enough for the sums to settle
+    (1, 900, 192, 1, 0.9, 0.99, "f32"),          # 24 lanes per group: the LDS reduction
+    (2, 333, 1024, 1, 0.95, 0.999, "bf16"),      # 128 lanes per group: the LDS reduction
+    (1, 100, 8192, 16, 0.9, 0.99, "bf16"),       # four 8-feature runs per thread, 64 lanes per group
 ])
 def test_tdn_matches_oracle(B, n, D, G, b1, b2, dtype):
     import torch
