@@ -43,6 +43,32 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8
   }
 }
 
+// Sum over aligned runs of cpg lanes (a power of two up to 64), the result in
+// every lane of the run: DPP lane moves within a row of 16 lanes (swap
+// neighbours, swap pairs, mirror each half-row, mirror the row: after each
+// step all lanes of a run of 2, 4, 8, 16 hold the same value), then lane
+// exchanges across rows.
+__device__ __forceinline__ float dpp_add(float s, int ctrl_sel) {
+  int t;
+  const int si = __float_as_int(s);
+  switch (ctrl_sel) {
+    case 0: t = __builtin_amdgcn_mov_dpp(si, 0xB1, 0xF, 0xF, true); break;   // quad_perm [1, 0, 3, 2]
+    case 1: t = __builtin_amdgcn_mov_dpp(si, 0x4E, 0xF, 0xF, true); break;   // quad_perm [2, 3, 0, 1]
+    case 2: t = __builtin_amdgcn_mov_dpp(si, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+    default: t = __builtin_amdgcn_mov_dpp(si, 0x140, 0xF, 0xF, true); break; // row_mirror
+  }
+  return s + __int_as_float(t);
+}
+
+__device__ __forceinline__ float run_sum(float s, int cpg) {
+  if (cpg >= 2) s = dpp_add(s, 0);
+  if (cpg >= 4) s = dpp_add(s, 1);
+  if (cpg >= 8) s = dpp_add(s, 2);
+  if (cpg >= 16) s = dpp_add(s, 3);
+  for (int o = 16; o < cpg; o <<= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
 constexpr int kT = 256;   // threads per row block
 constexpr int kR = 16;    // tokens per statistics block (one sub-chunk of the sequence)
 constexpr int kGPT = 4;   // groups per thread at most (G <= D / 8 <= 1024 = kGPT kT)
@@ -119,14 +145,14 @@ __global__ __launch_bounds__(kT) void tdn_stats_kernel(const void* x, float2* st
 #pragma unroll
           for (int j = 0; j < 8; ++j) s += cur[q][j];
         }
-        for (int o = 1; o < cpg; o <<= 1) s += __shfl_xor(s, o);
+        s = run_sum(s, cpg);
         const float mu = s * invF;
         float sq = 0.f;
         if (on) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) sq = fmaf(cur[q][j] - mu, cur[q][j] - mu, sq);
         }
-        for (int o = 1; o < cpg; o <<= 1) sq += __shfl_xor(sq, o);
+        sq = run_sum(sq, cpg);
         if (on && c % cpg == 0) {
           m[q] = fma(d1, m[q], e1 * (double)mu);
           v[q] = fma(d2, v[q], e2 * (double)(sq * invF));

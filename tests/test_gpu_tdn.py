@@ -47,6 +47,9 @@ def _dev(host):
     (1, 900, 192, 1, 0.9, 0.99, "f32"),          # 24 lanes per group: the LDS reduction
     (2, 333, 1024, 1, 0.95, 0.999, "bf16"),      # 128 lanes per group: the LDS reduction
     (1, 100, 8192, 16, 0.9, 0.99, "bf16"),       # four 8-feature runs per thread, 64 lanes per group
+    (1, 200, 128, 8, 0.9, 0.99, "f32"),          # 2 lanes per group
+    (1, 500, 512, 4, 0.9, 0.99, "bf16"),         # 16 lanes per group
+    (1, 300, 1024, 4, 0.9, 0.99, "f32"),         # 32 lanes per group
 ])
 def test_tdn_matches_oracle(B, n, D, G, b1, b2, dtype):
     import torch
