@@ -226,6 +226,19 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
     if (k.ws_bytes < w.bytes) return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", k.ws_bytes, w.bytes);
     if (reinterpret_cast<uintptr_t>(k.ws) & (kAlign - 1)) return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
     if (overlaps(k.out, ob, k.ws, w.bytes)) return fail(GECKO_EINVAL, "out aliases the workspace");
+    // the chunk pass and the scan write the workspace before the attention
+    // kernel reads z, v and the affine vectors
+    if (overlaps(k.ws, w.bytes, k.z, zb) || overlaps(k.ws, w.bytes, k.v, vb))
+      return fail(GECKO_EINVAL, "the workspace aliases z or v");
+    for (int i = 0; i < 8; ++i)
+      if (k.aff[i] && overlaps(k.ws, w.bytes, k.aff[i], (size_t)k.H * k.d * 4))
+        return fail(GECKO_EINVAL, "the workspace aliases affine vector %d", i);
+    if (k.lse && overlaps(k.ws, w.bytes, k.lse, (size_t)BH * k.n * 4))
+      return fail(GECKO_EINVAL, "the workspace aliases the log-sum-exp output");
+    if (k.o_sca && overlaps(k.ws, w.bytes, k.o_sca, (size_t)BH * k.n * k.dv * 4))
+      return fail(GECKO_EINVAL, "the workspace aliases the attention output");
+    if (k.stats && overlaps(k.ws, w.bytes, k.stats, (size_t)BH * k.n * 8))
+      return fail(GECKO_EINVAL, "the workspace aliases the attention statistics");
   }
   p.z = k.z; p.v = k.v; p.out = k.out;
   p.kappa_q = k.aff[0]; p.nu_q = k.aff[1]; p.kappa_k = k.aff[2]; p.nu_k = k.aff[3];

@@ -127,6 +127,22 @@ def _dtype_code(t) -> int:
     raise GeckoError(GECKO_EUNSUPPORTED, f"unsupported tensor dtype {t.dtype}")
 
 
+def _empty(shape, dtype, device, stream):
+    """torch.empty allocated on the stream the kernels are launched on.
+
+    The caching allocator hands a freed block to the next allocation on the
+    stream that allocated it without waiting for other streams; a buffer that
+    this module allocates and frees again (a workspace) must therefore belong
+    to the launch stream, or a later allocation on the current stream could
+    reuse it while the kernels still write it."""
+    import torch
+
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -165,13 +181,14 @@ def gecko_workspace_size(B, H, n, d, dv, c, dtype_code, flags=0) -> int:
     return r
 
 
-def alloc_workspace(z, v, c, flags=0):
-    """Device workspace (uint8 tensor, 256-byte aligned by torch) for a forward on z, v."""
+def alloc_workspace(z, v, c, flags=0, stream=None):
+    """Device workspace (uint8 tensor, 256-byte aligned by torch) for a forward on z, v,
+    allocated on ``stream`` (default: the current stream)."""
     import torch
 
     B, H, n, d, dv = _shape(z, v)
     nbytes = gecko_workspace_size(B, H, n, d, dv, c, _dtype_code(z), flags)
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+    return _empty(max(nbytes, 256), torch.uint8, z.device, stream)
 
 
 def _params(p, names, device, H, d):
@@ -196,9 +213,9 @@ def gecko_sca_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, wo
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     if workspace is None:
-        workspace = alloc_workspace(z, v, c, flags)
+        workspace = alloc_workspace(z, v, c, flags, stream)
     dt = _dtype_code(z)
     args = [_ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
             B, H, n, d, dv, c, dt, _dtype_code(out), flags, _ptr(workspace), workspace.numel(), _stream(stream)]
@@ -215,7 +232,7 @@ def gecko_sca_forward(z, params, v, c, out=None, out_dtype=None, stream=None):
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     _check(lib.gecko_sca_forward(_ptr(z), *_params(params, Q_NAMES, z.device, H, d), _ptr(v), _ptr(out),
                                  B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), _stream(stream)))
     return out
@@ -227,9 +244,9 @@ def gecko_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, worksp
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     if workspace is None:
-        workspace = alloc_workspace(z, v, c, flags)
+        workspace = alloc_workspace(z, v, c, flags, stream)
     _check(lib.gecko_awm_forward(_ptr(z), *_params(params, M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
                                  B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags,
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -258,11 +275,11 @@ def gecko_sca_awm_forward_stream(z, params, v, c, pos, state, out=None, out_dtyp
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     dt = _dtype_code(z)
     if workspace is None:
         nbytes = gecko_stream_workspace_size(B, H, n, d, dv, c, dt)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+        workspace = _empty(max(nbytes, 256), torch.uint8, z.device, stream)
     _check(lib.gecko_sca_awm_forward_stream(
         _ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
         B, H, n, d, dv, c, pos, dt, _dtype_code(out), flags, _ptr(state), state.numel(),
@@ -297,8 +314,8 @@ def gecko_cema_forward(x, params, reset=None, h0=None, out=None, out_dtype=None,
         if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or t.device != x.device:
             raise GeckoError(GECKO_EINVAL, f"CEMA parameter {k} must be a contiguous float32 {shape} device tensor")
     if out is None:
-        out = torch.empty((B, n, D), dtype=out_dtype or x.dtype, device=x.device)
-    hfin = torch.empty((B, D, h, 2), dtype=torch.float32, device=x.device) if want_state else None
+        out = _empty((B, n, D), out_dtype or x.dtype, x.device, stream)
+    hfin = _empty((B, D, h, 2), torch.float32, x.device, stream) if want_state else None
     for t, name in ((reset, "reset"), (h0, "h0")):
         if t is not None and (not t.is_contiguous() or t.device != x.device):
             raise GeckoError(GECKO_EINVAL, f"{name} must be a contiguous device tensor")
@@ -308,7 +325,7 @@ def gecko_cema_forward(x, params, reset=None, h0=None, out=None, out_dtype=None,
         raise GeckoError(GECKO_EINVAL, "h0 must be float32 [B, D, h, 2]")
     if workspace is None:
         nbytes = gecko_cema_workspace_size(B, n, D, h)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+        workspace = _empty(max(nbytes, 256), torch.uint8, x.device, stream)
     _check(lib.gecko_cema_forward(
         _ptr(x), *[_ptr(params[k]) for k in CEMA_NAMES], _ptr(params["eta"]), _ptr(reset), _ptr(h0), _ptr(out),
         _ptr(hfin), B, n, D, h, _dtype_code(x), _dtype_code(out), _ptr(workspace), workspace.numel(),
@@ -341,11 +358,11 @@ def gecko_tdn_forward(x, gamma, shift, G, beta1, beta2, eps=1e-5, state=None, ou
     if state is not None:
         m0, v0, t0 = state
     if out is None:
-        out = torch.empty((B, n, D), dtype=out_dtype or x.dtype, device=x.device)
-    m_out = torch.empty((B, G), dtype=torch.float32, device=x.device) if want_state else None
-    v_out = torch.empty((B, G), dtype=torch.float32, device=x.device) if want_state else None
+        out = _empty((B, n, D), out_dtype or x.dtype, x.device, stream)
+    m_out = _empty((B, G), torch.float32, x.device, stream) if want_state else None
+    v_out = _empty((B, G), torch.float32, x.device, stream) if want_state else None
     if workspace is None:
-        workspace = torch.empty(max(gecko_tdn_workspace_size(B, n, D, G), 256), dtype=torch.uint8, device=x.device)
+        workspace = _empty(max(gecko_tdn_workspace_size(B, n, D, G), 256), torch.uint8, x.device, stream)
     _check(lib.gecko_tdn_forward(_ptr(x), _ptr(gamma), _ptr(shift), _ptr(m0), _ptr(v0), int(t0), _ptr(out),
                                  _ptr(m_out), _ptr(v_out), B, n, D, G, float(beta1), float(beta2), float(eps),
                                  _dtype_code(x), _dtype_code(out), _ptr(workspace), workspace.numel(),
@@ -364,7 +381,7 @@ class Stream:
         self.B, self.H, self.d, self.dv, self.c = B, H, d, dv, c
         self.params, self.flags = params, flags
         nbytes = gecko_stream_state_size(B, H, d, dv, c, GECKO_BF16)
-        self.state = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.state = _empty(nbytes, torch.uint8, device, None)
         self.pos = 0
 
     def forward(self, z, v, out=None, out_dtype=None, workspace=None, stream=None):
@@ -435,11 +452,11 @@ def gecko_forward_lse(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, ou
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     if lse is None:
-        lse = torch.empty((B, H, n), dtype=torch.float32, device=z.device)
+        lse = _empty((B, H, n), torch.float32, z.device, stream)
     if workspace is None and parts & GECKO_PART_AWM:
-        workspace = alloc_workspace(z, v, c, flags)
+        workspace = alloc_workspace(z, v, c, flags, stream)
     _check(lib.gecko_forward_lse(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(out), _ptr(lse),
                                  B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags, parts,
                                  _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -454,13 +471,13 @@ def gecko_forward_train(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, 
 
     B, H, n, d, dv = _shape(z, v)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=out_dtype or z.dtype, device=z.device)
+        out = _empty((B, H, n, dv), out_dtype or z.dtype, z.device, stream)
     if o_sca is None:
-        o_sca = torch.empty((B, H, n, dv), dtype=torch.float32, device=z.device)
+        o_sca = _empty((B, H, n, dv), torch.float32, z.device, stream)
     if stats is None:
-        stats = torch.empty((B, H, n, 2), dtype=torch.float32, device=z.device)
+        stats = _empty((B, H, n, 2), torch.float32, z.device, stream)
     if workspace is None and parts & GECKO_PART_AWM:
-        workspace = alloc_workspace(z, v, c, flags)
+        workspace = alloc_workspace(z, v, c, flags, stream)
     _check(lib.gecko_forward_train(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(out),
                                    _ptr(o_sca), _ptr(stats), B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out),
                                    flags, parts, _ptr(workspace), 0 if workspace is None else workspace.numel(),
@@ -486,14 +503,14 @@ def gecko_backward(z, params, v, dout, c, parts=GECKO_PART_SCA | GECKO_PART_AWM,
     if tuple(dout.shape) != (B, H, n, dvs) or not dout.is_contiguous():
         raise GeckoError(GECKO_EINVAL, "dout must be a contiguous [B, H, n, dv] tensor")
     if dz is None:
-        dz = torch.empty((B, H, n, d), dtype=torch.float32, device=z.device)
+        dz = _empty((B, H, n, d), torch.float32, z.device, stream)
     if dv is None:
-        dv = torch.empty((B, H, n, dvs), dtype=torch.float32, device=z.device)
+        dv = _empty((B, H, n, dvs), torch.float32, z.device, stream)
     if daff is None:
-        daff = torch.empty((8, H, d), dtype=torch.float32, device=z.device)
+        daff = _empty((8, H, d), torch.float32, z.device, stream)
     if workspace is None:
         nbytes = gecko_backward_workspace_size(B, H, n, d, dvs, c, _dtype_code(z), _dtype_code(dout), flags, parts)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+        workspace = _empty(max(nbytes, 256), torch.uint8, z.device, stream)
     _check(lib.gecko_backward(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
                               _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c, _dtype_code(z),
                               _dtype_code(dout), flags, parts, _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -523,15 +540,15 @@ def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_S
             or tuple(stats.shape) != (B, H, n, 2) or stats.dtype != torch.float32 or not stats.is_contiguous()):
         raise GeckoError(GECKO_EINVAL, "o_sca must be float32 [B, H, n, dv] and stats float32 [B, H, n, 2]")
     if dz is None:
-        dz = torch.empty((B, H, n, d), dtype=torch.float32, device=z.device)
+        dz = _empty((B, H, n, d), torch.float32, z.device, stream)
     if dv is None:
-        dv = torch.empty((B, H, n, dvs), dtype=torch.float32, device=z.device)
+        dv = _empty((B, H, n, dvs), torch.float32, z.device, stream)
     if daff is None:
-        daff = torch.empty((8, H, d), dtype=torch.float32, device=z.device)
+        daff = _empty((8, H, d), torch.float32, z.device, stream)
     if workspace is None:
         nbytes = gecko_backward_saved_workspace_size(B, H, n, d, dvs, c, _dtype_code(z), _dtype_code(dout), flags,
                                                      parts)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=z.device)
+        workspace = _empty(max(nbytes, 256), torch.uint8, z.device, stream)
     _check(lib.gecko_backward_saved(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
                                     _ptr(o_sca), _ptr(stats), _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c,
                                     _dtype_code(z), _dtype_code(dout), flags, parts, _ptr(workspace),

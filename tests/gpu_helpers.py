@@ -51,6 +51,8 @@ def run_raw(host: dict, c: int, entry: str = "full", flags: int = 0, device_inpu
     else:
         raise ValueError(entry)
     torch.cuda.synchronize()
+    # the output starts as NaN (tests/conftest.py): every row must be written
+    assert bool(torch.isfinite(out).all()), f"{entry}: output holds unwritten or non-finite entries"
     return out
 
 

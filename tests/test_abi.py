@@ -108,6 +108,22 @@ def test_validation_errors(g):
     assert st == g.GECKO_EINVAL or st == g.GECKO_EUNSUPPORTED
 
 
+def test_workspace_must_not_alias_inputs(g):
+    """The chunk pass and the scan write the workspace before the attention
+    kernel reads z, v and the affine vectors: a workspace over any of them is
+    refused before any launch."""
+    wsb = g.gecko_workspace_size(1, 1, 1000, 128, 256, 100, g.GECKO_BF16)
+    assert wsb > FAKE  # so that a workspace at 16 FAKE covers affine vectors placed there
+    st, msg = call_full(g, ws=FAKE, wsb=wsb)
+    assert st == g.GECKO_EINVAL and "aliases z or v" in msg
+    st, msg = call_full(g, ws=(2 * FAKE + 4096 - wsb) & ~255, wsb=wsb)  # ends inside v, before out
+    assert st == g.GECKO_EINVAL and "aliases z or v" in msg
+    st, msg = call_full(g, ws=16 * FAKE, wsb=wsb, aff=[16 * FAKE + 64 * i for i in range(8)])
+    assert st == g.GECKO_EINVAL and "affine vector 0" in msg
+    st, msg = call_full(g, ws=16 * FAKE, wsb=wsb, aff=[FAKE + 64 * i for i in range(7)] + [16 * FAKE + 4096])
+    assert st == g.GECKO_EINVAL and "affine vector 7" in msg
+
+
 def test_sca_and_awm_entry_validation(g):
     st = g.lib.gecko_sca_forward(FAKE, FAKE, FAKE, FAKE, 0, 2 * FAKE, 3 * FAKE, 1, 1, 10, 128, 256, 4,
                                  g.GECKO_BF16, g.GECKO_BF16, None)

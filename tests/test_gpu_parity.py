@@ -154,3 +154,34 @@ def test_bf16_logits_beyond_first_tile_range(scale):
     want = _stack(ref, "o_sca", heads)
     assert np.all(np.isfinite(got))
     assert rms_err(got, want) <= BF16_TOL
+
+
+def test_side_stream_matches_current_stream():
+    """The forward and the backward launched on a stream other than the
+    current one give the results of the current stream bit for bit, while
+    the current stream allocates and writes fresh memory right after the
+    launches (the binding's workspaces belong to the launch stream, so the
+    caching allocator cannot hand their blocks to those writes)."""
+    import torch
+
+    from chunked_attention_memory_amd import gecko as g
+    from chunked_attention_memory_amd import inputs
+
+    host = make(1, 2, 1100, 128, 256, "bf16", tag=41)
+    dev = g.to_device_inputs(host)
+    z, v, p = dev
+    do = torch.from_numpy(inputs.make_dout(1, 2, 1100, 256, "bf16", tag=41)).to(device="cuda", dtype=torch.bfloat16)
+    ref = g.gecko_sca_awm_forward(z, p, v, 256)
+    ref_b = g.gecko_backward(z, p, v, do, 256)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = g.gecko_sca_awm_forward(z, p, v, 256, stream=side)
+    res = g.gecko_backward(z, p, v, do, 256, stream=side)
+    junk = [torch.full((1 << 22,), 7.0, device="cuda") for _ in range(16)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out, ref)
+    for k in ref_b:
+        assert torch.equal(res[k], ref_b[k]), k
