@@ -132,6 +132,8 @@ struct Call {
   // gecko_forward_train: float32 attention output and per-query (m, l) (bf16 only)
   float* o_sca;
   float* stats;
+  // gecko_sca_awm_forward_noalloc: the workspace is the library's scratch array
+  bool noalloc;
 };
 
 // memory steps and snapshot slots of a call (see gecko::Problem); lag 2 with
@@ -220,7 +222,14 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
     if (k.ws && overlaps(k.state, t.bytes, k.ws, k.ws_bytes))
       return fail(GECKO_EINVAL, "streaming state aliases the workspace");
   }
-  if (need_awm && nmem > 0) {
+  if (need_awm && nmem > 0 && k.noalloc) {
+    const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, nsnap, bf16, k.streaming);
+    if (w.bytes > gecko::noalloc_scratch_bytes())
+      return fail(GECKO_EWORKSPACE,
+                  "these sizes need %zu bytes of scratch, more than the %zu bytes the allocation-free forward "
+                  "holds per GPU; use gecko_sca_awm_forward with a caller workspace",
+                  w.bytes, gecko::noalloc_scratch_bytes());
+  } else if (need_awm && nmem > 0) {
     const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, nsnap, bf16, k.streaming);
     if (!k.ws) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", w.bytes);
     if (k.ws_bytes < w.bytes) return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", k.ws_bytes, w.bytes);
@@ -279,8 +288,22 @@ gecko_status run(const Call& k) {
   if (st != GECKO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(k.stream);
   const bool do_awm = (k.mode & kModeAwm) && p.nmem > 0;
+  void* ws = k.ws;
+  if (k.noalloc && do_awm) {
+    // the current device's copy of the scratch array; the stream must belong to it
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (s) {
+      int sdev = -1;
+      if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+      if (sdev != dev)
+        return fail(GECKO_EINVAL, "the stream belongs to device %d, but device %d is current", sdev, dev);
+    }
+    if ((e = gecko::noalloc_scratch(dev, &ws)) != hipSuccess) return hip_fail(e, "scratch address lookup");
+  }
   gecko::Workspace w{};
-  if (do_awm) w = gecko::carve_workspace(k.ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, p.nsnap, bf16, p.stream);
+  if (do_awm) w = gecko::carve_workspace(ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, p.nsnap, bf16, p.stream);
 
   hipEvent_t* ev = nullptr;
   if (k.timer && k.timer->used < k.timer->capacity) ev = &k.timer->ev[5 * k.timer->used++];
@@ -366,6 +389,22 @@ gecko_status gecko_sca_awm_forward(const void* z, const float* kappa_q, const fl
                                    unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   return gecko_sca_awm_forward_timed(z, kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k, v, out, B, H, n, d,
                                      dv, c, in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+gecko_status gecko_sca_awm_forward_noalloc(const void* z, const float* kappa_q, const float* nu_q,
+                                           const float* kappa_k, const float* nu_k, const float* eta_q,
+                                           const float* rho_q, const float* eta_k, const float* rho_k, const void* v,
+                                           void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                           int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                                           void* stream) {
+  try {
+    Call k{z, v, out, {kappa_q, nu_q, kappa_k, nu_k, eta_q, rho_q, eta_k, rho_k}, B, H, n, d, dv, c,
+           in_dtype, out_dtype, flags, nullptr, 0, stream, kModeSca | kModeAwm, nullptr};
+    k.noalloc = true;
+    return run(k);
+  } catch (...) {
+    return fail(GECKO_EHIP, "internal error");
+  }
 }
 
 gecko_status gecko_sca_forward(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,

@@ -66,6 +66,12 @@ struct Workspace {
 Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv,
                           int64_t nmem, int64_t nsnap, bool bf16, bool stream);
 
+// The library's own scratch array (noalloc.hip): its size, and the device
+// address of `device`'s copy (looked up once per device, with that device
+// current; never the array's host-side name).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(int device, void** ptr);
+
 // Launchers (stream-ordered, asynchronous). Each returns the launch status.
 hipError_t launch_awm_chunk_bf16(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t launch_awm_zscan(const Problem& p, const Workspace& w, hipStream_t s);

@@ -30,7 +30,11 @@ EXPORTED = (
     "gecko_tdn_workspace_size", "gecko_tdn_forward",
     "gecko_forward_lse", "gecko_backward_workspace_size", "gecko_backward",
     "gecko_forward_train", "gecko_backward_saved_workspace_size", "gecko_backward_saved",
+    "gecko_sca_awm_forward_noalloc",
 )
+
+# bytes of the scratch array gecko_sca_awm_forward_noalloc holds per GPU (GECKO_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class GeckoError(RuntimeError):
@@ -60,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.gecko_sca_awm_forward.argtypes = fwd
     lib.gecko_sca_awm_forward_timed.restype = I
     lib.gecko_sca_awm_forward_timed.argtypes = fwd + [P]
+    lib.gecko_sca_awm_forward_noalloc.restype = I
+    lib.gecko_sca_awm_forward_noalloc.argtypes = [P] + [F] * 8 + [P, P] + [I64] * 6 + [I, I, U, P]
     lib.gecko_sca_forward.restype = I
     lib.gecko_sca_forward.argtypes = [P] + [F] * 4 + [P, P] + [I64] * 6 + [I, I, P]
     lib.gecko_awm_forward.restype = I
@@ -223,6 +229,19 @@ def gecko_sca_awm_forward(z, params, v, c, out=None, out_dtype=None, flags=0, wo
         _check(lib.gecko_sca_awm_forward_timed(*args, timer.handle))
     else:
         _check(lib.gecko_sca_awm_forward(*args))
+    return out
+
+
+def gecko_sca_awm_forward_noalloc(z, params, v, c, out, flags=0, stream=None):
+    """O = O_SCA + O_m into the caller's ``out`` (bf16 or float32 [B, H, n, dv]),
+    with the library's own scratch memory in place of a workspace: nothing is
+    allocated, here or in the library. Calls on one GPU must not overlap in time."""
+    B, H, n, d, dv = _shape(z, v)
+    if tuple(out.shape) != (B, H, n, dv) or not out.is_contiguous() or out.device != z.device:
+        raise GeckoError(GECKO_EINVAL, "out must be a contiguous [B, H, n, dv] tensor on z's device")
+    _check(lib.gecko_sca_awm_forward_noalloc(
+        _ptr(z), *_params(params, Q_NAMES + M_NAMES, z.device, H, d), _ptr(v), _ptr(out),
+        B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out), flags, _stream(stream)))
     return out
 
 

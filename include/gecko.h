@@ -101,6 +101,36 @@ gecko_status gecko_sca_awm_forward(
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * gecko_sca_awm_forward (same arguments, same kernels, bit-identical output)
+ * without the workspace: the memory pass and the scan use a scratch array
+ * that the library holds on each GPU it runs on, GECKO_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU from the first call there until the process ends. The call
+ * allocates and frees nothing; the caller passes inputs and outputs as for
+ * gecko_sca_awm_forward. Sizes whose workspace (gecko_workspace_size_for)
+ * exceeds GECKO_NOALLOC_SCRATCH_BYTES are refused with GECKO_EWORKSPACE
+ * before anything reaches the device (B1 H8, 131072 tokens, c 2048, d 128,
+ * dv 256 in bf16 needs 109.5 MiB and fits).
+ *
+ * The scratch array is shared by every call on one GPU and keeps whatever
+ * the last call left in it (nothing in it needs to start at zero). Calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * threads without ordering) race on it and give undefined results: order
+ * them on one stream. The stream must belong to the current device
+ * (GECKO_EINVAL otherwise); NULL is the current device's null stream.
+ */
+#define GECKO_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gecko_status gecko_sca_awm_forward_noalloc(
+    const void* z,
+    const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
+    const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
+    const void* v, void* out,
+    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+    gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, void* stream);
+
 /* O = O_SCA only (needs no workspace; the memory vectors are not read). */
 gecko_status gecko_sca_forward(
     const void* z,

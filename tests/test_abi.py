@@ -124,6 +124,31 @@ def test_workspace_must_not_alias_inputs(g):
     assert st == g.GECKO_EINVAL and "affine vector 7" in msg
 
 
+def test_noalloc_forward_size_limit(g):
+    """The allocation-free forward states its scratch size in the header and
+    refuses sizes whose workspace exceeds it before touching the device."""
+    text = open(HEADER).read()
+    m = re.search(r"#define GECKO_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == g.NOALLOC_SCRATCH_BYTES
+    big = 1 << 40  # widely spaced fake addresses: nothing aliases, nothing is dereferenced
+
+    def call(n, H=8, **kw):
+        a = dict(z=big, v=2 * big, out=3 * big)
+        a.update(kw)
+        st = g.lib.gecko_sca_awm_forward_noalloc(a["z"], *[4 * big + 256 * i for i in range(8)], a["v"], a["out"],
+                                                 1, H, n, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16, 0, None)
+        return st, g.lib.gecko_last_error().decode()
+
+    need = g.gecko_workspace_size(1, 8, 262144, 128, 256, 2048, g.GECKO_BF16)
+    assert need > g.NOALLOC_SCRATCH_BYTES
+    st, msg = call(262144)
+    assert st == g.GECKO_EWORKSPACE and "scratch" in msg and str(need) in msg
+    st, msg = call(131072, z=0)
+    assert st == g.GECKO_EINVAL and "non-null" in msg
+    st, msg = call(131072, out=big + 4096)
+    assert st == g.GECKO_EINVAL and "alias" in msg
+
+
 def test_sca_and_awm_entry_validation(g):
     st = g.lib.gecko_sca_forward(FAKE, FAKE, FAKE, FAKE, 0, 2 * FAKE, 3 * FAKE, 1, 1, 10, 128, 256, 4,
                                  g.GECKO_BF16, g.GECKO_BF16, None)
