@@ -15,6 +15,10 @@ the library's stream between its kernels during the timed steps.
 algorithmic bytes and from the committed counter summary's measured bytes.
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
 workload on this host (not a target).
+
+``--workload`` picks the workload of the JSON line (default: the 128K-token
+headline); ``variants.workloads`` times the other bf16 workloads (B4 H8 16K,
+B1 H8 1M, B1 H4 4M tokens) with the same flop count and stage split.
 """
 
 from __future__ import annotations
@@ -68,9 +72,10 @@ def read_traffic(summary, launch_key: str):
 
 def cpu_baseline(host, w, budget_s: float):
     """Time the fp64 oracle on a bounded sample of the workload: the first m
-    chunks of head 0, m grown until one call takes most of the budget; if a
-    whole head takes less, further whole heads until the budget is spent.
-    Scaled to the workload's tokens/s (every token passes all H heads)."""
+    chunks of head 0 (of those ``host`` holds), m grown until one call takes
+    most of the budget; if a whole head takes less, further whole heads until
+    the budget is spent. Scaled to the workload's tokens/s (every token passes
+    all H heads)."""
     import numpy as np
 
     import oracle
@@ -78,15 +83,16 @@ def cpu_baseline(host, w, budget_s: float):
     p = host["params"]
     cores = len(os.sched_getaffinity(0))
     z, v = host["z"][0, 0], host["v"][0, 0]
+    m_max = -(-z.shape[0] // w.c)  # chunks held on the host (all, or a leading sample)
     m = 1
     while True:
-        ntok = min(m * w.c, w.n)
+        ntok = min(m * w.c, z.shape[0])
         t0 = time.perf_counter()
         oracle.forward_head(z[:ntok], v[:ntok], p, 0, w.c)
         dt = time.perf_counter() - t0
-        if ntok >= w.n or dt >= 0.6 * budget_s:
+        if ntok >= w.n or m >= m_max or dt >= 0.6 * budget_s:
             break
-        m = min(w.nchunks, max(2 * m, int(m * budget_s / max(dt, 1e-9))))
+        m = min(m_max, max(2 * m, int(m * budget_s / max(dt, 1e-9))))
     t_total, head_tokens, heads = dt, ntok, 1
     while ntok >= w.n and heads < w.H and t_total < budget_s:
         t0 = time.perf_counter()
@@ -96,10 +102,37 @@ def cpu_baseline(host, w, budget_s: float):
     value = head_tokens * heads / t_total / w.H
     what = (f"heads 0..{heads - 1} of {w.H}, all {w.nchunks} chunks" if ntok >= w.n
             else f"head 0 of {w.H}, first {m} of {w.nchunks} chunks")
+    cpu, blas = host_cpu_and_blas()
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu, "blas": blas,
             "sample": f"fp64 oracle on {what} ({head_tokens * heads} head-tokens) in {t_total:.2f} s; "
                       f"head-tokens/s divided by {w.H} heads; numpy {np.__version__}, "
                       f"BLAS threads up to {cores} host cores"}
+
+
+def host_cpu_and_blas():
+    """The host CPU model (/proc/cpuinfo) and the BLAS library numpy calls."""
+    import numpy as np
+
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        info = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{info.get('name')} {info.get('version')}".strip()
+        conf = info.get("openblas configuration")
+        if conf:
+            blas += f" ({conf})"
+    except Exception:
+        pass
+    return cpu, blas
 
 
 def time_variants(gecko, w, z, v, params, out, stream, args) -> dict:
@@ -284,16 +317,97 @@ def time_cema(gecko, stream, timed) -> dict:
                          "flops_per_launch": flops, "algorithmic_bytes": 4.0 * B * n * D}}
 
 
+def time_other_workloads(gecko, skip: int, stream, out_dtype) -> dict:
+    """The other bf16 workloads (B4 H8 16K; B1 H8 1M; B1 H4 4M tokens, all
+    c 2048, d 128, dv 256), one after the other on inputs drawn on the device
+    (same recipe), each freed before the next: ms per forward, tokens/s, the
+    fraction of the bf16 peak by the same flop count, and the per-stage split
+    from the library's stage events (the memory scan runs N - 2 dependent
+    steps: 6, 510 and 2046)."""
+    import torch
+
+    from chunked_attention_memory_amd import configs, inputs
+
+    res = {}
+    for key in (1, 3, 4):
+        if key == skip:
+            continue
+        w = configs.WORKLOADS[key]
+        dev = inputs.make_inputs_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed=0, tag=key)
+        z, v = dev["z"], dev["v"]
+        params = {k: torch.from_numpy(a).cuda() for k, a in dev["params"].items()}
+        steps, warmup = (10, 3) if key == 1 else (3, 1)
+        r = measure_forward(gecko, w, z, v, params, out_dtype, steps, warmup, stream)
+        flops = configs.workload_flops(w)["total"]
+        res[w.name] = {"B": w.B, "H": w.H, "n": w.n, "c": w.c, "ms_per_step": r["ms"],
+                       "tokens_per_s": w.B * w.n / (r["ms"] / 1e3),
+                       "pct_of_bf16_peak": flops / (r["ms"] / 1e3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0,
+                       "flops_per_step": flops, "stage_ms": r["stage_ms"], "steps": steps, "warmup": warmup,
+                       "finite": r["finite"]}
+        del dev, z, v, params, r
+        torch.cuda.empty_cache()
+    return res
+
+
+def measure_forward(gecko, w, z, v, params, out_dtype, steps, warmup, stream, per_call=False) -> dict:
+    """Time ``steps`` forwards (after ``warmup`` untimed ones) on resident
+    inputs: wall clock around the whole timed region (synchronised on both
+    sides), HIP events on the launch stream, the library's stage events, and
+    optionally each call again on its own (median and minimum)."""
+    import torch
+
+    out = torch.empty((w.B, w.H, w.n, w.dv), dtype=out_dtype, device=z.device)
+    ws = gecko.alloc_workspace(z, v, w.c, stream=stream)
+    timer = gecko.Timer(max(steps, 1))
+
+    def step(tm=None):
+        gecko.gecko_sca_awm_forward(z, params, v, w.c, out=out, workspace=ws, stream=stream, timer=tm)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step(timer)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stages, calls = timer.read()
+    timer.close()
+    res = {"ms": wall * 1e3 / steps, "ms_events": ev0.elapsed_time(ev1) / steps,
+           "stage_ms": {k: v_ / calls for k, v_ in stages.items()} if calls else {},
+           "finite": bool(torch.isfinite(out).all())}
+    if per_call:
+        evs = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        res["per_call_ms"] = {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)}
+    res["out"] = out
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, choices=(1, 2, 3, 4), default=2,
+                    help="workload of the JSON line: 2 is the 128K-token headline (default); 1 B4 H8 16K, "
+                         "3 B1 H8 1M, 4 B1 H4 4M tokens")
     ap.add_argument("--out-dtype", choices=("bf16", "f32"), default="bf16")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the variant timings (chunk-wise form; streaming in four calls), e.g. under a profiler")
+                    help="skip the variant timings (other workloads, chunk-wise form, streaming, backward, "
+                         "CEMA, TDN), e.g. under a profiler")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
@@ -309,53 +423,28 @@ def main(argv=None) -> int:
 
     from chunked_attention_memory_amd import configs, gecko, inputs
 
-    w = configs.WORKLOADS[2]
+    w = configs.WORKLOADS[args.workload]
     flops = configs.workload_flops(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     t0 = time.perf_counter()
-    host = inputs.make_inputs(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed=0, tag=2)
+    if args.workload <= 2:
+        host = inputs.make_inputs(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed=0, tag=args.workload)
+        z, v, params = gecko.to_device_inputs(host, device=dev)
+    else:
+        # too large to draw on the host quickly: the same recipe on the device
+        d_in = inputs.make_inputs_device(w.B, w.H, w.n, w.d, w.dv, w.dtype, seed=0, tag=args.workload)
+        z, v = d_in["z"], d_in["v"]
+        params = {k: torch.from_numpy(a).to(dev) for k, a in d_in["params"].items()}
+        host = None
+    torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
-    z, v, params = gecko.to_device_inputs(host, device=dev)
     out_dt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    out = torch.empty((w.B, w.H, w.n, w.dv), dtype=out_dt, device=dev)
-    ws = gecko.alloc_workspace(z, v, w.c)
     stream = torch.cuda.current_stream()
-    timer = gecko.Timer(max(args.steps, 1))
 
-    def step(tm=None):
-        gecko.gecko_sca_awm_forward(z, params, v, w.c, out=out, workspace=ws, stream=stream, timer=tm)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step(timer)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ev_ms = ev0.elapsed_time(ev1)
-    stages, calls = timer.read()
-    timer.close()
-
-    # per-call durations (an event pair around each call, after the timed
-    # region): median and minimum, beside the timed region's mean
-    per_call = []
-    for _ in range(args.steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        per_call.append((e0, e1))
-    torch.cuda.synchronize()
-    call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in per_call)
-    del per_call
+    r = measure_forward(gecko, w, z, v, params, out_dt, args.steps, args.warmup, stream, per_call=True)
+    out = r.pop("out")
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -365,13 +454,17 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    variants = None if args.no_variants else time_variants(gecko, w, z, v, params, out, stream, args)
+    variants = None
+    if not args.no_variants:
+        variants = {"workloads": time_other_workloads(gecko, args.workload, stream, out_dt)}
+        if args.workload == 2:
+            variants.update(time_variants(gecko, w, z, v, params, out, stream, args))
 
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = r["ms"]
     tokens = w.B * w.n
     value = tokens / (ms_per_step / 1e3)
     pct_peak = flops["total"] / (ms_per_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
-    stage_ms = {k: v_ / calls for k, v_ in stages.items()} if calls else {}
+    stage_ms = r["stage_ms"]
     sca_ms = stage_ms.get("sca_readout")
     sca_flops = flops["sca"] + flops["awm_read"]
     achieved = sca_flops / (sca_ms / 1e3) / 1e12 if sca_ms else None
@@ -384,7 +477,7 @@ def main(argv=None) -> int:
     scan_meas = read_traffic(PMC_SCAN, launch_key)
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == 2 else "SCA+AWM fwd tokens/s; % of bf16 MFMA peak",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -401,9 +494,10 @@ def main(argv=None) -> int:
         "pct_of_bf16_peak": pct_peak,
         "flops_per_step": flops["total"],
         "peak_tflops_used": PEAK_BF16_TFLOPS,
-        "ms_per_step_events": ev_ms / args.steps,
-        "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)},
+        "ms_per_step_events": r["ms_events"],
+        "per_call_ms": r["per_call_ms"],
         "stage_ms": stage_ms,
+        "output_finite": r["finite"],
         "roofline": {"kernel": "sca_bf16_kernel (attention + readout)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
@@ -418,6 +512,11 @@ def main(argv=None) -> int:
     if variants is not None:
         res["variants"] = variants
     if not args.no_cpu_baseline:
+        if host is None:
+            # the oracle's sample comes from head 0's first chunks on the device
+            m = max(1, min(w.nchunks, 16))
+            host = {"z": z[:, :1, :m * w.c].float().cpu().numpy(), "v": v[:, :1, :m * w.c].float().cpu().numpy(),
+                    "params": d_in["params"]}
         res["cpu_baseline"] = cpu_baseline(host, w, args.cpu_budget)
     print(json.dumps(res), flush=True)
     return 0
