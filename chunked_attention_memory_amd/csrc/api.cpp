@@ -176,7 +176,7 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
   bf16 = k.in_dtype == GECKO_BF16;
   if (!bf16 && k.out_dtype != GECKO_F32) return fail(GECKO_EUNSUPPORTED, "float32 input needs float32 output");
   if (bf16 && !gecko::bf16_shape_built(k.d, k.dv))
-    return fail(GECKO_EUNSUPPORTED, "bf16 kernels are built for (d, dv) in {(128,256), (128,128), (64,128), (64,64)}");
+    return fail(GECKO_EUNSUPPORTED, "no bf16 kernels for (d, dv) = (%lld, %lld)", (long long)k.d, (long long)k.dv);
   if (k.B > (1 << 20) || k.H > (1 << 20) || k.n > (int64_t(1) << 40))
     return fail(GECKO_EINVAL, "sizes out of range");
   const int64_t BH = k.B * k.H;

@@ -69,6 +69,7 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int D>
 __device__ __forceinline__ int zswz(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | (r & 3);
+  if constexpr (D == 32) return (r >> 2) & 3;  // rows of 64 bytes: 4 chunks
   const int rho = (r >> 1) & 3;
   return rho ^ ((rho & 1) << 2);
 }
@@ -79,8 +80,14 @@ struct ChunkTile {
   static constexpr int THREADS = 64 * NW;
   static constexpr int ZBYTES = kBT * D * 2;
   static constexpr int VBYTES = kBT * DV * 2;
-  static constexpr int ZLOADS = ZBYTES / 16 / THREADS;
-  static constexpr int VLOADS = VBYTES / 16 / THREADS;
+  // 16-byte loads per thread per tile, at least one (with fewer 1 KiB
+  // pieces than waves, waves share pieces; see stage_rows)
+  static constexpr int ZPIECES = ZBYTES / 1024;
+  static constexpr int VPIECES = VBYTES / 1024;
+  static constexpr int ZLOADS = ZBYTES / 16 / THREADS > 0 ? ZBYTES / 16 / THREADS : 1;
+  static constexpr int VLOADS = VBYTES / 16 / THREADS > 0 ? VBYTES / 16 / THREADS : 1;
+  static constexpr int ZMOD = ZPIECES < NW * ZLOADS ? ZPIECES : 0;  // piece count for stage_rows (0: no sharing)
+  static constexpr int VMOD = VPIECES < NW * VLOADS ? VPIECES : 0;
   static constexpr int PARTS = THREADS / kBT;  // threads per token row in the psi phase
   static constexpr int FPT = D / PARTS;        // features per thread in the psi phase
   static constexpr int KT = kBT / 16;          // 16-token k-steps per tile
@@ -179,13 +186,13 @@ struct ChunkLoop {
     rkf = a.rho_k[h * D + f] * kLog2e;
 #pragma unroll
     for (int i = 0; i < T::ZLOADS; ++i) {
-      const int P = (T::NW * i + w) * 64 + lane;
+      const int P = stage_piece(T::NW, w, i, T::ZMOD) * 64 + lane;
       const int r = P / (D / 8), p = P % (D / 8);
       zoff[i] = (uint32_t)(r * D + 8 * (p ^ zswz<D>(r))) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < T::VLOADS; ++i) {
-      const int P = (T::NW * i + w) * 64 + lane;
+      const int P = stage_piece(T::NW, w, i, T::VMOD) * 64 + lane;
       const int r = P / (DV / 8), p = P % (DV / 8);
       voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
     }
@@ -228,10 +235,10 @@ struct ChunkLoop {
   __device__ __forceinline__ const char* zs(int slot) const { return sb[slot]; }
   __device__ __forceinline__ const char* vs(int slot) const { return sb[slot] + T::ZBYTES; }
   __device__ __forceinline__ void stage_z(int it, int slot) const {
-    stage_rows(zbh, cbeg + it * kBT, n, D, sb[slot], T::NW, w, zoff, T::ZLOADS);
+    stage_rows(zbh, cbeg + it * kBT, n, D, sb[slot], T::NW, w, zoff, T::ZLOADS, T::ZMOD);
   }
   __device__ __forceinline__ void stage_v(int it, int slot) const {
-    stage_rows(vbh, cbeg + it * kBT, n, DV, sb[slot] + T::ZBYTES, T::NW, w, voff, T::VLOADS);
+    stage_rows(vbh, cbeg + it * kBT, n, DV, sb[slot] + T::ZBYTES, T::NW, w, voff, T::VLOADS, T::VMOD);
   }
 
   // eta_k z + shift for this lane's feature (log2 units) and tokens
@@ -813,10 +820,13 @@ hipError_t launch_awm_chunk_bf16(const Problem& p, const Workspace& w, hipStream
   a.vprev = static_cast<const uint16_t*>(p.vprev);
   a.n = p.n; a.c = p.c; a.nmem = p.nmem; a.H = (int)p.H; a.has_prev = p.has_prev ? 1 : 0;
   const int64_t BH = p.B * p.H;
-  if (p.d == 128 && p.dv == 256) return launch_chunk<128, 256>(a, BH, s);
-  if (p.d == 128 && p.dv == 128) return launch_chunk<128, 128>(a, BH, s);
-  if (p.d == 64 && p.dv == 128) return launch_chunk<64, 128>(a, BH, s);
-  if (p.d == 64 && p.dv == 64) return launch_chunk<64, 64>(a, BH, s);
+  switch (p.d * 1000 + p.dv) {
+#define GECKO_AWM_SHAPE(D_, DV_) \
+  case D_ * 1000 + DV_:          \
+    return launch_chunk<D_, DV_>(a, BH, s);
+    GECKO_BF16_SHAPES(GECKO_AWM_SHAPE)
+#undef GECKO_AWM_SHAPE
+  }
   return hipErrorInvalidValue;
 }
 
@@ -835,10 +845,13 @@ hipError_t launch_awm_scan_bf16(const Problem& p, const Workspace& w, hipStream_
   a.mstate = p.mstate; a.zstate = p.zstate; a.zfinal = w.zfinal; a.snap32 = w.snap32;
   a.has_prev = p.has_prev ? 1 : 0; a.stream = p.stream ? 1 : 0;
   const int64_t BH = p.B * p.H;
-  if (p.d == 128 && p.dv == 256) return launch_scan<128, 256>(a, BH, s);
-  if (p.d == 128 && p.dv == 128) return launch_scan<128, 128>(a, BH, s);
-  if (p.d == 64 && p.dv == 128) return launch_scan<64, 128>(a, BH, s);
-  if (p.d == 64 && p.dv == 64) return launch_scan<64, 64>(a, BH, s);
+  switch (p.d * 1000 + p.dv) {
+#define GECKO_AWM_SHAPE(D_, DV_) \
+  case D_ * 1000 + DV_:          \
+    return launch_scan<D_, DV_>(a, BH, s);
+    GECKO_BF16_SHAPES(GECKO_AWM_SHAPE)
+#undef GECKO_AWM_SHAPE
+  }
   return hipErrorInvalidValue;
 }
 

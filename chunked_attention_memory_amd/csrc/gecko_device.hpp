@@ -141,8 +141,18 @@ __device__ __forceinline__ void wait_vmem_leave() {
 // compiler through the input constraint, and the s_nop covers the M0 -> LDS
 // load hazard. A plain __device__ function on purpose: kernels' lambdas are
 // also compiled for the host.
+//
+// A tile of fewer 1 KiB pieces than nwaves * nloads (npieces, when positive)
+// is covered with pieces taken modulo npieces: several waves then load the
+// same piece into the same place (the same bytes), and every wave still
+// issues nloads loads, so that the waits that count them stay uniform.
+// off[i] must be computed from the same piece index.
+__device__ __forceinline__ int stage_piece(int nwaves, int w, int i, int npieces) {
+  const int p = nwaves * i + w;
+  return npieces > 0 ? p % npieces : p;
+}
 __device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n, int width, char* lds_tile,
-                                           int nwaves, int w, const uint32_t* off, int nloads) {
+                                           int nwaves, int w, const uint32_t* off, int nloads, int npieces = 0) {
   const uint32_t rows = (uint32_t)(n > row0 ? n - row0 : 0);
   const uint64_t addr = (uint64_t)(uintptr_t)(base + (size_t)row0 * width);
   i32x4 rs;  // buffer resource: base address, stride 0, size in bytes, raw-buffer flags
@@ -153,7 +163,7 @@ __device__ __forceinline__ void stage_rows(const uint16_t* base, int row0, int n
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_tile;
 #pragma unroll
   for (int i = 0; i < nloads; ++i) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((nwaves * i + w) * 1024));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(stage_piece(nwaves, w, i, npieces) * 1024));
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rs), "{m0}"(m0)
                  : "memory");
   }
@@ -168,7 +178,12 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
 
 // XOR swizzle of the 16-byte chunks of a staged row-major V row (dv values),
 // for transpose reads of 4 rows x 32 columns (32 lanes per pass, 64 banks).
+// It depends on the row mod 4 only. Rows of 64 bytes (dv = 32) hold 4 chunks.
 template <int DV>
-__device__ __forceinline__ int vswz(int r) { return DV >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (DV >= 128) return (r & 3) << 2;
+  if constexpr (DV == 64) return ((r >> 1) & 1) << 2;
+  return r & 3;
+}
 
 }  // namespace gecko

@@ -72,6 +72,12 @@ Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t 
 size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(int device, void** ptr);
 
+// The (d, dv) pairs the bf16 kernels are built for: every pair of
+// d in {32, 64, 128} and dv in {32, 64, 128, 256}.
+#define GECKO_BF16_SHAPES(X)                                      \
+  X(128, 256) X(128, 128) X(128, 64) X(128, 32) X(64, 256) X(64, 128) \
+  X(64, 64) X(64, 32) X(32, 256) X(32, 128) X(32, 64) X(32, 32)
+
 // Launchers (stream-ordered, asynchronous). Each returns the launch status.
 hipError_t launch_awm_chunk_bf16(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t launch_awm_zscan(const Problem& p, const Workspace& w, hipStream_t s);

@@ -99,8 +99,16 @@ struct ScaTile {
   static constexpr size_t lds_bytes(bool sca, bool read) {
     return sca ? STAGE_BYTES + (read && SNAP_EARLY ? SNAP_BYTES : 0) : (read ? SNAP_BYTES : 0);
   }
-  static constexpr int KLOADS = KBYTES / 16 / THREADS;  // 16-byte loads per thread per tile
-  static constexpr int VLOADS = VBYTES / 16 / THREADS;
+  // 1 KiB pieces of a tile, and 16-byte loads per thread per tile (at least
+  // one: with fewer pieces than waves, waves share pieces; see stage_rows)
+  static constexpr int KPIECES = KBYTES / 1024;
+  static constexpr int VPIECES = VBYTES / 1024;
+  static constexpr int KLOADS = KBYTES / 16 / THREADS > 0 ? KBYTES / 16 / THREADS : 1;
+  static constexpr int VLOADS = VBYTES / 16 / THREADS > 0 ? VBYTES / 16 / THREADS : 1;
+  // the piece count handed to stage_rows: 0 (no sharing) unless the waves
+  // have more loads than the tile has pieces
+  static constexpr int KMOD = KPIECES < NW * KLOADS ? KPIECES : 0;
+  static constexpr int VMOD = VPIECES < NW * VLOADS ? VPIECES : 0;
   static constexpr int LOADS = KLOADS + VLOADS;  // staging loads per lane and tile
   static_assert(32 * QB * NW == kBM, "tile shape");
 };
@@ -117,7 +125,11 @@ struct ScaShape {
 // 16-byte operand reads below touch each of the 64 LDS banks once per pass of
 // 16 lanes (V rows use vswz, for the 8-byte transpose reads).
 template <int D>
-__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) return r & 15;
+  if constexpr (D == 64) return (r >> 1) & 7;
+  return (r >> 2) & 3;  // rows of 64 bytes: 4 chunks
+}
 
 struct ScaArgs {
   const uint16_t* z;
@@ -228,13 +240,13 @@ struct ScaLoop {
     // logical chunk p ^ swz(r).
 #pragma unroll
     for (int i = 0; i < T::KLOADS; ++i) {
-      const int P = (NW * i + w) * 64 + lane;
+      const int P = stage_piece(NW, w, i, T::KMOD) * 64 + lane;
       const int r = P / KCH, p = P % KCH;
       koff[i] = (uint32_t)(r * D + 8 * (p ^ kswz<D>(r))) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < T::VLOADS; ++i) {
-      const int P = (NW * i + w) * 64 + lane;
+      const int P = stage_piece(NW, w, i, T::VMOD) * 64 + lane;
       const int r = P / VCH, p = P % VCH;
       voff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
     }
@@ -254,8 +266,8 @@ struct ScaLoop {
     const bool carried = row0 < 0;
     const int r = carried ? row0 + cl : row0;
     const int lim = carried ? cl : n;
-    stage_rows(carried ? zpv : zbh, r, lim, D, sb[slot], NW, w, koff, T::KLOADS);
-    stage_rows(carried ? vpv : vbh, r, lim, DV, sb[slot] + T::KBYTES, NW, w, voff, T::VLOADS);
+    stage_rows(carried ? zpv : zbh, r, lim, D, sb[slot], NW, w, koff, T::KLOADS, T::KMOD);
+    stage_rows(carried ? vpv : vbh, r, lim, DV, sb[slot] + T::KBYTES, NW, w, voff, T::VLOADS, T::VMOD);
   }
 
   __device__ __forceinline__ int k_addr(int mb, int ks) const { return ka[ks] + 32 * mb * (D * 2); }
@@ -517,20 +529,22 @@ template <int D, int DV, int THREADS, int FB0>
 __device__ __forceinline__ void stage_snapshot(const uint16_t* sn, char* sa, char* sbk, int w, int lane) {
   constexpr int NW = THREADS / 64;
   constexpr int RB = 32;  // rows per staging call: one feature block
-  constexpr int SLOADS = RB * DV * 2 / 16 / THREADS;
-  static_assert(SLOADS >= 1 && SLOADS * 16 * THREADS == RB * DV * 2, "snapshot staging shape");
+  constexpr int SPIECES = RB * DV * 2 / 1024;
+  constexpr int SLOADS = SPIECES * 64 >= THREADS ? SPIECES * 64 / THREADS : 1;
+  constexpr int SMOD = SPIECES < NW * SLOADS ? SPIECES : 0;
+  static_assert(SPIECES >= 1 && SLOADS * 16 * THREADS >= RB * DV * 2, "snapshot staging shape");
   constexpr int VCH = DV / 8;
   uint32_t soff[SLOADS];
 #pragma unroll
   for (int i = 0; i < SLOADS; ++i) {
-    const int P = (NW * i + w) * 64 + lane;
+    const int P = stage_piece(NW, w, i, SMOD) * 64 + lane;
     const int r = P / VCH, p = P % VCH;
     soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
   }
 #pragma unroll
   for (int rb = 0; rb < D / RB; ++rb)
     stage_rows(sn, rb * RB, D, DV, rb < FB0 ? sa + rb * RB * DV * 2 : sbk + (rb - FB0) * RB * DV * 2, NW, w, soff,
-               SLOADS);
+               SLOADS, SMOD);
 }
 
 // Byte offset, in a staged V tile (rows of DV values), of the transpose read
@@ -839,7 +853,14 @@ hipError_t launch_shape(const ScaArgs& a, int mode, bool out_f32, hipStream_t s)
 }  // namespace
 
 bool bf16_shape_built(int64_t d, int64_t dv) {
-  return (d == 128 && (dv == 256 || dv == 128)) || (d == 64 && (dv == 128 || dv == 64));
+  switch (d * 1000 + dv) {
+#define GECKO_SCA_SHAPE(D_, DV_) \
+  case D_ * 1000 + DV_:          \
+    return true;
+    GECKO_BF16_SHAPES(GECKO_SCA_SHAPE)
+#undef GECKO_SCA_SHAPE
+  }
+  return false;
 }
 
 hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipStream_t stream) {
@@ -868,10 +889,13 @@ hipError_t launch_sca_bf16(const Problem& p, const Workspace& w, int mode, hipSt
   const int64_t nblocks = p.B * p.H * p.nchunks * a.qtiles;
   a.nblocks = (int)nblocks;
   a.per_xcd = (int)((nblocks + 7) / 8);
-  if (p.d == 128 && p.dv == 256) return launch_shape<128, 256>(a, mode, p.out_f32, stream);
-  if (p.d == 128 && p.dv == 128) return launch_shape<128, 128>(a, mode, p.out_f32, stream);
-  if (p.d == 64 && p.dv == 128) return launch_shape<64, 128>(a, mode, p.out_f32, stream);
-  if (p.d == 64 && p.dv == 64) return launch_shape<64, 64>(a, mode, p.out_f32, stream);
+  switch (p.d * 1000 + p.dv) {
+#define GECKO_SCA_SHAPE(D_, DV_) \
+  case D_ * 1000 + DV_:          \
+    return launch_shape<D_, DV_>(a, mode, p.out_f32, stream);
+    GECKO_BF16_SHAPES(GECKO_SCA_SHAPE)
+#undef GECKO_SCA_SHAPE
+  }
   return hipErrorInvalidValue;
 }
 

@@ -47,6 +47,8 @@ def test_f32_tiny_workload():
     (1, 2, 640, 128, 64, 128),
     (1, 1, 450, 64, 64, 64),
     (1, 1, 4096, 512, 128, 256),
+    (1, 1, 600, 128, 32, 64),     # 64-byte key rows
+    (1, 2, 500, 64, 128, 32),     # 64-byte value rows
 ])
 def test_bf16_shapes(B, H, n, c, d, dv):
     host = make(B, H, n, d, dv, "bf16", tag=31)

@@ -63,6 +63,17 @@ BF16_SHAPES = [
     (1, 1, 777, 100, 128, 128),   # c not a multiple of the tile sizes
     (1, 1, 450, 64, 64, 64),
     (1, 1, 4096, 512, 128, 256),  # several full tiles per chunk
+    # the remaining (d, dv) pairs: 64-byte rows (d or dv = 32) and tiles with
+    # fewer staging pieces than waves
+    (1, 2, 700, 128, 128, 64),
+    (1, 1, 650, 100, 128, 32),    # c not a multiple of the tile sizes
+    (2, 1, 513, 64, 64, 256),
+    (1, 1, 700, 128, 64, 32),
+    (1, 2, 600, 128, 32, 256),
+    (1, 1, 777, 96, 32, 128),
+    (1, 1, 500, 64, 32, 64),
+    (2, 2, 333, 64, 32, 32),      # batch and heads, ragged tail
+    (1, 1, 1, 7, 32, 32),         # single token at the smallest shape
 ]
 
 

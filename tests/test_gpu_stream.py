@@ -60,6 +60,8 @@ SPLITS = [
     (1, 3 * 256 + 50, 256, 128, 128, [256, 256, 256, 50]),    # last call shorter than a chunk
     (1, 4 * 512, 512, 64, 128, [2048]),                       # one call
     (1, 1000, 2048, 128, 256, [1000]),                        # one call, c > n
+    (1, 6 * 128 + 30, 128, 32, 32, [256, 384, 158]),          # the smallest shape
+    (2, 5 * 64, 64, 32, 256, [128, 64, 128]),                 # 64-byte key rows, dv 256
 ]
 
 
