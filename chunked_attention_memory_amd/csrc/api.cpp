@@ -202,8 +202,14 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
         BH * (k.dv / 32) >= ((int64_t)1 << 31) || (k.streaming && k.c * k.dv * 2 > (int64_t)0xFFFFFFFF))
       return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
   }
-  if (!bf16 && (BH > 65535 || BH * nmem > 65535 || (k.dv / 32) > 65535))
-    return fail(GECKO_EUNSUPPORTED, "float32 path is limited to B*H*max(N-2,1) <= 65535");
+  if (!bf16) {
+    // one-dimensional grids (the fp32 kernels): fewer than 2^31 blocks each
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t ntok = nmem * k.c;
+    if (BH * ((k.n + 63) / 64) * (k.dv / 32) >= lim || BH * ((ntok + 127) / 128) >= lim ||
+        BH * nmem * ((k.d * (k.d + k.dv) + 255) / 256) >= lim)
+      return fail(GECKO_EUNSUPPORTED, "too many workgroups for one launch");
+  }
   const size_t esz = bf16 ? 2 : 4;
   const size_t osz = k.out_dtype == GECKO_BF16 ? 2 : 4;
   const size_t zb = (size_t)BH * k.n * k.d * esz, vb = (size_t)BH * k.n * k.dv * esz;

@@ -14,10 +14,12 @@ namespace gecko {
 namespace {
 
 // per-token (max, sum) of the memory-key row in log2 units, for psi(K_m)
+// (Grids are one-dimensional, block = (batch*head, part): the y and z grid
+// dimensions stop at 65535.)
 __global__ void f32_rowstat_kernel(const float* z, const float* eta_k, const float* rho_k, float* rowstat,
-                                   int64_t n, int64_t ntok, int d, int H) {
-  const int64_t bh = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                   int64_t n, int64_t ntok, int d, int H, int64_t nblk) {
+  const int64_t bh = blockIdx.x / nblk;
+  const int64_t i = (int64_t)(blockIdx.x % nblk) * blockDim.x + threadIdx.x;
   if (i >= ntok) return;
   const int h = (int)(bh % H);
   const float* zr = z + (bh * n + i) * d;
@@ -52,11 +54,11 @@ __global__ void f32_colstat_kernel(const float* z, const float* eta_k, const flo
 // one thread per output element of one chunk.
 __global__ void f32_products_kernel(const float* z, const float* v, const float* eta_k, const float* rho_k,
                                     const float* rowstat, const float* cmax, float* gout, float* hout,
-                                    int64_t n, int64_t c, int64_t nmem, int d, int dv, int H) {
-  const int64_t row = blockIdx.y;  // bh * nmem + t
+                                    int64_t n, int64_t c, int64_t nmem, int d, int dv, int H, int64_t nblk) {
+  const int64_t row = blockIdx.x / nblk;  // bh * nmem + t
   const int64_t bh = row / nmem, t = row % nmem;
   const int h = (int)(bh % H);
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = (int64_t)(blockIdx.x % nblk) * blockDim.x + threadIdx.x;
   const int width = dv + d;
   if (e >= (int64_t)d * width) return;
   const int f = (int)(e / width), x = (int)(e % width);
@@ -111,12 +113,13 @@ __global__ void f32_scan_kernel(const float* g, const float* hm, const float* de
 
 // One thread per (query, 32-column slice of the output). Logits, weights and
 // sums are carried in double so the float32 result is rounded once.
-__global__ void f32_sca_kernel(Problem p, const float* snap, int mode) {
-  const int64_t bh = blockIdx.z;
-  const int h = (int)(bh % p.H);
+__global__ void f32_sca_kernel(Problem p, const float* snap, int mode, int64_t nqblk) {
   const int d = (int)p.d, dv = (int)p.dv;
-  const int x0 = 32 * blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t slices = dv / 32;
+  const int64_t bh = blockIdx.x / (slices * nqblk);
+  const int h = (int)(bh % p.H);
+  const int x0 = 32 * (int)((blockIdx.x / nqblk) % slices);
+  const int64_t i = (int64_t)(blockIdx.x % nqblk) * blockDim.x + threadIdx.x;
   if (i >= p.n) return;
   const float* z = static_cast<const float*>(p.z) + bh * p.n * d;
   const float* v = static_cast<const float*>(p.v) + bh * p.n * dv;
@@ -171,8 +174,9 @@ hipError_t launch_awm_chunk_f32(const Problem& p, const Workspace& w, hipStream_
   const float* z = static_cast<const float*>(p.z);
   const float* v = static_cast<const float*>(p.v);
   const int64_t ntok = p.nmem * p.c;
-  hipLaunchKernelGGL(f32_rowstat_kernel, dim3((unsigned)((ntok + 127) / 128), (unsigned)BH), dim3(128), 0, s,
-                     z, p.eta_k, p.rho_k, w.rowstat, p.n, ntok, (int)p.d, (int)p.H);
+  const int64_t rblk = (ntok + 127) / 128;
+  hipLaunchKernelGGL(f32_rowstat_kernel, dim3((unsigned)(rblk * BH)), dim3(128), 0, s,
+                     z, p.eta_k, p.rho_k, w.rowstat, p.n, ntok, (int)p.d, (int)p.H, rblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(f32_colstat_kernel, dim3((unsigned)(BH * p.nmem)), dim3(128), 0, s, z, p.eta_k, p.rho_k,
@@ -180,9 +184,10 @@ hipError_t launch_awm_chunk_f32(const Problem& p, const Workspace& w, hipStream_
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t outs = p.d * (p.dv + p.d);
-  hipLaunchKernelGGL(f32_products_kernel, dim3((unsigned)((outs + 255) / 256), (unsigned)(BH * p.nmem)), dim3(256),
+  const int64_t pblk = (outs + 255) / 256;
+  hipLaunchKernelGGL(f32_products_kernel, dim3((unsigned)(pblk * BH * p.nmem)), dim3(256),
                      0, s, z, v, p.eta_k, p.rho_k, w.rowstat, w.cmax, w.g, static_cast<float*>(w.h), p.n, p.c,
-                     p.nmem, (int)p.d, (int)p.dv, (int)p.H);
+                     p.nmem, (int)p.d, (int)p.dv, (int)p.H, pblk);
   return hipGetLastError();
 }
 
@@ -196,8 +201,9 @@ hipError_t launch_awm_scan_f32(const Problem& p, const Workspace& w, hipStream_t
 
 hipError_t launch_sca_f32(const Problem& p, const Workspace& w, int mode, hipStream_t s) {
   const int64_t BH = p.B * p.H;
-  const dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)(p.dv / 32), (unsigned)BH);
-  hipLaunchKernelGGL(f32_sca_kernel, grid, dim3(64), 0, s, p, static_cast<const float*>(w.snap), mode);
+  const int64_t qblk = (p.n + 63) / 64;
+  hipLaunchKernelGGL(f32_sca_kernel, dim3((unsigned)(qblk * (p.dv / 32) * BH)), dim3(64), 0, s, p,
+                     static_cast<const float*>(w.snap), mode, qblk);
   return hipGetLastError();
 }
 

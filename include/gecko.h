@@ -67,8 +67,7 @@ enum {
 
 /*
  * Supported shapes: d in {32, 64, 128}; dv in {32, 64, 128, 256}; the bf16
- * and the float32 kernels are built for every pair of the two sets (float32:
- * B*H*max(N-2,1) <= 65535).
+ * and the float32 kernels are built for every pair of the two sets.
  * float32 input writes float32 output; bf16 input writes bf16 output
  * (round to nearest even of the fp32 accumulator) or float32 output (the
  * accumulator itself). n >= 1, c >= 1, B >= 1, H >= 1. z, v and out must be

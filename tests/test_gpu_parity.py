@@ -51,6 +51,19 @@ def test_f32_shapes(B, H, n, c, d, dv):
     assert floor_rel_err(got, _stack(ref, "o", heads)) <= F32_TOL
 
 
+def test_f32_more_than_65535_heads():
+    """66,000 (batch, head) pairs of 5 tokens in chunks of 2 (one memory step
+    each): more workgroups than a y or z grid dimension holds. Heads are
+    independent, so sampled heads (first, last, and one in between) are
+    checked against the oracle."""
+    H, n, c, d, dv = 66000, 5, 2, 32, 32
+    host = make(1, H, n, d, dv, "f32", tag=5)
+    got = run(host, c, "full")
+    heads = [(0, 0), (0, 40001), (0, H - 1)]
+    ref = oracle_parts(host, c, heads=heads)
+    assert floor_rel_err(_gpu_heads(got, heads), _stack(ref, "o", heads)) <= F32_TOL
+
+
 BF16_SHAPES = [
     (1, 2, 700, 128, 128, 256),   # ragged tail, 6 chunks
     (1, 1, 1000, 256, 128, 256),  # 4 chunks, ragged
