@@ -424,3 +424,22 @@ def test_backward_saved_workspace_size(g):
     with pytest.raises(g.GeckoError):
         g.gecko_backward_saved_workspace_size(1, 8, 131072, 128, 256, 2048, g.GECKO_BF16, g.GECKO_BF16,
                                               parts=g.GECKO_PART_AWM)
+
+
+def test_launch_failure_without_a_device(g):
+    """Arguments that pass validation on a machine with no HIP device: the
+    first launch fails and the call returns GECKO_EHIP with the runtime's
+    message, no exception crosses the ABI. Runs only where there is no
+    device, so that nothing is ever launched with these placeholder
+    addresses."""
+    import torch
+
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a HIP device is present: the call would launch kernels on placeholder addresses")
+    big = 1 << 40
+    # attention only (no workspace): B1 H1, 100 tokens in one chunk, (d, dv) = (128, 256)
+    st = g.lib.gecko_sca_forward(big, big + 4096, big + 8192, big + 12288, big + 16384, 2 * big, 3 * big,
+                                 1, 1, 100, 128, 256, 100, g.GECKO_BF16, g.GECKO_BF16, None)
+    msg = g.lib.gecko_last_error().decode()
+    assert st == g.GECKO_EHIP, (st, msg)
+    assert "launch" in msg
