@@ -76,6 +76,14 @@ Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t 
   return w;
 }
 
+size_t kept_memory_bytes(const Workspace& w, int64_t BH, int64_t nmem, int64_t d, int64_t dv) {
+  return nmem > 0 ? align_up(w.bytes) + (size_t)BH * (size_t)nmem * (size_t)d * (size_t)dv * 4 : 0;
+}
+
+float* kept_states(const void* base, const Workspace& w) {
+  return reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(base)) + align_up(w.bytes));
+}
+
 // Streaming state (caller-owned device memory, 256-byte aligned arrays):
 // the fp32 memory state M'^T in the scan's register layout, the running
 // denominator (M, L) per feature, and the carried chunk of Z' and V.
@@ -134,6 +142,9 @@ struct Call {
   float* stats;
   // gecko_sca_awm_forward_noalloc: the workspace is the library's scratch array
   bool noalloc;
+  // gecko_forward_train with mem_saved: ws is mem_saved, which also receives
+  // the states in float32 and the denominator steps the backward reads
+  bool keep;
 };
 
 // memory steps and snapshot slots of a call (see gecko::Problem); lag 2 with
@@ -237,23 +248,25 @@ gecko_status validate(const Call& k, gecko::Problem& p, bool& bf16) {
                   w.bytes, gecko::noalloc_scratch_bytes());
   } else if (need_awm && nmem > 0) {
     const gecko::Workspace w = gecko::carve_workspace(nullptr, BH, k.n, k.d, k.dv, nmem, nsnap, bf16, k.streaming);
-    if (!k.ws) return fail(GECKO_EWORKSPACE, "workspace is null (need %zu bytes)", w.bytes);
-    if (k.ws_bytes < w.bytes) return fail(GECKO_EWORKSPACE, "workspace too small: %zu < %zu bytes", k.ws_bytes, w.bytes);
-    if (reinterpret_cast<uintptr_t>(k.ws) & (kAlign - 1)) return fail(GECKO_EINVAL, "workspace must be 256-byte aligned");
-    if (overlaps(k.out, ob, k.ws, w.bytes)) return fail(GECKO_EINVAL, "out aliases the workspace");
+    const size_t need = k.keep ? gecko::kept_memory_bytes(w, BH, nmem, k.d, k.dv) : w.bytes;
+    const char* what = k.keep ? "mem_saved" : "workspace";
+    if (!k.ws) return fail(GECKO_EWORKSPACE, "%s is null (need %zu bytes)", what, need);
+    if (k.ws_bytes < need) return fail(GECKO_EWORKSPACE, "%s too small: %zu < %zu bytes", what, k.ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(k.ws) & (kAlign - 1)) return fail(GECKO_EINVAL, "%s must be 256-byte aligned", what);
+    if (overlaps(k.out, ob, k.ws, need)) return fail(GECKO_EINVAL, "out aliases the %s", what);
     // the chunk pass and the scan write the workspace before the attention
     // kernel reads z, v and the affine vectors
-    if (overlaps(k.ws, w.bytes, k.z, zb) || overlaps(k.ws, w.bytes, k.v, vb))
-      return fail(GECKO_EINVAL, "the workspace aliases z or v");
+    if (overlaps(k.ws, need, k.z, zb) || overlaps(k.ws, need, k.v, vb))
+      return fail(GECKO_EINVAL, "the %s aliases z or v", what);
     for (int i = 0; i < 8; ++i)
-      if (k.aff[i] && overlaps(k.ws, w.bytes, k.aff[i], (size_t)k.H * k.d * 4))
-        return fail(GECKO_EINVAL, "the workspace aliases affine vector %d", i);
-    if (k.lse && overlaps(k.ws, w.bytes, k.lse, (size_t)BH * k.n * 4))
-      return fail(GECKO_EINVAL, "the workspace aliases the log-sum-exp output");
-    if (k.o_sca && overlaps(k.ws, w.bytes, k.o_sca, (size_t)BH * k.n * k.dv * 4))
-      return fail(GECKO_EINVAL, "the workspace aliases the attention output");
-    if (k.stats && overlaps(k.ws, w.bytes, k.stats, (size_t)BH * k.n * 8))
-      return fail(GECKO_EINVAL, "the workspace aliases the attention statistics");
+      if (k.aff[i] && overlaps(k.ws, need, k.aff[i], (size_t)k.H * k.d * 4))
+        return fail(GECKO_EINVAL, "the %s aliases affine vector %d", what, i);
+    if (k.lse && overlaps(k.ws, need, k.lse, (size_t)BH * k.n * 4))
+      return fail(GECKO_EINVAL, "the %s aliases the log-sum-exp output", what);
+    if (k.o_sca && overlaps(k.ws, need, k.o_sca, (size_t)BH * k.n * k.dv * 4))
+      return fail(GECKO_EINVAL, "the %s aliases the attention output", what);
+    if (k.stats && overlaps(k.ws, need, k.stats, (size_t)BH * k.n * 8))
+      return fail(GECKO_EINVAL, "the %s aliases the attention statistics", what);
   }
   p.z = k.z; p.v = k.v; p.out = k.out;
   p.kappa_q = k.aff[0]; p.nu_q = k.aff[1]; p.kappa_k = k.aff[2]; p.nu_k = k.aff[3];
@@ -310,6 +323,7 @@ gecko_status run(const Call& k) {
   }
   gecko::Workspace w{};
   if (do_awm) w = gecko::carve_workspace(ws, p.B * p.H, p.n, p.d, p.dv, p.nmem, p.nsnap, bf16, p.stream);
+  if (do_awm && k.keep) w.snap32 = gecko::kept_states(ws, w);
 
   hipEvent_t* ev = nullptr;
   if (k.timer && k.timer->used < k.timer->capacity) ev = &k.timer->ev[5 * k.timer->used++];
@@ -321,7 +335,7 @@ gecko_status run(const Call& k) {
     e = bf16 ? gecko::launch_awm_chunk_bf16(p, w, s) : gecko::launch_awm_chunk_f32(p, w, s);
     if (e != hipSuccess) return hip_fail(e, "memory chunk pass launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if (!bf16) {  // the bf16 scan keeps the running denominator itself
+    if (!bf16 || k.keep) {  // the bf16 scan keeps the running denominator itself
       e = gecko::launch_awm_zscan(p, w, s);
       if (e != hipSuccess) return hip_fail(e, "denominator prefix launch");
     }
@@ -371,6 +385,16 @@ size_t gecko_workspace_size_for(int64_t B, int64_t H, int64_t n, int64_t d, int6
   int64_t nmem = 0, nsnap = 0;
   mem_counts(nchunks_of(n, c), false, false, lag_of(flags), nmem, nsnap);
   return gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, in_dtype == GECKO_BF16, false).bytes;
+}
+
+size_t gecko_memory_saved_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                               gecko_dtype in_dtype, unsigned flags) {
+  if (B < 1 || H < 1 || n < 1 || c < 1 || in_dtype != GECKO_BF16 || !gecko::bwd_shape_built(d, dv)) return (size_t)-1;
+  if (flags & ~(unsigned)(GECKO_AWM_NO_DELTA | GECKO_CHUNKWISE)) return (size_t)-1;
+  int64_t nmem = 0, nsnap = 0;
+  mem_counts(nchunks_of(n, c), false, false, lag_of(flags), nmem, nsnap);
+  const gecko::Workspace w = gecko::carve_workspace(nullptr, B * H, n, d, dv, nmem, nsnap, true, false);
+  return gecko::kept_memory_bytes(w, B * H, nmem, d, dv);
 }
 
 gecko_status gecko_sca_awm_forward_timed(const void* z, const float* kappa_q, const float* nu_q,
@@ -603,10 +627,10 @@ gecko_status gecko_forward_lse(const void* z, const float* kappa_q, const float*
 
 gecko_status gecko_forward_train(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
                                  const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
-                                 const float* rho_k, const void* v, void* out, float* o_sca, float* stats, int64_t B,
-                                 int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
-                                 gecko_dtype out_dtype, unsigned flags, unsigned parts, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 const float* rho_k, const void* v, void* out, float* o_sca, float* stats,
+                                 void* mem_saved, size_t mem_saved_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
+                                 int64_t dv, int64_t c, gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
+                                 unsigned parts, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (!(parts & GECKO_PART_SCA) || (parts & ~3u))
       return fail(GECKO_EINVAL, "parts must hold GECKO_PART_SCA (and may hold GECKO_PART_AWM)");
@@ -616,6 +640,12 @@ gecko_status gecko_forward_train(const void* z, const float* kappa_q, const floa
     if (!o_sca || !stats) return fail(GECKO_EINVAL, "o_sca and stats must be non-null");
     if (!aligned16(o_sca) || (reinterpret_cast<uintptr_t>(stats) & 7u))
       return fail(GECKO_EINVAL, "o_sca must be 16-byte and stats 8-byte aligned");
+    // with mem_saved, the memory pass writes there (and the workspace goes unused)
+    const bool keep = mem_saved && (parts & GECKO_PART_AWM);
+    if (keep) {
+      workspace = mem_saved;
+      workspace_bytes = mem_saved_bytes;
+    }
     if (B >= 1 && H >= 1 && n >= 1 && out && B <= (1 << 20) && H <= (1 << 20) && n <= (int64_t(1) << 40)) {
       const size_t BH = (size_t)B * H;
       const size_t sb = BH * n * 8, ab = BH * n * dv * 4;
@@ -625,7 +655,8 @@ gecko_status gecko_forward_train(const void* z, const float* kappa_q, const floa
       if (overlaps(o_sca, ab, stats, sb) || overlaps(o_sca, ab, out, ob) || overlaps(stats, sb, out, ob) ||
           (workspace && (overlaps(o_sca, ab, workspace, workspace_bytes) ||
                          overlaps(stats, sb, workspace, workspace_bytes))))
-        return fail(GECKO_EINVAL, "o_sca and stats must not alias each other, the output or the workspace");
+        return fail(GECKO_EINVAL, "o_sca and stats must not alias each other, the output or the %s",
+                    keep ? "mem_saved" : "workspace");
       for (int i = 0; i < 2; ++i)
         if (in[i] && (overlaps(o_sca, ab, in[i], ib[i]) || overlaps(stats, sb, in[i], ib[i])))
           return fail(GECKO_EINVAL, "o_sca and stats must not alias an input");
@@ -635,6 +666,7 @@ gecko_status gecko_forward_train(const void* z, const float* kappa_q, const floa
            in_dtype, out_dtype, flags, workspace, workspace_bytes, stream, mode, nullptr};
     k.o_sca = o_sca;
     k.stats = stats;
+    k.keep = keep;
     return run(k);
   } catch (...) {
     return fail(GECKO_EHIP, "internal error");
@@ -709,7 +741,7 @@ gecko_status bwd_problem(const void* z, const float* const (&aff)[8], const void
   f.stream = false; f.has_prev = false;
   p.dout = dout; p.dz = dz; p.dv = dv_out; p.daff = daff;
   p.sca = sca; p.awm = awm; p.out_f32 = out_dtype == GECKO_F32;
-  p.saved = false; p.o_sca = nullptr; p.stats = nullptr;
+  p.saved = false; p.o_sca = nullptr; p.stats = nullptr; p.mem_saved = nullptr;
   return GECKO_OK;
 }
 
@@ -724,9 +756,11 @@ BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p) {
   const size_t nm = (size_t)f.nmem;
   size_t off = 0;
   const bool mem = p.awm && f.nmem > 0;
+  const bool kept = mem && p.mem_saved;  // the training forward's memory pass, read in place
   if (mem) {
-    w.fw = carve_workspace(base, f.B * f.H, f.n, f.d, f.dv, f.nmem, f.nsnap, true, false);
-    off = align_up(w.fw.bytes);
+    w.fw = carve_workspace(kept ? const_cast<void*>(p.mem_saved) : base, f.B * f.H, f.n, f.d, f.dv, f.nmem, f.nsnap,
+                           true, false);
+    if (!kept) off = align_up(w.fw.bytes);
   }
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -752,7 +786,7 @@ BwdWorkspace carve_bwd_workspace(void* base, const BwdProblem& p) {
     w.part = reinterpret_cast<float*>(take(BH * nm * (dv / 32) * d * 2 * 4));
     w.zeta = reinterpret_cast<float*>(take(BH * nm * d * 4));
     w.x = reinterpret_cast<uint16_t*>(take(BH * nm * d * d * 2));
-    w.s32 = reinterpret_cast<float*>(take(BH * nm * d * dv * 4));
+    w.s32 = kept ? kept_states(p.mem_saved, w.fw) : reinterpret_cast<float*>(take(BH * nm * d * dv * 4));
     w.fw.snap32 = w.s32;
   }
   w.rows_per_blk = 256;
@@ -821,6 +855,14 @@ gecko_status run_backward(const gecko::BwdProblem& p, void* workspace, size_t wo
         for (int j = 3; j < 6; ++j)
           if (o[j] && overlaps(o[i], b[i], o[j], b[j]))
             return fail(GECKO_EINVAL, "o_sca and stats must not alias an output");
+    if (p.mem_saved) {
+      const gecko::Workspace mw = gecko::carve_workspace(nullptr, f.B * f.H, f.n, f.d, f.dv, f.nmem, f.nsnap, true, false);
+      const size_t mb = gecko::kept_memory_bytes(mw, f.B * f.H, f.nmem, f.d, f.dv);
+      if (overlaps(p.mem_saved, mb, workspace, need.bytes))
+        return fail(GECKO_EINVAL, "mem_saved aliases the workspace");
+      for (int j = 3; j < 6; ++j)
+        if (o[j] && overlaps(p.mem_saved, mb, o[j], b[j])) return fail(GECKO_EINVAL, "mem_saved aliases an output");
+    }
   }
   const gecko::BwdWorkspace w = gecko::carve_bwd_workspace(workspace, p);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -864,7 +906,8 @@ gecko_status gecko_backward(const void* z, const float* kappa_q, const float* nu
 gecko_status gecko_backward_saved(const void* z, const float* kappa_q, const float* nu_q, const float* kappa_k,
                                   const float* nu_k, const float* eta_q, const float* rho_q, const float* eta_k,
                                   const float* rho_k, const void* v, const void* dout, const float* o_sca,
-                                  const float* stats, float* dz, float* dv_out, float* daff, int64_t B, int64_t H,
+                                  const float* stats, const void* mem_saved, size_t mem_saved_bytes, float* dz,
+                                  float* dv_out, float* daff, int64_t B, int64_t H,
                                   int64_t n, int64_t d, int64_t dv, int64_t c, gecko_dtype in_dtype,
                                   gecko_dtype out_dtype, unsigned flags, unsigned parts, void* workspace,
                                   size_t workspace_bytes, void* stream) {
@@ -881,6 +924,16 @@ gecko_status gecko_backward_saved(const void* z, const float* kappa_q, const flo
     p.saved = true;
     p.o_sca = o_sca;
     p.stats = stats;
+    if (mem_saved && p.awm && p.f.nmem > 0) {
+      const gecko::Problem& f = p.f;
+      const gecko::Workspace mw = gecko::carve_workspace(nullptr, f.B * f.H, f.n, f.d, f.dv, f.nmem, f.nsnap, true, false);
+      const size_t mb = gecko::kept_memory_bytes(mw, f.B * f.H, f.nmem, f.d, f.dv);
+      if (mem_saved_bytes < mb)
+        return fail(GECKO_EWORKSPACE, "mem_saved too small: %zu < %zu bytes", mem_saved_bytes, mb);
+      if (reinterpret_cast<uintptr_t>(mem_saved) & (kAlign - 1))
+        return fail(GECKO_EINVAL, "mem_saved must be 256-byte aligned");
+      p.mem_saved = mem_saved;
+    }
     return run_backward(p, workspace, workspace_bytes, stream);
   } catch (...) {
     return fail(GECKO_EHIP, "internal error");
@@ -949,6 +1002,6 @@ const char* gecko_status_string(gecko_status status) {
 
 const char* gecko_last_error(void) { return g_last_error.c_str(); }
 
-int gecko_version(void) { return 103; }
+int gecko_version(void) { return 104; }
 
 }  // extern "C"

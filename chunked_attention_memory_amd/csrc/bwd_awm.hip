@@ -29,7 +29,8 @@
 // where rowsum(dPsi_Q * psi(Q)) is dO . O_m.
 //
 // The memory chunk pass and scan of the forward are run again first (their
-// snapshots S_t are the chunk-boundary states the backward needs); then:
+// snapshots S_t are the chunk-boundary states the backward needs), unless a
+// training forward kept them; then:
 //  rpass   R_t^T per chunk (like the forward's E^T V product, psi(Q) for E)
 //  htrans  H_t (Phi_t^T Psi_t up to the per-feature factor) in the order the
 //          reverse scan reads it
@@ -691,10 +692,13 @@ hipError_t launch_all(const BwdProblem& p, const BwdWorkspace& w, hipStream_t s)
   const uint16_t* dO = dout16(p, w);
   hipError_t e;
   if (f.nmem > 0) {
-    // the forward memory pass, denominator prefix and scan (snapshots S_t)
-    if ((e = launch_awm_chunk_bf16(f, w.fw, s)) != hipSuccess) return e;
-    if ((e = launch_awm_zscan(f, w.fw, s)) != hipSuccess) return e;
-    if ((e = launch_awm_scan_bf16(f, w.fw, s)) != hipSuccess) return e;
+    // the forward memory pass, denominator prefix and scan (snapshots S_t),
+    // unless the training forward kept them
+    if (!p.mem_saved) {
+      if ((e = launch_awm_chunk_bf16(f, w.fw, s)) != hipSuccess) return e;
+      if ((e = launch_awm_zscan(f, w.fw, s)) != hipSuccess) return e;
+      if ((e = launch_awm_scan_bf16(f, w.fw, s)) != hipSuccess) return e;
+    }
     RArgs ra;
     ra.z = static_cast<const uint16_t*>(f.z);
     ra.dO = dO;

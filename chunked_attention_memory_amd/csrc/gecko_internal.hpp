@@ -66,6 +66,13 @@ struct Workspace {
 Workspace carve_workspace(void* base, int64_t BH, int64_t n, int64_t d, int64_t dv,
                           int64_t nmem, int64_t nsnap, bool bf16, bool stream);
 
+// The memory pass a training forward keeps for its backward: the bf16
+// Workspace w of a one-call forward, then every state S_t again in float32
+// [bh][t][d][dv] (what the backward's reverse scan and readout reads),
+// 256-byte aligned. 0 bytes when no chunk reads the memory.
+size_t kept_memory_bytes(const Workspace& w, int64_t BH, int64_t nmem, int64_t d, int64_t dv);
+float* kept_states(const void* base, const Workspace& w);
+
 // The library's own scratch array (noalloc.hip): its size, and the device
 // address of `device`'s copy (looked up once per device, with that device
 // current; never the array's host-side name).
@@ -112,6 +119,9 @@ struct BwdProblem {
   bool saved;
   const float* o_sca;   // [BH][n][dv] float32 attention output
   const float* stats;   // [BH][n][2] offset m and sum l of the bf16 weights 2^(s - m)
+  // the training forward's memory pass and scan (kept_memory_bytes, laid out
+  // as a Workspace followed by the states in float32), else null: recomputed
+  const void* mem_saved;
 };
 
 // Backward workspace. Arrays indexed [bh][t] have t = 0..nmem-1, the chunk

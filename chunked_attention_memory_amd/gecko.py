@@ -29,7 +29,7 @@ EXPORTED = (
     "gecko_workspace_size_for", "gecko_cema_workspace_size", "gecko_cema_forward",
     "gecko_tdn_workspace_size", "gecko_tdn_forward",
     "gecko_forward_lse", "gecko_backward_workspace_size", "gecko_backward",
-    "gecko_forward_train", "gecko_backward_saved_workspace_size", "gecko_backward_saved",
+    "gecko_forward_train", "gecko_memory_saved_size", "gecko_backward_saved_workspace_size", "gecko_backward_saved",
     "gecko_sca_awm_forward_noalloc",
 )
 
@@ -106,11 +106,13 @@ def _load() -> ctypes.CDLL:
     lib.gecko_backward.restype = I
     lib.gecko_backward.argtypes = [P] + [F] * 8 + [P, P, P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
     lib.gecko_forward_train.restype = I
-    lib.gecko_forward_train.argtypes = [P] + [F] * 8 + [P, P, P, P] + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_forward_train.argtypes = [P] + [F] * 8 + [P, P, P, P, P, SZ] + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_memory_saved_size.restype = SZ
+    lib.gecko_memory_saved_size.argtypes = [I64] * 6 + [I, U]
     lib.gecko_backward_saved_workspace_size.restype = SZ
     lib.gecko_backward_saved_workspace_size.argtypes = [I64] * 6 + [I, I, U, U]
     lib.gecko_backward_saved.restype = I
-    lib.gecko_backward_saved.argtypes = [P] + [F] * 8 + [P] * 7 + [I64] * 6 + [I, I, U, U, P, SZ, P]
+    lib.gecko_backward_saved.argtypes = [P] + [F] * 8 + [P] * 5 + [SZ] + [P] * 3 + [I64] * 6 + [I, I, U, U, P, SZ, P]
     return lib
 
 
@@ -483,9 +485,11 @@ def gecko_forward_lse(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, ou
 
 
 def gecko_forward_train(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, out=None, o_sca=None, stats=None,
-                        out_dtype=None, flags=0, workspace=None, stream=None):
+                        out_dtype=None, flags=0, workspace=None, keep_memory=False, mem_saved=None, stream=None):
     """O of the selected parts, the attention output alone (``o_sca`` [B, H, n, dv] float32) and the per-query
-    offset and bf16-weight sum (``stats`` [B, H, n, 2] float32) that gecko_backward_saved reuses."""
+    offset and bf16-weight sum (``stats`` [B, H, n, 2] float32) that gecko_backward_saved reuses. With
+    ``keep_memory`` (or a ``mem_saved`` uint8 tensor of gecko_memory_saved_size bytes) the memory pass is
+    written to that buffer, returned fourth, for gecko_backward_saved to read instead of recomputing it."""
     import torch
 
     B, H, n, d, dv = _shape(z, v)
@@ -495,13 +499,27 @@ def gecko_forward_train(z, params, v, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, 
         o_sca = _empty((B, H, n, dv), torch.float32, z.device, stream)
     if stats is None:
         stats = _empty((B, H, n, 2), torch.float32, z.device, stream)
-    if workspace is None and parts & GECKO_PART_AWM:
+    keep = keep_memory or mem_saved is not None
+    if mem_saved is not None and (mem_saved.dtype != torch.uint8 or not mem_saved.is_contiguous()):
+        raise GeckoError(GECKO_EINVAL, "mem_saved must be a contiguous uint8 tensor")
+    if keep and mem_saved is None:
+        nbytes = gecko_memory_saved_size(B, H, n, d, dv, c, _dtype_code(z), flags)
+        mem_saved = _empty(max(nbytes, 256), torch.uint8, z.device, stream)
+    if workspace is None and parts & GECKO_PART_AWM and not keep:
         workspace = alloc_workspace(z, v, c, flags, stream)
     _check(lib.gecko_forward_train(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(out),
-                                   _ptr(o_sca), _ptr(stats), B, H, n, d, dv, c, _dtype_code(z), _dtype_code(out),
-                                   flags, parts, _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                                   _stream(stream)))
-    return out, o_sca, stats
+                                   _ptr(o_sca), _ptr(stats), _ptr(mem_saved),
+                                   0 if mem_saved is None else mem_saved.numel(), B, H, n, d, dv, c, _dtype_code(z),
+                                   _dtype_code(out), flags, parts, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream(stream)))
+    return (out, o_sca, stats, mem_saved) if keep else (out, o_sca, stats)
+
+
+def gecko_memory_saved_size(B, H, n, d, dv, c, in_code=None, flags=0) -> int:
+    r = lib.gecko_memory_saved_size(B, H, n, d, dv, c, GECKO_BF16 if in_code is None else in_code, flags)
+    if r == ctypes.c_size_t(-1).value:
+        raise GeckoError(GECKO_EINVAL, "invalid or unsupported arguments for gecko_memory_saved_size")
+    return r
 
 
 def gecko_backward_workspace_size(B, H, n, d, dv, c, in_code, out_code, flags=0,
@@ -548,8 +566,9 @@ def gecko_backward_saved_workspace_size(B, H, n, d, dv, c, in_code, out_code, fl
 
 
 def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_SCA | GECKO_PART_AWM, flags=0,
-                         dz=None, dv=None, daff=None, workspace=None, stream=None):
-    """gecko_backward with the attention statistics of gecko_forward_train (same inputs, c, parts and flags)."""
+                         dz=None, dv=None, daff=None, workspace=None, mem_saved=None, stream=None):
+    """gecko_backward with the attention statistics of gecko_forward_train (same inputs, c, parts and flags),
+    and its memory pass when ``mem_saved`` (that forward's kept buffer) is given."""
     import torch
 
     B, H, n, d, dvs = _shape(z, v)
@@ -558,6 +577,8 @@ def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_S
     if (tuple(o_sca.shape) != (B, H, n, dvs) or o_sca.dtype != torch.float32 or not o_sca.is_contiguous()
             or tuple(stats.shape) != (B, H, n, 2) or stats.dtype != torch.float32 or not stats.is_contiguous()):
         raise GeckoError(GECKO_EINVAL, "o_sca must be float32 [B, H, n, dv] and stats float32 [B, H, n, 2]")
+    if mem_saved is not None and (mem_saved.dtype != torch.uint8 or not mem_saved.is_contiguous()):
+        raise GeckoError(GECKO_EINVAL, "mem_saved must be a contiguous uint8 tensor")
     if dz is None:
         dz = _empty((B, H, n, d), torch.float32, z.device, stream)
     if dv is None:
@@ -569,7 +590,9 @@ def gecko_backward_saved(z, params, v, dout, o_sca, stats, c, parts=GECKO_PART_S
                                                      parts)
         workspace = _empty(max(nbytes, 256), torch.uint8, z.device, stream)
     _check(lib.gecko_backward_saved(_ptr(z), *_part_params(params, parts, z.device, H, d), _ptr(v), _ptr(dout),
-                                    _ptr(o_sca), _ptr(stats), _ptr(dz), _ptr(dv), _ptr(daff), B, H, n, d, dvs, c,
+                                    _ptr(o_sca), _ptr(stats), _ptr(mem_saved),
+                                    0 if mem_saved is None else mem_saved.numel(), _ptr(dz), _ptr(dv), _ptr(daff),
+                                    B, H, n, d, dvs, c,
                                     _dtype_code(z), _dtype_code(dout), flags, parts, _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
     res = {"dz": dz, "dv": dv}

@@ -336,11 +336,11 @@ gecko_status gecko_backward(
 
 /* Training forward: out exactly as gecko_forward_lse / gecko_sca_awm_forward
  * with the same arguments, plus what gecko_backward_saved reuses in place of
- * its statistics pass over the attention window (the quantities are those of
- * the attention step, paper.rainbus.top, "Method steps" (3); the pages'
- * training recomputes the memory from chunk-boundary states, paperlayer.ai
- * summary, Appendix B.1, which gecko_backward_saved still does; keeping the
- * attention's per-query statistics instead is this library's choice):
+ * recomputing (the quantities are those of the attention step,
+ * paper.rainbus.top, "Method steps" (3), and the memory's chunk-boundary
+ * states, paperlayer.ai summary, Appendix B.1, "Method steps" (4)-(5); the
+ * pages' training recomputes the memory from such states; keeping the
+ * attention's per-query statistics as well is this library's choice):
  *   o_sca: [B][H][n][dv] float32, 16-byte aligned, caller-owned, fully
  *       overwritten: the attention output O_SCA alone.
  *   stats: [B][H][n][2] float32, 8-byte aligned, fully overwritten: per query
@@ -348,21 +348,40 @@ gecko_status gecko_backward(
  *       as the attention's value product used them; s is the query's logit
  *       less q . nu_k, times log2(e) (a shift shared by the query's keys).
  *       O_SCA = (sum_j bf16(2^(s_j - m)) v_j) / l.
+ *   mem_saved: null, or (with GECKO_PART_AWM) a 256-byte aligned device
+ *       buffer of mem_saved_bytes >= gecko_memory_saved_size bytes,
+ *       caller-owned: the memory pass writes its results there (every
+ *       chunk's write and correction products, denominator steps and the
+ *       states S_t in bf16 and float32), and the call then uses no
+ *       workspace (workspace may be null). Ignored without GECKO_PART_AWM or
+ *       when no chunk reads the memory (n <= 2c, or n <= c chunk-wise).
  * bf16 inputs, (d, dv) in {(128, 256), (128, 128)}; parts must include
  * GECKO_PART_SCA. o_sca and stats must not alias each other, an input, the
- * output or the workspace (GECKO_EINVAL). Workspace as gecko_workspace_size. */
+ * output, mem_saved or the workspace, nor mem_saved an input or the output
+ * (GECKO_EINVAL); mem_saved too small: GECKO_EWORKSPACE. Without mem_saved,
+ * workspace as gecko_workspace_size. */
 gecko_status gecko_forward_train(
     const void* z,
     const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
     const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
     const void* v, void* out, float* o_sca, float* stats,
+    void* mem_saved, size_t mem_saved_bytes,
     int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the memory pass gecko_forward_train keeps in mem_saved for these
+ * sizes and flags (0 when no chunk reads the memory; (size_t)-1 if the
+ * arguments are invalid or not built: bf16 inputs and (d, dv) in
+ * {(128, 256), (128, 128)} only). */
+size_t gecko_memory_saved_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
+                               gecko_dtype in_dtype, unsigned flags);
+
 /* Bytes of device workspace gecko_backward_saved needs: gecko_backward's
  * plus the per-query scaled copy of dO ((size_t)-1 if the arguments are
- * invalid, not built, or parts lacks GECKO_PART_SCA). */
+ * invalid, not built, or parts lacks GECKO_PART_SCA). With mem_saved the
+ * call needs less (the recomputed memory pass and its float32 states are not
+ * taken from the workspace); this size is enough either way. */
 size_t gecko_backward_saved_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
                                            gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags,
                                            unsigned parts);
@@ -371,13 +390,19 @@ size_t gecko_backward_saved_workspace_size(int64_t B, int64_t H, int64_t n, int6
  * same inputs, c, parts and flags (o_sca, stats as written there; read only,
  * not aliasing an output or the workspace): the same gradients, with the
  * attention weights taken as the forward's own bf16-rounded ones, and no
- * statistics pass over the key window. parts must include GECKO_PART_SCA;
- * other arguments and errors as gecko_backward. */
+ * statistics pass over the key window. mem_saved: null (the memory pass and
+ * scan are run again), or the buffer that forward filled (read only,
+ * mem_saved_bytes >= gecko_memory_saved_size, 256-byte aligned, not aliasing
+ * an output or the workspace): the backward reads the memory pass there,
+ * with bit-identical results. Ignored without GECKO_PART_AWM or when no
+ * chunk reads the memory. parts must include GECKO_PART_SCA; other
+ * arguments and errors as gecko_backward. */
 gecko_status gecko_backward_saved(
     const void* z,
     const float* kappa_q, const float* nu_q, const float* kappa_k, const float* nu_k,
     const float* eta_q, const float* rho_q, const float* eta_k, const float* rho_k,
     const void* v, const void* dout, const float* o_sca, const float* stats,
+    const void* mem_saved, size_t mem_saved_bytes,
     float* dz, float* dv_out, float* daff,
     int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int64_t c,
     gecko_dtype in_dtype, gecko_dtype out_dtype, unsigned flags, unsigned parts,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gecko_version() == 103
+    assert g.gecko_version() == 104
     for s in range(5):
         assert g.gecko_status_string(s).startswith("GECKO_")
     assert "unknown" in g.gecko_status_string(99)
@@ -359,14 +359,33 @@ def test_forward_lse_host_checks(g):
     st, msg = call()  # the memory part needs the workspace
     assert st == g.GECKO_EWORKSPACE
 
+def test_memory_saved_size(g):
+    # no chunk reads the memory at n <= 2c (sliding) or n <= c (chunk-wise)
+    assert g.gecko_memory_saved_size(1, 2, 256, 128, 256, 128) == 0
+    assert g.gecko_memory_saved_size(1, 2, 128, 128, 256, 128, flags=g.GECKO_CHUNKWISE) == 0
+    one = g.gecko_memory_saved_size(1, 2, 257, 128, 256, 128)  # one memory step
+    assert one > 0
+    # at least the float32 states, the bf16 snapshots and the float32 write products
+    BH, d, dv = 2, 128, 256
+    assert one >= BH * d * dv * (4 + 2 + 4)
+    two = g.gecko_memory_saved_size(1, 2, 385, 128, 256, 128)
+    assert two > one
+    assert g.gecko_memory_saved_size(2, 1, 385, 128, 256, 128) == two  # only B * H matters
+    assert g.gecko_memory_saved_size(1, 2, 385, 128, 128, 128) < two
+    for bad in (dict(in_code=g.GECKO_F32), dict(flags=1 << 7)):
+        with pytest.raises(g.GeckoError):
+            g.gecko_memory_saved_size(1, 2, 385, 128, 256, 128, **bad)
+    with pytest.raises(g.GeckoError):
+        g.gecko_memory_saved_size(1, 2, 385, 64, 64, 128)  # no backward built for this pair
+
 
 def test_forward_train_host_checks(g):
     def call(**kw):
-        a = dict(parts=3, o=4 * FAKE, stats=5 * FAKE, din=g.GECKO_BF16, d=128, dvs=256, ws=0, wsb=0)
+        a = dict(parts=3, o=4 * FAKE, stats=5 * FAKE, din=g.GECKO_BF16, d=128, dvs=256, ws=0, wsb=0, mem=0, memb=0)
         a.update(kw)
         st = g.lib.gecko_forward_train(FAKE, *[FAKE + 64 * i for i in range(8)], 2 * FAKE, 3 * FAKE, a["o"],
-                                       a["stats"], 1, 1, 1000, a["d"], a["dvs"], 100, a["din"], g.GECKO_BF16, 0,
-                                       a["parts"], a["ws"], a["wsb"], None)
+                                       a["stats"], a["mem"], a["memb"], 1, 1, 1000, a["d"], a["dvs"], 100, a["din"],
+                                       g.GECKO_BF16, 0, a["parts"], a["ws"], a["wsb"], None)
         return st, g.lib.gecko_last_error().decode()
 
     st, msg = call(parts=g.GECKO_PART_AWM)
@@ -385,15 +404,68 @@ def test_forward_train_host_checks(g):
     assert st == g.GECKO_EINVAL and "alias" in msg
     st, msg = call()  # the memory part needs the workspace
     assert st == g.GECKO_EWORKSPACE
+    # mem_saved in place of the workspace: size, alignment, aliasing
+    need = g.gecko_memory_saved_size(1, 1, 1000, 128, 256, 100)
+    st, msg = call(mem=6 * FAKE, memb=need - 1)
+    assert st == g.GECKO_EWORKSPACE and "mem_saved too small" in msg
+    st, msg = call(mem=6 * FAKE + 16, memb=need)
+    assert st == g.GECKO_EINVAL and "mem_saved must be 256-byte aligned" in msg
+    far = dict(o=64 * FAKE, stats=80 * FAKE, memb=need)
+    st, msg = call(mem=3 * FAKE - 256, **far)  # runs into out
+    assert st == g.GECKO_EINVAL and "out aliases the mem_saved" in msg
+    st, msg = call(mem=80 * FAKE - 256, **far)  # runs into stats
+    assert st == g.GECKO_EINVAL and "alias" in msg and "mem_saved" in msg
+    st, msg = call(mem=FAKE, **far)  # on top of z
+    assert st == g.GECKO_EINVAL and "alias" in msg and "mem_saved" in msg
+    # without the memory part, mem_saved is not used
+    st, msg = call(parts=g.GECKO_PART_SCA, mem=6 * FAKE + 16, memb=1)
+    assert st != g.GECKO_EINVAL or "mem_saved" not in msg
+
+    # mem_saved in place of the workspace: size, alignment, aliasing
+    need = g.gecko_memory_saved_size(1, 1, 1000, 128, 256, 100)
+    st, msg = call(mem=6 * FAKE, memb=need - 1)
+    assert st == g.GECKO_EWORKSPACE and "mem_saved too small" in msg
+    st, msg = call(mem=6 * FAKE + 16, memb=need)
+    assert st == g.GECKO_EINVAL and "mem_saved must be 256-byte aligned" in msg
+    far = dict(o=64 * FAKE, stats=80 * FAKE, memb=need)
+    st, msg = call(mem=3 * FAKE - 256, **far)  # runs into out
+    assert st == g.GECKO_EINVAL and "out aliases the mem_saved" in msg
+    st, msg = call(mem=80 * FAKE - 256, **far)  # runs into stats
+    assert st == g.GECKO_EINVAL and "alias" in msg and "mem_saved" in msg
+    st, msg = call(mem=FAKE, **far)  # on top of z
+    assert st == g.GECKO_EINVAL and "alias" in msg and "mem_saved" in msg
+    # without the memory part, mem_saved is not used
+    st, msg = call(parts=g.GECKO_PART_SCA, mem=6 * FAKE + 16, memb=1)
+    assert st != g.GECKO_EINVAL or "mem_saved" not in msg
+
+
+def test_memory_saved_size(g):
+    # no chunk reads the memory at n <= 2c (sliding) or n <= c (chunk-wise)
+    assert g.gecko_memory_saved_size(1, 2, 256, 128, 256, 128) == 0
+    assert g.gecko_memory_saved_size(1, 2, 128, 128, 256, 128, flags=g.GECKO_CHUNKWISE) == 0
+    one = g.gecko_memory_saved_size(1, 2, 257, 128, 256, 128)  # one memory step
+    assert one > 0
+    # at least the float32 states, the bf16 snapshots and the float32 write products
+    BH, d, dv = 2, 128, 256
+    assert one >= BH * d * dv * (4 + 2 + 4)
+    two = g.gecko_memory_saved_size(1, 2, 385, 128, 256, 128)
+    assert two > one
+    assert g.gecko_memory_saved_size(2, 1, 385, 128, 256, 128) == two  # only B * H matters
+    assert g.gecko_memory_saved_size(1, 2, 385, 128, 128, 128) < two
+    for bad in (dict(in_code=g.GECKO_F32), dict(flags=1 << 7)):
+        with pytest.raises(g.GeckoError):
+            g.gecko_memory_saved_size(1, 2, 385, 128, 256, 128, **bad)
+    with pytest.raises(g.GeckoError):
+        g.gecko_memory_saved_size(1, 2, 385, 64, 64, 128)  # no backward built for this pair
 
 
 def call_bwd_saved(g, **kw):
     a = dict(z=FAKE, aff=[FAKE + 64 * i for i in range(8)], v=2 * FAKE, dout=5 * FAKE, o=3 * FAKE, stats=4 * FAKE,
-             dz=6 * FAKE, dv=7 * FAKE, daff=8 * FAKE, parts=3, ws=0, wsb=0)
+             dz=6 * FAKE, dv=7 * FAKE, daff=8 * FAKE, parts=3, ws=0, wsb=0, mem=0, memb=0)
     a.update(kw)
-    st = g.lib.gecko_backward_saved(a["z"], *a["aff"], a["v"], a["dout"], a["o"], a["stats"], a["dz"], a["dv"],
-                                    a["daff"], 1, 1, 1000, 128, 256, 128, g.GECKO_BF16, g.GECKO_BF16, 0, a["parts"],
-                                    a["ws"], a["wsb"], None)
+    st = g.lib.gecko_backward_saved(a["z"], *a["aff"], a["v"], a["dout"], a["o"], a["stats"], a["mem"], a["memb"],
+                                    a["dz"], a["dv"], a["daff"], 1, 1, 1000, 128, 256, 128, g.GECKO_BF16,
+                                    g.GECKO_BF16, 0, a["parts"], a["ws"], a["wsb"], None)
     return st, g.lib.gecko_last_error().decode()
 
 
@@ -414,6 +486,19 @@ def test_backward_saved_host_checks(g):
     assert st == g.GECKO_EINVAL and "alias" in msg
     st, msg = call_bwd_saved(g, stats=ws + 4096, ws=ws, wsb=1 << 40)  # stats inside the workspace
     assert st == g.GECKO_EINVAL and "alias" in msg
+    # the training forward's kept memory pass: size, alignment, aliasing
+    need = g.gecko_memory_saved_size(1, 1, 1000, 128, 256, 128)
+    st, msg = call_bwd_saved(g, mem=64 * FAKE, memb=need - 1)
+    assert st == g.GECKO_EWORKSPACE and "mem_saved too small" in msg
+    st, msg = call_bwd_saved(g, mem=64 * FAKE + 128, memb=need)
+    assert st == g.GECKO_EINVAL and "mem_saved must be 256-byte aligned" in msg
+    st, msg = call_bwd_saved(g, mem=ws, memb=need, ws=ws, wsb=1 << 40)
+    assert st == g.GECKO_EINVAL and "mem_saved aliases the workspace" in msg
+    st, msg = call_bwd_saved(g, mem=7 * FAKE - 256, memb=need, ws=ws, wsb=1 << 40)  # runs into dv
+    assert st == g.GECKO_EINVAL and "mem_saved aliases an output" in msg
+    # ignored without the memory part: the call goes on to its workspace check
+    st, msg = call_bwd_saved(g, parts=g.GECKO_PART_SCA, mem=64 * FAKE + 128, memb=1)
+    assert st == g.GECKO_EWORKSPACE and "mem_saved" not in msg
 
 
 def test_backward_saved_workspace_size(g):

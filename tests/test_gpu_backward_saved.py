@@ -32,7 +32,7 @@ def _names(g, parts):
     return (("sca",) if parts & g.GECKO_PART_SCA else ()) + (("awm",) if parts & g.GECKO_PART_AWM else ())
 
 
-def _saved_case(B, H, n, dv, c, parts, flags=0, out_dtype="bf16", sharp=1.0, tag=400, host=None):
+def _saved_case(B, H, n, dv, c, parts, flags=0, out_dtype="bf16", sharp=1.0, tag=400, host=None, keep=False):
     import torch
 
     g = gecko()
@@ -44,9 +44,13 @@ def _saved_case(B, H, n, dv, c, parts, flags=0, out_dtype="bf16", sharp=1.0, tag
     z, v, p = g.to_device_inputs(host)
     odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     do = torch.from_numpy(dout).to(device="cuda", dtype=odt)
-    announce(f"saved backward B,H,n,d,dv={tuple(z.shape)}+{dv} c={c} parts={parts} flags={flags} out={out_dtype}")
-    _, o_sca, stats = g.gecko_forward_train(z, p, v, c, parts=parts, flags=flags)
-    res = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c, parts=parts, flags=flags)
+    announce(f"saved backward B,H,n,d,dv={tuple(z.shape)}+{dv} c={c} parts={parts} flags={flags} out={out_dtype} "
+             f"keep={keep}")
+    if keep:
+        _, o_sca, stats, mem = g.gecko_forward_train(z, p, v, c, parts=parts, flags=flags, keep_memory=True)
+    else:
+        (_, o_sca, stats), mem = g.gecko_forward_train(z, p, v, c, parts=parts, flags=flags), None
+    res = g.gecko_backward_saved(z, p, v, do, o_sca, stats, c, parts=parts, flags=flags, mem_saved=mem)
     torch.cuda.synchronize()
     got = {k: to_numpy(t) for k, t in res.items()}
     names = _names(g, parts)
@@ -167,6 +171,51 @@ def test_backward_saved_agrees_with_recompute_and_repeats():
     for k in ("dz", "dv"):
         fro, mx = _errors(to_numpy(a[k]), to_numpy(r[k]))
         assert fro <= GRAD_TOL and mx <= GRAD_TOL, (k, fro, mx)
+
+
+def test_kept_memory_oracle():
+    """Backward with the training forward's kept memory pass, against the
+    oracle: both parts, 12 chunks, sliding and chunk-wise."""
+    g = gecko()
+    _saved_case(1, 2, 1500, 256, 128, g.GECKO_PART_SCA | g.GECKO_PART_AWM, tag=410, keep=True)
+    _saved_case(1, 1, 1500, 128, 128, g.GECKO_PART_SCA | g.GECKO_PART_AWM, flags=g.GECKO_CHUNKWISE, tag=411,
+                keep=True)
+
+
+@pytest.mark.parametrize("B,H,n,dv,c,flags", [
+    (1, 2, 2300, 256, 256, 0),          # 9 chunks, ragged tail
+    (2, 1, 1100, 128, 128, 1),          # without the delta correction (GECKO_AWM_NO_DELTA)
+    (1, 2, 1100, 256, 128, 2),          # chunk-wise
+    (1, 1, 256, 256, 128, 0),           # two chunks: nothing reads the memory, nothing kept
+    (1, 2, 16384, 256, 2048, 0),        # the bench's chunk size, 8 chunks
+])
+def test_kept_memory_bit_identical(B, H, n, dv, c, flags):
+    """The training forward that keeps its memory pass writes the same output,
+    O_SCA and statistics as the one that does not, and the backward that reads
+    the kept pass returns the same bits as the one that recomputes it, twice
+    in a row (the kept buffer is only read)."""
+    import torch
+
+    g = gecko()
+    parts = g.GECKO_PART_SCA | g.GECKO_PART_AWM
+    host = inputs.make_inputs(B, H, n, 128, dv, "bf16", seed=2, tag=412)
+    dout = inputs.make_dout(B, H, n, dv, "bf16", seed=2, tag=412)
+    z, v, p = g.to_device_inputs(host)
+    do = torch.from_numpy(dout).to(device="cuda", dtype=torch.bfloat16)
+    announce(f"kept memory B,H,n,dv,c,flags={(B, H, n, dv, c, flags)}")
+    out_k, o_k, st_k, mem = g.gecko_forward_train(z, p, v, c, parts=parts, flags=flags, keep_memory=True)
+    out_r, o_r, st_r = g.gecko_forward_train(z, p, v, c, parts=parts, flags=flags)
+    assert mem.numel() == max(g.gecko_memory_saved_size(B, H, n, 128, dv, c, flags=flags), 256)
+    a = g.gecko_backward_saved(z, p, v, do, o_k, st_k, c, parts=parts, flags=flags, mem_saved=mem)
+    b = g.gecko_backward_saved(z, p, v, do, o_k, st_k, c, parts=parts, flags=flags, mem_saved=mem)
+    r = g.gecko_backward_saved(z, p, v, do, o_r, st_r, c, parts=parts, flags=flags)
+    torch.cuda.synchronize()
+    for x, y, name in ((out_k, out_r, "out"), (o_k, o_r, "o_sca"), (st_k, st_r, "stats")):
+        assert torch.equal(x, y), name
+    for k in r:
+        assert torch.isfinite(a[k]).all(), k
+        assert torch.equal(a[k], r[k]), k
+        assert torch.equal(b[k], r[k]), k
 
 
 def test_backward_saved_full_size():
