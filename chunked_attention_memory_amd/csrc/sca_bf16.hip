@@ -11,10 +11,11 @@
 // so that one wave's exponentials overlap the other's matrix instructions;
 // with dv <= 128: 4 waves x 64 queries, one wave per SIMD, each K / V operand
 // read serving two MFMAs. The key window [(s-1)c, last query] is streamed in
-// tiles of 64 keys, processed as two 32-key halves; a wave skips the halves
-// that lie past all of its queries.
+// tiles of 32 keys; a wave skips the tiles that lie past all of its queries.
+// (64-key tiles processed as two halves measured 1.4% slower at 128K tokens:
+// twice the workgroup barriers, but each wave waits less at each.)
 //
-// Per 32-key half-tile and wave:
+// Per 32-key tile and wave:
 //   S^T (32 keys x 32 queries) = K Q^T            (A = K from LDS, B = Q in VGPRs)
 //   P^T = exp2(S^T - m), lane-local per query (a query's 32 keys are split
 //   between lane l and lane l ^ 32)
@@ -30,11 +31,10 @@
 // read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i
 // of a 4-row x 16-column block).
 //
-// Pipeline: three LDS stages; tile kt+2 is loaded while tile kt is computed.
-// Each stage is a separate LDS variable, which lets the compiler see that
-// reads of one stage do not alias the loads still writing another (with one
-// LDS array it waits for every load in flight before the first V read of a
-// tile). Operand reads from LDS run a few MFMAs ahead of their use, and the
+// Pipeline: three LDS stages, one LDS array (the memory state for the
+// readout goes there after the loop); tile kt+2 is loaded while tile kt is
+// computed, and the wait at the end of a tile leaves tile kt+2's loads in
+// flight. Operand reads from LDS run a few MFMAs ahead of their use, and the
 // loop is unrolled by three tiles so every LDS address is a per-lane base
 // plus a constant offset.
 //
@@ -74,7 +74,7 @@ namespace {
 #endif
 
 constexpr int kBM = 256;               // queries per workgroup
-constexpr int kBN = 64;                // keys per tile
+constexpr int kBN = 32;                // keys per tile
 constexpr float kOverflow = 0x1p63f;   // row-sum range of the offset-free pass
 constexpr float kUnderflow = 0x1p-60f;
 
@@ -93,11 +93,12 @@ struct ScaTile {
   static constexpr size_t STAGE1 = (size_t)KBYTES + (size_t)VBYTES;  // one stage: K tile, then V tile
   static constexpr size_t STAGE_BYTES = NSTAGE * STAGE1;
   static constexpr size_t SNAP_BYTES = (size_t)D * DV * 2;  // the memory state for the readout
-  // The state goes to its own LDS region at kernel start when that fits
-  // beside the stages; otherwise into the stage memory after the loop.
-  static constexpr bool SNAP_EARLY = STAGE_BYTES + SNAP_BYTES <= 160 * 1024;
+  // With the attention the state goes into the stage memory after the loop
+  // (staged at kernel start into a region of its own it measured slower);
+  // without it, into a region of its own at kernel start.
+  static_assert(STAGE_BYTES >= SNAP_BYTES, "the state fits the stage memory");
   static constexpr size_t lds_bytes(bool sca, bool read) {
-    return sca ? STAGE_BYTES + (read && SNAP_EARLY ? SNAP_BYTES : 0) : (read ? SNAP_BYTES : 0);
+    return sca ? STAGE_BYTES : (read ? SNAP_BYTES : 0);
   }
   // 1 KiB pieces of a tile, and 16-byte loads per thread per tile (at least
   // one: with fewer pieces than waves, waves share pieces; see stage_rows)
@@ -172,9 +173,8 @@ struct ScaLoop {
   const uint16_t* zpv;  // carried chunk (keys at negative rows), streaming only
   const uint16_t* vpv;
   int cl;               // chunk length
-  // stage i: K tile at sb[i], V tile at sb[i] + KBYTES. Each stage is its
-  // own LDS variable, so the compiler can tell a stage being read from the
-  // stages the tile loads are still writing (and does not wait for them).
+  // stage i: K tile at sb[i], V tile at sb[i] + KBYTES (consecutive parts
+  // of one LDS array).
   char* sb[T::NSTAGE];
   int n, kbeg, kend, ntiles, myq0, wave_q0, wave_last, w, g, lq;
   u32x4 qf[QB][KS];
@@ -414,7 +414,8 @@ struct ScaLoop {
     const bool ahead = k + 2 < ntiles;
     if (ahead) stage(k + 2, (STG + 2) % T::NSTAGE);
     if (live(k, 0)) half<STG, kSub>(k, 0, msub, lrun, oacc);
-    if (live(k, 1)) half<STG, kSub>(k, 1, msub, lrun, oacc);
+    if constexpr (kBN > 32)
+      if (live(k, 1)) half<STG, kSub>(k, 1, msub, lrun, oacc);
     if (ahead)
       wait_vmem_leave<T::LOADS>();
     else
@@ -483,7 +484,7 @@ struct ScaLoop {
         wait_vmem();
         __syncthreads();
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < kBN / 32; ++mb) {
           f32x16 sc[QB];
           qk(0, mb, sc);
 #pragma unroll
@@ -511,22 +512,22 @@ struct ScaLoop {
 // fb = (i / 2) % NFB, half hh = i % 2) from the staged state: the V^T
 // transpose reads of ScaLoop::v_addr with features in the role of keys.
 // A plain device function: a lambda in a kernel is compiled for the host too.
-// The staged state holds feature blocks [0, FB0) in region sa and the rest
-// in region sbk (32 rows of DV values per block).
-template <int D, int DV, int FB0>
-__device__ __forceinline__ u32x4 snap_operand(const char* sa, const char* sbk, const int (&va)[DV / 32], int i) {
+// The staged state at sa holds the feature blocks in order (32 rows of DV
+// values per block).
+template <int D, int DV>
+__device__ __forceinline__ u32x4 snap_operand(const char* sa, const int (&va)[DV / 32], int i) {
   constexpr int NFB = D / 32;
   const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
-  const char* base = (fb < FB0 ? sa + 32 * fb * (DV * 2) : sbk + 32 * (fb - FB0) * (DV * 2)) + va[mv];
+  const char* base = sa + 32 * fb * (DV * 2) + va[mv];
   const u32x2 l2 = lds_read_tr(base + (16 * hh) * (DV * 2));
   const u32x2 h2 = lds_read_tr(base + (16 * hh + 8) * (DV * 2));
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-// Stage the memory state [D][DV] (bf16, feature rows) into LDS with the V
-// tiles' layout and swizzle: feature blocks [0, FB0) into sa, the rest into sbk.
-template <int D, int DV, int THREADS, int FB0>
-__device__ __forceinline__ void stage_snapshot(const uint16_t* sn, char* sa, char* sbk, int w, int lane) {
+// Stage the memory state [D][DV] (bf16, feature rows) into LDS at sa with
+// the V tiles' layout and swizzle.
+template <int D, int DV, int THREADS>
+__device__ __forceinline__ void stage_snapshot(const uint16_t* sn, char* sa, int w, int lane) {
   constexpr int NW = THREADS / 64;
   constexpr int RB = 32;  // rows per staging call: one feature block
   constexpr int SPIECES = RB * DV * 2 / 1024;
@@ -542,9 +543,7 @@ __device__ __forceinline__ void stage_snapshot(const uint16_t* sn, char* sa, cha
     soff[i] = (uint32_t)(r * DV + 8 * (p ^ vswz<DV>(r))) * 2u;
   }
 #pragma unroll
-  for (int rb = 0; rb < D / RB; ++rb)
-    stage_rows(sn, rb * RB, D, DV, rb < FB0 ? sa + rb * RB * DV * 2 : sbk + (rb - FB0) * RB * DV * 2, NW, w, soff,
-               SLOADS, SMOD);
+  for (int rb = 0; rb < D / RB; ++rb) stage_rows(sn, rb * RB, D, DV, sa + rb * RB * DV * 2, NW, w, soff, SLOADS, SMOD);
 }
 
 // Byte offset, in a staged V tile (rows of DV values), of the transpose read
@@ -610,28 +609,18 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   // LDS: the three (K, V) stages, and the memory state M'_{s-1} ([d][dv],
   // feature rows) with the V tiles' layout and swizzle (the readout
   // psi(Q_m) M' is the PV product with features in the role of keys). The
-  // state is final before this kernel starts: where it fits beside the stages
-  // it is staged now, behind the attention loop; otherwise into the stage
-  // memory after the loop (feature blocks [0, FB0) in stage 0, the rest in
-  // stage 1).
+  // state is final before this kernel starts; with the attention it goes
+  // into the stage memory after the loop, without it into its own region
+  // now.
   using T = ScaTile<D, DV, QB>;
   constexpr int NFB = D / 32;
-  constexpr bool kEarly = !kSca || T::SNAP_EARLY;
-  constexpr int FB0 = kEarly ? NFB : (int)(T::STAGE1 / (32 * DV * 2)) < NFB ? (int)(T::STAGE1 / (32 * DV * 2)) : NFB;
-  static_assert(kEarly || (size_t)(NFB - FB0) * 32 * DV * 2 <= T::STAGE1, "state split over two stages");
-  __shared__ __attribute__((aligned(16))) char S0[kSca ? T::STAGE1 : 16];
-  __shared__ __attribute__((aligned(16))) char S1[kSca ? T::STAGE1 : 16];
-  __shared__ __attribute__((aligned(16))) char S2[kSca ? T::STAGE1 : 16];
+  constexpr bool kEarly = !kSca;
+  __shared__ __attribute__((aligned(16))) char SM[kSca ? T::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(16))) char SN[kRead && kEarly ? T::SNAP_BYTES : 16];
-  char* snap_a;
-  char* snap_b;
-  if constexpr (kEarly) {
-    snap_a = SN;
-    snap_b = SN;
-  } else {
-    snap_a = S0;
-    snap_b = S1;
-  }
+  char* const S0 = SM;
+  char* const S1 = SM + (kSca ? T::STAGE1 : 0);
+  char* const S2 = SM + (kSca ? 2 * T::STAGE1 : 0);
+  char* const snap_a = kEarly ? SN : SM;
   // chunk s reads the state holding the chunks before its previous one
   // (chunk-wise variant: the chunks before it): snapshot slot
   // s - lag + 2 has_prev (with a carried chunk, slot 0 is the incoming
@@ -640,7 +629,7 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   const bool reads = s >= a.first_read;
   const uint16_t* sn = a.snap + ((size_t)bh * a.nsnap + rslot) * (size_t)(D * DV);
   if constexpr (kRead && kEarly) {
-    if (reads) stage_snapshot<D, DV, T::THREADS, FB0>(sn, snap_a, snap_b, w, lane);
+    if (reads) stage_snapshot<D, DV, T::THREADS>(sn, snap_a, w, lane);
   }
 
   // attention row sums: O = oacc / lsum (+ readout)
@@ -712,7 +701,7 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
     }
   }
   if constexpr (kRead && !kEarly) {  // every wave is past the loop's last barrier
-    if (reads) stage_snapshot<D, DV, T::THREADS, FB0>(sn, snap_a, snap_b, w, lane);
+    if (reads) stage_snapshot<D, DV, T::THREADS>(sn, snap_a, w, lane);
   }
 
   if constexpr (kRead) {
@@ -774,10 +763,10 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
       constexpr int NI = NMV * NFB * 2, AH = 2;
       u32x4 op[AH + 1];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV, FB0>(snap_a, snap_b, va, i);
+      for (int i = 0; i < AH; ++i) op[i] = snap_operand<D, DV>(snap_a, va, i);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV, FB0>(snap_a, snap_b, va, i + AH);
+        if (i + AH < NI) op[(i + AH) % (AH + 1)] = snap_operand<D, DV>(snap_a, va, i + AH);
         const int mv = i / (2 * NFB), fb = (i / 2) % NFB, hh = i % 2;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[qb][mv] = mfma_bf16(op[i % (AH + 1)], pf[qb][fb][hh], oacc[qb][mv]);
