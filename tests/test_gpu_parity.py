@@ -197,11 +197,16 @@ def test_side_stream_matches_current_stream():
     do = torch.from_numpy(inputs.make_dout(1, 2, 1100, 256, "bf16", tag=41)).to(device="cuda", dtype=torch.bfloat16)
     ref = g.gecko_sca_awm_forward(z, p, v, 256)
     ref_b = g.gecko_backward(z, p, v, do, 256)
+    _, o_r, st_r, mem_r = g.gecko_forward_train(z, p, v, 256, keep_memory=True)
+    ref_s = g.gecko_backward_saved(z, p, v, do, o_r, st_r, 256, mem_saved=mem_r)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     out = g.gecko_sca_awm_forward(z, p, v, 256, stream=side)
     res = g.gecko_backward(z, p, v, do, 256, stream=side)
+    # the training pair with the kept memory pass (buffer allocated by the binding on the side stream)
+    _, o_s, st_s, mem_s = g.gecko_forward_train(z, p, v, 256, keep_memory=True, stream=side)
+    res_s = g.gecko_backward_saved(z, p, v, do, o_s, st_s, 256, mem_saved=mem_s, stream=side)
     junk = [torch.full((1 << 22,), 7.0, device="cuda") for _ in range(16)]
     side.synchronize()
     torch.cuda.synchronize()
@@ -209,3 +214,5 @@ def test_side_stream_matches_current_stream():
     assert torch.equal(out, ref)
     for k in ref_b:
         assert torch.equal(res[k], ref_b[k]), k
+    for k in ref_s:
+        assert torch.equal(res_s[k], ref_s[k]), k
