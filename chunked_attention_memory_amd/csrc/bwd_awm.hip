@@ -382,6 +382,33 @@ struct SideArgs {
   uint32_t nblocks, per_xcd;
 };
 
+// Per-token gradients leave the side kernels through a wave-private LDS
+// block: their MFMA accumulators hold one token per lane, so storing them
+// directly writes 16 bytes into each of 64 different rows per instruction.
+// block_store takes a 32-token x 32-column float32 block in accumulator
+// order (lane (lq, g): token lq, column 16 (r >> 3) + 8 g + (r & 7) for
+// element r), and stores it so that each instruction writes eight whole
+// 128-byte row pieces. Rows are padded to kTS floats (conflict-free writes).
+// LDS accesses of one wave are processed in order, so neither the read after
+// the write nor the next block's write after this block's read needs a wait
+// of its own.
+constexpr int kTS = 36;
+__device__ __forceinline__ void block_store(float* buf, const float (&x)[16], int lane, float* dst, int64_t ld,
+                                            int nvalid) {
+  const int lq = lane & 31, g = lane >> 5;
+  float* wp = buf + lq * kTS + 8 * g;
+  *reinterpret_cast<f32x4*>(wp) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(wp + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  *reinterpret_cast<f32x4*>(wp + 16) = f32x4{x[8], x[9], x[10], x[11]};
+  *reinterpret_cast<f32x4*>(wp + 20) = f32x4{x[12], x[13], x[14], x[15]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (lane >> 3) + 8 * i, c4 = 4 * (lane & 7);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(buf + tr * kTS + c4);
+    if (tr < nvalid) *reinterpret_cast<f32x4*>(dst + tr * ld + c4) = y;
+  }
+}
+
 // Workgroups go to the 8 XCDs round-robin, each with its own L2; logical
 // block (b mod 8) per_xcd + b / 8 keeps the blocks of one chunk (which all
 // stage that chunk's state-sized operands) on one XCD.
@@ -429,6 +456,7 @@ __global__ __launch_bounds__(512, 1) void bwd_qside_kernel(SideArgs a) {
   constexpr int MB = D * DV * 2;
   __shared__ __attribute__((aligned(16))) char Ms[MB];
   __shared__ float CS[512];
+  __shared__ __attribute__((aligned(16))) float TB[8][32 * kTS];
   const uint32_t lb = side_block(a);
   if (lb >= a.nblocks) return;
   const int blk = (int)(lb % (unsigned)a.blocks_per_chunk);
@@ -510,22 +538,18 @@ __global__ __launch_bounds__(512, 1) void bwd_qside_kernel(SideArgs a) {
     for (int r = 0; r < 16; ++r) rs += acc[fb][r] * psi[16 * fb + r];
   rs = other_half_sum(rs);
   (void)KS;
-  if (valid) {
-    float* o = a.dqm + trow * D;
+  {
+    // rows t0 + 32 w + [0, 32) of dQ_m, those before cend
+    const int64_t w0 = t0 + 32 * w;
+    const int nvalid = (int)min((int64_t)32, cend - w0);
+    float* o = a.dqm + (bh * n + w0) * D;
 #pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
+    for (int fb = 0; fb < NF; ++fb) {
+      float y[16];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int f = 32 * fb + 16 * hh + 8 * g;
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const int r = 8 * hh + 4 * qq;
-          f32x4 y;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = psi[16 * fb + r + i] * (acc[fb][r + i] - rs);
-          *reinterpret_cast<f32x4*>(o + f + 4 * qq) = y;
-        }
-      }
+      for (int r = 0; r < 16; ++r) y[r] = psi[16 * fb + r] * (acc[fb][r] - rs);
+      block_store(TB[w], y, lane, o + 32 * fb, D, nvalid);
+    }
   }
 }
 
@@ -540,6 +564,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kside_kernel(SideArgs a) {
   __shared__ __attribute__((aligned(16))) char DSs[DSB];
   __shared__ __attribute__((aligned(16))) char Xs[kNoDelta ? 16 : XB];
   __shared__ __attribute__((aligned(16))) float FV[2 * D];  // log2 z_t, zeta_t
+  __shared__ __attribute__((aligned(16))) float TB[8][32 * kTS];
   const uint32_t lb = side_block(a);
   if (lb >= a.nblocks) return;
   const int blk = (int)(lb % (unsigned)a.blocks_per_chunk);
@@ -598,23 +623,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kside_kernel(SideArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) psf[ks] = pack8(km + 8 * ks);
   }
+  // rows t0 + 32 w + [0, 32) of dV and dK_m, those before cend
+  const int64_t w0 = t0 + 32 * w;
+  const int nvalid = (int)min((int64_t)32, cend - w0);
   // dV^T = dS_t^T Phi^T, block by block
   {
-    float* ov = a.dv + trow * DV;
+    float* ov = a.dv + (bh * n + w0) * DV;
 #pragma unroll
     for (int mv = 0; mv < NMV; ++mv) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(lds_tr<DV>(DSs, 16 * ks, 32 * mv, lane), phf[ks], acc);
-      if (valid) {
+      float x[16];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int col = 32 * mv + 16 * hh + 8 * g;
-          *reinterpret_cast<f32x4*>(ov + col) = f32x4{acc[8 * hh], acc[8 * hh + 1], acc[8 * hh + 2], acc[8 * hh + 3]};
-          *reinterpret_cast<f32x4*>(ov + col + 4) =
-              f32x4{acc[8 * hh + 4], acc[8 * hh + 5], acc[8 * hh + 6], acc[8 * hh + 7]};
-        }
-      }
+      for (int r = 0; r < 16; ++r) x[r] = acc[r];
+      block_store(TB[w], x, lane, ov + 32 * mv, DV, nvalid);
     }
   }
   // dPhi^T = dS_t V^T - X_t Psi^T,  dPsi^T = -X_t^T Phi^T
@@ -659,24 +682,25 @@ __global__ __launch_bounds__(512, 1) void bwd_kside_kernel(SideArgs a) {
       }
     rs = other_half_sum(rs);
   }
-  if (valid) {
-    float* o = a.dkm + trow * D;
+  {
+    float* o = a.dkm + (bh * n + w0) * D;
 #pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
+    for (int fb = 0; fb < NF; ++fb) {
+      float y[16];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int f = 32 * fb + 16 * hh + 8 * g;
-        float ph[8], ps[8], y[8];
+        float ph[8], ps[8];
         unpack8(phf[2 * fb + hh], ph);
         if constexpr (!kNoDelta) unpack8(psf[2 * fb + hh], ps);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          y[i] = ph[i] * (dph[fb][8 * hh + i] + FV[D + f + i]);
-          if constexpr (!kNoDelta) y[i] += ps[i] * (dps[fb][8 * hh + i] - rs);
+          y[8 * hh + i] = ph[i] * (dph[fb][8 * hh + i] + FV[D + f + i]);
+          if constexpr (!kNoDelta) y[8 * hh + i] += ps[i] * (dps[fb][8 * hh + i] - rs);
         }
-        *reinterpret_cast<f32x4*>(o + f) = f32x4{y[0], y[1], y[2], y[3]};
-        *reinterpret_cast<f32x4*>(o + f + 4) = f32x4{y[4], y[5], y[6], y[7]};
       }
+      block_store(TB[w], y, lane, o + 32 * fb, D, nvalid);
+    }
   }
 }
 

@@ -563,6 +563,64 @@ __device__ __forceinline__ int v_operand_base(int lane, int mv) {
   return (4 * g + (sl >> 2)) * (DV * 2) + 16 * ((col >> 3) ^ vswz<DV>(sl >> 2)) + 2 * (col & 7);
 }
 
+// Output rows through LDS. A lane holds one query's row of O, so a store
+// straight from the accumulators writes 16 or 32 bytes into each of 32 rows
+// per instruction. With the stage memory free, each wave instead passes its
+// 32 rows, CPR columns at a time, through its own part of that memory and
+// stores whole row pieces of CPR elements. Accumulator register r of block
+// mv holds column 32 mv + 16 (r >> 3) + 8 g + (r & 7) (two runs of 8 per
+// lane). CPR is the most columns (a power of two, at most DV) for which the
+// waves' rows fit the stage memory, with 16 bytes of padding per row.
+template <int D, int DV, int QB, int EB>
+struct OutStage {
+  using T = ScaTile<D, DV, QB>;
+  static constexpr bool fits(int cpr) { return (size_t)T::NW * 32 * (EB * cpr + 16) <= T::STAGE_BYTES; }
+  // (shapes whose stage memory is too small store straight from the accumulators)
+  static constexpr bool kUse = fits(32);
+  static constexpr int CPR = fits(DV) ? DV : fits(DV / 2) ? DV / 2 : fits(DV / 4) ? DV / 4 : 32;
+  static constexpr int RW = EB * CPR + 16;  // row pitch in LDS
+  static constexpr int PPR = EB * CPR / 16, RPI = 64 / PPR;  // 16-byte pieces per row, rows per instruction
+  static_assert(!kUse || (CPR >= 32 && fits(CPR) && RPI >= 1 && 32 % RPI == 0), "output staging shape");
+  static constexpr size_t wave_bytes() { return (size_t)32 * RW; }
+
+  // rows [row0, row0 + nvalid) of orow's matrix (row pitch DV elements,
+  // bf16 for EB = 2, float32 for EB = 4), scaled by `scale`; buf is the
+  // wave's part. A wave's LDS accesses are processed in order: the reads see
+  // the writes before them, and the next piece's writes follow the reads.
+  template <typename E>
+  __device__ __forceinline__ static void store(char* buf, const f32x16 (&o)[DV / 32], float scale, E* orow,
+                                               int nvalid, int lane) {
+    static_assert(sizeof(E) == EB, "element size");
+    const int lq = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int m0 = 0; m0 < DV / 32; m0 += CPR / 32) {
+#pragma unroll
+      for (int mv = m0; mv < m0 + CPR / 32; ++mv)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          char* dst = buf + lq * RW + EB * (32 * (mv - m0) + 16 * hh + 8 * g);
+          const f32x16& x = o[mv];
+          if constexpr (EB == 2) {
+            *reinterpret_cast<u32x4*>(dst) =
+                u32x4{pack2(x[8 * hh + 0] * scale, x[8 * hh + 1] * scale), pack2(x[8 * hh + 2] * scale, x[8 * hh + 3] * scale),
+                      pack2(x[8 * hh + 4] * scale, x[8 * hh + 5] * scale), pack2(x[8 * hh + 6] * scale, x[8 * hh + 7] * scale)};
+          } else {
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{x[8 * hh + 0] * scale, x[8 * hh + 1] * scale, x[8 * hh + 2] * scale, x[8 * hh + 3] * scale};
+            *reinterpret_cast<f32x4*>(dst + 16) =
+                f32x4{x[8 * hh + 4] * scale, x[8 * hh + 5] * scale, x[8 * hh + 6] * scale, x[8 * hh + 7] * scale};
+          }
+        }
+#pragma unroll
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int r = lane / PPR + RPI * k, cb = 16 * (lane % PPR);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * RW + cb);
+        if (r < nvalid) st16(reinterpret_cast<char*>(orow + (size_t)r * DV + 32 * m0) + cb, v);
+      }
+    }
+  }
+};
+
 template <int D, int DV, bool kSca, bool kRead, bool kOutF32>
 __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) void sca_bf16_kernel(ScaArgs a) {
   constexpr int QB = ScaShape<D, DV>::QB;
@@ -651,23 +709,40 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int myq = myq0 + 32 * qb;
-      if (myq >= qend) continue;
-      if (a.stats && g == 0)
+      if (myq < qend && a.stats && g == 0)
         *reinterpret_cast<float2*>(a.stats + 2 * ((size_t)bh * n + myq)) = make_float2(msub[qb], lsum[qb]);
-      if (a.o_sca) {
-        const float inv = 1.f / lsum[qb];
-        float* orow = a.o_sca + ((size_t)bh * n + myq) * DV;
+    }
+    if (a.o_sca) {
+      using OS = OutStage<D, DV, QB, 4>;
+      if constexpr (OS::kUse) {  // the stage memory is free: every wave is past the loop's last barrier
+        char* buf = SM + w * OS::wave_bytes();
 #pragma unroll
-        for (int mv = 0; mv < NMV; ++mv)
+        for (int qb = 0; qb < QB; ++qb) {
+          const int row0 = q0 + 32 * QB * w + 32 * qb;
+          const int nvalid = min(32, qend - row0);
+          if (nvalid > 0)
+            OS::store(buf, oacc[qb], 1.f / lsum[qb], a.o_sca + ((size_t)bh * n + row0) * DV, nvalid, lane);
+        }
+        __syncthreads();  // the readout's state may go into the stage memory now
+      } else {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const f32x16& o = oacc[qb][mv];
-            float* dst = orow + 32 * mv + 16 * hh + 8 * g;
-            *reinterpret_cast<f32x4*>(dst) =
-                f32x4{o[8 * hh + 0] * inv, o[8 * hh + 1] * inv, o[8 * hh + 2] * inv, o[8 * hh + 3] * inv};
-            *reinterpret_cast<f32x4*>(dst + 4) =
-                f32x4{o[8 * hh + 4] * inv, o[8 * hh + 5] * inv, o[8 * hh + 6] * inv, o[8 * hh + 7] * inv};
-          }
+        for (int qb = 0; qb < QB; ++qb) {
+          const int myq = myq0 + 32 * qb;
+          if (myq >= qend) continue;
+          const float inv = 1.f / lsum[qb];
+          float* orow = a.o_sca + ((size_t)bh * n + myq) * DV;
+#pragma unroll
+          for (int mv = 0; mv < NMV; ++mv)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const f32x16& o = oacc[qb][mv];
+              float* dst = orow + 32 * mv + 16 * hh + 8 * g;
+              *reinterpret_cast<f32x4*>(dst) =
+                  f32x4{o[8 * hh + 0] * inv, o[8 * hh + 1] * inv, o[8 * hh + 2] * inv, o[8 * hh + 3] * inv};
+              *reinterpret_cast<f32x4*>(dst + 4) =
+                  f32x4{o[8 * hh + 4] * inv, o[8 * hh + 5] * inv, o[8 * hh + 6] * inv, o[8 * hh + 7] * inv};
+            }
+        }
       }
     }
     if (a.lse) {
@@ -783,7 +858,24 @@ __global__ __launch_bounds__((ScaTile<D, DV, ScaShape<D, DV>::QB>::THREADS), 1) 
   }
 
   // accumulator register r of block mv holds value column
-  // 32 mv + 16 (r >> 3) + 8 g + (r & 7): two runs of 8 per lane
+  // 32 mv + 16 (r >> 3) + 8 g + (r & 7): two runs of 8 per lane. A lane
+  // holds one query, so a bf16 store straight from the accumulators writes
+  // 32 bytes into each of 32 rows per instruction; with the stage memory
+  // free, each wave instead passes its 32 x CPR-column pieces of O through
+  // its own part of it and stores whole 2 CPR-byte row pieces.
+  if constexpr (kSca && !kOutF32 && OutStage<D, DV, QB, 2>::kUse) {
+    using OS = OutStage<D, DV, QB, 2>;
+    __syncthreads();  // every wave is past its reads of the stage memory
+    char* buf = SM + w * OS::wave_bytes();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row0 = q0 + 32 * QB * w + 32 * qb;
+      const int nvalid = min(32, qend - row0);
+      if (nvalid > 0)
+        OS::store(buf, oacc[qb], 1.f, static_cast<uint16_t*>(a.out) + ((size_t)bh * n + row0) * DV, nvalid, lane);
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int myq = myq0 + 32 * qb;
