@@ -604,7 +604,7 @@ struct ScanStep {
 // feature). M'^T H_t^T is one MFMA chain: A = M'^T read (transposed) from a
 // bf16 copy of the slice in LDS ([f][v]), B = rows of H_t from HBM. The copy
 // is also the snapshot that chunk t + 2 reads. Step operands are prefetched
-// kDepth steps ahead; block b handles slice b / BH of batch*head b % BH, so
+// kDepth - 1 steps ahead; block b handles slice b / BH of batch*head b % BH, so
 // with BH a multiple of 8 all slices of a head run on one XCD.
 template <int D, int DV, bool kNoDelta>
 __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
@@ -629,16 +629,22 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
   const int trb = (4 * g + (sl >> 2)) * 64 + (16 * grp2 + 4 * (sl & 3)) * 2;
 
   ScanStep<D> ring[kDepth];
-  auto load_step = [&](int64_t t, ScanStep<D>& q) {
+  // operands of step t in three parts: H_t k-steps [0, KS / 2), [KS / 2, KS);
+  // then G_t^T and the chunk's max and sum
+  auto load_part = [&](int64_t t, ScanStep<D>& q, int part) {
     const int64_t row = bh * nmem + t;
-    const uint16_t* ht = a.hm + row * (int64_t)D * D + ((int64_t)w * 64 + lane) * 8;
+    if (part < 2) {
+      const uint16_t* ht = a.hm + row * (int64_t)D * D + ((int64_t)w * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(ht + (int64_t)ks * NW * 64 * 8);
-    const f32x4* gt = reinterpret_cast<const f32x4*>(a.g + ((((row * NMV + j) * NW + w) * 64) + lane) * 16);
+      for (int ks = 0; ks < KS; ++ks)
+        if (ks / (KS / 2) == part) q.hf[ks] = ld16(ht + (int64_t)ks * NW * 64 * 8);
+    } else {
+      const f32x4* gt = reinterpret_cast<const f32x4*>(a.g + ((((row * NMV + j) * NW + w) * 64) + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q.gv[i] = gt[i];
-    q.cm = a.cmax[row * D + f];
-    q.cs = a.csum[row * D + f];
+      for (int i = 0; i < 4; ++i) q.gv[i] = gt[i];
+      q.cm = a.cmax[row * D + f];
+      q.cs = a.csum[row * D + f];
+    }
   };
 
   f32x16 mst = f32x16{};
@@ -656,7 +662,14 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
       st16(sn + (int64_t)r * DV + cc, ld16(&src[r * 32 + cc]));
     }
   };
-  auto step = [&](int64_t t, const ScanStep<D>& q) {
+  const int64_t last = nmem - 1;
+  // nxt: the ring slot that the operands of step t + kDepth - 1 go into. A
+  // wave waits while its loads are issued (about 900 cycles for a step's
+  // 48 KiB through the CU's load path), so they are issued in three parts
+  // at the step's own waits: after the products are issued, after the state
+  // copy is written and after the snapshot is stored. (All at the end of the
+  // step the scan took 89 us at 128K tokens, in three parts 78 us.)
+  auto step = [&](int64_t t, const ScanStep<D>& q, ScanStep<D>& nxt) {
     // running denominator of feature f
     const float Mn = fmaxf(zM, q.cm);
     const float old = zM == kNegInf ? 0.f : zL * exp2_fast(zM - Mn);
@@ -677,6 +690,8 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
         p1 = mfma_bf16(u32x4{b0[0], b0[1], b1[0], b1[1]}, q.hf[ks + 1], p1);
       }
     }
+    const int64_t tn = min(t + kDepth - 1, last);
+    load_part(tn, nxt, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mst[r] = dc * mst[r] + ws * (q.gv[r >> 2][r & 3] - (p0[r] + p1[r]));
     // bf16 copy: column f, values 8 qq + 4 g + [0, 4)
@@ -685,10 +700,12 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
       const u32x2 pk{pack2(mst[4 * qq], mst[4 * qq + 1]), pack2(mst[4 * qq + 2], mst[4 * qq + 3])};
       *reinterpret_cast<u32x2*>(&mt[buf ^ 1][f * 32 + 8 * qq + 4 * g]) = pk;
     }
+    load_part(tn, nxt, 1);
     __syncthreads();
     // snapshot rows f of the state after step t, values 32 j .. 32 j + 31:
     // 64 bytes per row
     write_snap(t + hp, mt[buf ^ 1]);
+    load_part(tn, nxt, 2);
     if (a.snap32) {  // float32 copy: row f, values 32 j + 8 qq + 4 g + [0, 4)
       float* s32 = a.snap32 + (bh * a.nsnap + t + hp) * (int64_t)D * DV + (int64_t)f * DV + 32 * j + 4 * g;
 #pragma unroll
@@ -724,21 +741,21 @@ __global__ __launch_bounds__(2 * D, 1) void awm_scan_bf16_kernel(ScanArgs a) {
     __syncthreads();
   }
   // Steady state without branches, so that the compiler can count the loads
-  // in flight exactly; loads past the last step re-read it (unused).
-  const int64_t last = nmem - 1;
+  // in flight exactly; loads past the last step re-read it (unused). Step t
+  // uses slot t mod kDepth and fills slot (t - 1) mod kDepth, which step
+  // t - 1 is done with, with the operands of step t + kDepth - 1.
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k) load_step(min((int64_t)k, last), ring[k]);
+  for (int k = 0; k < kDepth - 1; ++k)
+#pragma unroll
+    for (int part = 0; part < 3; ++part) load_part(min((int64_t)k, last), ring[k], part);
   int64_t t0 = 0;
   for (; t0 + kDepth <= nmem; t0 += kDepth) {
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      step(t0 + k, ring[k]);
-      load_step(min(t0 + k + kDepth, last), ring[k]);
-    }
+    for (int k = 0; k < kDepth; ++k) step(t0 + k, ring[k], ring[(k + kDepth - 1) % kDepth]);
   }
 #pragma unroll
   for (int k = 0; k < kDepth; ++k)
-    if (t0 + k < nmem) step(t0 + k, ring[k]);
+    if (t0 + k < nmem) step(t0 + k, ring[k], ring[(k + kDepth - 1) % kDepth]);
 
   if (a.stream) {  // the state after the last step, for the next call
     f32x4* ms = reinterpret_cast<f32x4*>(a.mstate + scell);
