@@ -212,7 +212,7 @@ struct RStep {
 // and B = H_{t+1} in transposed order.
 template <int D, int DV, bool kNoDelta>
 __global__ __launch_bounds__(2 * D, 1) void bwd_rscan_kernel(RScanArgs a) {
-  constexpr int NMV = DV / 32, NW = D / 32, KS = D / 16, kDepth = 2;
+  constexpr int NMV = DV / 32, NW = D / 32, KS = D / 16, kDepth = 3;
   __shared__ __attribute__((aligned(16))) uint16_t mt[2][D * 32];
   const int64_t BH = gridDim.x / NMV;
   const int64_t bh = blockIdx.x % BH;
@@ -223,25 +223,34 @@ __global__ __launch_bounds__(2 * D, 1) void bwd_rscan_kernel(RScanArgs a) {
   const int sl = lane & 15, grp2 = (lane >> 4) & 1;
   const int trb = (4 * g + (sl >> 2)) * 64 + (16 * grp2 + 4 * (sl & 3)) * 2;
 
-  auto load = [&](int64_t t, RStep<D>& q) {
+  // operands of step t in three parts: H_{t+1}; R_t and S_t; the decay and
+  // scale. A wave waits while its loads are issued (64 KiB a step through
+  // the CU's load path), so each step issues them at its own waits (see step)
+  auto load = [&](int64_t t, RStep<D>& q, int part) {
     const int64_t row = bh * nmem + t;
-    const f32x4* rt = reinterpret_cast<const f32x4*>(a.r + ((((row * NMV + j) * NW + w) * 64) + lane) * 16);
+    if (part == 0) {
+      const int64_t t1 = t + 1 < nmem ? t + 1 : t;  // (unused at the last step)
+      const uint16_t* hp = a.ht + (bh * nmem + t1) * (int64_t)D * D + ((int64_t)w * 64 + lane) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q.rv[i] = rt[i];
-    const int64_t t1 = t + 1 < nmem ? t + 1 : t;  // (unused at the last step)
-    const uint16_t* hp = a.ht + (bh * nmem + t1) * (int64_t)D * D + ((int64_t)w * 64 + lane) * 8;
+      for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(hp + (int64_t)ks * NW * 64 * 8);
+    } else if (part == 1) {
+      const f32x4* rt = reinterpret_cast<const f32x4*>(a.r + ((((row * NMV + j) * NW + w) * 64) + lane) * 16);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q.hf[ks] = ld16(hp + (int64_t)ks * NW * 64 * 8);
-    const float* sp = a.s32 + row * (int64_t)D * DV + (int64_t)f * DV + 32 * j + 4 * g;
+      for (int i = 0; i < 4; ++i) q.rv[i] = rt[i];
+      const float* sp = a.s32 + row * (int64_t)D * DV + (int64_t)f * DV + 32 * j + 4 * g;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) q.sv[qq] = *reinterpret_cast<const f32x4*>(sp + 8 * qq);
-    q.dn = t + 1 < nmem ? a.decay[(bh * nmem + t + 1) * D + f] : 0.f;
-    q.ws = a.wscale[row * D + f];
+      for (int qq = 0; qq < 4; ++qq) q.sv[qq] = *reinterpret_cast<const f32x4*>(sp + 8 * qq);
+    } else {
+      q.dn = t + 1 < nmem ? a.decay[(bh * nmem + t + 1) * D + f] : 0.f;
+      q.ws = a.wscale[row * D + f];
+    }
   };
 
   f32x16 cur = f32x16{};  // dS_{t+1}^T
   int buf = 0;
-  auto step = [&](int64_t t, const RStep<D>& q) {
+  // step t (in decreasing t) fills nxt, the slot the step before it in the
+  // loop used, with the operands of step tn
+  auto step = [&](int64_t t, const RStep<D>& q, RStep<D>& nxt, int64_t tn) {
     f32x16 p0 = f32x16{}, p1 = f32x16{};
     if constexpr (!kNoDelta) {
       if (t + 1 < nmem) {  // mt[buf] holds wscale_{t+1} dS_{t+1}
@@ -255,6 +264,7 @@ __global__ __launch_bounds__(2 * D, 1) void bwd_rscan_kernel(RScanArgs a) {
         }
       }
     }
+    load(tn, nxt, 0);
     // rowsums of R_t * S_t and C_t * S_t over this lane's cells (zeta)
     float s_r = 0.f, s_c = 0.f;
 #pragma unroll
@@ -264,6 +274,7 @@ __global__ __launch_bounds__(2 * D, 1) void bwd_rscan_kernel(RScanArgs a) {
       s_c += cv * sv;
       cur[r] = rv + q.dn * cur[r] - cv;
     }
+    load(tn, nxt, 1);
     s_r = other_half_sum(s_r);
     s_c = other_half_sum(s_c);
     if (g == 0)
@@ -280,23 +291,30 @@ __global__ __launch_bounds__(2 * D, 1) void bwd_rscan_kernel(RScanArgs a) {
       *reinterpret_cast<u32x2*>(&mt[buf ^ 1][f * 32 + 8 * qq + 4 * g]) =
           u32x2{pack2(q.ws * cur[4 * qq], q.ws * cur[4 * qq + 1]), pack2(q.ws * cur[4 * qq + 2], q.ws * cur[4 * qq + 3])};
     __syncthreads();
+    load(tn, nxt, 2);
     buf ^= 1;
   };
 
+  // loop step i (t = nmem - 1 - i) uses slot i mod kDepth and fills slot
+  // (i - 1) mod kDepth, done with, for step i + kDepth - 1; loads past the
+  // last step re-read it (unused)
   RStep<D> ring[kDepth];
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k) load(max(nmem - 1 - k, (int64_t)0), ring[k]);
+  for (int k = 0; k < kDepth - 1; ++k)
+#pragma unroll
+    for (int part = 0; part < 3; ++part) load(max(nmem - 1 - k, (int64_t)0), ring[k], part);
   int64_t k0 = 0;
   for (; k0 + kDepth <= nmem; k0 += kDepth) {
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      step(nmem - 1 - (k0 + k), ring[k]);
-      load(max(nmem - 1 - (k0 + k + kDepth), (int64_t)0), ring[k]);
-    }
+    for (int k = 0; k < kDepth; ++k)
+      step(nmem - 1 - (k0 + k), ring[k], ring[(k + kDepth - 1) % kDepth],
+           max(nmem - 1 - (k0 + k + kDepth - 1), (int64_t)0));
   }
 #pragma unroll
   for (int k = 0; k < kDepth; ++k)
-    if (k0 + k < nmem) step(nmem - 1 - (k0 + k), ring[k]);
+    if (k0 + k < nmem)
+      step(nmem - 1 - (k0 + k), ring[k], ring[(k + kDepth - 1) % kDepth],
+           max(nmem - 1 - (k0 + k + kDepth - 1), (int64_t)0));
 }
 
 // ---------------------------------------------------------------- zscan
