@@ -56,28 +56,40 @@ __global__ __launch_bounds__(128) void bwd_combine_kernel(CombineArgs a) {
   for (int i = 0; i < 8; ++i) out[(int64_t)i * D] = sums[i];
 }
 
-// daff[i][h][f] = sum over b and runs of apart[b h][run][i][f]
-__global__ __launch_bounds__(128) void bwd_affine_reduce_kernel(const float* __restrict__ apart,
-                                                               float* __restrict__ daff, int64_t B, int H,
-                                                               int nblk, int D) {
-  const int f = threadIdx.x;
-  if (f >= D) return;
+// daff[i][h][f] = sum over b and runs of apart[b h][run][i][f]: kSplit
+// threads per feature, each summing a contiguous share of the runs with
+// eight partial sums in flight (a single thread per feature waits on one
+// load after another: 512 runs at 128K tokens), then the shares added in
+// LDS. The order of every addition is fixed, so the result does not depend
+// on timing.
+constexpr int kSplit = 8;
+__global__ __launch_bounds__(1024) void bwd_affine_reduce_kernel(const float* __restrict__ apart,
+                                                                float* __restrict__ daff, int64_t B, int H,
+                                                                int nblk, int D) {
+  __shared__ float red[kSplit][128];
+  const int f = threadIdx.x % D, sp = threadIdx.x / D;  // D <= 128, blockDim.x = kSplit * D
   const int i = blockIdx.x % 8;
   const int h = blockIdx.x / 8;
+  const int per = (nblk + kSplit - 1) / kSplit;
+  const int k0 = sp * per, k1 = min(k0 + per, nblk);
   float s = 0.f;
   for (int64_t b = 0; b < B; ++b) {
     const float* p = apart + (((b * H + h) * nblk) * 8 + i) * (int64_t)D + f;
-    // four independent partial sums keep several loads in flight; they are
-    // combined in a fixed order, so the result does not depend on timing
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    int k = 0;
-    for (; k + 4 <= nblk; k += 4)
+    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int k = k0;
+    for (; k + 8 <= k1; k += 8)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s4[u] += p[(int64_t)(k + u) * 8 * D];
-    for (; k < nblk; ++k) s4[0] += p[(int64_t)k * 8 * D];
-    s += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      for (int u = 0; u < 8; ++u) s8[u] += p[(int64_t)(k + u) * 8 * D];
+    for (; k < k1; ++k) s8[0] += p[(int64_t)k * 8 * D];
+    red[sp][f] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    __syncthreads();
+    if (sp == 0) {
+#pragma unroll
+      for (int q = 0; q < kSplit; ++q) s += red[q][f];
+    }
+    __syncthreads();
   }
-  daff[((int64_t)i * H + h) * D + f] = s;
+  if (sp == 0) daff[((int64_t)i * H + h) * D + f] = s;
 }
 
 }  // namespace
@@ -102,8 +114,9 @@ hipError_t launch_bwd_combine(const BwdProblem& p, const BwdWorkspace& w, hipStr
   hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)(BH * w.nblk)), dim3(128), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_affine_reduce_kernel, dim3((unsigned)(8 * p.f.H)), dim3(128), 0, s, w.apart, p.daff, p.f.B,
-                     (int)p.f.H, (int)w.nblk, (int)p.f.d);
+  if (p.f.d > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_affine_reduce_kernel, dim3((unsigned)(8 * p.f.H)), dim3((unsigned)(kSplit * p.f.d)), 0, s,
+                     w.apart, p.daff, p.f.B, (int)p.f.H, (int)w.nblk, (int)p.f.d);
   return hipGetLastError();
 }
 
