@@ -98,10 +98,12 @@ struct CemaQuad {
 
   // four tokens x[0..3]; reset bits r (bit u: M = 0 at token u). A reset at
   // u drops the state and every input before u, so only the last one counts.
+  // kReset = false: r is known to be 0 (no state scaling).
+  template <bool kReset>
   __device__ __forceinline__ void step4(const float* xin, uint32_t r, float (&hr)[H], float (&hi)[H]) const {
     float x[4] = {xin[0], xin[1], xin[2], xin[3]};
     float keep = 1.f;
-    if (r) {
+    if (kReset && r) {
       const int u = 31 - __builtin_clz(r);  // the last reset of the four
       keep = 0.f;
 #pragma unroll
@@ -109,7 +111,7 @@ struct CemaQuad {
     }
 #pragma unroll
     for (int j = 0; j < H; ++j) {
-      const float pr = keep * hr[j], pi = keep * hi[j];
+      const float pr = kReset ? keep * hr[j] : hr[j], pi = kReset ? keep * hi[j] : hi[j];
       float nr = fmaf(q4r[j], pr, fmaf(-q4i[j], pi, w[j] * x[3]));
       float ni = fmaf(q4r[j], pi, q4i[j] * pr);
       nr = fmaf(c3r[j], x[0], fmaf(c2r[j], x[1], fmaf(c1r[j], x[2], nr)));
@@ -158,6 +160,8 @@ struct CemaPair {
     }
   }
 
+  // kReset = false: r0 and r1 are known to be false (no state scaling)
+  template <bool kReset>
   __device__ __forceinline__ void step2(float x0, float x1, bool r0, bool r1, float (&hr)[H], float (&hi)[H],
                                         float& y0, float& y1) const {
     const float keep = r0 ? 0.f : 1.f, keep1 = r1 ? 0.f : keep, xa = r1 ? 0.f : x0;
@@ -166,7 +170,7 @@ struct CemaPair {
     for (int j = 0; j < H; ++j) {
       s0 = fmaf(aqr[j], hr[j], fmaf(-aqi[j], hi[j], s0));
       s1 = fmaf(bqr[j], hr[j], fmaf(-bqi[j], hi[j], s1));
-      const float pr = keep1 * hr[j], pi = keep1 * hi[j];
+      const float pr = kReset ? keep1 * hr[j] : hr[j], pi = kReset ? keep1 * hi[j] : hi[j];
       const float nr = fmaf(q2r[j], pr, fmaf(-q2i[j], pi, fmaf(cwr[j], xa, w[j] * x1)));
       const float ni = fmaf(q2r[j], pi, fmaf(q2i[j], pr, cwi[j] * xa));
       hr[j] = nr;
@@ -192,8 +196,36 @@ struct CemaPair {
   }
 };
 
+// The kU tokens of one loop step (reset bytes rb, byte u for token u),
+// written to y at element i0 + u D in phase C. kReset = false: no reset
+// among them, so the steps skip the state scaling that a reset needs.
+template <bool kReset, bool kOutBf16, bool kOut, int HP, int HQ>
+__device__ __forceinline__ void steps(const CemaPair<HP>& P, const CemaQuad<HQ>& Q, const float (&xv)[kU], uint64_t rb,
+                                      bool live, int64_t i0, int64_t D, float (&hr)[kOut ? HP : HQ],
+                                      float (&hi)[kOut ? HP : HQ], void* y) {
+  if constexpr (kOut) {
+#pragma unroll
+    for (int u = 0; u < kU; u += 2) {
+      float y0, y1;
+      P.template step2<kReset>(xv[u], xv[u + 1], (rb >> (8 * u)) & 1u, (rb >> (8 * u + 8)) & 1u, hr, hi, y0, y1);
+      if (live) {
+        store_y<kOutBf16>(y, i0 + u * D, y0);
+        store_y<kOutBf16>(y, i0 + (u + 1) * D, y1);
+      }
+    }
+  } else {  // four tokens at a time; reset byte u of rb becomes bit u
+#pragma unroll
+    for (int u = 0; u < kU; u += 4) {
+      const uint32_t r4 = (uint32_t)((rb >> (8 * u)) & 0x01010101u);
+      const uint32_t bits = (r4 & 1u) | ((r4 >> 7) & 2u) | ((r4 >> 14) & 4u) | ((r4 >> 21) & 8u);
+      Q.template step4<kReset>(xv + u, bits, hr, hi);
+    }
+  }
+}
+
 // Phases A and C: one wave per (b, 64 dimensions, chunk). kOut: phase C.
-template <int H, bool kInBf16, bool kOutBf16, bool kOut>
+// kReset: a reset array is given (without one, no step scales the state).
+template <int H, bool kInBf16, bool kOutBf16, bool kOut, bool kReset>
 __global__ __launch_bounds__(64) void cema_chunk_kernel(CemaArgs a) {
   const int blk = blockIdx.x;
   const int c = blk % a.C;
@@ -246,32 +278,15 @@ __global__ __launch_bounds__(64) void cema_chunk_kernel(CemaArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) xv[u] = load_x<kInBf16>(a.x, base + (t + u) * D);
     uint64_t rb = 0;  // reset bytes of the kU tokens (wave-uniform)
-    if (rs) {
+    if constexpr (kReset) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) rb |= (uint64_t)(rs[t + u] != 0) << (8 * u);
     }
     any_reset |= rb != 0;
-    if constexpr (kOut) {
-#pragma unroll
-      for (int u = 0; u < kU; u += 2) {
-        float y0, y1;
-        P.step2(xv[u], xv[u + 1], (rb >> (8 * u)) & 1u, (rb >> (8 * u + 8)) & 1u, hr, hi, y0, y1);
-        if (live) {
-          store_y<kOutBf16>(a.y, base + (t + u) * D, y0);
-          store_y<kOutBf16>(a.y, base + (t + u + 1) * D, y1);
-        }
-      }
-    } else {  // four tokens at a time; reset byte u of rb becomes bit u
-#pragma unroll
-      for (int u = 0; u < kU; u += 4) {
-        const uint32_t r4 = (uint32_t)((rb >> (8 * u)) & 0x01010101u);
-        const uint32_t bits = (r4 & 1u) | ((r4 >> 7) & 2u) | ((r4 >> 14) & 4u) | ((r4 >> 21) & 8u);
-        Q.step4(xv + u, bits, hr, hi);
-      }
-    }
+    steps<kReset, kOutBf16, kOut>(P, Q, xv, rb, live, base + t * D, D, hr, hi, a.y);
   }
   for (; t < t1; ++t) {  // ragged end of the sequence
-    const bool r = rs && rs[t] != 0;
+    const bool r = kReset && rs[t] != 0;
     any_reset |= r;
     const float xt = load_x<kInBf16>(a.x, base + t * D);
     if constexpr (kOut) {  // phase A covers full chunks only (L is a multiple of kU)
@@ -338,11 +353,11 @@ __global__ void cema_carry_kernel(CemaArgs a, int H) {
   }
 }
 
-template <int H, bool kIn, bool kOut>
-hipError_t launch_h(const CemaArgs& a, int64_t B, hipStream_t s) {
+template <int H, bool kIn, bool kOut, bool kReset>
+hipError_t launch_hr(const CemaArgs& a, int64_t B, hipStream_t s) {
   const unsigned blocks = (unsigned)(B * a.nwd * a.C);
   if (a.C > 1) {
-    hipLaunchKernelGGL((cema_chunk_kernel<H, kIn, kOut, false>), dim3(blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((cema_chunk_kernel<H, kIn, kOut, false, kReset>), dim3(blocks), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)a.D * H;
@@ -351,8 +366,13 @@ hipError_t launch_h(const CemaArgs& a, int64_t B, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((cema_chunk_kernel<H, kIn, kOut, true>), dim3(blocks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((cema_chunk_kernel<H, kIn, kOut, true, kReset>), dim3(blocks), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+template <int H, bool kIn, bool kOut>
+hipError_t launch_h(const CemaArgs& a, int64_t B, hipStream_t s) {
+  return a.reset ? launch_hr<H, kIn, kOut, true>(a, B, s) : launch_hr<H, kIn, kOut, false>(a, B, s);
 }
 
 template <bool kIn, bool kOut>
