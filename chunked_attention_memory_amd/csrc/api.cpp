@@ -940,14 +940,22 @@ gecko_status gecko_backward_saved(const void* z, const float* kappa_q, const flo
   }
 }
 
+#ifndef GECKO_TIMER_EVENT_FLAGS
+#define GECKO_TIMER_EVENT_FLAGS hipEventDisableSystemFence
+#endif
+
 gecko_status gecko_timer_create(int capacity, gecko_timer** timer) {
   if (!timer || capacity < 1 || capacity > (1 << 20)) return fail(GECKO_EINVAL, "bad timer arguments");
   gecko_timer* t = new (std::nothrow) gecko_timer;
   if (!t) return fail(GECKO_EINVAL, "out of host memory");
   t->capacity = capacity;
   t->ev.resize((size_t)capacity * 5);
+  // The events only time the stages: without the system-scope fence an event
+  // record writes back and invalidates no cache, so the kernel after it
+  // starts with the L2 the one before it left (what an untimed call sees).
+  // The elapsed times are read after the last event of a call has completed.
   for (size_t i = 0; i < t->ev.size(); ++i) {
-    hipError_t e = hipEventCreate(&t->ev[i]);
+    hipError_t e = hipEventCreateWithFlags(&t->ev[i], GECKO_TIMER_EVENT_FLAGS);
     if (e != hipSuccess) {
       for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
       delete t;

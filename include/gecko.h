@@ -255,7 +255,9 @@ gecko_status gecko_tdn_forward(
  * capacity are not recorded). gecko_timer_read waits for the recorded events
  * and writes, per stage, the summed milliseconds over the recorded calls:
  * ms[0] memory chunk pass, ms[1] denominator prefix, ms[2] memory scan,
- * ms[3] attention + readout kernel; *calls receives the number of calls. */
+ * ms[3] attention + readout kernel; *calls receives the number of calls.
+ * The events are created with hipEventDisableSystemFence: they carry timing
+ * only, and recording one flushes no cache between the kernels. */
 typedef struct gecko_timer gecko_timer;
 gecko_status gecko_timer_create(int capacity, gecko_timer** timer);
 gecko_status gecko_timer_reset(gecko_timer* timer);
