@@ -7,7 +7,8 @@ rms(x) <= 1e-4 on float32 output, the same for the final state. The bf16
 output is the round-to-nearest-even of the float32 one. Cases: every
 supported h, a dimension count that is not a multiple of a wave, one token,
 resets (at the first token, consecutive, across the chunk boundaries of the
-chunked three-phase path), a carried state in and out, and two calls that
+chunked three-phase path), calls without a reset array (the kernels built
+without reset handling), a carried state in and out, and two calls that
 continue one sequence."""
 
 from __future__ import annotations
@@ -126,3 +127,34 @@ def test_cema_two_calls_continue_one_sequence_and_bf16_output():
     u = y.cpu().numpy().view(np.uint32)
     want16 = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     np.testing.assert_array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), want16)
+
+
+@pytest.mark.parametrize("B,n,D,h,dtype,with_h0", [
+    (1, 300, 64, 16, "f32", False),    # one chunk: phase C only
+    (2, 257, 100, 8, "bf16", True),    # D not a multiple of 64
+    (1, 16384, 64, 16, "bf16", True),  # the chunked three-phase path
+    (2, 9000, 128, 4, "f32", False),   # chunked, ragged last chunk
+])
+def test_cema_without_reset_array(B, n, D, h, dtype, with_h0):
+    """No reset array: the kernels built without reset handling (no step
+    scales the state) against the oracle with no resets, and against the
+    kernels that take an all-zero reset array."""
+    import torch
+
+    g = gecko()
+    host = inputs.make_cema_inputs(B, n, D, h, dtype, tag=70 + h, reset_rate=0.0)
+    assert not host["reset"].any()
+    h0 = h0t = None
+    if with_h0:
+        rng = np.random.default_rng(11)
+        h0 = (rng.standard_normal((B, D, h)) + 1j * rng.standard_normal((B, D, h))).astype(np.complex64)
+        h0t = torch.from_numpy(np.stack([h0.real, h0.imag], axis=-1).astype(np.float32)).cuda().contiguous()
+    if n >= 8192:
+        assert g.gecko_cema_workspace_size(B, n, D, h) > 0  # the chunked path
+    y, hf = _run(host, use_reset=False, h0=h0t)
+    yz, hz = _run(host, use_reset=True, h0=h0t)
+    for b in range(B):
+        want, hn = _oracle(host, b, h0=None if h0 is None else h0[b].astype(np.complex128))
+        assert _err(y[b].cpu().numpy().astype(np.float64), want) <= TOL
+        assert _err(_state64(hf[b]), hn) <= TOL
+        assert _err(y[b].cpu().numpy().astype(np.float64), yz[b].cpu().numpy().astype(np.float64)) <= TOL
